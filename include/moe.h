@@ -1,0 +1,228 @@
+/*
+ * moe.h -- C ABI of the MoE expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer: route every token to k of E experts, sort the (token, slot) rows
+ * by expert, run each expert's SwiGLU FFN over its group as one grouped GEMM,
+ * and sum the expert outputs back per token with the gate weights; plus the
+ * backward pass of every step for full fine-tuning.
+ *
+ * Pages cited (by title and section):
+ *   [P3] "Accelerating Transformers fine-tuning with NVIDIA NeMo AutoModel"
+ *        (zh-CN translation on neows.pages.dev);
+ *   [P1] "NVIDIA NeMo AutoModel MoE 微調的 3.7 倍加速突破" (digest).
+ * [P3] section 背景 (background) states the problem: route tokens across
+ * hundreds of experts and fuse the expert matmuls into a single kernel.
+ * [P3] section 专家后端 (expert backends), grouped_mm row: sort tokens by their
+ * assigned expert, then one grouped GEMM.  [P3] section 加速来源, DeepEP item:
+ * token dispatch and combine are their own fused kernels.  Each entry point
+ * below is one of those steps.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer is a DEVICE pointer (memory of the current HIP device) unless
+ *   stated otherwise.  Matrices are row-major and dense (no padding).
+ * - The caller owns every buffer.  The library never allocates, frees or keeps
+ *   device memory; it keeps no state between calls except the optional kernel
+ *   timer (moe_prof_*) and a thread-local error string.
+ * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the
+ *   default stream) and returns without waiting for them.  Data-dependent sizes
+ *   (group sizes, the routed row count R) stay on the device: buffers are sized
+ *   for the capacity R_cap and kernels read the true counts from group_offsets.
+ * - Arguments are validated before anything is launched.  On a non-OK status
+ *   nothing was enqueued and no output was touched; moe_last_error() then
+ *   holds a one-line description.  MOE_ERR_HIP means a launch failed after
+ *   validation (earlier kernels of the same call may have run).
+ * - dtype MOE_F32: every float tensor is fp32.  dtype MOE_BF16: activations,
+ *   weights and their gradients are bf16 (uint16 bit patterns); logits, gate
+ *   weights and their gradients are fp32; every accumulation is fp32 and every
+ *   conversion to bf16 rounds to nearest even.
+ * - Supported shapes: d % 64 == 0, I % 64 == 0, E % 8 == 0 or E <= 8, E <= 512,
+ *   1 <= k <= min(E, 32), T*k < 2^31, and every pointer 16-byte aligned.
+ *   Others return MOE_ERR_UNSUPPORTED.
+ * - Results are deterministic: no floating-point atomics; every sum has a fixed
+ *   order, so two identical calls give bit-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,         /* null pointer where one is required, k > E, bad enum, e_lo/e_hi out of range */
+  MOE_ERR_SHAPE = 2,       /* non-positive or overflowing sizes */
+  MOE_ERR_DTYPE = 3,       /* unknown dtype */
+  MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 5,         /* a HIP launch failed; moe_last_error() has the HIP message */
+  MOE_ERR_UNSUPPORTED = 6  /* valid but outside the supported shapes listed above */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* The gate.  The pages fix neither the gate function nor tie-breaking:
+ * MOE_GATE_SOFTMAX_TOPK takes the k largest logits (ties toward the lower
+ * expert id, slots in descending-logit order) and softmax over those k.
+ * MOE_GATE_BALANCED is the balanced routing gate of [P3] section
+ * 单节点30B MoE基准测试 (note on the routing gate: tokens are forced evenly
+ * over the experts): slot i of token t goes to expert (t mod P) + i*P with
+ * P = E/k, weight 1/k.  It needs k | E. */
+typedef enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_BALANCED = 1 } moe_gate_t;
+
+/* Which call a workspace size is asked for. */
+typedef enum {
+  MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
+  MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7
+} moe_op_t;
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/* Layer shape.  E counts ALL experts; this GPU holds the local experts
+ * [e_lo, e_hi) (expert parallelism shards experts along the expert dimension,
+ * [P3] section 专家并行与DeepEP).  On one GPU holding every expert: 0, E.
+ * R_cap is the row capacity of the permuted buffers (0 means T*k): rows whose
+ * expert-sorted position is >= R_cap are dropped (see moe_permute). */
+typedef struct {
+  int32_t T, d, E, k, I;
+  int32_t e_lo, e_hi;
+  int32_t R_cap;
+  moe_dtype_t dtype;
+  moe_gate_t gate;
+} moe_shape_t;
+
+/* ---------------------------------------------------------------- utility */
+const char* moe_status_string(moe_status_t s);    /* static string, never NULL */
+const char* moe_last_error(void);                 /* thread-local, valid until the next call on this thread */
+const char* moe_version(void);                    /* static string */
+
+/* Host-side query: bytes of workspace `op` needs for `shape` (0 if none).
+ * Errors: MOE_ERR_ARG if shape or bytes is NULL or op unknown; the shape
+ * errors of the op itself. */
+moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, size_t* bytes);
+
+/* ------------------------------------------------------------- forward */
+
+/* a1 -- route.  [P3] section 背景: route tokens across many experts.
+ * softmax_topk: logits = x * w_router (+ bias) with fp32 accumulation, then the
+ *   k largest per token (ties -> lower id), topk_w = softmax over those k.
+ * balanced: topk_idx/topk_w from the balanced gate; x, w_router, bias and
+ *   logits are not read or written (they may be NULL).
+ * x [T,d] (dtype); w_router [d,E] (dtype); bias [E] fp32 or NULL;
+ * logits [T,E] fp32 (required for softmax_topk); topk_idx [T,k] int32 (global
+ * expert ids); topk_w [T,k] fp32.  No workspace. */
+moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_router,
+                       const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                       moe_stream_t stream);
+
+/* a2 -- permute ("sort tokens by their assigned expert", [P3] section 专家后端).
+ * Rows r = t*k + j whose expert e = topk_idx[t,j] is local (e_lo <= e < e_hi)
+ * are ordered by expert and, inside an expert, by r (a stable sort; the
+ * result is unique).  Outputs:
+ *   group_offsets [E_loc+1] int32: exclusive prefix of the group sizes,
+ *     clamped to R_cap; rows of local expert e_lo+i are [o_i, o_{i+1});
+ *   perm [R_cap] int32: perm[p] = r of the row at sorted position p
+ *     (positions >= group_offsets[E_loc] are left untouched);
+ *   inv [T*k] int32: sorted position of row r, or -1 if r is not local, was
+ *     dropped by the capacity, or has an expert id outside [0, E);
+ *   xp [R_cap, d] (dtype): xp[p] = x[perm[p] / k] (rows past the end untouched).
+ * ws/ws_bytes: workspace of moe_workspace_size(MOE_OP_PERMUTE). */
+moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, const void* x,
+                         int32_t* group_offsets, int32_t* perm, int32_t* inv, void* xp,
+                         void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* a3 + a4 -- expert FFN over the expert groups as grouped GEMMs ("a single
+ * grouped GEMM", [P3] section 专家后端; experts are fused 3-D weight tensors,
+ * [P3] note under the Qwen3 table).  For each local expert i and every row p
+ * in [o_i, o_{i+1}):
+ *   Hg = xp[p] * w_gate[i], Hu = xp[p] * w_up[i]      (fp32 accumulation)
+ *   A  = silu(Hg) * Hu,  silu(z) = z / (1 + exp(-z))
+ *   yp[p] = A * w_down[i]
+ * xp [R_cap,d]; w_gate, w_up [E_loc,d,I]; w_down [E_loc,I,d];
+ * h_save [R_cap,2I] receives [Hg | Hu] (NULL for inference);
+ * a_save [R_cap,I] receives A (required: it also feeds the down GEMM);
+ * yp [R_cap,d].  Rows past group_offsets[E_loc] are untouched.
+ * ws: moe_workspace_size(MOE_OP_FFN_FWD). */
+moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void* xp,
+                                 const int32_t* group_offsets, const void* w_gate,
+                                 const void* w_up, const void* w_down, void* h_save,
+                                 void* a_save, void* yp, void* ws, size_t ws_bytes,
+                                 moe_stream_t stream);
+
+/* a5 -- combine (the "combine" half of dispatch/combine, [P3] section 加速来源):
+ * y[t] = sum_j topk_w[t,j] * yp[inv[t*k+j]] over the slots with inv >= 0, in
+ * ascending j, fp32 accumulation; a token with no local slot gets y[t] = 0.
+ * yp [R_cap,d]; inv [T*k]; topk_w [T,k] fp32; y [T,d].  No workspace. */
+moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,
+                         const float* topk_w, void* y, moe_stream_t stream);
+
+/* ------------------------------------------------------------ backward */
+/* Full-parameter fine-tuning needs every gradient ([P3] Qwen3 and Nemotron
+ * tables report the backward pass on its own row). */
+
+/* a6 -- combine backward.  For every slot with p = inv[t*k+j] >= 0:
+ * dyp[p] = topk_w[t,j] * dy[t];  dtopk_w[t,j] = <dy[t], yp[p]> (fp32);
+ * slots with inv < 0 get dtopk_w = 0.  dy [T,d]; dyp [R_cap,d]; dtopk_w [T,k]. */
+moe_status_t moe_combine_bwd(const moe_shape_t* shape, const void* dy, const void* yp,
+                             const int32_t* inv, const float* topk_w, void* dyp,
+                             float* dtopk_w, moe_stream_t stream);
+
+/* a7..a10 -- expert FFN backward (grouped GEMMs).  Per local expert i, rows
+ * [o_i, o_{i+1}):
+ *   dA = dyp * w_down[i]^T;  s = sigmoid(Hg)
+ *   dHg = dA * Hu * s * (1 + Hg (1 - s)),  dHu = dA * Hg * s
+ *   dxp = dHg * w_gate[i]^T + dHu * w_up[i]^T
+ *   dw_down[i] = A^T dyp,  dw_gate[i] = xp^T dHg,  dw_up[i] = xp^T dHu
+ * Experts with no rows get dw = 0 exactly.  h_save/a_save are the buffers
+ * moe_grouped_ffn_fwd filled.  dxp [R_cap,d]; dw_gate, dw_up [E_loc,d,I];
+ * dw_down [E_loc,I,d].  ws: moe_workspace_size(MOE_OP_FFN_BWD) (it holds
+ * [dHg | dHu]). */
+moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void* xp,
+                                 const int32_t* group_offsets, const void* w_gate,
+                                 const void* w_up, const void* w_down, const void* h_save,
+                                 const void* a_save, const void* dyp, void* dxp,
+                                 void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                                 size_t ws_bytes, moe_stream_t stream);
+
+/* a11 -- permute backward: dx[t] = sum_j dxp[inv[t*k+j]] over slots with
+ * inv >= 0, ascending j, fp32 accumulation (tokens with no slot get 0).
+ * dxp [R_cap,d]; dx [T,d] (overwritten). */
+moe_status_t moe_permute_bwd(const moe_shape_t* shape, const void* dxp, const int32_t* inv,
+                             void* dx, moe_stream_t stream);
+
+/* a12 -- route backward.
+ * softmax_topk: dlogits[t, idx[t,j]] = g_j (dg_j - sum_i g_i dg_i), every other
+ *   entry 0; dw_router = x^T dlogits; dbias = sum_t dlogits (if non-NULL);
+ *   dx += dlogits * w_router^T (read-modify-write of dx, which moe_permute_bwd
+ *   wrote first).
+ * balanced: the gate weights are constants: dlogits (if non-NULL), dw_router
+ *   and dbias (if non-NULL) are set to 0 and dx is not touched.
+ * x [T,d]; w_router [d,E]; topk_idx, topk_w, dtopk_w [T,k]; dlogits [T,E] fp32
+ * (required for softmax_topk); dw_router [d,E] (dtype); dbias [E] fp32;
+ * dx [T,d].  ws: moe_workspace_size(MOE_OP_ROUTE_BWD). */
+moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* w_router,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const float* dtopk_w, float* dlogits, void* dw_router,
+                           float* dbias, void* dx, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
+/* ---------------------------------------------------------- kernel timer */
+/* Optional per-kernel timing with HIP events recorded on the launch stream
+ * around each kernel of the calls above.  Off by default.  Host-side calls;
+ * moe_prof_read waits for the recorded events.
+ * moe_prof_read(name, ...): total milliseconds and launch count of the kernels
+ * whose name equals `name` since the last reset; unknown names read 0.
+ * moe_prof_names(): the names recorded so far, comma-separated (static buffer
+ * valid until the next moe_prof_* call). */
+moe_status_t moe_prof_enable(int on);
+moe_status_t moe_prof_reset(void);
+moe_status_t moe_prof_read(const char* name, double* total_ms, int64_t* launches);
+const char* moe_prof_names(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

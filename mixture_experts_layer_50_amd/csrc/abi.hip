@@ -1,0 +1,487 @@
+// C ABI of the MoE layer library: argument checks, workspace sizing, the
+// order of kernel launches of each call, and the optional kernel timer.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gemm.h"
+#include "kernels.h"
+
+using namespace moe;
+
+// ---------------------------------------------------------------- errors
+static thread_local char g_err[512] = "";
+
+namespace moe {
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+moe_status_t check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- timer
+namespace {
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+std::string g_names;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+int prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof_on) return -1;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, pool_get(), pool_get()};
+  if (!r.a || !r.b) return -1;
+  (void)hipEventRecord(r.a, s);
+  g_recs.push_back(r);
+  return (int)g_recs.size() - 1;
+}
+
+void prof_end(int tok, hipStream_t s) {
+  if (tok < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (tok < (int)g_recs.size()) (void)hipEventRecord(g_recs[tok].b, s);
+}
+}  // namespace moe
+
+extern "C" moe_status_t moe_prof_enable(int on) {
+  g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_prof_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_recs) {
+    (void)hipEventSynchronize(r.b);
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_prof_read(const char* name, double* total_ms, int64_t* launches) {
+  if (!name || !total_ms || !launches) {
+    set_error("moe_prof_read: null argument");
+    return MOE_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double tot = 0;
+  int64_t n = 0;
+  for (auto& r : g_recs) {
+    if (r.name != name) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) {
+      set_error("moe_prof_read: event wait failed");
+      return MOE_ERR_HIP;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      set_error("moe_prof_read: elapsed time failed");
+      return MOE_ERR_HIP;
+    }
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return MOE_OK;
+}
+
+extern "C" const char* moe_prof_names(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_names.clear();
+  std::vector<std::string> seen;
+  for (auto& r : g_recs) {
+    bool dup = false;
+    for (auto& s : seen) dup = dup || s == r.name;
+    if (dup) continue;
+    seen.push_back(r.name);
+    if (!g_names.empty()) g_names += ",";
+    g_names += r.name;
+  }
+  return g_names.c_str();
+}
+
+// ---------------------------------------------------------------- utility
+extern "C" const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+extern "C" const char* moe_last_error(void) { return g_err; }
+
+extern "C" const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+// ---------------------------------------------------------------- checks
+namespace {
+
+#define MOE_TRY(x)                      \
+  do {                                  \
+    moe_status_t _st = (x);             \
+    if (_st != MOE_OK) return _st;      \
+  } while (0)
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+struct Dims {
+  int T, d, E, k, I, e_lo, e_hi, E_loc, R_cap;
+  bool bf16;
+  int eb;  // element bytes
+  bool balanced;
+};
+
+moe_status_t check_shape(const moe_shape_t* s, const char* fn, Dims* o) {
+  if (!s) return fail(MOE_ERR_ARG, "%s: shape is NULL", fn);
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)s->dtype);
+  if (s->gate != MOE_GATE_SOFTMAX_TOPK && s->gate != MOE_GATE_BALANCED)
+    return fail(MOE_ERR_ARG, "%s: unknown gate %d", fn, (int)s->gate);
+  if (s->T <= 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->I <= 0)
+    return fail(MOE_ERR_SHAPE, "%s: T, d, E, k, I must be positive", fn);
+  if (s->k > s->E) return fail(MOE_ERR_ARG, "%s: k=%d > E=%d", fn, s->k, s->E);
+  if (s->e_lo < 0 || s->e_hi > s->E || s->e_lo >= s->e_hi)
+    return fail(MOE_ERR_ARG, "%s: local experts [%d,%d) not inside [0,%d)", fn, s->e_lo, s->e_hi, s->E);
+  const int64_t rows = (int64_t)s->T * s->k;
+  if (rows >= ((int64_t)1 << 31)) return fail(MOE_ERR_SHAPE, "%s: T*k overflows int32", fn);
+  if (s->R_cap < 0 || s->R_cap > rows) return fail(MOE_ERR_SHAPE, "%s: R_cap=%d outside [0, T*k]", fn, s->R_cap);
+  if (s->gate == MOE_GATE_BALANCED && s->E % s->k)
+    return fail(MOE_ERR_ARG, "%s: the balanced gate needs k | E", fn);
+  if (s->d % 64 || s->I % 64) return fail(MOE_ERR_UNSUPPORTED, "%s: d and I must be multiples of 64", fn);
+  if (s->E > 512) return fail(MOE_ERR_UNSUPPORTED, "%s: E > 512", fn);
+  if (s->dtype == MOE_BF16 && s->E % 8) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 needs E %% 8 == 0", fn);
+  if (s->k > 32) return fail(MOE_ERR_UNSUPPORTED, "%s: k > 32", fn);
+  if ((int64_t)s->R_cap * 2 * s->I >= ((int64_t)1 << 40) || (int64_t)rows * s->d >= ((int64_t)1 << 40))
+    return fail(MOE_ERR_SHAPE, "%s: buffers too large", fn);
+  o->T = s->T; o->d = s->d; o->E = s->E; o->k = s->k; o->I = s->I;
+  o->e_lo = s->e_lo; o->e_hi = s->e_hi; o->E_loc = s->e_hi - s->e_lo;
+  o->R_cap = s->R_cap ? s->R_cap : (int)rows;
+  o->bf16 = s->dtype == MOE_BF16;
+  o->eb = o->bf16 ? 2 : 4;
+  o->balanced = s->gate == MOE_GATE_BALANCED;
+  return MOE_OK;
+}
+
+// Every listed pointer must be non-NULL and 16-byte aligned.
+moe_status_t need(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
+  for (auto& p : ptrs) {
+    if (!p.second) return fail(MOE_ERR_ARG, "%s: %s is NULL", fn, p.first);
+    if ((uintptr_t)p.second & 15) return fail(MOE_ERR_UNSUPPORTED, "%s: %s is not 16-byte aligned", fn, p.first);
+  }
+  return MOE_OK;
+}
+
+// Optional pointers: NULL allowed, else 16-byte aligned.
+moe_status_t opt(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ptrs) {
+  for (auto& p : ptrs)
+    if (p.second && ((uintptr_t)p.second & 15))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: %s is not 16-byte aligned", fn, p.first);
+  return MOE_OK;
+}
+
+constexpr int BM_ROWS = 256;  // M tile of the row-grouped bf16 GEMMs
+
+int64_t tile_table_bytes(const Dims& D) {
+  return (1 + 2 * ((int64_t)D.R_cap / BM_ROWS + D.E_loc)) * 4;
+}
+int max_m_tiles(const Dims& D) { return D.R_cap / BM_ROWS + D.E_loc; }
+
+int64_t ws_bytes(const Dims& D, int op) {
+  switch (op) {
+    case MOE_OP_PERMUTE: return round_up(permute_ws_bytes(D.T, D.E_loc), 256);
+    case MOE_OP_FFN_FWD: return D.bf16 ? round_up(tile_table_bytes(D), 256) : 0;
+    case MOE_OP_FFN_BWD:
+      return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
+             (D.bf16 ? round_up(tile_table_bytes(D), 256) : 0);
+    case MOE_OP_ROUTE_BWD:
+      return (D.bf16 && !D.balanced) ? round_up((int64_t)D.T * D.E * 2, 256) : 0;
+    default: return 0;
+  }
+}
+
+moe_status_t check_ws(const char* fn, const Dims& D, int op, const void* ws, size_t bytes) {
+  int64_t want = ws_bytes(D, op);
+  if (want == 0) return MOE_OK;
+  if (!ws || (int64_t)bytes < want)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %lld bytes needed, %zu given", fn, (long long)want, bytes);
+  if ((uintptr_t)ws & 255) return fail(MOE_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+  return MOE_OK;
+}
+
+hipStream_t S(moe_stream_t s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, size_t* bytes) {
+  Dims D;
+  if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
+  MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
+  if (op < MOE_OP_ROUTE || op > MOE_OP_ROUTE_BWD) return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
+  *bytes = (size_t)ws_bytes(D, op);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- forward
+extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_router,
+                                  const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                                  moe_stream_t stream) {
+  const char* fn = "moe_route";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"topk_idx", topk_idx}, {"topk_w", topk_w}}));
+  if (D.balanced) return launch_balanced_gate(D.T, D.E, D.k, topk_idx, topk_w, S(stream));
+  MOE_TRY(need(fn, {{"x", x}, {"w_router", w_router}, {"logits", logits}}));
+  MOE_TRY(opt(fn, {{"bias", bias}}));
+  GemmParams p{};
+  p.A = x; p.lda = D.d;
+  p.B0 = w_router; p.ldb = D.E;
+  p.M = D.T; p.N = D.E; p.K = D.d;
+  p.m_tiles = (int)ceil_div(D.T, 64); p.n_tiles = (int)ceil_div(D.E, 64);
+  p.groups = 1;
+  p.C0 = logits; p.ldc = D.E; p.bias = bias;
+  MOE_TRY(launch_gemm(D.bf16, A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS, TILE_64x64, p,
+                      p.m_tiles, S(stream), "route_logits"));
+  return launch_topk_softmax(logits, D.T, D.E, D.k, topk_idx, topk_w, S(stream));
+}
+
+extern "C" moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, const void* x,
+                                    int32_t* group_offsets, int32_t* perm, int32_t* inv, void* xp,
+                                    void* ws, size_t ws_bytes_, moe_stream_t stream) {
+  const char* fn = "moe_permute";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"topk_idx", topk_idx}, {"x", x}, {"group_offsets", group_offsets},
+                    {"perm", perm}, {"inv", inv}, {"xp", xp}}));
+  MOE_TRY(check_ws(fn, D, MOE_OP_PERMUTE, ws, ws_bytes_));
+  return launch_permute(topk_idx, x, D.T, D.d, D.k, D.e_lo, D.e_hi, D.R_cap, D.eb, group_offsets,
+                        perm, inv, xp, ws, S(stream));
+}
+
+extern "C" moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void* xp,
+                                            const int32_t* group_offsets, const void* w_gate,
+                                            const void* w_up, const void* w_down, void* h_save,
+                                            void* a_save, void* yp, void* ws, size_t ws_bytes_,
+                                            moe_stream_t stream) {
+  const char* fn = "moe_grouped_ffn_fwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"xp", xp}, {"group_offsets", group_offsets}, {"w_gate", w_gate},
+                    {"w_up", w_up}, {"w_down", w_down}, {"a_save", a_save}, {"yp", yp}}));
+  MOE_TRY(opt(fn, {{"h_save", h_save}}));
+  MOE_TRY(check_ws(fn, D, MOE_OP_FFN_FWD, ws, ws_bytes_));
+  int32_t* tiles = static_cast<int32_t*>(ws);
+  const int rows_or_tiles = D.bf16 ? max_m_tiles(D) : D.R_cap;
+  if (D.bf16) MOE_TRY(launch_tile_table(group_offsets, D.E_loc, BM_ROWS, tiles, S(stream)));
+
+  GemmParams g{};
+  g.A = xp; g.lda = D.d;
+  g.B0 = w_gate; g.B1 = w_up; g.ldb = D.I; g.b_estride = (int64_t)D.d * D.I;
+  g.N = D.I; g.K = D.d;
+  g.off = group_offsets; g.tiles = tiles; g.groups = D.E_loc;
+  g.n_tiles = D.I / 64;
+  g.C0 = h_save; g.C2 = a_save; g.I = D.I;
+  MOE_TRY(launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU, TILE_256x128, g,
+                      rows_or_tiles, S(stream), "ffn_gateup_fwd"));
+
+  GemmParams p{};
+  p.A = a_save; p.lda = D.I;
+  p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
+  p.N = D.d; p.K = D.I;
+  p.off = group_offsets; p.tiles = tiles; p.groups = D.E_loc;
+  p.n_tiles = (int)ceil_div(D.d, 128);
+  p.C0 = yp; p.ldc = D.d;
+  return launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE, TILE_256x128, p,
+                     rows_or_tiles, S(stream), "ffn_down_fwd");
+}
+
+extern "C" moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,
+                                    const float* topk_w, void* y, moe_stream_t stream) {
+  const char* fn = "moe_combine";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"yp", yp}, {"inv", inv}, {"topk_w", topk_w}, {"y", y}}));
+  return launch_gather_sum(yp, inv, topk_w, D.T, D.d, D.k, D.eb, y, S(stream), "combine");
+}
+
+// ---------------------------------------------------------------- backward
+extern "C" moe_status_t moe_combine_bwd(const moe_shape_t* shape, const void* dy, const void* yp,
+                                        const int32_t* inv, const float* topk_w, void* dyp,
+                                        float* dtopk_w, moe_stream_t stream) {
+  const char* fn = "moe_combine_bwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"dy", dy}, {"yp", yp}, {"inv", inv}, {"topk_w", topk_w}, {"dyp", dyp},
+                    {"dtopk_w", dtopk_w}}));
+  return launch_combine_bwd(dy, yp, inv, topk_w, D.T, D.d, D.k, D.eb, dyp, dtopk_w, S(stream));
+}
+
+extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void* xp,
+                                            const int32_t* group_offsets, const void* w_gate,
+                                            const void* w_up, const void* w_down,
+                                            const void* h_save, const void* a_save,
+                                            const void* dyp, void* dxp, void* dw_gate,
+                                            void* dw_up, void* dw_down, void* ws,
+                                            size_t ws_bytes_, moe_stream_t stream) {
+  const char* fn = "moe_grouped_ffn_bwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"xp", xp}, {"group_offsets", group_offsets}, {"w_gate", w_gate},
+                    {"w_up", w_up}, {"w_down", w_down}, {"h_save", h_save}, {"a_save", a_save},
+                    {"dyp", dyp}, {"dxp", dxp}, {"dw_gate", dw_gate}, {"dw_up", dw_up},
+                    {"dw_down", dw_down}}));
+  MOE_TRY(check_ws(fn, D, MOE_OP_FFN_BWD, ws, ws_bytes_));
+  char* wsb = static_cast<char*>(ws);
+  void* dH = wsb;
+  int32_t* tiles = reinterpret_cast<int32_t*>(wsb + round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256));
+  const int rows_or_tiles = D.bf16 ? max_m_tiles(D) : D.R_cap;
+  hipStream_t s = S(stream);
+  if (D.bf16) MOE_TRY(launch_tile_table(group_offsets, D.E_loc, BM_ROWS, tiles, s));
+
+  {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
+    GemmParams p{};
+    p.A = dyp; p.lda = D.d;
+    p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
+    p.N = D.I; p.K = D.d;
+    p.off = group_offsets; p.tiles = tiles; p.groups = D.E_loc;
+    p.n_tiles = (int)ceil_div(D.I, 128);
+    p.C0 = dH; p.aux = h_save; p.I = D.I;
+    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU, TILE_256x128, p,
+                        rows_or_tiles, s, "ffn_down_dgrad"));
+  }
+  {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
+    GemmParams p{};
+    p.A = dH; p.lda = 2 * (int64_t)D.I;
+    p.B0 = w_gate; p.B1 = w_up; p.ldb = D.I; p.b_estride = (int64_t)D.d * D.I;
+    p.k_split = D.I;
+    p.N = D.d; p.K = 2 * D.I;
+    p.off = group_offsets; p.tiles = tiles; p.groups = D.E_loc;
+    p.n_tiles = (int)ceil_div(D.d, 128);
+    p.C0 = dxp; p.ldc = D.d;
+    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE, TILE_256x128, p,
+                        rows_or_tiles, s, "ffn_gateup_dgrad"));
+  }
+  {  // a8: dWd[e] = A_e^T dYp_e
+    GemmParams p{};
+    p.A = a_save; p.lda = D.I;
+    p.B0 = dyp; p.ldb = D.d;
+    p.M = D.I; p.N = D.d;
+    p.off = group_offsets; p.groups = D.E_loc;
+    p.m_tiles = (int)ceil_div(D.I, 256); p.n_tiles = (int)ceil_div(D.d, 128);
+    p.C0 = dw_down; p.ldc = D.d; p.c_estride = (int64_t)D.I * D.d;
+    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, TILE_256x128, p,
+                        p.m_tiles, s, "ffn_down_wgrad"));
+  }
+  {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
+    GemmParams p{};
+    p.A = xp; p.lda = D.d;
+    p.B0 = dH; p.ldb = 2 * (int64_t)D.I;
+    p.M = D.d; p.N = 2 * D.I;
+    p.off = group_offsets; p.groups = D.E_loc;
+    p.m_tiles = (int)ceil_div(D.d, 256); p.n_tiles = (int)ceil_div(2 * D.I, 128);
+    p.C0 = dw_gate; p.C1 = dw_up; p.n_split = D.I; p.ldc = D.I;
+    p.c_estride = (int64_t)D.d * D.I;
+    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, TILE_256x128, p,
+                        p.m_tiles, s, "ffn_gateup_wgrad"));
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_permute_bwd(const moe_shape_t* shape, const void* dxp, const int32_t* inv,
+                                        void* dx, moe_stream_t stream) {
+  const char* fn = "moe_permute_bwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"dxp", dxp}, {"inv", inv}, {"dx", dx}}));
+  return launch_gather_sum(dxp, inv, nullptr, D.T, D.d, D.k, D.eb, dx, S(stream), "permute_bwd");
+}
+
+extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* w_router,
+                                      const int32_t* topk_idx, const float* topk_w,
+                                      const float* dtopk_w, float* dlogits, void* dw_router,
+                                      float* dbias, void* dx, void* ws, size_t ws_bytes_,
+                                      moe_stream_t stream) {
+  const char* fn = "moe_route_bwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  hipStream_t s = S(stream);
+  if (D.balanced) {
+    MOE_TRY(opt(fn, {{"dlogits", dlogits}, {"dw_router", dw_router}, {"dbias", dbias}}));
+    if (dlogits) MOE_TRY(launch_fill_zero(dlogits, (int64_t)D.T * D.E * 4, s));
+    if (dw_router) MOE_TRY(launch_fill_zero(dw_router, (int64_t)D.d * D.E * D.eb, s));
+    if (dbias) MOE_TRY(launch_fill_zero(dbias, (int64_t)D.E * 4, s));
+    return MOE_OK;
+  }
+  MOE_TRY(need(fn, {{"x", x}, {"w_router", w_router}, {"topk_idx", topk_idx}, {"topk_w", topk_w},
+                    {"dtopk_w", dtopk_w}, {"dlogits", dlogits}, {"dw_router", dw_router}, {"dx", dx}}));
+  MOE_TRY(opt(fn, {{"dbias", dbias}}));
+  MOE_TRY(check_ws(fn, D, MOE_OP_ROUTE_BWD, ws, ws_bytes_));
+  bf16_t* dl16 = D.bf16 ? static_cast<bf16_t*>(ws) : nullptr;
+  MOE_TRY(launch_route_bwd_dl(topk_idx, topk_w, dtopk_w, D.T, D.E, D.k, dlogits, dl16, s));
+  const void* dl = D.bf16 ? static_cast<const void*>(dl16) : static_cast<const void*>(dlogits);
+  {  // dWr = x^T dL
+    GemmParams p{};
+    p.A = x; p.lda = D.d;
+    p.B0 = dl; p.ldb = D.E;
+    p.M = D.d; p.N = D.E; p.K = D.T;
+    p.off = nullptr; p.groups = 1;
+    p.m_tiles = (int)ceil_div(D.d, 64); p.n_tiles = (int)ceil_div(D.E, 64);
+    p.C0 = dw_router; p.ldc = D.E;
+    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, TILE_64x64, p,
+                        p.m_tiles, s, "route_bwd_dw"));
+  }
+  if (dbias) MOE_TRY(launch_col_sum(dlogits, D.T, D.E, dbias, s));
+  {  // dX += dL Wr^T
+    GemmParams p{};
+    p.A = dl; p.lda = D.E;
+    p.B0 = w_router; p.ldb = D.E;
+    p.M = D.T; p.N = D.d; p.K = D.E;
+    p.m_tiles = (int)ceil_div(D.T, 64); p.n_tiles = (int)ceil_div(D.d, 64);
+    p.groups = 1;
+    p.C0 = dx; p.ldc = D.d;
+    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM, TILE_64x64, p,
+                        p.m_tiles, s, "route_bwd_dx"));
+  }
+  return MOE_OK;
+}

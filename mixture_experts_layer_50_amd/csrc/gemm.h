@@ -1,0 +1,82 @@
+// Grouped GEMM engine of the MoE layer: problem description shared by the
+// bf16 MFMA kernels and the fp32 kernels (gemm.hip), and the launchers the
+// C ABI (abi.hip) calls.
+//
+// Every GEMM of the layer is C[m][n] = sum_k A(m,k) * B(k,n) with
+//   A(m,k) stored k-contiguous (a[m*lda + k])  -- A_KC
+//             or m-contiguous (a[k*lda + m])  -- A_MC
+//   B(k,n) stored n-contiguous (b[k*ldb + n])  -- B_NC
+//             or k-contiguous (b[n*ldb + k])  -- B_KC
+// and one of three groupings:
+//   G_DENSE  one plain GEMM of M x N x K;
+//   G_MROWS  expert groups along M: the rows of local expert e are
+//            [off[e], off[e+1]) of A and C, and B is expert e's weight matrix
+//            (forward and input-gradient GEMMs; "sort tokens by expert, then
+//            one grouped GEMM", page "Accelerating Transformers fine-tuning
+//            with NVIDIA NeMo AutoModel", section 专家后端);
+//   G_KROWS  expert groups along K: C for expert e sums over the rows
+//            [off[e], off[e+1]) of A and B (weight gradients); an expert
+//            with no rows gets C = 0.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+enum AMode { A_KC = 0, A_MC = 1 };
+enum BMode { B_NC = 0, B_KC = 1 };
+enum GMode { G_DENSE = 0, G_MROWS = 1, G_KROWS = 2 };
+// B with two sources: none; tile columns split in halves (gate | up); K split.
+enum B2Mode { B2_NONE = 0, B2_NHALF = 1, B2_KSPLIT = 2 };
+enum EpiMode {
+  EPI_STORE = 0,      // C0[m,n] = acc  (cols >= n_split go to C1[m, n-n_split] when n_split > 0)
+  EPI_ACCUM = 1,      // C0[m,n] += acc
+  EPI_F32_BIAS = 2,   // fp32 C0[m,n] = acc + bias[n]
+  EPI_SWIGLU = 3,     // gate/up pair -> H = [Hg|Hu] (C0, optional), A = silu(Hg)*Hu (C2)
+  EPI_DSWIGLU = 4     // acc = dA; with H from `aux`: dH = [dHg|dHu] into C0
+};
+
+struct GemmParams {
+  const void* A;
+  int64_t lda;
+  const void* B0;
+  const void* B1;
+  int64_t ldb;
+  int64_t b_estride;   // element stride between experts' B (G_MROWS)
+  int M, N, K;         // G_DENSE: all; G_MROWS: N, K (M = row capacity); G_KROWS: M, N
+  int k_split;         // B2_KSPLIT: k < k_split from B0, else B1 at k - k_split
+  const int32_t* off;  // group offsets [groups+1] (G_MROWS, G_KROWS); NULL in G_KROWS = one group [0,K)
+  const int32_t* tiles;// G_MROWS tile table: tiles[0] = count, then (expert, first row) pairs
+  int groups;          // number of local experts
+  int m_tiles, n_tiles;
+  void* C0;
+  void* C1;
+  void* C2;
+  int64_t ldc;
+  int64_t c_estride;   // element stride between experts' C (G_KROWS)
+  int n_split;         // EPI_STORE: columns >= n_split go to C1
+  int I;               // EPI_SWIGLU / EPI_DSWIGLU: expert width (H row stride is 2I)
+  const void* aux;     // EPI_DSWIGLU: saved H
+  const float* bias;   // EPI_F32_BIAS (may be NULL)
+};
+
+// Tile shapes of the bf16 MFMA kernels.
+enum TileCfg { TILE_256x128 = 0, TILE_64x64 = 1 };
+
+// Launch one GEMM.  `is_bf16` selects the bf16 MFMA kernel or the fp32 kernel;
+// the template-like mode arguments select the instantiation.  For G_MROWS the
+// caller has already built the tile table (launch_tile_table) with the BM the
+// chosen tile shape uses (tile_bm()).  `name` labels the kernel for the timer.
+moe_status_t launch_gemm(bool is_bf16, int amode, int bmode, int gmode, int b2, int epi,
+                         TileCfg cfg, const GemmParams& p, int max_m_tiles,
+                         hipStream_t s, const char* name);
+
+int tile_bm(TileCfg cfg);
+int tile_bn(TileCfg cfg);
+
+// Tile table for G_MROWS: tiles[0] = number of M tiles, then for each tile
+// (expert, first row) in expert order; at most max_tiles entries.
+moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* tiles,
+                               hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,554 @@
+// Grouped GEMM kernels of the MoE layer for gfx950.
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 (fp32 accumulation) on LDS-staged
+// 64-deep K slices, double-buffered (the next slice is fetched from HBM into
+// registers while the current one is multiplied), four waves per workgroup.
+// Both operands sit in LDS k-contiguous, 16-byte chunks XOR-swizzled by row;
+// operands that are stored with k strided in memory are loaded as 8x8 blocks
+// and transposed in registers before the LDS write.  Workgroup ids are remapped
+// so that consecutive tiles land on the same XCD (its own L2), and tiles that
+// share an A row block or a weight column block run together (GROUP_M order).
+//
+// fp32 path: a plain fp32 kernel (one output per thread, fp32 FMA) used for
+// fp32 layers, which are small parity workloads.
+#include "gemm.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 64;  // K extent of one LDS stage: 8 chunks of 8 bf16
+constexpr int NXCD = 8;
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (conflict-free for
+// 8 or 16 consecutive rows reading the same logical chunk).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Hardware dispatches workgroup ids round-robin over the 8 XCDs.  Give each
+// XCD a contiguous range of the `count` real tiles instead.
+__device__ __forceinline__ int remap_xcd(int pid, int count) {
+  int xcd = pid % NXCD, idx = pid / NXCD;
+  int per = count / NXCD, rem = count % NXCD;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
+// Linear tile id -> (m tile, n tile), GM m tiles at a time over all n tiles.
+__device__ __forceinline__ void group_order(int L, int mt_count, int nt_count, int& mt, int& nt) {
+  constexpr int GM = 4;
+  int per_group = GM * nt_count;
+  int g = L / per_group;
+  int first = g * GM;
+  int gsize = min(mt_count - first, GM);
+  int r = L - g * per_group;
+  mt = first + r % gsize;
+  nt = r / gsize;
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// 8x8 transpose of 16-bit elements: in[kk] holds 8 values along the row
+// dimension at depth kk; out[mm] holds the 8 depths of row mm.
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+  const uint32_t* v = reinterpret_cast<const uint32_t*>(in);  // v[kk*4 + q]
+  uint32_t* w = reinterpret_cast<uint32_t*>(out);             // w[mm*4 + p]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t lo = v[(2 * p) * 4 + q], hi = v[(2 * p + 1) * 4 + q];
+      w[(2 * q) * 4 + p] = (lo & 0xffffu) | (hi << 16);
+      w[(2 * q + 1) * 4 + p] = (lo >> 16) | (hi & 0xffff0000u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile loaders.  A tile holds ROWS rows x 64 k of one operand, stored in LDS
+// as [ROWS][64] bf16, k-contiguous, chunk-swizzled.
+// ---------------------------------------------------------------------------
+
+// Operand stored k-contiguous: row r of the tile is src[(row0 + r) * ld + k].
+// Two sources split along k (k < ksplit -> s0, else s1 at k - ksplit) when
+// TWO is set.
+template <int ROWS, bool TWO>
+struct LoaderKC {
+  static constexpr int CH = ROWS * 8;
+  static constexpr int NR = (CH + 255) / 256;
+  uint4 r[NR];
+  __device__ __forceinline__ void load(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
+                                       int row_hi, int k0, int k_hi, int ksplit, int tid) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      int q = tid + 256 * i;
+      r[i] = zero4();
+      if (CH % 256 == 0 || q < CH) {
+        int row = row0 + (q >> 3);
+        int k = k0 + (q & 7) * 8;
+        if (row < row_hi && k < k_hi) {
+          const bf16_t* src = s0;
+          if (TWO && k >= ksplit) { src = s1; k -= ksplit; }
+          r[i] = *reinterpret_cast<const uint4*>(src + (int64_t)row * ld + k);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      int q = tid + 256 * i;
+      if (CH % 256 == 0 || q < CH) {
+        int row = q >> 3, c = q & 7;
+        *reinterpret_cast<uint4*>(lds + row * BK + swz(row, c) * 8) = r[i];
+      }
+    }
+  }
+};
+
+// Operand stored with k as the row index: element (r, k) of the tile is
+// src[k * ld + col0 + r].  Loaded as 8x8 blocks, transposed in registers.
+// HALF: tile rows [0, ROWS/2) come from s0 at col0 + r, rows [ROWS/2, ROWS)
+// from s1 at col0 + r - ROWS/2 (the gate | up halves of one tile).
+template <int ROWS, bool HALF>
+struct LoaderT {
+  static constexpr int RB = ROWS / 8;
+  static constexpr int NB = RB * 8;
+  static constexpr int NR = (NB + 255) / 256;
+  uint4 r[NR][8];
+  __device__ __forceinline__ void load(const bf16_t* s0, const bf16_t* s1, int64_t ld, int col0,
+                                       int col_hi, int k0, int k_hi, int tid) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      int q = tid + 256 * i;
+      if (NB % 256 == 0 || q < NB) {
+        int ib = q % RB, kb = q / RB;
+        int rr = ib * 8;
+        const bf16_t* src = s0;
+        if (HALF && rr >= ROWS / 2) { src = s1; rr -= ROWS / 2; }
+        int col = col0 + rr;
+        bool colok = col < col_hi;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          int k = k0 + kb * 8 + kk;
+          r[i][kk] = (colok && k < k_hi)
+                         ? *reinterpret_cast<const uint4*>(src + (int64_t)k * ld + col)
+                         : zero4();
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      int q = tid + 256 * i;
+      if (NB % 256 == 0 || q < NB) {
+        int ib = q % RB, kb = q / RB;
+        uint4 w[8];
+        transpose8x8(r[i], w);
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+          int row = ib * 8 + mm;
+          *reinterpret_cast<uint4*>(lds + row * BK + swz(row, kb) * 8) = w[mm];
+        }
+      }
+    }
+  }
+};
+
+template <bool KC, int ROWS, bool TWO> struct PickLoader;
+template <int ROWS, bool TWO> struct PickLoader<true, ROWS, TWO> { typedef LoaderKC<ROWS, TWO> type; };
+template <int ROWS, bool TWO> struct PickLoader<false, ROWS, TWO> { typedef LoaderT<ROWS, TWO> type; };
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int GMD, int B2, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(WGM * WGN == 4, "four waves");
+  static_assert(FM >= 1 && FN >= 1, "wave tile of at least 32x32");
+  static_assert(B2 != B2_NHALF || (FN == 2 && BN / 2 == WGN * 32), "gate|up halves");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // ---- which tile
+  int mt_count = (GMD == G_MROWS) ? p.tiles[0] : p.m_tiles;
+  int per_group = mt_count * p.n_tiles;
+  int count = (GMD == G_KROWS) ? per_group * p.groups : per_group;
+  if ((int)blockIdx.x >= count) return;
+  int L = remap_xcd(blockIdx.x, count);
+  int e = 0;
+  if (GMD == G_KROWS) { e = L / per_group; L -= e * per_group; }
+  int mt, nt;
+  group_order(L, mt_count, p.n_tiles, mt, nt);
+  int m_lo, m_hi, k_lo, k_hi;
+  if (GMD == G_MROWS) {
+    e = p.tiles[1 + 2 * mt];
+    m_lo = p.tiles[2 + 2 * mt];
+    m_hi = min(m_lo + BM, p.off[e + 1]);
+    k_lo = 0;
+    k_hi = p.K;
+  } else {
+    m_lo = mt * BM;
+    m_hi = min(m_lo + BM, p.M);
+    if (GMD == G_KROWS && p.off) { k_lo = p.off[e]; k_hi = p.off[e + 1]; }
+    else { k_lo = 0; k_hi = p.K; }
+  }
+  const int n0 = nt * ((B2 == B2_NHALF) ? BN / 2 : BN);
+  const int n_hi = p.N;  // column bound in the B source's column space
+
+  const bf16_t* A = static_cast<const bf16_t*>(p.A);
+  const bf16_t* B0 = static_cast<const bf16_t*>(p.B0);
+  const bf16_t* B1 = static_cast<const bf16_t*>(p.B1);
+  if (GMD == G_MROWS) {
+    B0 += (int64_t)e * p.b_estride;
+    if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
+  }
+
+  typename PickLoader<AM == A_KC, BM, false>::type la;
+  typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE>::type lb;
+
+  auto load_tiles = [&](int k0) {
+    if constexpr (AM == A_KC) la.load(A, A, p.lda, m_lo, m_hi, k0, k_hi, 0, tid);
+    else la.load(A, A, p.lda, m_lo, m_hi, k0, k_hi, tid);
+    if constexpr (BMD == B_KC) lb.load(B0, B1, p.ldb, n0, n_hi, k0, k_hi, p.k_split, tid);
+    else lb.load(B0, B1, p.ldb, n0, n_hi, k0, k_hi, tid);
+  };
+  auto store_tiles = [&](int buf) {
+    bf16_t* as = smem + buf * (BM + BN) * BK;
+    la.store(as, tid);
+    lb.store(as + BM * BK, tid);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (k_hi - k_lo + BK - 1) / BK;
+  if (nk > 0) {
+    load_tiles(k_lo);
+    store_tiles(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) load_tiles(k_lo + (kt + 1) * BK);
+    const bf16_t* as = smem + (kt & 1) * (BM + BN) * BK;
+    const bf16_t* bs = as + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8 af[FM], bfg[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        int row = wm * WTM + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + swz(row, c) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        int nb = (B2 == B2_NHALF) ? (j * (BN / 2) + wn * 32) : (wn * WTN + j * 32);
+        int row = nb + (lane & 31);
+        bfg[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + swz(row, c) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    if (more) store_tiles((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Lane holds C[m][n..n+3] with m = row of the wave tile
+  // (lane & 31), n = 8q + 4 (lane >> 5) within each 32-column block.
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m_lo + wm * WTM + i * 32 + (lane & 31);
+    if (m >= m_hi) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      bf16_t* H = static_cast<bf16_t*>(p.C0);
+      bf16_t* Aout = static_cast<bf16_t*>(p.C2);
+      const int64_t I = p.I;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 32 + 8 * q + 4 * half;
+        float g[4], u[4], a[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          g[s] = acc[i][0][4 * q + s];
+          u[s] = acc[i][1][4 * q + s];
+          a[s] = g[s] / (1.0f + expf(-g[s])) * u[s];
+        }
+        if (H) {
+          *reinterpret_cast<uint2*>(H + m * 2 * I + n) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+          *reinterpret_cast<uint2*>(H + m * 2 * I + I + n) = make_uint2(pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]));
+        }
+        *reinterpret_cast<uint2*>(Aout + m * I + n) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * half;
+          if (n >= p.N) continue;
+          float v[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) v[s] = acc[i][j][4 * q + s];
+          if constexpr (EPI == EPI_STORE) {
+            bf16_t* C = static_cast<bf16_t*>(p.C0);
+            if (p.n_split > 0 && n >= p.n_split) { C = static_cast<bf16_t*>(p.C1); n -= p.n_split; }
+            if (GMD == G_KROWS) C += (int64_t)e * p.c_estride;
+            *reinterpret_cast<uint2*>(C + (int64_t)m * p.ldc + n) =
+                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+          } else if constexpr (EPI == EPI_ACCUM) {
+            bf16_t* C = static_cast<bf16_t*>(p.C0) + (int64_t)m * p.ldc + n;
+            uint2 o = *reinterpret_cast<const uint2*>(C);
+            float w0 = bf2f((bf16_t)(o.x & 0xffff)) + v[0], w1 = bf2f((bf16_t)(o.x >> 16)) + v[1];
+            float w2 = bf2f((bf16_t)(o.y & 0xffff)) + v[2], w3 = bf2f((bf16_t)(o.y >> 16)) + v[3];
+            *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf2(w0, w1), pack_bf2(w2, w3));
+          } else if constexpr (EPI == EPI_F32_BIAS) {
+            float* C = static_cast<float*>(p.C0) + (int64_t)m * p.ldc + n;
+            if (p.bias) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) v[s] += p.bias[n + s];
+            }
+            *reinterpret_cast<float4*>(C) = make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_DSWIGLU) {
+            const bf16_t* H = static_cast<const bf16_t*>(p.aux);
+            bf16_t* dH = static_cast<bf16_t*>(p.C0);
+            const int64_t I = p.I;
+            uint2 hg = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + n);
+            uint2 hu = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + I + n);
+            float g[4] = {bf2f((bf16_t)(hg.x & 0xffff)), bf2f((bf16_t)(hg.x >> 16)),
+                          bf2f((bf16_t)(hg.y & 0xffff)), bf2f((bf16_t)(hg.y >> 16))};
+            float u[4] = {bf2f((bf16_t)(hu.x & 0xffff)), bf2f((bf16_t)(hu.x >> 16)),
+                          bf2f((bf16_t)(hu.y & 0xffff)), bf2f((bf16_t)(hu.y >> 16))};
+            float dg[4], du[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              float sg = 1.0f / (1.0f + expf(-g[s]));
+              dg[s] = v[s] * u[s] * sg * (1.0f + g[s] * (1.0f - sg));
+              du[s] = v[s] * g[s] * sg;
+            }
+            *reinterpret_cast<uint2*>(dH + (int64_t)m * 2 * I + n) =
+                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(dH + (int64_t)m * 2 * I + I + n) =
+                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: one output (or one gate/up pair) per thread, fp32 FMA.
+// ---------------------------------------------------------------------------
+template <int AM, int BMD, int GMD, int B2, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+  const int n = blockIdx.x * 16 + (threadIdx.x & 15);
+  const int m = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const float* A = static_cast<const float*>(p.A);
+  const float* B0 = static_cast<const float*>(p.B0);
+  const float* B1 = static_cast<const float*>(p.B1);
+  int e = 0, k_lo = 0, k_hi = p.K;
+  const int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? p.I : p.N;
+  if (n >= ncols) return;
+  if (GMD == G_MROWS) {
+    if (m >= p.off[p.groups]) return;
+    int lo = 0, hi = p.groups - 1;  // last e with off[e] <= m
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (p.off[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    B0 += (int64_t)e * p.b_estride;
+    if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
+  } else {
+    if (m >= p.M) return;
+    if (GMD == G_KROWS) {
+      e = blockIdx.z;
+      if (p.off) { k_lo = p.off[e]; k_hi = p.off[e + 1]; }
+    }
+  }
+  auto a_at = [&](int k) -> float {
+    return AM == A_KC ? A[(int64_t)m * p.lda + k] : A[(int64_t)k * p.lda + m];
+  };
+  auto b_at = [&](const float* B, int k, int col) -> float {
+    return BMD == B_NC ? B[(int64_t)k * p.ldb + col] : B[(int64_t)col * p.ldb + k];
+  };
+  float acc = 0.f, acc2 = 0.f;
+  for (int k = k_lo; k < k_hi; ++k) {
+    float a = a_at(k);
+    if (B2 == B2_NHALF) {
+      acc = fmaf(a, b_at(B0, k, n), acc);
+      acc2 = fmaf(a, b_at(B1, k, n), acc2);
+    } else if (B2 == B2_KSPLIT) {
+      acc = fmaf(a, k < p.k_split ? b_at(B0, k, n) : b_at(B1, k - p.k_split, n), acc);
+    } else {
+      acc = fmaf(a, b_at(B0, k, n), acc);
+    }
+  }
+  if constexpr (EPI == EPI_STORE) {
+    float* C = static_cast<float*>(p.C0);
+    int nn = n;
+    if (p.n_split > 0 && nn >= p.n_split) { C = static_cast<float*>(p.C1); nn -= p.n_split; }
+    if (GMD == G_KROWS) C += (int64_t)e * p.c_estride;
+    C[(int64_t)m * p.ldc + nn] = acc;
+  } else if constexpr (EPI == EPI_ACCUM) {
+    static_cast<float*>(p.C0)[(int64_t)m * p.ldc + n] += acc;
+  } else if constexpr (EPI == EPI_F32_BIAS) {
+    static_cast<float*>(p.C0)[(int64_t)m * p.ldc + n] = acc + (p.bias ? p.bias[n] : 0.f);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int64_t I = p.I;
+    float* H = static_cast<float*>(p.C0);
+    if (H) { H[m * 2 * I + n] = acc; H[m * 2 * I + I + n] = acc2; }
+    static_cast<float*>(p.C2)[m * I + n] = acc / (1.0f + expf(-acc)) * acc2;
+  } else if constexpr (EPI == EPI_DSWIGLU) {
+    const int64_t I = p.I;
+    const float* H = static_cast<const float*>(p.aux);
+    float g = H[m * 2 * I + n], u = H[m * 2 * I + I + n];
+    float sg = 1.0f / (1.0f + expf(-g));
+    float* dH = static_cast<float*>(p.C0);
+    dH[m * 2 * I + n] = acc * u * sg * (1.0f + g * (1.0f - sg));
+    dH[m * 2 * I + I + n] = acc * g * sg;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile table for row-grouped GEMMs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups, int bm,
+                                                          int32_t* tiles) {
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < groups; base += 1024) {
+    int e = base + threadIdx.x;
+    int cnt = 0, o = 0;
+    if (e < groups) {
+      o = off[e];
+      cnt = (off[e + 1] - o + bm - 1) / bm;
+    }
+    scan[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int s = 1; s < 1024; s <<= 1) {  // inclusive Hillis-Steele scan
+      int v = threadIdx.x >= s ? scan[threadIdx.x - s] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int first = carry + scan[threadIdx.x] - cnt;
+    for (int t = 0; t < cnt; ++t) {
+      tiles[1 + 2 * (first + t)] = e;
+      tiles[2 + 2 * (first + t)] = o + t * bm;
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += scan[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tiles[0] = carry;
+}
+
+moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* tiles,
+                               hipStream_t s) {
+  ProfScope prof("tile_table", s);
+  tile_table_kernel<<<1, 1024, 0, s>>>(off, groups, bm, tiles);
+  return check_launch("tile_table_kernel");
+}
+
+int tile_bm(TileCfg cfg) { return cfg == TILE_256x128 ? 256 : 64; }
+int tile_bn(TileCfg cfg) { return cfg == TILE_256x128 ? 128 : 64; }
+
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+#define MOE_KEY(am, bm, gm, b2, epi) ((am) | ((bm) << 1) | ((gm) << 2) | ((b2) << 4) | ((epi) << 6))
+
+template <int BMt, int BNt, int AM, int BMD, int GMD, int B2, int EPI>
+static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
+  gemm_bf16_kernel<BMt, BNt, 2, 2, AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
+}
+
+template <int AM, int BMD, int GMD, int B2, int EPI>
+static void launch_f32(const GemmParams& p, int max_rows, hipStream_t s) {
+  int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? p.I : p.N;
+  dim3 grid((unsigned)ceil_div(ncols, 16), (unsigned)ceil_div(max_rows, 16),
+            GMD == G_KROWS ? (unsigned)p.groups : 1u);
+  gemm_f32_kernel<AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
+}
+
+moe_status_t launch_gemm(bool is_bf16, int am, int bmd, int gmd, int b2, int epi, TileCfg cfg,
+                         const GemmParams& p, int max_m_tiles, hipStream_t s, const char* name) {
+  const int key = MOE_KEY(am, bmd, gmd, b2, epi);
+  ProfScope prof(name, s);
+  if (!is_bf16) {
+    // rows to cover: G_MROWS row capacity (max_m_tiles is then the row count), else M
+    int rows = (gmd == G_MROWS) ? max_m_tiles : p.M;
+    if (rows <= 0) return MOE_OK;
+    switch (key) {
+#define F32CASE(a, b, g, t, e) \
+  case MOE_KEY(a, b, g, t, e): launch_f32<a, b, g, t, e>(p, rows, s); break;
+      F32CASE(A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)
+      F32CASE(A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU)
+      F32CASE(A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)
+      F32CASE(A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU)
+      F32CASE(A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE)
+      F32CASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
+      F32CASE(A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
+#undef F32CASE
+      default:
+        set_error("internal: no fp32 GEMM variant for key %d (%s)", key, name);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    return check_launch(name);
+  }
+  int tiles_per_group = max_m_tiles * p.n_tiles;
+  int64_t grid = (gmd == G_KROWS) ? (int64_t)tiles_per_group * p.groups : tiles_per_group;
+  if (grid <= 0) return MOE_OK;
+  if (grid > 0x7fffffff) {
+    set_error("GEMM %s: grid too large", name);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (cfg == TILE_256x128) {
+    switch (key) {
+#define BFCASE(a, b, g, t, e) \
+  case MOE_KEY(a, b, g, t, e): launch_bf16<256, 128, a, b, g, t, e>(p, (int)grid, s); break;
+      BFCASE(A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU)
+      BFCASE(A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)
+      BFCASE(A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU)
+      BFCASE(A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE)
+      BFCASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
+#undef BFCASE
+      default:
+        set_error("internal: no bf16 256x128 GEMM variant for key %d (%s)", key, name);
+        return MOE_ERR_UNSUPPORTED;
+    }
+  } else {
+    switch (key) {
+#define BFCASE(a, b, g, t, e) \
+  case MOE_KEY(a, b, g, t, e): launch_bf16<64, 64, a, b, g, t, e>(p, (int)grid, s); break;
+      BFCASE(A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)
+      BFCASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
+      BFCASE(A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
+#undef BFCASE
+      default:
+        set_error("internal: no bf16 64x64 GEMM variant for key %d (%s)", key, name);
+        return MOE_ERR_UNSUPPORTED;
+    }
+  }
+  return check_launch(name);
+}
+
+}  // namespace moe

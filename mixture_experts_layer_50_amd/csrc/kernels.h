@@ -1,0 +1,34 @@
+// Launchers of the token-level kernels (gate, permutation, combine).  Each
+// enqueues on stream `s`, records itself in the kernel timer, and returns
+// MOE_OK or MOE_ERR_HIP.
+#pragma once
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+// route.hip
+moe_status_t launch_balanced_gate(int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
+moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                                 hipStream_t s);
+moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
+                                 int k, float* dl, bf16_t* dl_bf16, hipStream_t s);
+moe_status_t launch_col_sum(const float* dl, int T, int E, float* db, hipStream_t s);
+moe_status_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+// permute.hip
+constexpr int PERM_TOKENS = 256;  // tokens per block of the counting sort
+int64_t permute_ws_bytes(int T, int E_loc);
+moe_status_t launch_permute(const int32_t* idx, const void* x, int T, int d, int k, int e_lo,
+                            int e_hi, int R_cap, int elt_bytes, int32_t* offsets, int32_t* perm,
+                            int32_t* inv, void* xp, void* ws, hipStream_t s);
+// y[t] = sum_j w[t,j] * src[inv[t*k+j]] (w == NULL: weight 1), fp32 accumulation.
+moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float* w, int T, int d,
+                               int k, int elt_bytes, void* y, hipStream_t s, const char* name);
+moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv, const float* w,
+                                int T, int d, int k, int elt_bytes, void* dyp, float* dw,
+                                hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,182 @@
+// Gate kernels of the MoE layer: balanced gate, wavefront top-k + softmax,
+// and the router backward (softmax Jacobian, bias column sums).
+//
+// Routing tokens over many experts is the first problem the page "Accelerating
+// Transformers fine-tuning with NVIDIA NeMo AutoModel" lists (section 背景);
+// its balanced gate (section 单节点30B MoE基准测试, routing-gate note) forces
+// tokens evenly over the experts.  The gate function itself is not on the
+// pages: top-k by logit (ties toward the lower expert id) with softmax over
+// the k selected logits.
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- balanced
+__global__ void balanced_gate_kernel(int T, int E, int k, int32_t* idx, float* w) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * k) return;
+  int t = (int)(i / k), j = (int)(i - (int64_t)t * k);
+  int P = E / k;
+  idx[i] = (t % P) + j * P;
+  w[i] = 1.0f / (float)k;
+}
+
+moe_status_t launch_balanced_gate(int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
+  ProfScope prof("route_balanced", s);
+  int64_t n = (int64_t)T * k;
+  balanced_gate_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(T, E, k, idx, w);
+  return check_launch("balanced_gate_kernel");
+}
+
+// ---------------------------------------------------------------- top-k
+// One wavefront per token.  Lane l holds the logits of experts l + 64 v.
+// k rounds: every lane proposes its best untaken expert, a butterfly over the
+// wavefront keeps the larger logit (the lower id on equal logits), the owner
+// marks it taken.  Lane j keeps the j-th winner; softmax over lanes < k.
+__device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
+  return v > bv || (v == bv && id < bid);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* logits, int T, int E, int k,
+                                                           int32_t* idx, float* w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  float v[VPL];
+  bool taken[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) {
+    int e = lane + 64 * q;
+    v[q] = e < E ? row[e] : -INFINITY;
+    taken[q] = e >= E;
+  }
+  float my_v = -INFINITY;
+  int my_id = 0x7fffffff;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      int e = lane + 64 * q;
+      if (!taken[q] && better(v[q], e, bv, bid)) { bv = v[q]; bid = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off, 64);
+      int oid = __shfl_xor(bid, off, 64);
+      if (better(ov, oid, bv, bid)) { bv = ov; bid = oid; }
+    }
+#pragma unroll
+    for (int q = 0; q < VPL; ++q)
+      if (lane + 64 * q == bid) taken[q] = true;
+    if (lane == j) { my_v = bv; my_id = bid; }
+  }
+  const float vmax = __shfl(my_v, 0, 64);
+  float z = lane < k ? expf(my_v - vmax) : 0.f;
+  float sum = z;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane < k) {
+    idx[(int64_t)t * k + lane] = my_id;
+    w[(int64_t)t * k + lane] = z / sum;
+  }
+}
+
+moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                                 hipStream_t s) {
+  ProfScope prof("route_topk", s);
+  unsigned grid = (unsigned)ceil_div(T, 4);
+  if (E <= 64) topk_softmax_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  else if (E <= 128) topk_softmax_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  else if (E <= 256) topk_softmax_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  else topk_softmax_kernel<8><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
+  return check_launch("topk_softmax_kernel");
+}
+
+// ---------------------------------------------------------------- backward
+// dL[t, idx[t,j]] = g_j (dg_j - sum_i g_i dg_i); all other logits get 0.
+// One wavefront per token; lane l writes experts l + 64 v.  The optional bf16
+// copy feeds the bf16 router-gradient GEMMs.
+__global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, const float* g,
+                                                           const float* dg, int T, int E, int k,
+                                                           float* dl, bf16_t* dl_bf16) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float gj = 0.f, dgj = 0.f;
+  int ij = -1;
+  if (lane < k) {
+    gj = g[(int64_t)t * k + lane];
+    dgj = dg[(int64_t)t * k + lane];
+    ij = idx[(int64_t)t * k + lane];
+  }
+  float s = gj * dgj;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  const float val = gj * (dgj - s);
+  for (int base = 0; base < E; base += 64) {
+    int e = base + lane;
+    float out = 0.f;
+    for (int j = 0; j < k; ++j) {
+      int ej = __shfl(ij, j, 64);
+      float vj = __shfl(val, j, 64);
+      if (ej == e) out = vj;
+    }
+    if (e < E) {
+      dl[(int64_t)t * E + e] = out;
+      if (dl_bf16) dl_bf16[(int64_t)t * E + e] = f2bf(out);
+    }
+  }
+}
+
+// db[e] = sum_t dL[t,e]: 4 fixed row strides per column, combined in order.
+__global__ __launch_bounds__(256) void col_sum_kernel(const float* dl, int T, int E, float* db) {
+  __shared__ float part[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int s = threadIdx.x >> 6;
+  float acc = 0.f;
+  if (c < E)
+    for (int t = s; t < T; t += 4) acc += dl[(int64_t)t * E + c];
+  part[s][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (s == 0 && c < E) {
+    float v = part[0][threadIdx.x];
+    v += part[1][threadIdx.x];
+    v += part[2][threadIdx.x];
+    v += part[3][threadIdx.x];
+    db[c] = v;
+  }
+}
+
+moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
+                                 int k, float* dl, bf16_t* dl_bf16, hipStream_t s) {
+  ProfScope prof("route_bwd_dlogits", s);
+  route_bwd_dl_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16);
+  return check_launch("route_bwd_dl_kernel");
+}
+
+moe_status_t launch_col_sum(const float* dl, int T, int E, float* db, hipStream_t s) {
+  ProfScope prof("route_bwd_dbias", s);
+  col_sum_kernel<<<(unsigned)ceil_div(E, 64), 256, 0, s>>>(dl, T, E, db);
+  return check_launch("col_sum_kernel");
+}
+
+// ---------------------------------------------------------------- fill
+__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = 0u;
+}
+
+moe_status_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
+  if (bytes <= 0) return MOE_OK;
+  ProfScope prof("fill_zero", s);
+  int64_t words = bytes / 4;  // every buffer here is a multiple of 4 bytes
+  unsigned grid = (unsigned)std::min<int64_t>(ceil_div(words, 256), 4096);
+  fill_zero_kernel<<<grid, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+  return check_launch("fill_zero_kernel");
+}
+
+}  // namespace moe

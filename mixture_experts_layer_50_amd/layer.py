@@ -1,0 +1,94 @@
+"""Device buffers for one MoE layer and the order of C-ABI calls of a
+forward and a backward pass.  Plumbing only: torch allocates device memory,
+every step runs in libmoe.so."""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import torch
+
+from . import binding as B
+
+
+def torch_dtype(shape: B.MoEShape):
+    return torch.bfloat16 if shape.dtype == B.DTYPES["bf16"] else torch.float32
+
+
+@dataclass
+class LayerBuffers:
+    """Every intermediate and gradient buffer of the layer, sized for the
+    row capacity R_cap (T*k unless the shape says otherwise)."""
+    shape: B.MoEShape
+    device: str = "cuda"
+    training: bool = True
+    t: Dict[str, torch.Tensor] = field(default_factory=dict)
+
+    def __post_init__(self):
+        s, dev = self.shape, self.device
+        dt = torch_dtype(s)
+        R, T, d, E, k, I, El = s.rows_cap, s.T, s.d, s.E, s.k, s.I, s.E_loc
+        f32, i32 = torch.float32, torch.int32
+
+        def e(*shp, dtype=dt):
+            return torch.empty(shp, dtype=dtype, device=dev)
+
+        t = self.t
+        t["logits"] = e(T, E, dtype=f32)
+        t["topk_idx"] = e(T, k, dtype=i32)
+        t["topk_w"] = e(T, k, dtype=f32)
+        t["offsets"] = e(El + 1, dtype=i32)
+        t["perm"] = e(R, dtype=i32)
+        t["inv"] = e(T * k, dtype=i32)
+        t["xp"] = e(R, d)
+        t["h"] = e(R, 2 * I) if self.training else None
+        t["a"] = e(R, I)
+        t["yp"] = e(R, d)
+        t["y"] = e(T, d)
+        for op in ("permute", "ffn_fwd"):
+            t["ws_" + op] = self._ws(op)
+        if self.training:
+            t["dyp"] = e(R, d)
+            t["dtopk_w"] = e(T, k, dtype=f32)
+            t["dxp"] = e(R, d)
+            t["dw_gate"] = e(El, d, I)
+            t["dw_up"] = e(El, d, I)
+            t["dw_down"] = e(El, I, d)
+            t["dx"] = e(T, d)
+            t["dlogits"] = e(T, E, dtype=f32)
+            t["dw_router"] = e(d, E)
+            t["dbias"] = e(E, dtype=f32)
+            for op in ("ffn_bwd", "route_bwd"):
+                t["ws_" + op] = self._ws(op)
+
+    def _ws(self, op) -> Optional[torch.Tensor]:
+        n = B.workspace_size(self.shape, op)
+        return torch.empty(n, dtype=torch.uint8, device=self.device) if n else None
+
+    def __getitem__(self, k):
+        return self.t[k]
+
+
+def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
+            stream=None):
+    """route -> permute -> grouped SwiGLU FFN -> combine; y lands in buf['y']."""
+    t = buf.t
+    B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
+    B.moe_permute(shape, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"],
+                  t["ws_permute"], stream)
+    B.moe_grouped_ffn_fwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
+                          t["yp"], t["ws_ffn_fwd"], stream)
+    B.moe_combine(shape, t["yp"], t["inv"], t["topk_w"], t["y"], stream)
+
+
+def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up, w_down,
+             stream=None):
+    """combine_bwd -> grouped FFN bwd -> permute_bwd -> route_bwd."""
+    t = buf.t
+    B.moe_combine_bwd(shape, dy, t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"], stream)
+    B.moe_grouped_ffn_bwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
+                          t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"],
+                          t["ws_ffn_bwd"], stream)
+    B.moe_permute_bwd(shape, t["dxp"], t["inv"], t["dx"], stream)
+    B.moe_route_bwd(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"], t["dlogits"],
+                    t["dw_router"], t["dbias"], t["dx"], t["ws_route_bwd"], stream)

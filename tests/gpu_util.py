@@ -1,0 +1,190 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the layer through
+the C ABI, and compare with the CPU oracle (fully, or on sampled rows)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_inputs as MI
+from mixture_experts_layer_50_amd import binding as B
+from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward
+from oracle import moe_oracle as O
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def shape_of(w: MI.Workload, R_cap=0) -> B.MoEShape:
+    return B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate, e_lo=w.e_lo,
+                           e_hi=w.e_end, R_cap=R_cap)
+
+
+def upload(w: MI.Workload, arrays):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = {}
+    for k, a in arrays.items():
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        dev[k] = (t if k == "b" else t.to(dt)).cuda()
+    return dev
+
+
+def run_layer(w: MI.Workload, dev, R_cap=0, training=True, poison=False):
+    s = shape_of(w, R_cap)
+    buf = LayerBuffers(s, training=training)
+    if poison:
+        for v in buf.t.values():
+            if v is not None and v.is_floating_point():
+                v.fill_(float("nan"))
+            elif v is not None and v.dtype == torch.int32:
+                v.fill_(-7)
+    forward(s, buf, dev["x"], dev.get("Wr"), dev.get("b"), dev["Wg"], dev["Wu"], dev["Wd"])
+    if training:
+        backward(s, buf, dev["dY"], dev["x"], dev.get("Wr"), dev["Wg"], dev["Wu"], dev["Wd"])
+    torch.cuda.synchronize()
+    return s, buf
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def relerr(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    scale = np.abs(ref).max() if ref.size else 0.0
+    err = np.abs(got - ref).max() if ref.size else 0.0
+    if not np.isfinite(err):
+        return np.inf
+    return err / scale if scale > 0 else err
+
+
+def check(name, got, ref, tol):
+    e = relerr(got, ref)
+    assert e <= tol, f"{name}: max|err|/max|ref| = {e:.3e} > {tol:.1e}"
+    return e
+
+
+def oracle_full(w: MI.Workload, a, R_cap=None):
+    f = O.layer_fwd(a["x"], a["Wr"], a.get("b"), a["Wg"], a["Wu"], a["Wd"], w.k, w.gate, w.E,
+                    w.e_lo, w.e_end, R_cap)
+    bw = O.layer_bwd(f, a["dY"], a["x"], a["Wr"], a["Wg"], a["Wu"], a["Wd"], w.k, w.gate) \
+        if "dY" in a else None
+    return f, bw
+
+
+def compare_full(w: MI.Workload, a, buf, f, bw):
+    """Element-by-element comparison of every output with the oracle."""
+    tol = TOL[w.dtype]
+    t = buf.t
+    R = int(f["offsets"][-1])
+    out = {}
+    if w.gate == "softmax_topk":
+        out["logits"] = check("logits", np64(t["logits"]), f["logits"], 1e-5)
+    assert np.array_equal(t["topk_idx"].cpu().numpy(), f["idx"]), "topk_idx differs"
+    out["topk_w"] = check("topk_w", np64(t["topk_w"]), f["g"], 1e-5)
+    assert np.array_equal(t["offsets"].cpu().numpy(), f["offsets"]), "group offsets differ"
+    assert np.array_equal(t["perm"][:R].cpu().numpy(), f["perm"]), "perm differs"
+    assert np.array_equal(t["inv"].cpu().numpy(), f["inv"]), "inv differs"
+    assert np.array_equal(np64(t["xp"][:R]), f["Xp"]), "xp is not an exact copy"
+    if t["h"] is not None:
+        out["h"] = check("h", np64(t["h"][:R]), np.concatenate([f["Hg"], f["Hu"]], 1), tol)
+    out["a"] = check("a", np64(t["a"][:R]), f["A"], tol)
+    out["yp"] = check("yp", np64(t["yp"][:R]), f["Yp"], tol)
+    out["y"] = check("y", np64(t["y"]), f["y"], tol)
+    if bw is None:
+        return out
+    out["dyp"] = check("dyp", np64(t["dyp"][:R]), bw["dYp"], tol)
+    out["dtopk_w"] = check("dtopk_w", np64(t["dtopk_w"]), bw["dG"], tol)
+    out["dxp"] = check("dxp", np64(t["dxp"][:R]), bw["dXp"], tol)
+    for gname, oname in (("dw_gate", "dWg"), ("dw_up", "dWu"), ("dw_down", "dWd")):
+        g = np64(t[gname])
+        out[gname] = check(gname, g, bw[oname], tol)
+        for e in range(w.E_loc):
+            check(f"{gname}[{e}]", g[e], bw[oname][e], tol)
+            if f["counts"][e] == 0:
+                assert not g[e].any(), f"{gname}[{e}] of an empty expert is not exactly 0"
+    out["dx"] = check("dx", np64(t["dx"]), bw["dX"], tol)
+    if w.gate == "softmax_topk":
+        out["dlogits"] = check("dlogits", np64(t["dlogits"]), bw["dL"], tol)
+        out["dw_router"] = check("dw_router", np64(t["dw_router"]), bw["dWr"], tol)
+        out["dbias"] = check("dbias", np64(t["dbias"]), bw["db"], tol)
+    else:
+        assert not t["dw_router"].float().abs().max().item()
+        assert not t["dlogits"].abs().max().item()
+    return out
+
+
+def subset_rows(f, tokens, k):
+    """Sorted positions of the sampled tokens' slots and the compact inverse map."""
+    inv = f["inv"].reshape(-1, k)[tokens]
+    rows = np.unique(inv[inv >= 0])
+    pos = {int(p): i for i, p in enumerate(rows)}
+    inv_sub = np.array([[pos[int(p)] if p >= 0 else -1 for p in r] for r in inv])
+    E_loc = len(f["offsets"]) - 1
+    sub_off = np.searchsorted(rows, f["offsets"]).astype(np.int64)
+    sub_off[-1] = len(rows)
+    assert len(sub_off) == E_loc + 1
+    return rows, inv_sub, sub_off
+
+
+def compare_sampled(w: MI.Workload, a, buf, tokens, experts, route_full=True):
+    """Full-size check on sampled tokens (every row they touch) and on the
+    weight gradients of sampled experts (every row of those experts)."""
+    tol = TOL[w.dtype]
+    t = buf.t
+    x = a["x"]
+    L, idx, g = O.route(x, a.get("Wr"), a.get("b"), w.k, w.gate)
+    p = O.permute(idx, None, w.E, w.e_lo, w.e_end)
+    f = dict(offsets=p["offsets"], inv=p["inv"], perm=p["perm"], counts=p["counts"])
+    R = int(p["offsets"][-1])
+    # routing and permutation: whole arrays, exact
+    assert np.array_equal(t["topk_idx"].cpu().numpy(), idx), "topk_idx differs"
+    check("topk_w", np64(t["topk_w"]), g, 1e-5)
+    if L is not None:
+        check("logits", np64(t["logits"]), L, 1e-5)
+    assert np.array_equal(t["offsets"].cpu().numpy(), p["offsets"])
+    assert np.array_equal(t["perm"][:R].cpu().numpy(), p["perm"])
+    assert np.array_equal(t["inv"].cpu().numpy(), p["inv"])
+    # sampled tokens: every row they touch
+    rows, inv_sub, sub_off = subset_rows(f, tokens, w.k)
+    Xp = x[p["perm"][rows] // w.k].astype(np.float64)
+    assert np.array_equal(np64(t["xp"][torch.from_numpy(rows).cuda()]), Xp)
+    ff = O.expert_ffn_fwd(Xp, sub_off, a["Wg"], a["Wu"], a["Wd"])
+    rsel = torch.from_numpy(rows).cuda()
+    if t["h"] is not None:
+        check("h(rows)", np64(t["h"][rsel]), np.concatenate([ff["Hg"], ff["Hu"]], 1), tol)
+    check("a(rows)", np64(t["a"][rsel]), ff["A"], tol)
+    check("yp(rows)", np64(t["yp"][rsel]), ff["Yp"], tol)
+    gs = g[tokens]
+    y = O.combine(ff["Yp"], inv_sub, gs, len(tokens), w.k)
+    tsel = torch.from_numpy(np.asarray(tokens)).cuda()
+    check("y(tokens)", np64(t["y"][tsel]), y, tol)
+    if "dY" not in a:
+        return
+    dYp, dG = O.combine_bwd(a["dY"][tokens], ff["Yp"], inv_sub, gs, len(tokens), w.k)
+    check("dyp(rows)", np64(t["dyp"][rsel]), dYp, tol)
+    check("dtopk_w(tokens)", np64(t["dtopk_w"][tsel]), dG, tol)
+    fb = O.expert_ffn_bwd(Xp, sub_off, a["Wg"], a["Wu"], a["Wd"], ff["Hg"], ff["Hu"], ff["A"], dYp)
+    check("dxp(rows)", np64(t["dxp"][rsel]), fb["dXp"], tol)
+    dX = O.permute_bwd(fb["dXp"], inv_sub, len(tokens), w.k)
+    if w.gate == "softmax_topk":
+        rb = O.route_bwd(x[tokens], a["Wr"], idx[tokens], gs, dG, w.gate)
+        dX = dX + rb["dX"]
+        check("dlogits(tokens)", np64(t["dlogits"][tsel]), rb["dL"], tol)
+    check("dx(tokens)", np64(t["dx"][tsel]), dX, tol)
+    # sampled experts: every row of the expert
+    for e in experts:
+        s0, s1 = int(p["offsets"][e]), int(p["offsets"][e + 1])
+        rr = p["perm"][s0:s1]
+        tok, slot = rr // w.k, rr % w.k
+        Xe = x[tok].astype(np.float64)
+        one = np.array([0, s1 - s0])
+        Wg, Wu, Wd = a["Wg"][e:e + 1], a["Wu"][e:e + 1], a["Wd"][e:e + 1]
+        fe = O.expert_ffn_fwd(Xe, one, Wg, Wu, Wd)
+        dYe = g[tok, slot][:, None] * a["dY"][tok].astype(np.float64)
+        be = O.expert_ffn_bwd(Xe, one, Wg, Wu, Wd, fe["Hg"], fe["Hu"], fe["A"], dYe)
+        for gname, oname in (("dw_gate", "dWg"), ("dw_up", "dWu"), ("dw_down", "dWd")):
+            got = np64(t[gname][e])
+            check(f"{gname}[{e}]", got, be[oname][0], tol)
+            if s1 == s0:
+                assert not got.any()

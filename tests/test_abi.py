@@ -1,0 +1,146 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments before anything reaches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixture_experts_layer_50_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        from mixture_experts_layer_50_amd.build import build
+        build()
+    return B.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code, name in B.STATUS.items():
+        assert lib.moe_status_string(code).decode() == name
+    assert b"gfx950" in lib.moe_version()
+
+
+FAKE = 1 << 20   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def shape(**kw):
+    base = dict(T=64, d=128, E=8, k=2, I=256, dtype="bf16", gate="softmax_topk")
+    base.update(kw)
+    return B.MoEShape.make(**base)
+
+
+def call_route(lib, s, **ptrs):
+    p = dict(x=FAKE, w=FAKE, b=None, logits=FAKE, idx=FAKE, g=FAKE)
+    p.update(ptrs)
+    st = lib.moe_route(ctypes.byref(s) if s is not None else None, p["x"], p["w"], p["b"],
+                       p["logits"], p["idx"], p["g"], None)
+    return B.STATUS[st], lib.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(k=9), "MOE_ERR_ARG", "k=9 > E=8"),
+    (dict(T=0), "MOE_ERR_SHAPE", "positive"),
+    (dict(dtype=7), "MOE_ERR_DTYPE", "dtype"),
+    (dict(gate=5), "MOE_ERR_ARG", "gate"),
+    (dict(d=96), "MOE_ERR_UNSUPPORTED", "multiples of 64"),
+    (dict(I=100), "MOE_ERR_UNSUPPORTED", "multiples of 64"),
+    (dict(E=12, k=2), "MOE_ERR_UNSUPPORTED", "E % 8"),
+    (dict(E=1024, k=2), "MOE_ERR_UNSUPPORTED", "E > 512"),
+    (dict(E=64, k=33), "MOE_ERR_UNSUPPORTED", "k > 32"),
+    (dict(e_lo=4, e_hi=2), "MOE_ERR_ARG", "local experts"),
+    (dict(e_lo=0, e_hi=9), "MOE_ERR_ARG", "local experts"),
+    (dict(R_cap=129), "MOE_ERR_SHAPE", "R_cap"),
+    (dict(E=8, k=3, gate="balanced"), "MOE_ERR_ARG", "k | E"),
+    (dict(T=1 << 28, k=8), "MOE_ERR_SHAPE", "overflows"),
+])
+def test_route_rejects_bad_shapes(lib, kw, status, text):
+    st, msg = call_route(lib, shape(**kw))
+    assert st == status, msg
+    assert text in msg
+
+
+def test_null_and_misaligned_pointers(lib):
+    st, msg = call_route(lib, None)
+    assert st == "MOE_ERR_ARG" and "shape is NULL" in msg
+    st, msg = call_route(lib, shape(), logits=None)
+    assert st == "MOE_ERR_ARG" and "logits is NULL" in msg
+    st, msg = call_route(lib, shape(), x=FAKE + 2)
+    assert st == "MOE_ERR_UNSUPPORTED" and "aligned" in msg
+    st, msg = call_route(lib, shape(), b=FAKE + 8)
+    assert st == "MOE_ERR_UNSUPPORTED" and "bias" in msg
+
+
+def test_workspace_sizes_and_short_workspace(lib):
+    s = shape(T=4096, d=2048, E=128, k=8, I=768, gate="balanced")
+    R = 4096 * 8
+    assert B.workspace_size(s, "route") == 0
+    assert B.workspace_size(s, "combine") == 0
+    assert B.workspace_size(s, "permute") == 16 * 128 * 4          # 16 blocks of 256 tokens
+    tiles = (1 + 2 * (R // 256 + 128)) * 4
+    assert B.workspace_size(s, "ffn_fwd") == -(-tiles // 256) * 256
+    assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + -(-tiles // 256) * 256
+    assert B.workspace_size(s, "route_bwd") == 0                    # balanced gate: no dL copy
+    n = B.workspace_size(shape(T=4096, d=2048, E=128, k=8, I=768), "route_bwd")
+    assert n == 4096 * 128 * 2
+    with pytest.raises(B.MoEError) as ei:
+        B.workspace_size(s, 99)
+    assert ei.value.status_name == "MOE_ERR_ARG"
+    st = lib.moe_permute(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None)
+    assert B.STATUS[st] == "MOE_ERR_WORKSPACE"
+    assert "workspace" in lib.moe_last_error().decode()
+
+
+def test_every_entry_point_validates_before_launch(lib):
+    s = shape(k=9)   # invalid: k > E
+    P = FAKE
+    calls = [
+        lambda: lib.moe_permute(ctypes.byref(s), P, P, P, P, P, P, P, 1 << 20, None),
+        lambda: lib.moe_grouped_ffn_fwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, 1 << 20, None),
+        lambda: lib.moe_combine(ctypes.byref(s), P, P, P, P, None),
+        lambda: lib.moe_combine_bwd(ctypes.byref(s), P, P, P, P, P, P, None),
+        lambda: lib.moe_grouped_ffn_bwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                        1 << 30, None),
+        lambda: lib.moe_permute_bwd(ctypes.byref(s), P, P, P, None),
+        lambda: lib.moe_route_bwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, 1 << 20, None),
+    ]
+    for c in calls:
+        assert B.STATUS[c()] == "MOE_ERR_ARG"
+    good = shape()
+    st = lib.moe_grouped_ffn_fwd(ctypes.byref(good), P, P, P, P, P, None, None, P, P, 1 << 20, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "a_save" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_ffn_bwd(ctypes.byref(good), P, P, P, P, P, None, P, P, P, P, P, P, P,
+                                 1 << 30, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "h_save" in lib.moe_last_error().decode()
+
+
+def test_profiler_api_without_gpu(lib):
+    B.prof_enable(False)
+    B.prof_reset()
+    assert B.prof_read("ffn_gateup_fwd") == (0.0, 0)
+    assert B.prof_names() == []
