@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 math.
-FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
+FLAGS = ["-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -1,16 +1,18 @@
 // Grouped GEMM kernels of the MoE layer for gfx950.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 (fp32 accumulation) on LDS-staged
-// 64-deep K slices, double-buffered (the next slice is fetched from HBM into
-// registers while the current one is multiplied), four waves per workgroup.
-// Both operands sit in LDS k-contiguous, 16-byte chunks XOR-swizzled by row;
-// operands that are stored with k strided in memory are loaded as 8x8 blocks
-// and transposed in registers before the LDS write.  Workgroup ids are remapped
+// 64-deep K slices in two LDS buffers, with several further slices in flight
+// in registers, four waves per workgroup.  Operands stored k-contiguous sit in
+// LDS the same way (16-byte chunks XOR-swizzled by row); operands stored
+// n-contiguous (weights [K][N], activations read transposed) are copied as is
+// and read back with the gfx950 LDS transpose read.  Workgroup ids are remapped
 // so that consecutive tiles land on the same XCD (its own L2), and tiles that
 // share an A row block or a weight column block run together (GROUP_M order).
 //
 // fp32 path: a plain fp32 kernel (one output per thread, fp32 FMA) used for
 // fp32 layers, which are small parity workloads.
+#include <utility>
+
 #include "gemm.h"
 
 namespace moe {
@@ -47,51 +49,74 @@ __device__ __forceinline__ void group_order(int L, int mt_count, int nt_count, i
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// 8x8 transpose of 16-bit elements: in[kk] holds 8 values along the row
-// dimension at depth kk; out[mm] holds the 8 depths of row mm.
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  const uint32_t* v = reinterpret_cast<const uint32_t*>(in);  // v[kk*4 + q]
-  uint32_t* w = reinterpret_cast<uint32_t*>(out);             // w[mm*4 + p]
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t lo = v[(2 * p) * 4 + q], hi = v[(2 * p + 1) * 4 + q];
-      w[(2 * q) * 4 + p] = (lo & 0xffffu) | (hi << 16);
-      w[(2 * q + 1) * 4 + p] = (lo >> 16) | (hi & 0xffff0000u);
-    }
-  }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts.  One K slice is 64 deep.
+//  k-contiguous operand ("KC"): [ROWS][64] bf16; 16-byte chunk c of row r sits
+//    at chunk swz(r, c).  A lane reads its 8 k values with one 16-byte read.
+//  k-major operand ("KN", stored n-contiguous in memory, e.g. a weight matrix
+//    [K][N]): copied as is into [64][COLS]; chunk c of row k sits at
+//    kn_swz(k, c).  A lane gathers 8 k values of one column with two
+//    ds_read_b64_tr_b16 reads: in each group of 16 lanes, lane 4r+q addresses
+//    row r, columns 4q..4q+3, and lane i receives column i of rows 0..3.
+// ---------------------------------------------------------------------------
+template <int COLS>
+__device__ __forceinline__ int kn_swz(int k, int c) {
+  return c ^ (((k & 3) << 2) & (COLS / 8 - 1));
 }
 
-// ---------------------------------------------------------------------------
-// Tile loaders.  A tile holds ROWS rows x 64 k of one operand, stored in LDS
-// as [ROWS][64] bf16, k-contiguous, chunk-swizzled.
-// ---------------------------------------------------------------------------
+// Buffer loads: the hardware returns zeros for a byte offset past num_records,
+// so masked lanes get offset OOB and no lane branches around a load.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int OOB = (int)0x80000000u;
 
-// Operand stored k-contiguous: row r of the tile is src[(row0 + r) * ld + k].
-// Two sources split along k (k < ksplit -> s0, else s1 at k - ksplit) when
-// TWO is set.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Loader of a KC tile: row r of the tile is src[(row0 + r) * ld + k], rows
+// r >= row_hi - row0 read as zeros.  With TWO, k < ksplit comes from s0 and
+// k >= ksplit from s1 at k - ksplit (ksplit is a multiple of 64, so one K
+// slice never straddles it).
 template <int ROWS, bool TWO>
 struct LoaderKC {
   static constexpr int CH = ROWS * 8;
   static constexpr int NR = (CH + 255) / 256;
   uint4 r[NR];
-  __device__ __forceinline__ void load(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
-                                       int row_hi, int k0, int k_hi, int ksplit, int tid) {
+  int voff[NR];
+  int kc[NR];
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  int ksplit, k_lo, k_hi;
+  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
+                                       int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid) {
+    rs0 = make_rsrc(s0 + (int64_t)row0 * ld);
+    rs1 = make_rsrc(TWO ? s1 + (int64_t)row0 * ld : s0);
+    ksplit = ksplit_;
+    k_lo = k_lo_;
+    k_hi = k_hi_;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       int q = tid + 256 * i;
-      r[i] = zero4();
-      if (CH % 256 == 0 || q < CH) {
-        int row = row0 + (q >> 3);
-        int k = k0 + (q & 7) * 8;
-        if (row < row_hi && k < k_hi) {
-          const bf16_t* src = s0;
-          if (TWO && k >= ksplit) { src = s1; k -= ksplit; }
-          r[i] = *reinterpret_cast<const uint4*>(src + (int64_t)row * ld + k);
-        }
-      }
+      int row = q >> 3;
+      kc[i] = (q & 7) * 8;
+      bool ok = (CH % 256 == 0 || q < CH) && row0 + row < row_hi;
+      voff[i] = ok ? (int)(((int64_t)row * ld + kc[i]) * 2) : OOB;
     }
+  }
+  // K slice starting at k_lo + kofs
+  __device__ __forceinline__ void load(int kofs) {
+    int k0 = k_lo + kofs;
+    __amdgpu_buffer_rsrc_t rs = rs0;
+    if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; }
+    const int lim = (TWO && k_lo + kofs >= ksplit) ? k_hi - ksplit - k0 : k_hi - k0;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) r[i] = buf_load16(rs, kc[i] < lim ? voff[i] : OOB, k0 * 2);
   }
   __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
 #pragma unroll
@@ -105,50 +130,58 @@ struct LoaderKC {
   }
 };
 
-// Operand stored with k as the row index: element (r, k) of the tile is
-// src[k * ld + col0 + r].  Loaded as 8x8 blocks, transposed in registers.
-// HALF: tile rows [0, ROWS/2) come from s0 at col0 + r, rows [ROWS/2, ROWS)
-// from s1 at col0 + r - ROWS/2 (the gate | up halves of one tile).
-template <int ROWS, bool HALF>
-struct LoaderT {
-  static constexpr int RB = ROWS / 8;
-  static constexpr int NB = RB * 8;
-  static constexpr int NR = (NB + 255) / 256;
-  uint4 r[NR][8];
-  __device__ __forceinline__ void load(const bf16_t* s0, const bf16_t* s1, int64_t ld, int col0,
-                                       int col_hi, int k0, int k_hi, int tid) {
+// Loader of a KN tile: element (k, c) of the tile is src[(k_lo + kofs + k) * ld
+// + col0 + c]; rows at or past k_hi and columns at or past col_hi read as
+// zeros.  HALF: tile columns [0, COLS/2) come from s0 at col0 + c, columns
+// [COLS/2, COLS) from s1 at col0 + c - COLS/2 (the gate | up halves); each
+// load instruction reads one half only, so its buffer descriptor is uniform.
+template <int COLS, bool HALF>
+struct LoaderKN {
+  static constexpr int CPR = HALF ? COLS / 16 : COLS / 8;  // chunks per row and source
+  static constexpr int CH = BK * CPR;                        // chunks per source
+  static constexpr int NS = (CH + 255) / 256;                // loads per source
+  static constexpr int NR = HALF ? 2 * NS : NS;
+  uint4 r[NR];
+  int voff[NS];
+  int krow[NS];
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  int64_t ld;
+  int k_lo, k_hi;
+  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld_, int col0,
+                                       int col_hi, int k_lo_, int k_hi_, int, int tid) {
+    ld = ld_;
+    k_lo = k_lo_;
+    k_hi = k_hi_;
+    rs0 = make_rsrc(s0 + (int64_t)k_lo * ld + col0);
+    rs1 = make_rsrc((HALF ? s1 : s0) + (int64_t)k_lo * ld + col0);
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NS; ++i) {
       int q = tid + 256 * i;
-      if (NB % 256 == 0 || q < NB) {
-        int ib = q % RB, kb = q / RB;
-        int rr = ib * 8;
-        const bf16_t* src = s0;
-        if (HALF && rr >= ROWS / 2) { src = s1; rr -= ROWS / 2; }
-        int col = col0 + rr;
-        bool colok = col < col_hi;
+      krow[i] = q / CPR;
+      int col = (q % CPR) * 8;
+      bool ok = (CH % 256 == 0 || q < CH) && col0 + col < col_hi;
+      voff[i] = ok ? (int)(((int64_t)krow[i] * ld + col) * 2) : OOB;
+    }
+  }
+  __device__ __forceinline__ void load(int kofs) {
+    const int lim = k_hi - k_lo - kofs;
+    const int soff = (int)((int64_t)kofs * ld * 2);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          int k = k0 + kb * 8 + kk;
-          r[i][kk] = (colok && k < k_hi)
-                         ? *reinterpret_cast<const uint4*>(src + (int64_t)k * ld + col)
-                         : zero4();
-        }
-      }
+    for (int i = 0; i < NS; ++i) {
+      const int v = krow[i] < lim ? voff[i] : OOB;
+      r[i] = buf_load16(rs0, v, soff);
+      if (HALF) r[NS + i] = buf_load16(rs1, v, soff);
     }
   }
   __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      int q = tid + 256 * i;
-      if (NB % 256 == 0 || q < NB) {
-        int ib = q % RB, kb = q / RB;
-        uint4 w[8];
-        transpose8x8(r[i], w);
+    for (int h = 0; h < (HALF ? 2 : 1); ++h) {
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-          int row = ib * 8 + mm;
-          *reinterpret_cast<uint4*>(lds + row * BK + swz(row, kb) * 8) = w[mm];
+      for (int i = 0; i < NS; ++i) {
+        int q = tid + 256 * i;
+        if (CH % 256 == 0 || q < CH) {
+          int k = q / CPR, c = q % CPR + h * CPR;
+          *reinterpret_cast<uint4*>(lds + k * COLS + kn_swz<COLS>(k, c) * 8) = r[h * NS + i];
         }
       }
     }
@@ -157,12 +190,35 @@ struct LoaderT {
 
 template <bool KC, int ROWS, bool TWO> struct PickLoader;
 template <int ROWS, bool TWO> struct PickLoader<true, ROWS, TWO> { typedef LoaderKC<ROWS, TWO> type; };
-template <int ROWS, bool TWO> struct PickLoader<false, ROWS, TWO> { typedef LoaderT<ROWS, TWO> type; };
+template <int ROWS, bool TWO> struct PickLoader<false, ROWS, TWO> { typedef LoaderKN<ROWS, TWO> type; };
+
+// MFMA operand fragment (32 rows x 16 k): lane l holds row base + (l & 31),
+// k = 16 ks + 8 (l >> 5) + 0..7.
+__device__ __forceinline__ bf16x8 frag_kc(const bf16_t* lds, int base, int ks, int lane) {
+  const int row = base + (lane & 31);
+  const int c = ks * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(lds + row * BK + swz(row, c) * 8);
+}
+
+template <int COLS>
+__device__ __forceinline__ bf16x8 frag_kn(const bf16_t* lds, int base, int ks, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int col = base + ((g & 1) << 4) + ((j & 3) << 2);
+  const int k = ks * 16 + ((g >> 1) << 3) + (j >> 2);
+  const int off = k * COLS + kn_swz<COLS>(k, col >> 3) * 8 + (col & 7);  // k+4: same swizzle
+  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off));
+  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off + 4 * COLS));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM
+// bf16 MFMA grouped GEMM.  P register stages: while the MFMAs work on K slice
+// kt from LDS, slice kt+1 is written to the other LDS buffer and the loads of
+// slices kt+2 .. kt+P are in flight.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int GMD, int B2, int EPI>
+template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -208,20 +264,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
   }
 
-  typename PickLoader<AM == A_KC, BM, false>::type la;
-  typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE>::type lb;
-
-  auto load_tiles = [&](int k0) {
-    if constexpr (AM == A_KC) la.load(A, A, p.lda, m_lo, m_hi, k0, k_hi, 0, tid);
-    else la.load(A, A, p.lda, m_lo, m_hi, k0, k_hi, tid);
-    if constexpr (BMD == B_KC) lb.load(B0, B1, p.ldb, n0, n_hi, k0, k_hi, p.k_split, tid);
-    else lb.load(B0, B1, p.ldb, n0, n_hi, k0, k_hi, tid);
-  };
-  auto store_tiles = [&](int buf) {
-    bf16_t* as = smem + buf * (BM + BN) * BK;
-    la.store(as, tid);
-    lb.store(as + BM * BK, tid);
-  };
+  typedef typename PickLoader<AM == A_KC, BM, false>::type LA;
+  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE>::type LB;
+  LA la[P];
+  LB lb[P];
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -232,30 +278,53 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (k_hi - k_lo + BK - 1) / BK;
-  if (nk > 0) {
-    load_tiles(k_lo);
-    store_tiles(0);
-    __syncthreads();
+  // per-lane address parts are the same for every slot; set them up once
+#pragma unroll
+  for (int s = 0; s < P; ++s) {
+    la[s].init(A, A, p.lda, m_lo, m_hi, k_lo, k_hi, 0, tid);
+    lb[s].init(B0, B1, p.ldb, n0, n_hi, k_lo, k_hi, p.k_split, tid);
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load_tiles(k_lo + (kt + 1) * BK);
+#pragma unroll
+  for (int s = 0; s < P; ++s) {
+    if (s < nk) {
+      la[s].load(s * BK);
+      lb[s].load(s * BK);
+    }
+  }
+  if (nk > 0) {
+    la[0].store(smem, tid);
+    lb[0].store(smem + BM * BK, tid);
+  }
+  __syncthreads();
+
+  // One K slice: refill the register slot of slice kt with slice kt+P, multiply
+  // slice kt from LDS, write slice kt+1 (loaded P-1 slices ago) to the other
+  // LDS buffer, barrier.  U = kt mod P is a compile-time constant.
+  auto step = [&](auto Uc, int kt, bool do_load, bool do_store) {
+    constexpr int U = decltype(Uc)::value;
+    if (do_load) {
+      la[U].load((kt + P) * BK);
+      lb[U].load((kt + P) * BK);
+    }
+    // keep the refill loads at the top of the step: the scheduler would
+    // otherwise sink them below the MFMAs and expose their latency
+    __builtin_amdgcn_sched_barrier(0);
     const bf16_t* as = smem + (kt & 1) * (BM + BN) * BK;
     const bf16_t* bs = as + BM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
       bf16x8 af[FM], bfg[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        int row = wm * WTM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + swz(row, c) * 8);
+        const int base = wm * WTM + i * 32;
+        if constexpr (AM == A_KC) af[i] = frag_kc(as, base, ks, lane);
+        else af[i] = frag_kn<BM>(as, base, ks, lane);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        int nb = (B2 == B2_NHALF) ? (j * (BN / 2) + wn * 32) : (wn * WTN + j * 32);
-        int row = nb + (lane & 31);
-        bfg[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + swz(row, c) * 8);
+        const int base = (B2 == B2_NHALF) ? (j * (BN / 2) + wn * 32) : (wn * WTN + j * 32);
+        if constexpr (BMD == B_KC) bfg[j] = frag_kc(bs, base, ks, lane);
+        else bfg[j] = frag_kn<BN>(bs, base, ks, lane);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -263,9 +332,29 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (more) store_tiles((kt + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_store) {
+      bf16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BK;
+      la[(U + 1) % P].store(nxt, tid);
+      lb[(U + 1) % P].store(nxt + BM * BK, tid);
+    }
     __syncthreads();
+  };
+
+  int kt0 = 0;
+  // steady state: every step loads and stores
+  for (; kt0 + 2 * P <= nk; kt0 += P) {
+    [&]<int... Us>(std::integer_sequence<int, Us...>) {
+      (step(std::integral_constant<int, Us>{}, kt0 + Us, true, true), ...);
+    }(std::make_integer_sequence<int, P>{});
   }
+  // drain: at most 2P-1 slices left
+  [&]<int... Us>(std::integer_sequence<int, Us...>) {
+    ((kt0 + Us < nk ? step(std::integral_constant<int, Us % P>{}, kt0 + Us, kt0 + Us + P < nk,
+                           kt0 + Us + 1 < nk)
+                    : void()),
+     ...);
+  }(std::make_integer_sequence<int, 2 * P - 1>{});
 
   // ---- epilogue.  Lane holds C[m][n..n+3] with m = row of the wave tile
   // (lane & 31), n = 8q + 4 (lane >> 5) within each 32-column block.
@@ -286,7 +375,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
         for (int s = 0; s < 4; ++s) {
           g[s] = acc[i][0][4 * q + s];
           u[s] = acc[i][1][4 * q + s];
-          a[s] = g[s] / (1.0f + expf(-g[s])) * u[s];
+          a[s] = g[s] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[s])) * u[s];
         }
         if (H) {
           *reinterpret_cast<uint2*>(H + m * 2 * I + n) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
@@ -336,7 +425,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
             float dg[4], du[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              float sg = 1.0f / (1.0f + expf(-g[s]));
+              float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[s]));
               dg[s] = v[s] * u[s] * sg * (1.0f + g[s] * (1.0f - sg));
               du[s] = v[s] * g[s] * sg;
             }
@@ -478,7 +567,11 @@ int tile_bn(TileCfg cfg) { return cfg == TILE_256x128 ? 128 : 64; }
 
 template <int BMt, int BNt, int AM, int BMD, int GMD, int B2, int EPI>
 static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
-  gemm_bf16_kernel<BMt, BNt, 2, 2, AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 3
+#endif
+  constexpr int P = (BMt >= 256) ? MOE_GEMM_STAGES : 2;  // register stages in flight
+  gemm_bf16_kernel<BMt, BNt, 2, 2, P, AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
 }
 
 template <int AM, int BMD, int GMD, int B2, int EPI>
