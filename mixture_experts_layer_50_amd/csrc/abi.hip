@@ -221,20 +221,63 @@ moe_status_t opt(const char* fn, std::initializer_list<std::pair<const char*, co
   return MOE_OK;
 }
 
-constexpr int BM_ROWS = 256;  // M tile of the row-grouped bf16 GEMMs
+// Tile shape of each bf16 expert GEMM.
+#ifndef MOE_TILE_GATEUP_FWD
+#define MOE_TILE_GATEUP_FWD TILE_256x256
+#endif
+#ifndef MOE_TILE_DOWN_FWD
+#define MOE_TILE_DOWN_FWD TILE_256x256
+#endif
+#ifndef MOE_TILE_DOWN_DGRAD
+#define MOE_TILE_DOWN_DGRAD TILE_256x128
+#endif
+#ifndef MOE_TILE_GATEUP_DGRAD
+#define MOE_TILE_GATEUP_DGRAD TILE_256x256
+#endif
+#ifndef MOE_WGRAD_TILE
+#define MOE_WGRAD_TILE TILE_128x128
+#endif
+constexpr TileCfg TILE_GATEUP_FWD = MOE_TILE_GATEUP_FWD;
+constexpr TileCfg TILE_DOWN_FWD = MOE_TILE_DOWN_FWD;
+constexpr TileCfg TILE_DOWN_DGRAD = MOE_TILE_DOWN_DGRAD;
+constexpr TileCfg TILE_GATEUP_DGRAD = MOE_TILE_GATEUP_DGRAD;
+constexpr TileCfg WGRAD_TILE = MOE_WGRAD_TILE;
 
-int64_t tile_table_bytes(const Dims& D) {
-  return (1 + 2 * ((int64_t)D.R_cap / BM_ROWS + D.E_loc)) * 4;
+// Tile tables of the row-grouped GEMMs: one for 256-row and one for 128-row
+// tiles, each (1 + 2 * (R_cap / BM + E_loc)) int32.
+int64_t one_table_bytes(const Dims& D, int bm) {
+  return round_up((1 + 2 * ((int64_t)D.R_cap / bm + D.E_loc)) * 4, 256);
 }
-int max_m_tiles(const Dims& D) { return D.R_cap / BM_ROWS + D.E_loc; }
+int64_t tile_table_bytes(const Dims& D) { return one_table_bytes(D, 256) + one_table_bytes(D, 128); }
+int max_m_tiles(const Dims& D, int bm) { return D.R_cap / bm + D.E_loc; }
+
+// Builds the tile tables a call needs, once each, in its workspace.
+struct TileTables {
+  const Dims& D;
+  int32_t* base;
+  const int32_t* off;
+  hipStream_t s;
+  bool built256 = false, built128 = false;
+  moe_status_t get(TileCfg cfg, const int32_t** out) {
+    const int bm = tile_bm(cfg);
+    int32_t* t = bm == 256 ? base : base + one_table_bytes(D, 256) / 4;
+    bool& built = bm == 256 ? built256 : built128;
+    if (!built) {
+      MOE_TRY(launch_tile_table(off, D.E_loc, bm, t, s));
+      built = true;
+    }
+    *out = t;
+    return MOE_OK;
+  }
+};
 
 int64_t ws_bytes(const Dims& D, int op) {
   switch (op) {
     case MOE_OP_PERMUTE: return round_up(permute_ws_bytes(D.T, D.E_loc), 256);
-    case MOE_OP_FFN_FWD: return D.bf16 ? round_up(tile_table_bytes(D), 256) : 0;
+    case MOE_OP_FFN_FWD: return D.bf16 ? tile_table_bytes(D) : 0;
     case MOE_OP_FFN_BWD:
       return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
-             (D.bf16 ? round_up(tile_table_bytes(D), 256) : 0);
+             (D.bf16 ? tile_table_bytes(D) : 0);
     case MOE_OP_ROUTE_BWD:
       return (D.bf16 && !D.balanced) ? round_up((int64_t)D.T * D.E * 2, 256) : 0;
     default: return 0;
@@ -311,29 +354,31 @@ extern "C" moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void
                     {"w_up", w_up}, {"w_down", w_down}, {"a_save", a_save}, {"yp", yp}}));
   MOE_TRY(opt(fn, {{"h_save", h_save}}));
   MOE_TRY(check_ws(fn, D, MOE_OP_FFN_FWD, ws, ws_bytes_));
-  int32_t* tiles = static_cast<int32_t*>(ws);
-  const int rows_or_tiles = D.bf16 ? max_m_tiles(D) : D.R_cap;
-  if (D.bf16) MOE_TRY(launch_tile_table(group_offsets, D.E_loc, BM_ROWS, tiles, S(stream)));
+  TileTables tt{D, static_cast<int32_t*>(ws), group_offsets, S(stream)};
+  // fp32: the row count; bf16: the most M tiles the tile table can hold
+  auto rows_or_tiles = [&](TileCfg c) { return D.bf16 ? max_m_tiles(D, tile_bm(c)) : D.R_cap; };
 
   GemmParams g{};
   g.A = xp; g.lda = D.d;
   g.B0 = w_gate; g.B1 = w_up; g.ldb = D.I; g.b_estride = (int64_t)D.d * D.I;
   g.N = D.I; g.K = D.d;
-  g.off = group_offsets; g.tiles = tiles; g.groups = D.E_loc;
-  g.n_tiles = D.I / 64;
+  g.off = group_offsets; g.groups = D.E_loc;
+  g.n_tiles = (int)ceil_div(D.I, tile_bn(TILE_GATEUP_FWD) / 2);
   g.C0 = h_save; g.C2 = a_save; g.I = D.I;
-  MOE_TRY(launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU, TILE_256x128, g,
-                      rows_or_tiles, S(stream), "ffn_gateup_fwd"));
+  if (D.bf16) MOE_TRY(tt.get(TILE_GATEUP_FWD, &g.tiles));
+  MOE_TRY(launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU, TILE_GATEUP_FWD, g,
+                      rows_or_tiles(TILE_GATEUP_FWD), S(stream), "ffn_gateup_fwd"));
 
   GemmParams p{};
   p.A = a_save; p.lda = D.I;
   p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
   p.N = D.d; p.K = D.I;
-  p.off = group_offsets; p.tiles = tiles; p.groups = D.E_loc;
-  p.n_tiles = (int)ceil_div(D.d, 128);
+  p.off = group_offsets; p.groups = D.E_loc;
+  p.n_tiles = (int)ceil_div(D.d, tile_bn(TILE_DOWN_FWD));
   p.C0 = yp; p.ldc = D.d;
-  return launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE, TILE_256x128, p,
-                     rows_or_tiles, S(stream), "ffn_down_fwd");
+  if (D.bf16) MOE_TRY(tt.get(TILE_DOWN_FWD, &p.tiles));
+  return launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE, TILE_DOWN_FWD, p,
+                     rows_or_tiles(TILE_DOWN_FWD), S(stream), "ffn_down_fwd");
 }
 
 extern "C" moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,
@@ -374,21 +419,22 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
   MOE_TRY(check_ws(fn, D, MOE_OP_FFN_BWD, ws, ws_bytes_));
   char* wsb = static_cast<char*>(ws);
   void* dH = wsb;
-  int32_t* tiles = reinterpret_cast<int32_t*>(wsb + round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256));
-  const int rows_or_tiles = D.bf16 ? max_m_tiles(D) : D.R_cap;
   hipStream_t s = S(stream);
-  if (D.bf16) MOE_TRY(launch_tile_table(group_offsets, D.E_loc, BM_ROWS, tiles, s));
+  TileTables tt{D, reinterpret_cast<int32_t*>(wsb + round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256)),
+                group_offsets, s};
+  auto rows_or_tiles = [&](TileCfg c) { return D.bf16 ? max_m_tiles(D, tile_bm(c)) : D.R_cap; };
 
   {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
     GemmParams p{};
     p.A = dyp; p.lda = D.d;
     p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
     p.N = D.I; p.K = D.d;
-    p.off = group_offsets; p.tiles = tiles; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.I, 128);
+    p.off = group_offsets; p.groups = D.E_loc;
+    p.n_tiles = (int)ceil_div(D.I, tile_bn(TILE_DOWN_DGRAD));
     p.C0 = dH; p.aux = h_save; p.I = D.I;
-    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU, TILE_256x128, p,
-                        rows_or_tiles, s, "ffn_down_dgrad"));
+    if (D.bf16) MOE_TRY(tt.get(TILE_DOWN_DGRAD, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU, TILE_DOWN_DGRAD, p,
+                        rows_or_tiles(TILE_DOWN_DGRAD), s, "ffn_down_dgrad"));
   }
   {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
     GemmParams p{};
@@ -396,11 +442,12 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = w_gate; p.B1 = w_up; p.ldb = D.I; p.b_estride = (int64_t)D.d * D.I;
     p.k_split = D.I;
     p.N = D.d; p.K = 2 * D.I;
-    p.off = group_offsets; p.tiles = tiles; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.d, 128);
+    p.off = group_offsets; p.groups = D.E_loc;
+    p.n_tiles = (int)ceil_div(D.d, tile_bn(TILE_GATEUP_DGRAD));
     p.C0 = dxp; p.ldc = D.d;
-    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE, TILE_256x128, p,
-                        rows_or_tiles, s, "ffn_gateup_dgrad"));
+    if (D.bf16) MOE_TRY(tt.get(TILE_GATEUP_DGRAD, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE, TILE_GATEUP_DGRAD, p,
+                        rows_or_tiles(TILE_GATEUP_DGRAD), s, "ffn_gateup_dgrad"));
   }
   {  // a8: dWd[e] = A_e^T dYp_e
     GemmParams p{};
@@ -408,9 +455,9 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = dyp; p.ldb = D.d;
     p.M = D.I; p.N = D.d;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.m_tiles = (int)ceil_div(D.I, 256); p.n_tiles = (int)ceil_div(D.d, 128);
+    p.m_tiles = (int)ceil_div(D.I, tile_bm(WGRAD_TILE)); p.n_tiles = (int)ceil_div(D.d, tile_bn(WGRAD_TILE));
     p.C0 = dw_down; p.ldc = D.d; p.c_estride = (int64_t)D.I * D.d;
-    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, TILE_256x128, p,
+    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, WGRAD_TILE, p,
                         p.m_tiles, s, "ffn_down_wgrad"));
   }
   {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
@@ -419,10 +466,10 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = dH; p.ldb = 2 * (int64_t)D.I;
     p.M = D.d; p.N = 2 * D.I;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.m_tiles = (int)ceil_div(D.d, 256); p.n_tiles = (int)ceil_div(2 * D.I, 128);
+    p.m_tiles = (int)ceil_div(D.d, tile_bm(WGRAD_TILE)); p.n_tiles = (int)ceil_div(2 * D.I, tile_bn(WGRAD_TILE));
     p.C0 = dw_gate; p.C1 = dw_up; p.n_split = D.I; p.ldc = D.I;
     p.c_estride = (int64_t)D.d * D.I;
-    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, TILE_256x128, p,
+    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, WGRAD_TILE, p,
                         p.m_tiles, s, "ffn_gateup_wgrad"));
   }
   return MOE_OK;

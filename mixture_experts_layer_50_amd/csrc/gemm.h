@@ -61,7 +61,7 @@ struct GemmParams {
 };
 
 // Tile shapes of the bf16 MFMA kernels.
-enum TileCfg { TILE_256x128 = 0, TILE_64x64 = 1 };
+enum TileCfg { TILE_256x256 = 0, TILE_256x128 = 1, TILE_64x64 = 2, TILE_128x128 = 3 };
 
 // Launch one GEMM.  `is_bf16` selects the bf16 MFMA kernel or the fp32 kernel;
 // the template-like mode arguments select the instantiation.  For G_MROWS the

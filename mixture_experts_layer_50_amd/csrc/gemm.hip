@@ -83,14 +83,14 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
 // Loader of a KC tile: row r of the tile is src[(row0 + r) * ld + k], rows
 // r >= row_hi - row0 read as zeros.  With TWO, k < ksplit comes from s0 and
 // k >= ksplit from s1 at k - ksplit (ksplit is a multiple of 64, so one K
-// slice never straddles it).
+// slice never straddles it).  The per-lane address state is kept once; the
+// loaded data lives in a separate register array per pipeline stage.
 template <int ROWS, bool TWO>
 struct LoaderKC {
   static constexpr int CH = ROWS * 8;
   static constexpr int NR = (CH + 255) / 256;
-  uint4 r[NR];
+  struct Data { uint4 r[NR]; };
   int voff[NR];
-  int kc[NR];
   __amdgpu_buffer_rsrc_t rs0, rs1;
   int ksplit, k_lo, k_hi;
   __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
@@ -104,27 +104,29 @@ struct LoaderKC {
     for (int i = 0; i < NR; ++i) {
       int q = tid + 256 * i;
       int row = q >> 3;
-      kc[i] = (q & 7) * 8;
       bool ok = (CH % 256 == 0 || q < CH) && row0 + row < row_hi;
-      voff[i] = ok ? (int)(((int64_t)row * ld + kc[i]) * 2) : OOB;
+      voff[i] = ok ? (int)(((int64_t)row * ld + (q & 7) * 8) * 2) : OOB;
     }
   }
   // K slice starting at k_lo + kofs
-  __device__ __forceinline__ void load(int kofs) {
+  __device__ __forceinline__ void load(Data& d, int kofs, int tid) const {
     int k0 = k_lo + kofs;
     __amdgpu_buffer_rsrc_t rs = rs0;
-    if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; }
-    const int lim = (TWO && k_lo + kofs >= ksplit) ? k_hi - ksplit - k0 : k_hi - k0;
+    int lim = k_hi - k0;
+    if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
 #pragma unroll
-    for (int i = 0; i < NR; ++i) r[i] = buf_load16(rs, kc[i] < lim ? voff[i] : OOB, k0 * 2);
+    for (int i = 0; i < NR; ++i) {
+      const int kc = ((tid + 256 * i) & 7) * 8;
+      d.r[i] = buf_load16(rs, kc < lim ? voff[i] : OOB, k0 * 2);
+    }
   }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
+  __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       int q = tid + 256 * i;
       if (CH % 256 == 0 || q < CH) {
         int row = q >> 3, c = q & 7;
-        *reinterpret_cast<uint4*>(lds + row * BK + swz(row, c) * 8) = r[i];
+        *reinterpret_cast<uint4*>(lds + row * BK + swz(row, c) * 8) = d.r[i];
       }
     }
   }
@@ -141,9 +143,8 @@ struct LoaderKN {
   static constexpr int CH = BK * CPR;                        // chunks per source
   static constexpr int NS = (CH + 255) / 256;                // loads per source
   static constexpr int NR = HALF ? 2 * NS : NS;
-  uint4 r[NR];
+  struct Data { uint4 r[NR]; };
   int voff[NS];
-  int krow[NS];
   __amdgpu_buffer_rsrc_t rs0, rs1;
   int64_t ld;
   int k_lo, k_hi;
@@ -157,23 +158,22 @@ struct LoaderKN {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       int q = tid + 256 * i;
-      krow[i] = q / CPR;
       int col = (q % CPR) * 8;
       bool ok = (CH % 256 == 0 || q < CH) && col0 + col < col_hi;
-      voff[i] = ok ? (int)(((int64_t)krow[i] * ld + col) * 2) : OOB;
+      voff[i] = ok ? (int)(((int64_t)(q / CPR) * ld + col) * 2) : OOB;
     }
   }
-  __device__ __forceinline__ void load(int kofs) {
+  __device__ __forceinline__ void load(Data& d, int kofs, int tid) const {
     const int lim = k_hi - k_lo - kofs;
     const int soff = (int)((int64_t)kofs * ld * 2);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int v = krow[i] < lim ? voff[i] : OOB;
-      r[i] = buf_load16(rs0, v, soff);
-      if (HALF) r[NS + i] = buf_load16(rs1, v, soff);
+      const int v = (tid + 256 * i) / CPR < lim ? voff[i] : OOB;
+      d.r[i] = buf_load16(rs0, v, soff);
+      if (HALF) d.r[NS + i] = buf_load16(rs1, v, soff);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
+  __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
 #pragma unroll
     for (int h = 0; h < (HALF ? 2 : 1); ++h) {
 #pragma unroll
@@ -181,7 +181,7 @@ struct LoaderKN {
         int q = tid + 256 * i;
         if (CH % 256 == 0 || q < CH) {
           int k = q / CPR, c = q % CPR + h * CPR;
-          *reinterpret_cast<uint4*>(lds + k * COLS + kn_swz<COLS>(k, c) * 8) = r[h * NS + i];
+          *reinterpret_cast<uint4*>(lds + k * COLS + kn_swz<COLS>(k, c) * 8) = d.r[h * NS + i];
         }
       }
     }
@@ -214,21 +214,23 @@ __device__ __forceinline__ bf16x8 frag_kn(const bf16_t* lds, int base, int ks, i
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM.  P register stages: while the MFMAs work on K slice
-// kt from LDS, slice kt+1 is written to the other LDS buffer and the loads of
-// slices kt+2 .. kt+P are in flight.
+// bf16 MFMA grouped GEMM.  Four waves in a 2 x 2 grid, each owning a
+// (BM/2) x (BN/2) block of 32x32 MFMA tiles.  P register stages: while the
+// MFMAs work on K slice kt from LDS, slice kt+1 is written to the other LDS
+// buffer and the loads of slices kt+2 .. kt+P are in flight.
+// With the gate|up halves (B2_NHALF) the first FN/2 column blocks of a wave
+// are gate columns and the last FN/2 the matching up columns.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI>
+template <int BM, int BN, int P, int AM, int BMD, int GMD, int B2, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  static_assert(WGM * WGN == 4, "four waves");
   static_assert(FM >= 1 && FN >= 1, "wave tile of at least 32x32");
-  static_assert(B2 != B2_NHALF || (FN == 2 && BN / 2 == WGN * 32), "gate|up halves");
+  static_assert(B2 != B2_NHALF || FN % 2 == 0, "gate|up halves need an even block count");
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wave >> 1, wn = wave & 1;
 
   // ---- which tile
   int mt_count = (GMD == G_MROWS) ? p.tiles[0] : p.m_tiles;
@@ -266,8 +268,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
 
   typedef typename PickLoader<AM == A_KC, BM, false>::type LA;
   typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE>::type LB;
-  LA la[P];
-  LB lb[P];
+  LA la;
+  LB lb;
+  typename LA::Data da[P];
+  typename LB::Data db[P];
+  la.init(A, A, p.lda, m_lo, m_hi, k_lo, k_hi, 0, tid);
+  lb.init(B0, B1, p.ldb, n0, n_hi, k_lo, k_hi, p.k_split, tid);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -278,33 +284,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (k_hi - k_lo + BK - 1) / BK;
-  // per-lane address parts are the same for every slot; set them up once
-#pragma unroll
-  for (int s = 0; s < P; ++s) {
-    la[s].init(A, A, p.lda, m_lo, m_hi, k_lo, k_hi, 0, tid);
-    lb[s].init(B0, B1, p.ldb, n0, n_hi, k_lo, k_hi, p.k_split, tid);
-  }
 #pragma unroll
   for (int s = 0; s < P; ++s) {
     if (s < nk) {
-      la[s].load(s * BK);
-      lb[s].load(s * BK);
+      la.load(da[s], s * BK, tid);
+      lb.load(db[s], s * BK, tid);
     }
   }
   if (nk > 0) {
-    la[0].store(smem, tid);
-    lb[0].store(smem + BM * BK, tid);
+    LA::store(da[0], smem, tid);
+    LB::store(db[0], smem + BM * BK, tid);
   }
   __syncthreads();
 
   // One K slice: refill the register slot of slice kt with slice kt+P, multiply
   // slice kt from LDS, write slice kt+1 (loaded P-1 slices ago) to the other
   // LDS buffer, barrier.  U = kt mod P is a compile-time constant.
-  auto step = [&](auto Uc, int kt, bool do_load, bool do_store) {
+  auto step = [&](auto Uc, int kt, bool do_load, bool do_store) __attribute__((always_inline)) {
     constexpr int U = decltype(Uc)::value;
     if (do_load) {
-      la[U].load((kt + P) * BK);
-      lb[U].load((kt + P) * BK);
+      la.load(da[U], (kt + P) * BK, tid);
+      lb.load(db[U], (kt + P) * BK, tid);
     }
     // keep the refill loads at the top of the step: the scheduler would
     // otherwise sink them below the MFMAs and expose their latency
@@ -322,7 +322,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int base = (B2 == B2_NHALF) ? (j * (BN / 2) + wn * 32) : (wn * WTN + j * 32);
+        int base;
+        if constexpr (B2 == B2_NHALF)
+          base = (j < FN / 2) ? (wn * (WTN / 2) + j * 32) : (BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 32);
+        else
+          base = wn * WTN + j * 32;
         if constexpr (BMD == B_KC) bfg[j] = frag_kc(bs, base, ks, lane);
         else bfg[j] = frag_kn<BN>(bs, base, ks, lane);
       }
@@ -335,8 +339,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     if (do_store) {
       bf16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BK;
-      la[(U + 1) % P].store(nxt, tid);
-      lb[(U + 1) % P].store(nxt + BM * BK, tid);
+      LA::store(da[(U + 1) % P], nxt, tid);
+      LB::store(db[(U + 1) % P], nxt + BM * BK, tid);
     }
     __syncthreads();
   };
@@ -344,12 +348,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   int kt0 = 0;
   // steady state: every step loads and stores
   for (; kt0 + 2 * P <= nk; kt0 += P) {
-    [&]<int... Us>(std::integer_sequence<int, Us...>) {
+    [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
       (step(std::integral_constant<int, Us>{}, kt0 + Us, true, true), ...);
     }(std::make_integer_sequence<int, P>{});
   }
   // drain: at most 2P-1 slices left
-  [&]<int... Us>(std::integer_sequence<int, Us...>) {
+  [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
     ((kt0 + Us < nk ? step(std::integral_constant<int, Us % P>{}, kt0 + Us, kt0 + Us + P < nk,
                            kt0 + Us + 1 < nk)
                     : void()),
@@ -368,20 +372,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       bf16_t* Aout = static_cast<bf16_t*>(p.C2);
       const int64_t I = p.I;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 32 + 8 * q + 4 * half;
-        float g[4], u[4], a[4];
+      for (int jp = 0; jp < FN / 2; ++jp) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          g[s] = acc[i][0][4 * q + s];
-          u[s] = acc[i][1][4 * q + s];
-          a[s] = g[s] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[s])) * u[s];
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * (WTN / 2) + jp * 32 + 8 * q + 4 * half;
+          if (n >= I) continue;
+          float g[4], u[4], a[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            g[s] = acc[i][jp][4 * q + s];
+            u[s] = acc[i][jp + FN / 2][4 * q + s];
+            a[s] = g[s] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[s])) * u[s];
+          }
+          if (H) {
+            *reinterpret_cast<uint2*>(H + m * 2 * I + n) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+            *reinterpret_cast<uint2*>(H + m * 2 * I + I + n) = make_uint2(pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]));
+          }
+          *reinterpret_cast<uint2*>(Aout + m * I + n) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
         }
-        if (H) {
-          *reinterpret_cast<uint2*>(H + m * 2 * I + n) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
-          *reinterpret_cast<uint2*>(H + m * 2 * I + I + n) = make_uint2(pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]));
-        }
-        *reinterpret_cast<uint2*>(Aout + m * I + n) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
       }
     } else {
 #pragma unroll
@@ -557,21 +565,24 @@ moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* 
   return check_launch("tile_table_kernel");
 }
 
-int tile_bm(TileCfg cfg) { return cfg == TILE_256x128 ? 256 : 64; }
-int tile_bn(TileCfg cfg) { return cfg == TILE_256x128 ? 128 : 64; }
+int tile_bm(TileCfg cfg) { return cfg == TILE_64x64 ? 64 : cfg == TILE_128x128 ? 128 : 256; }
+int tile_bn(TileCfg cfg) {
+  return cfg == TILE_256x256 ? 256 : (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128 : 64;
+}
 
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
 #define MOE_KEY(am, bm, gm, b2, epi) ((am) | ((bm) << 1) | ((gm) << 2) | ((b2) << 4) | ((epi) << 6))
 
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 2
+#endif
+
 template <int BMt, int BNt, int AM, int BMD, int GMD, int B2, int EPI>
 static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 3
-#endif
-  constexpr int P = (BMt >= 256) ? MOE_GEMM_STAGES : 2;  // register stages in flight
-  gemm_bf16_kernel<BMt, BNt, 2, 2, P, AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
+  constexpr int P = (BMt >= 128) ? MOE_GEMM_STAGES : 2;  // register stages in flight
+  gemm_bf16_kernel<BMt, BNt, P, AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
 }
 
 template <int AM, int BMD, int GMD, int B2, int EPI>
@@ -614,33 +625,60 @@ moe_status_t launch_gemm(bool is_bf16, int am, int bmd, int gmd, int b2, int epi
     set_error("GEMM %s: grid too large", name);
     return MOE_ERR_UNSUPPORTED;
   }
-  if (cfg == TILE_256x128) {
-    switch (key) {
+#define MOE_ROW_GEMMS(X)                          \
+  X(A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU)     \
+  X(A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)       \
+  X(A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU)     \
+  X(A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE)     \
+  X(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
+  switch (cfg) {
+    case TILE_256x256:
+      switch (key) {
+#define BFCASE(a, b, g, t, e) \
+  case MOE_KEY(a, b, g, t, e): launch_bf16<256, 256, a, b, g, t, e>(p, (int)grid, s); break;
+        MOE_ROW_GEMMS(BFCASE)
+#undef BFCASE
+        default:
+          set_error("internal: no bf16 256x256 GEMM variant for key %d (%s)", key, name);
+          return MOE_ERR_UNSUPPORTED;
+      }
+      break;
+    case TILE_256x128:
+      switch (key) {
 #define BFCASE(a, b, g, t, e) \
   case MOE_KEY(a, b, g, t, e): launch_bf16<256, 128, a, b, g, t, e>(p, (int)grid, s); break;
-      BFCASE(A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU)
-      BFCASE(A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)
-      BFCASE(A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU)
-      BFCASE(A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE)
-      BFCASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
+        MOE_ROW_GEMMS(BFCASE)
 #undef BFCASE
-      default:
-        set_error("internal: no bf16 256x128 GEMM variant for key %d (%s)", key, name);
-        return MOE_ERR_UNSUPPORTED;
-    }
-  } else {
-    switch (key) {
+        default:
+          set_error("internal: no bf16 256x128 GEMM variant for key %d (%s)", key, name);
+          return MOE_ERR_UNSUPPORTED;
+      }
+      break;
+    case TILE_128x128:
+      switch (key) {
+#define BFCASE(a, b, g, t, e) \
+  case MOE_KEY(a, b, g, t, e): launch_bf16<128, 128, a, b, g, t, e>(p, (int)grid, s); break;
+        MOE_ROW_GEMMS(BFCASE)
+#undef BFCASE
+        default:
+          set_error("internal: no bf16 128x128 GEMM variant for key %d (%s)", key, name);
+          return MOE_ERR_UNSUPPORTED;
+      }
+      break;
+    default:
+      switch (key) {
 #define BFCASE(a, b, g, t, e) \
   case MOE_KEY(a, b, g, t, e): launch_bf16<64, 64, a, b, g, t, e>(p, (int)grid, s); break;
-      BFCASE(A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)
-      BFCASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
-      BFCASE(A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
+        BFCASE(A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)
+        BFCASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
+        BFCASE(A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
 #undef BFCASE
-      default:
-        set_error("internal: no bf16 64x64 GEMM variant for key %d (%s)", key, name);
-        return MOE_ERR_UNSUPPORTED;
-    }
+        default:
+          set_error("internal: no bf16 64x64 GEMM variant for key %d (%s)", key, name);
+          return MOE_ERR_UNSUPPORTED;
+      }
   }
+#undef MOE_ROW_GEMMS
   return check_launch(name);
 }
 

@@ -102,9 +102,11 @@ def test_workspace_sizes_and_short_workspace(lib):
     assert B.workspace_size(s, "route") == 0
     assert B.workspace_size(s, "combine") == 0
     assert B.workspace_size(s, "permute") == 16 * 128 * 4          # 16 blocks of 256 tokens
-    tiles = (1 + 2 * (R // 256 + 128)) * 4
-    assert B.workspace_size(s, "ffn_fwd") == -(-tiles // 256) * 256
-    assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + -(-tiles // 256) * 256
+    def table(bm):  # one tile table per M-tile height, 256-byte aligned
+        return -(-(1 + 2 * (R // bm + 128)) * 4 // 256) * 256
+    tiles = table(256) + table(128)
+    assert B.workspace_size(s, "ffn_fwd") == tiles
+    assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + tiles
     assert B.workspace_size(s, "route_bwd") == 0                    # balanced gate: no dL copy
     n = B.workspace_size(shape(T=4096, d=2048, E=128, k=8, I=768), "route_bwd")
     assert n == 4096 * 128 * 2
