@@ -85,10 +85,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
 // k >= ksplit from s1 at k - ksplit (ksplit is a multiple of 64, so one K
 // slice never straddles it).  The per-lane address state is kept once; the
 // loaded data lives in a separate register array per pipeline stage.
-template <int ROWS, bool TWO>
+template <int ROWS, bool TWO, int NT>
 struct LoaderKC {
   static constexpr int CH = ROWS * 8;
-  static constexpr int NR = (CH + 255) / 256;
+  static constexpr int NR = (CH + NT - 1) / NT;
   struct Data { uint4 r[NR]; };
   int voff[NR];
   __amdgpu_buffer_rsrc_t rs0, rs1;
@@ -102,9 +102,9 @@ struct LoaderKC {
     k_hi = k_hi_;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      int q = tid + 256 * i;
+      int q = tid + NT * i;
       int row = q >> 3;
-      bool ok = (CH % 256 == 0 || q < CH) && row0 + row < row_hi;
+      bool ok = (CH % NT == 0 || q < CH) && row0 + row < row_hi;
       voff[i] = ok ? (int)(((int64_t)row * ld + (q & 7) * 8) * 2) : OOB;
     }
   }
@@ -116,15 +116,15 @@ struct LoaderKC {
     if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      const int kc = ((tid + 256 * i) & 7) * 8;
+      const int kc = ((tid + NT * i) & 7) * 8;
       d.r[i] = buf_load16(rs, kc < lim ? voff[i] : OOB, k0 * 2);
     }
   }
   __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      int q = tid + 256 * i;
-      if (CH % 256 == 0 || q < CH) {
+      int q = tid + NT * i;
+      if (CH % NT == 0 || q < CH) {
         int row = q >> 3, c = q & 7;
         *reinterpret_cast<uint4*>(lds + row * BK + swz(row, c) * 8) = d.r[i];
       }
@@ -137,11 +137,11 @@ struct LoaderKC {
 // zeros.  HALF: tile columns [0, COLS/2) come from s0 at col0 + c, columns
 // [COLS/2, COLS) from s1 at col0 + c - COLS/2 (the gate | up halves); each
 // load instruction reads one half only, so its buffer descriptor is uniform.
-template <int COLS, bool HALF>
+template <int COLS, bool HALF, int NT>
 struct LoaderKN {
   static constexpr int CPR = HALF ? COLS / 16 : COLS / 8;  // chunks per row and source
   static constexpr int CH = BK * CPR;                        // chunks per source
-  static constexpr int NS = (CH + 255) / 256;                // loads per source
+  static constexpr int NS = (CH + NT - 1) / NT;              // loads per source
   static constexpr int NR = HALF ? 2 * NS : NS;
   struct Data { uint4 r[NR]; };
   int voff[NS];
@@ -157,9 +157,9 @@ struct LoaderKN {
     rs1 = make_rsrc((HALF ? s1 : s0) + (int64_t)k_lo * ld + col0);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      int q = tid + 256 * i;
+      int q = tid + NT * i;
       int col = (q % CPR) * 8;
-      bool ok = (CH % 256 == 0 || q < CH) && col0 + col < col_hi;
+      bool ok = (CH % NT == 0 || q < CH) && col0 + col < col_hi;
       voff[i] = ok ? (int)(((int64_t)(q / CPR) * ld + col) * 2) : OOB;
     }
   }
@@ -168,7 +168,7 @@ struct LoaderKN {
     const int soff = (int)((int64_t)kofs * ld * 2);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int v = (tid + 256 * i) / CPR < lim ? voff[i] : OOB;
+      const int v = (tid + NT * i) / CPR < lim ? voff[i] : OOB;
       d.r[i] = buf_load16(rs0, v, soff);
       if (HALF) d.r[NS + i] = buf_load16(rs1, v, soff);
     }
@@ -178,8 +178,8 @@ struct LoaderKN {
     for (int h = 0; h < (HALF ? 2 : 1); ++h) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        int q = tid + 256 * i;
-        if (CH % 256 == 0 || q < CH) {
+        int q = tid + NT * i;
+        if (CH % NT == 0 || q < CH) {
           int k = q / CPR, c = q % CPR + h * CPR;
           *reinterpret_cast<uint4*>(lds + k * COLS + kn_swz<COLS>(k, c) * 8) = d.r[h * NS + i];
         }
@@ -188,9 +188,9 @@ struct LoaderKN {
   }
 };
 
-template <bool KC, int ROWS, bool TWO> struct PickLoader;
-template <int ROWS, bool TWO> struct PickLoader<true, ROWS, TWO> { typedef LoaderKC<ROWS, TWO> type; };
-template <int ROWS, bool TWO> struct PickLoader<false, ROWS, TWO> { typedef LoaderKN<ROWS, TWO> type; };
+template <bool KC, int ROWS, bool TWO, int NT> struct PickLoader;
+template <int ROWS, bool TWO, int NT> struct PickLoader<true, ROWS, TWO, NT> { typedef LoaderKC<ROWS, TWO, NT> type; };
+template <int ROWS, bool TWO, int NT> struct PickLoader<false, ROWS, TWO, NT> { typedef LoaderKN<ROWS, TWO, NT> type; };
 
 // MFMA operand fragment (32 rows x 16 k): lane l holds row base + (l & 31),
 // k = 16 ks + 8 (l >> 5) + 0..7.
@@ -213,24 +213,116 @@ __device__ __forceinline__ bf16x8 frag_kn(const bf16_t* lds, int base, int ks, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Epilogue shared by the bf16 kernels.  Lane holds C[m][n..n+3] of every
+// 32x32 block of its wave tile: m = row (lane & 31), n = 8q + 4 (lane >> 5).
+template <int FM, int FN, int WTM, int WTN, int GMD, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][FN], int m_lo,
+                                         int m_hi, int n0, int e, int wm, int wn, int lane) {
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m_lo + wm * WTM + i * 32 + (lane & 31);
+    if (m >= m_hi) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      bf16_t* H = static_cast<bf16_t*>(p.C0);
+      bf16_t* Aout = static_cast<bf16_t*>(p.C2);
+      const int64_t I = p.I;
+#pragma unroll
+      for (int jp = 0; jp < FN / 2; ++jp) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * (WTN / 2) + jp * 32 + 8 * q + 4 * half;
+          if (n >= I) continue;
+          float g[4], u[4], a[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            g[s] = acc[i][jp][4 * q + s];
+            u[s] = acc[i][jp + FN / 2][4 * q + s];
+            a[s] = g[s] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[s])) * u[s];
+          }
+          if (H) {
+            *reinterpret_cast<uint2*>(H + m * 2 * I + n) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+            *reinterpret_cast<uint2*>(H + m * 2 * I + I + n) = make_uint2(pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]));
+          }
+          *reinterpret_cast<uint2*>(Aout + m * I + n) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * half;
+          if (n >= p.N) continue;
+          float v[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) v[s] = acc[i][j][4 * q + s];
+          if constexpr (EPI == EPI_STORE) {
+            bf16_t* C = static_cast<bf16_t*>(p.C0);
+            if (p.n_split > 0 && n >= p.n_split) { C = static_cast<bf16_t*>(p.C1); n -= p.n_split; }
+            if (GMD == G_KROWS) C += (int64_t)e * p.c_estride;
+            *reinterpret_cast<uint2*>(C + (int64_t)m * p.ldc + n) =
+                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+          } else if constexpr (EPI == EPI_ACCUM) {
+            bf16_t* C = static_cast<bf16_t*>(p.C0) + (int64_t)m * p.ldc + n;
+            uint2 o = *reinterpret_cast<const uint2*>(C);
+            float w0 = bf2f((bf16_t)(o.x & 0xffff)) + v[0], w1 = bf2f((bf16_t)(o.x >> 16)) + v[1];
+            float w2 = bf2f((bf16_t)(o.y & 0xffff)) + v[2], w3 = bf2f((bf16_t)(o.y >> 16)) + v[3];
+            *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf2(w0, w1), pack_bf2(w2, w3));
+          } else if constexpr (EPI == EPI_F32_BIAS) {
+            float* C = static_cast<float*>(p.C0) + (int64_t)m * p.ldc + n;
+            if (p.bias) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) v[s] += p.bias[n + s];
+            }
+            *reinterpret_cast<float4*>(C) = make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_DSWIGLU) {
+            const bf16_t* H = static_cast<const bf16_t*>(p.aux);
+            bf16_t* dH = static_cast<bf16_t*>(p.C0);
+            const int64_t I = p.I;
+            uint2 hg = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + n);
+            uint2 hu = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + I + n);
+            float g[4] = {bf2f((bf16_t)(hg.x & 0xffff)), bf2f((bf16_t)(hg.x >> 16)),
+                          bf2f((bf16_t)(hg.y & 0xffff)), bf2f((bf16_t)(hg.y >> 16))};
+            float u[4] = {bf2f((bf16_t)(hu.x & 0xffff)), bf2f((bf16_t)(hu.x >> 16)),
+                          bf2f((bf16_t)(hu.y & 0xffff)), bf2f((bf16_t)(hu.y >> 16))};
+            float dg[4], du[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[s]));
+              dg[s] = v[s] * u[s] * sg * (1.0f + g[s] * (1.0f - sg));
+              du[s] = v[s] * g[s] * sg;
+            }
+            *reinterpret_cast<uint2*>(dH + (int64_t)m * 2 * I + n) =
+                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(dH + (int64_t)m * 2 * I + I + n) =
+                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM.  Four waves in a 2 x 2 grid, each owning a
-// (BM/2) x (BN/2) block of 32x32 MFMA tiles.  P register stages: while the
+// bf16 MFMA grouped GEMM.  WGM x WGN waves, each owning a (BM/WGM) x
+// (BN/WGN) block of 32x32 MFMA tiles.  P register stages: while the
 // MFMAs work on K slice kt from LDS, slice kt+1 is written to the other LDS
 // buffer and the loads of slices kt+2 .. kt+P are in flight.
 // With the gate|up halves (B2_NHALF) the first FN/2 column blocks of a wave
 // are gate columns and the last FN/2 the matching up columns.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int P, int AM, int BMD, int GMD, int B2, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile of at least 32x32");
   static_assert(B2 != B2_NHALF || FN % 2 == 0, "gate|up halves need an even block count");
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- which tile
   int mt_count = (GMD == G_MROWS) ? p.tiles[0] : p.m_tiles;
@@ -266,8 +358,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
   }
 
-  typedef typename PickLoader<AM == A_KC, BM, false>::type LA;
-  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE>::type LB;
+  typedef typename PickLoader<AM == A_KC, BM, false, NT>::type LA;
+  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT>::type LB;
   LA la;
   LB lb;
   typename LA::Data da[P];
@@ -360,92 +452,278 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
      ...);
   }(std::make_integer_sequence<int, 2 * P - 1>{});
 
-  // ---- epilogue.  Lane holds C[m][n..n+3] with m = row of the wave tile
-  // (lane & 31), n = 8q + 4 (lane >> 5) within each 32-column block.
-  const int half = lane >> 5;
+  epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
+}
+
+// ===========================================================================
+// Direct-to-LDS variant.  Every K slice goes from HBM/L2 straight into LDS
+// with the 16-byte buffer-load-to-LDS instruction (no register staging, no
+// LDS store instructions).  Lane l of a load lands at LDS base + 16 l, so the
+// swizzled layouts are produced by choosing each lane's source address.  Each
+// pipeline stage is a separate __shared__ array so the compiler can tell that
+// fragment reads of one stage do not alias loads into another.
+// ===========================================================================
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, bf16_t* lds_dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// KC tile [ROWS][64]: slot s (16 bytes) holds row s >> 3, physical chunk s & 7,
+// i.e. logical chunk (s & 7) ^ swz(row).
+template <int ROWS, bool TWO, int NT>
+struct DmaKC {
+  static constexpr int CH = ROWS * 8;
+  static constexpr int NR = CH / NT;
+  static_assert(CH % NT == 0, "whole load instructions");
+  int voff[NR];
+  int kcol[NR];
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  int ksplit, k_lo, k_hi;
+  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
+                                       int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid) {
+    rs0 = make_rsrc(s0 + (int64_t)row0 * ld);
+    rs1 = make_rsrc(TWO ? s1 + (int64_t)row0 * ld : s0);
+    ksplit = ksplit_;
+    k_lo = k_lo_;
+    k_hi = k_hi_;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m_lo + wm * WTM + i * 32 + (lane & 31);
-    if (m >= m_hi) continue;
-    if constexpr (EPI == EPI_SWIGLU) {
-      bf16_t* H = static_cast<bf16_t*>(p.C0);
-      bf16_t* Aout = static_cast<bf16_t*>(p.C2);
-      const int64_t I = p.I;
-#pragma unroll
-      for (int jp = 0; jp < FN / 2; ++jp) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * (WTN / 2) + jp * 32 + 8 * q + 4 * half;
-          if (n >= I) continue;
-          float g[4], u[4], a[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            g[s] = acc[i][jp][4 * q + s];
-            u[s] = acc[i][jp + FN / 2][4 * q + s];
-            a[s] = g[s] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[s])) * u[s];
-          }
-          if (H) {
-            *reinterpret_cast<uint2*>(H + m * 2 * I + n) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
-            *reinterpret_cast<uint2*>(H + m * 2 * I + I + n) = make_uint2(pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]));
-          }
-          *reinterpret_cast<uint2*>(Aout + m * I + n) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * half;
-          if (n >= p.N) continue;
-          float v[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) v[s] = acc[i][j][4 * q + s];
-          if constexpr (EPI == EPI_STORE) {
-            bf16_t* C = static_cast<bf16_t*>(p.C0);
-            if (p.n_split > 0 && n >= p.n_split) { C = static_cast<bf16_t*>(p.C1); n -= p.n_split; }
-            if (GMD == G_KROWS) C += (int64_t)e * p.c_estride;
-            *reinterpret_cast<uint2*>(C + (int64_t)m * p.ldc + n) =
-                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-          } else if constexpr (EPI == EPI_ACCUM) {
-            bf16_t* C = static_cast<bf16_t*>(p.C0) + (int64_t)m * p.ldc + n;
-            uint2 o = *reinterpret_cast<const uint2*>(C);
-            float w0 = bf2f((bf16_t)(o.x & 0xffff)) + v[0], w1 = bf2f((bf16_t)(o.x >> 16)) + v[1];
-            float w2 = bf2f((bf16_t)(o.y & 0xffff)) + v[2], w3 = bf2f((bf16_t)(o.y >> 16)) + v[3];
-            *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf2(w0, w1), pack_bf2(w2, w3));
-          } else if constexpr (EPI == EPI_F32_BIAS) {
-            float* C = static_cast<float*>(p.C0) + (int64_t)m * p.ldc + n;
-            if (p.bias) {
-#pragma unroll
-              for (int s = 0; s < 4; ++s) v[s] += p.bias[n + s];
-            }
-            *reinterpret_cast<float4*>(C) = make_float4(v[0], v[1], v[2], v[3]);
-          } else if constexpr (EPI == EPI_DSWIGLU) {
-            const bf16_t* H = static_cast<const bf16_t*>(p.aux);
-            bf16_t* dH = static_cast<bf16_t*>(p.C0);
-            const int64_t I = p.I;
-            uint2 hg = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + n);
-            uint2 hu = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + I + n);
-            float g[4] = {bf2f((bf16_t)(hg.x & 0xffff)), bf2f((bf16_t)(hg.x >> 16)),
-                          bf2f((bf16_t)(hg.y & 0xffff)), bf2f((bf16_t)(hg.y >> 16))};
-            float u[4] = {bf2f((bf16_t)(hu.x & 0xffff)), bf2f((bf16_t)(hu.x >> 16)),
-                          bf2f((bf16_t)(hu.y & 0xffff)), bf2f((bf16_t)(hu.y >> 16))};
-            float dg[4], du[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[s]));
-              dg[s] = v[s] * u[s] * sg * (1.0f + g[s] * (1.0f - sg));
-              du[s] = v[s] * g[s] * sg;
-            }
-            *reinterpret_cast<uint2*>(dH + (int64_t)m * 2 * I + n) =
-                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(dH + (int64_t)m * 2 * I + I + n) =
-                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-          }
-        }
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int slot = tid + NT * i;
+      const int row = slot >> 3;
+      const int c = (slot & 7) ^ (row & 7) ^ ((row >> 3) & 1);  // inverse of swz
+      kcol[i] = c * 8;
+      voff[i] = row0 + row < row_hi ? (int)(((int64_t)row * ld + c * 8) * 2) : OOB;
     }
   }
+  __device__ __forceinline__ void issue(bf16_t* tile, int kofs, int tid) const {
+    int k0 = k_lo + kofs;
+    __amdgpu_buffer_rsrc_t rs = rs0;
+    int lim = k_hi - k0;
+    if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
+    bf16_t* dst = tile + (tid >> 6) * 64 * 8;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) dma16(rs, dst + i * NT * 8, kcol[i] < lim ? voff[i] : OOB, k0 * 2);
+  }
+};
+
+// KN tile [64][COLS] (HALF: two sub-tiles [64][COLS/2], gate then up): slot s
+// of a (sub-)tile of width W holds row s / (W/8), physical chunk s % (W/8).
+template <int COLS, bool HALF, int NT>
+struct DmaKN {
+  static constexpr int W = HALF ? COLS / 2 : COLS;  // width of one (sub-)tile
+  static constexpr int CPR = W / 8;
+  static constexpr int CH = BK * CPR;
+  static constexpr int NR = CH / NT;
+  static_assert(CH % NT == 0, "whole load instructions");
+  int voff[NR];
+  int krow[NR];
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  int64_t ld;
+  int k_lo, k_hi;
+  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld_, int col0,
+                                       int col_hi, int k_lo_, int k_hi_, int, int tid) {
+    ld = ld_;
+    k_lo = k_lo_;
+    k_hi = k_hi_;
+    rs0 = make_rsrc(s0 + (int64_t)k_lo * ld + col0);
+    rs1 = make_rsrc((HALF ? s1 : s0) + (int64_t)k_lo * ld + col0);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int slot = tid + NT * i;
+      const int k = slot / CPR;
+      const int col = kn_swz<W>(k, slot % CPR) * 8;  // the swizzle is its own inverse
+      krow[i] = k;
+      voff[i] = col0 + col < col_hi ? (int)(((int64_t)k * ld + col) * 2) : OOB;
+    }
+  }
+  __device__ __forceinline__ void issue(bf16_t* tile, int kofs, int tid) const {
+    const int lim = k_hi - k_lo - kofs;
+    const int soff = (int)((int64_t)kofs * ld * 2);
+    bf16_t* dst = tile + (tid >> 6) * 64 * 8;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int v = krow[i] < lim ? voff[i] : OOB;
+      dma16(rs0, dst + i * NT * 8, v, soff);
+      if (HALF) dma16(rs1, dst + BK * W + i * NT * 8, v, soff);
+    }
+  }
+};
+
+template <bool KC, int ROWS, bool TWO, int NT> struct PickDma;
+template <int ROWS, bool TWO, int NT> struct PickDma<true, ROWS, TWO, NT> { typedef DmaKC<ROWS, TWO, NT> type; };
+template <int ROWS, bool TWO, int NT> struct PickDma<false, ROWS, TWO, NT> { typedef DmaKN<ROWS, TWO, NT> type; };
+
+// s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WGM, int WGN, int S, int AM, int BMD, int GMD, int B2, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(GemmParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int SZ = (BM + BN) * BK;  // elements per stage
+  static_assert(FM >= 1 && FN >= 1, "wave tile of at least 32x32");
+  static_assert(B2 != B2_NHALF || FN % 2 == 0, "gate|up halves need an even block count");
+  static_assert(S == 2 || S == 3, "two or three LDS stages");
+  __shared__ __attribute__((aligned(16))) bf16_t st0[SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t st1[SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t st2[S > 2 ? SZ : 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // ---- which tile
+  int mt_count = (GMD == G_MROWS) ? p.tiles[0] : p.m_tiles;
+  int per_group = mt_count * p.n_tiles;
+  int count = (GMD == G_KROWS) ? per_group * p.groups : per_group;
+  if ((int)blockIdx.x >= count) return;
+  int L = remap_xcd(blockIdx.x, count);
+  int e = 0;
+  if (GMD == G_KROWS) { e = L / per_group; L -= e * per_group; }
+  int mt, nt;
+  group_order(L, mt_count, p.n_tiles, mt, nt);
+  int m_lo, m_hi, k_lo, k_hi;
+  if (GMD == G_MROWS) {
+    e = p.tiles[1 + 2 * mt];
+    m_lo = p.tiles[2 + 2 * mt];
+    m_hi = min(m_lo + BM, p.off[e + 1]);
+    k_lo = 0;
+    k_hi = p.K;
+  } else {
+    m_lo = mt * BM;
+    m_hi = min(m_lo + BM, p.M);
+    if (GMD == G_KROWS && p.off) { k_lo = p.off[e]; k_hi = p.off[e + 1]; }
+    else { k_lo = 0; k_hi = p.K; }
+  }
+  const int n0 = nt * ((B2 == B2_NHALF) ? BN / 2 : BN);
+  const int n_hi = p.N;
+
+  const bf16_t* A = static_cast<const bf16_t*>(p.A);
+  const bf16_t* B0 = static_cast<const bf16_t*>(p.B0);
+  const bf16_t* B1 = static_cast<const bf16_t*>(p.B1);
+  if (GMD == G_MROWS) {
+    B0 += (int64_t)e * p.b_estride;
+    if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
+  }
+
+  typedef typename PickDma<AM == A_KC, BM, false, NT>::type LA;
+  typedef typename PickDma<BMD == B_KC, BN, B2 != B2_NONE, NT>::type LB;
+  constexpr int LPS = LA::NR + LB::NR * ((B2 == B2_NHALF) ? 2 : 1);  // loads per thread per stage
+  LA la;
+  LB lb;
+  la.init(A, A, p.lda, m_lo, m_hi, k_lo, k_hi, 0, tid);
+  lb.init(B0, B1, p.ldb, n0, n_hi, k_lo, k_hi, p.k_split, tid);
+
+  auto buf = [&](auto Ic) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int I = decltype(Ic)::value;
+    if constexpr (I == 0) return st0;
+    else if constexpr (I == 1) return st1;
+    else return st2;
+  };
+  auto issue = [&](bf16_t* b, int s) __attribute__((always_inline)) {
+    la.issue(b, s * BK, tid);
+    lb.issue(b + BM * BK, s * BK, tid);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (k_hi - k_lo + BK - 1) / BK;
+  if (nk > 0) issue(st0, 0);
+  if (S > 2 && nk > 1) {
+    issue(st1, 1);
+    wait_vmcnt<LPS>();  // slice 0 landed, slice 1 may still be in flight
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+
+  // Fragment reads of operands in the k-major layout use the LDS transpose
+  // read, which the compiler cannot tie to one stage buffer: it would wait for
+  // every load in flight before such a read.  So a step reads all of them
+  // first, then issues the next slice's loads, then runs the MFMAs (with the
+  // plain reads of k-contiguous operands interleaved).
+  constexpr bool A_TR = AM != A_KC, B_TR = BMD != B_KC;
+  auto step = [&](auto Uc, int kt) __attribute__((always_inline)) {
+    constexpr int U = decltype(Uc)::value;
+    const bf16_t* as = buf(std::integral_constant<int, U>{});
+    const bf16_t* bs = as + BM * BK;
+    auto a_frag = [&](int i, int ks) __attribute__((always_inline)) -> bf16x8 {
+      const int base = wm * WTM + i * 32;
+      if constexpr (AM == A_KC) return frag_kc(as, base, ks, lane);
+      else return frag_kn<BM>(as, base, ks, lane);
+    };
+    auto b_frag = [&](int j, int ks) __attribute__((always_inline)) -> bf16x8 {
+      if constexpr (B2 == B2_NHALF) {
+        const int h = j < FN / 2 ? 0 : 1;
+        const int base = wn * (WTN / 2) + (j - h * (FN / 2)) * 32;
+        return frag_kn<BN / 2>(bs + h * BK * (BN / 2), base, ks, lane);
+      } else {
+        const int base = wn * WTN + j * 32;
+        if constexpr (BMD == B_KC) return frag_kc(bs, base, ks, lane);
+        else return frag_kn<BN>(bs, base, ks, lane);
+      }
+    };
+    bf16x8 apre[A_TR ? BK / 16 : 1][A_TR ? FM : 1];
+    bf16x8 bpre[B_TR ? BK / 16 : 1][B_TR ? FN : 1];
+    if constexpr (A_TR) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) apre[ks][i] = a_frag(i, ks);
+    }
+    if constexpr (B_TR) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bpre[ks][j] = b_frag(j, ks);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + S - 1 < nk) issue(buf(std::integral_constant<int, (U + S - 1) % S>{}), kt + S - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[FM], bfg[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = A_TR ? apre[A_TR ? ks : 0][A_TR ? i : 0] : a_frag(i, ks);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfg[j] = B_TR ? bpre[B_TR ? ks : 0][B_TR ? j : 0] : b_frag(j, ks);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      // slice kt+1 must have landed; slices after it may stay in flight
+      if (S > 2 && kt + 2 < nk) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+    }
+  };
+
+  int kt0 = 0;
+  for (; kt0 + S <= nk; kt0 += S) {
+    [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+      (step(std::integral_constant<int, Us>{}, kt0 + Us), ...);
+    }(std::make_integer_sequence<int, S>{});
+  }
+  [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+    ((kt0 + Us < nk ? step(std::integral_constant<int, Us>{}, kt0 + Us) : void()), ...);
+  }(std::make_integer_sequence<int, S - 1>{});
+
+  epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,10 +857,26 @@ int tile_bn(TileCfg cfg) {
 #define MOE_GEMM_STAGES 2
 #endif
 
+#ifndef MOE_WIDE_WAVES
+#define MOE_WIDE_WAVES 8
+#endif
+
+#ifndef MOE_GEMM_DMA
+#define MOE_GEMM_DMA 0
+#endif
+
 template <int BMt, int BNt, int AM, int BMD, int GMD, int B2, int EPI>
 static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   constexpr int P = (BMt >= 128) ? MOE_GEMM_STAGES : 2;  // register stages in flight
-  gemm_bf16_kernel<BMt, BNt, P, AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
+  // 256x256 tiles: MOE_WIDE_WAVES = 8 runs two waves per SIMD (2 x 4 grid)
+  constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
+  if constexpr (MOE_GEMM_DMA) {
+    // LDS stages: three when they fit in 160 KB next to nothing else
+    constexpr int S = ((BMt + BNt) * BK * 2 * 3 <= 160 * 1024 && !(BMt == 128 && BNt == 128)) ? 3 : 2;
+    gemm_bf16_dma_kernel<BMt, BNt, 2, WGN, S, AM, BMD, GMD, B2, EPI><<<grid, 64 * 2 * WGN, 0, s>>>(p);
+  } else {
+    gemm_bf16_kernel<BMt, BNt, 2, WGN, P, AM, BMD, GMD, B2, EPI><<<grid, 64 * 2 * WGN, 0, s>>>(p);
+  }
 }
 
 template <int AM, int BMD, int GMD, int B2, int EPI>

@@ -117,16 +117,18 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_scatter_kernel(const int32_t
 }
 
 // One wavefront per token: read x[t] once, write it to every sorted position.
+// Lane j < k holds the token's j-th sorted position; the chunk loop reads it
+// back with a lane broadcast instead of reloading it.
 __global__ __launch_bounds__(256) void perm_gather_kernel(const uint4* x, const int32_t* inv, int T,
                                                           int k, int chunks, uint4* xp) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int32_t* iv = inv + (int64_t)t * k;
+  const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
   for (int c = lane; c < chunks; c += 64) {
-    uint4 v = x[(int64_t)t * chunks + c];
+    const uint4 v = x[(int64_t)t * chunks + c];
     for (int j = 0; j < k; ++j) {
-      int p = iv[j];
+      const int p = __builtin_amdgcn_readlane(myp, j);
       if (p >= 0) xp[(int64_t)p * chunks + c] = v;
     }
   }
@@ -196,27 +198,43 @@ template <> struct Chunk<float> {
 };
 
 // y[t] = sum_j w[t,j] * src[inv[t,j]] in ascending j (w NULL: weight 1).
+// One wavefront per token; lane j < k holds slot j's position and weight,
+// broadcast to the wavefront in the chunk loop; the k row loads of a chunk are
+// all issued before the first is used.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_sum_kernel(const uint4* src, const int32_t* inv,
                                                          const float* w, int Tn, int k, int chunks,
                                                          uint4* y) {
   constexpr int N = Chunk<T>::N;
+  constexpr int G = 8;  // rows in flight per lane
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  const int32_t* iv = inv + (int64_t)t * k;
+  const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
+  const float myw = lane < k ? (w ? w[(int64_t)t * k + lane] : 1.0f) : 0.0f;
   for (int c = lane; c < chunks; c += 64) {
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      int p = iv[j];
-      if (p < 0) continue;
-      float g = w ? w[(int64_t)t * k + j] : 1.0f;
-      float f[N];
-      Chunk<T>::unpack(src[(int64_t)p * chunks + c], f);
+    for (int j0 = 0; j0 < k; j0 += G) {
+      uint4 v[G];
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      for (int jj = 0; jj < G; ++jj) {
+        const int j = j0 + jj;
+        const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
+        v[jj] = p >= 0 ? src[(int64_t)p * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) {
+        const int j = j0 + jj;
+        const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
+        if (p < 0) continue;
+        const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), j));
+        float f[N];
+        Chunk<T>::unpack(v[jj], f);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      }
     }
     y[(int64_t)t * chunks + c] = Chunk<T>::pack(acc);
   }
@@ -237,6 +255,7 @@ moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float*
 }
 
 // dyp[inv[t,j]] = w[t,j] * dy[t];  dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when dropped).
+// One wavefront per token, slot data broadcast from lane j as above.
 constexpr int MAXK = 32;
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const uint4* yp,
@@ -247,7 +266,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  const int32_t* iv = inv + (int64_t)t * k;
+  const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
+  const float myw = lane < k ? w[(int64_t)t * k + lane] : 0.0f;
   float part[MAXK];
 #pragma unroll
   for (int j = 0; j < MAXK; ++j) part[j] = 0.f;
@@ -255,19 +275,30 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
     float fy[N];
     Chunk<T>::unpack(dy[(int64_t)t * chunks + c], fy);
 #pragma unroll
-    for (int j = 0; j < MAXK; ++j) {
-      const int p = j < k ? iv[j] : -1;
-      if (p >= 0) {
+    for (int j0 = 0; j0 < MAXK; j0 += 8) {
+      if (j0 >= k) break;  // uniform
+      uint4 v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
+        v[jj] = p >= 0 ? yp[(int64_t)p * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
+        if (p < 0) continue;
+        const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), j));
         float f[N], o[N];
-        Chunk<T>::unpack(yp[(int64_t)p * chunks + c], f);
-        const float g = w[(int64_t)t * k + j];
-        float acc = 0.f;
+        Chunk<T>::unpack(v[jj], f);
+        float a = 0.f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-          acc = fmaf(fy[i], f[i], acc);
+          a = fmaf(fy[i], f[i], a);
           o[i] = g * fy[i];
         }
-        part[j] += acc;
+        part[j] += a;
         dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
       }
     }
@@ -278,7 +309,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
       float v = part[j];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) dw[(int64_t)t * k + j] = iv[j] >= 0 ? v : 0.f;
+      if (lane == 0) dw[(int64_t)t * k + j] = __builtin_amdgcn_readlane(myp, j) >= 0 ? v : 0.f;
     }
   }
 }
