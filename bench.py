@@ -82,12 +82,62 @@ def cpu_baseline(budget_s: float):
         O.layer_bwd(f, dY, x, a["Wr"], a["Wg"], a["Wu"], a["Wd"], w.k, w.gate)
         return time.perf_counter() - t0
 
-    t_probe = step(256)
-    Ts = int(min(w.T, max(256, 256 * budget_s / max(t_probe, 1e-3))) // 256 * 256)
+    t_probe = step(512)
+    est_full = t_probe * w.T / 512  # overestimates: the probe carries fixed costs
+    Ts = w.T if est_full <= 2 * budget_s else int(max(512, 512 * budget_s / t_probe)) // 256 * 256
     dt = step(Ts)
     return {"value": round(Ts / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one fwd+bwd of the layer on the first {Ts} of {w.T} tokens "
                       f"(balanced gate, all {w.E} experts), numpy fp64, {dt:.1f} s"}
+
+
+# GEMM roles: the last template argument of the GEMM kernels
+ROLE_NAMES = {0: "route_logits", 1: "ffn_gateup_fwd", 2: "ffn_down_fwd", 3: "ffn_down_dgrad",
+              4: "ffn_gateup_dgrad", 5: "ffn_down_wgrad", 6: "ffn_gateup_wgrad", 7: "route_bwd_dw",
+              8: "route_bwd_dx"}
+
+
+def gemm_role_of(kernel_name: str):
+    if "gemm_bf16" not in kernel_name:
+        return None
+    args = kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")
+    return ROLE_NAMES.get(int(args[-1]))
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int) -> dict:
+    """HBM bytes per launch of each layer kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for a fill (writes) and a sum (reads) of calib_mib MiB."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        vals = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    calib = calib_mib * (1 << 20)
+    rd = [v for k, v in fetch.items() if "reduce" in k.lower()]
+    wr = [v for k, v in write.items() if "FillFunctor" in k]
+    f_read = calib / (max(rd[0]) * 1024) if rd else 1.0
+    f_write = calib / (max(wr[0]) * 1024) if wr else 1.0
+    out = {"source_hash": kernel_source_hash(), "calibration": {
+        "read_factor": round(f_read, 4), "write_factor": round(f_write, 4),
+        "calib_bytes": calib}, "kernels": {}, "raw_kib_per_dispatch": {}}
+    for k in fetch:
+        f = sum(fetch[k]) / len(fetch[k])
+        w_ = sum(write.get(k, [0.0])) / max(len(write.get(k, [])), 1)
+        out["raw_kib_per_dispatch"][k] = {"FETCH_SIZE": round(f, 1), "WRITE_SIZE": round(w_, 1)}
+        role = gemm_role_of(k)
+        if role:
+            out["kernels"][role] = {"bytes_per_launch": int(f * 1024 * f_read + w_ * 1024 * f_write),
+                                    "read_bytes": int(f * 1024 * f_read),
+                                    "write_bytes": int(w_ * 1024 * f_write)}
+    return out
 
 
 def main():
@@ -97,10 +147,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one device copy of this size (HBM counter calibration)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--calib-mib", type=int, default=0,
+                    help="also run a fill and a sum of this size (HBM counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calib_mib or 1024)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(res, fh, indent=1)
+        print(json.dumps(res["kernels"]))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -135,21 +193,34 @@ def main():
         if w.backward:
             backward(shape, buf, dev["dY"], dev["x"], dev.get("Wr"), dev["Wg"], dev["Wu"], dev["Wd"])
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20)
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+    if args.calib_mib:
+        # HBM counter calibration: a fill that writes, and a sum that reads,
+        # exactly calib_mib MiB (their FETCH_SIZE / WRITE_SIZE give the scale)
+        n = args.calib_mib * (1 << 20) // 4
+        t = torch.ones(n, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        del src, dst
+        t.sum()
+        torch.cuda.synchronize()
+        del t
 
-    B.prof_enable(True)
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # calibration (untimed): one step with every kernel on the HIP-event timer
+    # to find the dominant grouped GEMM
+    B.prof_select(None)
+    B.prof_enable(True)
     B.prof_reset()
-    log(f"[bench] timing {args.steps} steps")
+    step()
+    torch.cuda.synchronize()
+    calib = {n: B.prof_read(n)[0] for n in B.prof_names()}
+    dom = max((n for n in calib if n in GEMMS), key=lambda n: calib[n])
+    # timed region: only the dominant kernel carries HIP events (recorded on
+    # the stream it is launched on), so other kernels run back to back
+    B.prof_select([dom])
+    B.prof_reset()
+    log(f"[bench] timing {args.steps} steps (event-timed kernel: {dom})")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -160,20 +231,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    dom_ms, dom_n = B.prof_read(dom)
+    # every kernel's average, from an instrumented pass after the timed region
+    B.prof_select(None)
+    B.prof_reset()
+    for _ in range(max(3, args.steps // 4)):
+        step()
+    torch.cuda.synchronize()
     kernels = {}
     for name in B.prof_names():
         tot, n = B.prof_read(name)
-        kernels[name] = {"ms_total": tot, "launches": n, "us_avg": 1000.0 * tot / max(n, 1)}
+        kernels[name] = {"us_avg": 1000.0 * tot / max(n, 1), "launches": n}
+    kernels[dom] = {"us_avg": 1000.0 * dom_ms / max(dom_n, 1), "launches": dom_n}
     B.prof_enable(False)
-
-    # the same number of steps without the kernel timer (its events add gaps)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_plain = e0.elapsed_time(e1) / args.steps
 
     R = int(buf["offsets"][-1].item())
     El = w.E_loc
@@ -185,7 +255,6 @@ def main():
             gem[name] = {"us": round(us, 2), "tflops": round(f / us / 1e6, 1),
                          "gbs": round(b / us / 1e3, 1), "mfma_frac": round(f / us / 1e6 / PEAK_BF16_TFLOPS, 3),
                          "hbm_frac": round(b / us / 1e3 / PEAK_HBM_GBS, 3)}
-    dom = max(gem, key=lambda k: kernels[k]["ms_total"])
     fl, by = GEMMS[dom]
     flops = fl(R, w.d, w.I, El)
     achieved = flops / kernels[dom]["us_avg"] / 1e6
@@ -220,7 +289,6 @@ def main():
         "grouped_gemm": {"tflops_all_six": round(gemm_flops / gemm_total_us / 1e6, 1),
                          "mfma_frac_all_six": round(gemm_flops / gemm_total_us / 1e6 / PEAK_BF16_TFLOPS, 4),
                          "kernels": gem},
-        "ms_per_step_without_kernel_timer": round(ms_plain, 4),
         "wall_s_timed": round(wall, 3),
         "kernels_us_avg": {k: round(v["us_avg"], 2) for k, v in kernels.items()},
     }

@@ -36,9 +36,9 @@
  *   weights and their gradients are bf16 (uint16 bit patterns); logits, gate
  *   weights and their gradients are fp32; every accumulation is fp32 and every
  *   conversion to bf16 rounds to nearest even.
- * - Supported shapes: d % 64 == 0, I % 64 == 0, E % 8 == 0 or E <= 8, E <= 512,
- *   1 <= k <= min(E, 32), T*k < 2^31, and every pointer 16-byte aligned.
- *   Others return MOE_ERR_UNSUPPORTED.
+ * - Supported shapes: d % 64 == 0, I % 64 == 0, E <= 512 (and E % 8 == 0 for
+ *   bf16), 1 <= k <= min(E, 32), T*k < 2^31, and every pointer 16-byte aligned
+ *   (workspaces 256-byte aligned).  Others return MOE_ERR_UNSUPPORTED.
  * - Results are deterministic: no floating-point atomics; every sum has a fixed
  *   order, so two identical calls give bit-identical outputs.
  */
@@ -127,7 +127,8 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
  *   perm [R_cap] int32: perm[p] = r of the row at sorted position p
  *     (positions >= group_offsets[E_loc] are left untouched);
  *   inv [T*k] int32: sorted position of row r, or -1 if r is not local, was
- *     dropped by the capacity, or has an expert id outside [0, E);
+ *     dropped by the capacity, or repeats an expert id an earlier slot of the
+ *     same token already holds (routing never produces repeats);
  *   xp [R_cap, d] (dtype): xp[p] = x[perm[p] / k] (rows past the end untouched).
  * ws/ws_bytes: workspace of moe_workspace_size(MOE_OP_PERMUTE). */
 moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, const void* x,
@@ -218,6 +219,9 @@ moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* 
  * moe_prof_names(): the names recorded so far, comma-separated (static buffer
  * valid until the next moe_prof_* call). */
 moe_status_t moe_prof_enable(int on);
+/* Record only the kernels named in `names` (comma-separated); NULL or "" records
+ * every kernel.  Each recorded launch adds two event records to its stream. */
+moe_status_t moe_prof_select(const char* names);
 moe_status_t moe_prof_reset(void);
 moe_status_t moe_prof_read(const char* name, double* total_ms, int64_t* launches);
 const char* moe_prof_names(void);

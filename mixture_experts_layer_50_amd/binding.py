@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_size",
            "moe_route", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine", "moe_combine_bwd",
            "moe_grouped_ffn_bwd", "moe_permute_bwd", "moe_route_bwd", "moe_prof_enable",
-           "moe_prof_reset", "moe_prof_read", "moe_prof_names"]
+           "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names"]
 
 
 class MoEError(RuntimeError):
@@ -90,6 +90,7 @@ def load_library() -> ctypes.CDLL:
         "moe_permute_bwd": [S, P, P, P, P],
         "moe_route_bwd": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_prof_enable": [I32],
+        "moe_prof_select": [ctypes.c_char_p],
         "moe_prof_reset": [],
         "moe_prof_read": [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                           ctypes.POINTER(ctypes.c_int64)],
@@ -186,6 +187,12 @@ def moe_route_bwd(shape, x, w_router, topk_idx, topk_w, dtopk_w, dlogits, dw_rou
 
 def prof_enable(on: bool = True):
     _check("moe_prof_enable", load_library().moe_prof_enable(1 if on else 0))
+
+
+def prof_select(names=None):
+    """Record only these kernel names (iterable of str); None records all."""
+    arg = None if not names else ",".join(names).encode()
+    _check("moe_prof_select", load_library().moe_prof_select(arg))
 
 
 def prof_reset():

@@ -44,6 +44,14 @@ bool g_prof_on = false;
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 std::string g_names;
+std::vector<std::string> g_select;  // names to record; empty = every kernel
+
+bool selected(const char* name) {
+  if (g_select.empty()) return true;
+  for (auto& n : g_select)
+    if (n == name) return true;
+  return false;
+}
 
 hipEvent_t pool_get() {
   if (!g_pool.empty()) {
@@ -60,6 +68,7 @@ hipEvent_t pool_get() {
 int prof_begin(const char* name, hipStream_t s) {
   if (!g_prof_on) return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!selected(name)) return -1;
   ProfRec r{name, pool_get(), pool_get()};
   if (!r.a || !r.b) return -1;
   (void)hipEventRecord(r.a, s);
@@ -76,6 +85,23 @@ void prof_end(int tok, hipStream_t s) {
 
 extern "C" moe_status_t moe_prof_enable(int on) {
   g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status_t moe_prof_select(const char* names) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_select.clear();
+  if (!names) return MOE_OK;
+  std::string cur;
+  for (const char* c = names;; ++c) {
+    if (*c == ',' || *c == 0) {
+      if (!cur.empty()) g_select.push_back(cur);
+      cur.clear();
+      if (*c == 0) break;
+    } else {
+      cur += *c;
+    }
+  }
   return MOE_OK;
 }
 
@@ -221,28 +247,6 @@ moe_status_t opt(const char* fn, std::initializer_list<std::pair<const char*, co
   return MOE_OK;
 }
 
-// Tile shape of each bf16 expert GEMM.
-#ifndef MOE_TILE_GATEUP_FWD
-#define MOE_TILE_GATEUP_FWD TILE_256x256
-#endif
-#ifndef MOE_TILE_DOWN_FWD
-#define MOE_TILE_DOWN_FWD TILE_256x256
-#endif
-#ifndef MOE_TILE_DOWN_DGRAD
-#define MOE_TILE_DOWN_DGRAD TILE_256x128
-#endif
-#ifndef MOE_TILE_GATEUP_DGRAD
-#define MOE_TILE_GATEUP_DGRAD TILE_256x256
-#endif
-#ifndef MOE_WGRAD_TILE
-#define MOE_WGRAD_TILE TILE_128x128
-#endif
-constexpr TileCfg TILE_GATEUP_FWD = MOE_TILE_GATEUP_FWD;
-constexpr TileCfg TILE_DOWN_FWD = MOE_TILE_DOWN_FWD;
-constexpr TileCfg TILE_DOWN_DGRAD = MOE_TILE_DOWN_DGRAD;
-constexpr TileCfg TILE_GATEUP_DGRAD = MOE_TILE_GATEUP_DGRAD;
-constexpr TileCfg WGRAD_TILE = MOE_WGRAD_TILE;
-
 // Tile tables of the row-grouped GEMMs: one for 256-row and one for 128-row
 // tiles, each (1 + 2 * (R_cap / BM + E_loc)) int32.
 int64_t one_table_bytes(const Dims& D, int bm) {
@@ -258,8 +262,8 @@ struct TileTables {
   const int32_t* off;
   hipStream_t s;
   bool built256 = false, built128 = false;
-  moe_status_t get(TileCfg cfg, const int32_t** out) {
-    const int bm = tile_bm(cfg);
+  moe_status_t get(GemmRole role, const int32_t** out) {
+    const int bm = tile_bm(role_tile(role));
     int32_t* t = bm == 256 ? base : base + one_table_bytes(D, 256) / 4;
     bool& built = bm == 256 ? built256 : built128;
     if (!built) {
@@ -324,8 +328,7 @@ extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const
   p.m_tiles = (int)ceil_div(D.T, 64); p.n_tiles = (int)ceil_div(D.E, 64);
   p.groups = 1;
   p.C0 = logits; p.ldc = D.E; p.bias = bias;
-  MOE_TRY(launch_gemm(D.bf16, A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS, TILE_64x64, p,
-                      p.m_tiles, S(stream), "route_logits"));
+  MOE_TRY(launch_gemm(D.bf16, R_ROUTE_LOGITS, p, p.m_tiles, S(stream)));
   return launch_topk_softmax(logits, D.T, D.E, D.k, topk_idx, topk_w, S(stream));
 }
 
@@ -356,29 +359,27 @@ extern "C" moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void
   MOE_TRY(check_ws(fn, D, MOE_OP_FFN_FWD, ws, ws_bytes_));
   TileTables tt{D, static_cast<int32_t*>(ws), group_offsets, S(stream)};
   // fp32: the row count; bf16: the most M tiles the tile table can hold
-  auto rows_or_tiles = [&](TileCfg c) { return D.bf16 ? max_m_tiles(D, tile_bm(c)) : D.R_cap; };
+  auto rows_or_tiles = [&](GemmRole r) { return D.bf16 ? max_m_tiles(D, tile_bm(role_tile(r))) : D.R_cap; };
 
   GemmParams g{};
   g.A = xp; g.lda = D.d;
   g.B0 = w_gate; g.B1 = w_up; g.ldb = D.I; g.b_estride = (int64_t)D.d * D.I;
   g.N = D.I; g.K = D.d;
   g.off = group_offsets; g.groups = D.E_loc;
-  g.n_tiles = (int)ceil_div(D.I, tile_bn(TILE_GATEUP_FWD) / 2);
+  g.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_GATEUP_FWD)) / 2);
   g.C0 = h_save; g.C2 = a_save; g.I = D.I;
-  if (D.bf16) MOE_TRY(tt.get(TILE_GATEUP_FWD, &g.tiles));
-  MOE_TRY(launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU, TILE_GATEUP_FWD, g,
-                      rows_or_tiles(TILE_GATEUP_FWD), S(stream), "ffn_gateup_fwd"));
+  if (D.bf16) MOE_TRY(tt.get(R_GATEUP_FWD, &g.tiles));
+  MOE_TRY(launch_gemm(D.bf16, R_GATEUP_FWD, g, rows_or_tiles(R_GATEUP_FWD), S(stream)));
 
   GemmParams p{};
   p.A = a_save; p.lda = D.I;
   p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
   p.N = D.d; p.K = D.I;
   p.off = group_offsets; p.groups = D.E_loc;
-  p.n_tiles = (int)ceil_div(D.d, tile_bn(TILE_DOWN_FWD));
+  p.n_tiles = (int)ceil_div(D.d, tile_bn(role_tile(R_DOWN_FWD)));
   p.C0 = yp; p.ldc = D.d;
-  if (D.bf16) MOE_TRY(tt.get(TILE_DOWN_FWD, &p.tiles));
-  return launch_gemm(D.bf16, A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE, TILE_DOWN_FWD, p,
-                     rows_or_tiles(TILE_DOWN_FWD), S(stream), "ffn_down_fwd");
+  if (D.bf16) MOE_TRY(tt.get(R_DOWN_FWD, &p.tiles));
+  return launch_gemm(D.bf16, R_DOWN_FWD, p, rows_or_tiles(R_DOWN_FWD), S(stream));
 }
 
 extern "C" moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,
@@ -422,7 +423,7 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
   hipStream_t s = S(stream);
   TileTables tt{D, reinterpret_cast<int32_t*>(wsb + round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256)),
                 group_offsets, s};
-  auto rows_or_tiles = [&](TileCfg c) { return D.bf16 ? max_m_tiles(D, tile_bm(c)) : D.R_cap; };
+  auto rows_or_tiles = [&](GemmRole r) { return D.bf16 ? max_m_tiles(D, tile_bm(role_tile(r))) : D.R_cap; };
 
   {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
     GemmParams p{};
@@ -430,11 +431,10 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
     p.N = D.I; p.K = D.d;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.I, tile_bn(TILE_DOWN_DGRAD));
+    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_DOWN_DGRAD)));
     p.C0 = dH; p.aux = h_save; p.I = D.I;
-    if (D.bf16) MOE_TRY(tt.get(TILE_DOWN_DGRAD, &p.tiles));
-    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU, TILE_DOWN_DGRAD, p,
-                        rows_or_tiles(TILE_DOWN_DGRAD), s, "ffn_down_dgrad"));
+    if (D.bf16) MOE_TRY(tt.get(R_DOWN_DGRAD, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, R_DOWN_DGRAD, p, rows_or_tiles(R_DOWN_DGRAD), s));
   }
   {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
     GemmParams p{};
@@ -443,11 +443,10 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.k_split = D.I;
     p.N = D.d; p.K = 2 * D.I;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.d, tile_bn(TILE_GATEUP_DGRAD));
+    p.n_tiles = (int)ceil_div(D.d, tile_bn(role_tile(R_GATEUP_DGRAD)));
     p.C0 = dxp; p.ldc = D.d;
-    if (D.bf16) MOE_TRY(tt.get(TILE_GATEUP_DGRAD, &p.tiles));
-    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE, TILE_GATEUP_DGRAD, p,
-                        rows_or_tiles(TILE_GATEUP_DGRAD), s, "ffn_gateup_dgrad"));
+    if (D.bf16) MOE_TRY(tt.get(R_GATEUP_DGRAD, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, R_GATEUP_DGRAD, p, rows_or_tiles(R_GATEUP_DGRAD), s));
   }
   {  // a8: dWd[e] = A_e^T dYp_e
     GemmParams p{};
@@ -455,10 +454,10 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = dyp; p.ldb = D.d;
     p.M = D.I; p.N = D.d;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.m_tiles = (int)ceil_div(D.I, tile_bm(WGRAD_TILE)); p.n_tiles = (int)ceil_div(D.d, tile_bn(WGRAD_TILE));
+    const TileCfg t = role_tile(R_DOWN_WGRAD);
+    p.m_tiles = (int)ceil_div(D.I, tile_bm(t)); p.n_tiles = (int)ceil_div(D.d, tile_bn(t));
     p.C0 = dw_down; p.ldc = D.d; p.c_estride = (int64_t)D.I * D.d;
-    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, WGRAD_TILE, p,
-                        p.m_tiles, s, "ffn_down_wgrad"));
+    MOE_TRY(launch_gemm(D.bf16, R_DOWN_WGRAD, p, p.m_tiles, s));
   }
   {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
     GemmParams p{};
@@ -466,11 +465,11 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = dH; p.ldb = 2 * (int64_t)D.I;
     p.M = D.d; p.N = 2 * D.I;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.m_tiles = (int)ceil_div(D.d, tile_bm(WGRAD_TILE)); p.n_tiles = (int)ceil_div(2 * D.I, tile_bn(WGRAD_TILE));
+    const TileCfg t = role_tile(R_GATEUP_WGRAD);
+    p.m_tiles = (int)ceil_div(D.d, tile_bm(t)); p.n_tiles = (int)ceil_div(2 * D.I, tile_bn(t));
     p.C0 = dw_gate; p.C1 = dw_up; p.n_split = D.I; p.ldc = D.I;
     p.c_estride = (int64_t)D.d * D.I;
-    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, WGRAD_TILE, p,
-                        p.m_tiles, s, "ffn_gateup_wgrad"));
+    MOE_TRY(launch_gemm(D.bf16, R_GATEUP_WGRAD, p, p.m_tiles, s));
   }
   return MOE_OK;
 }
@@ -515,8 +514,7 @@ extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, c
     p.off = nullptr; p.groups = 1;
     p.m_tiles = (int)ceil_div(D.d, 64); p.n_tiles = (int)ceil_div(D.E, 64);
     p.C0 = dw_router; p.ldc = D.E;
-    MOE_TRY(launch_gemm(D.bf16, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE, TILE_64x64, p,
-                        p.m_tiles, s, "route_bwd_dw"));
+    MOE_TRY(launch_gemm(D.bf16, R_ROUTE_DW, p, p.m_tiles, s));
   }
   if (dbias) MOE_TRY(launch_col_sum(dlogits, D.T, D.E, dbias, s));
   {  // dX += dL Wr^T
@@ -527,8 +525,7 @@ extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, c
     p.m_tiles = (int)ceil_div(D.T, 64); p.n_tiles = (int)ceil_div(D.d, 64);
     p.groups = 1;
     p.C0 = dx; p.ldc = D.d;
-    MOE_TRY(launch_gemm(D.bf16, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM, TILE_64x64, p,
-                        p.m_tiles, s, "route_bwd_dx"));
+    MOE_TRY(launch_gemm(D.bf16, R_ROUTE_DX, p, p.m_tiles, s));
   }
   return MOE_OK;
 }

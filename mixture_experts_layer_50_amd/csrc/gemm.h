@@ -63,19 +63,34 @@ struct GemmParams {
 // Tile shapes of the bf16 MFMA kernels.
 enum TileCfg { TILE_256x256 = 0, TILE_256x128 = 1, TILE_64x64 = 2, TILE_128x128 = 3 };
 
-// Launch one GEMM.  `is_bf16` selects the bf16 MFMA kernel or the fp32 kernel;
-// the template-like mode arguments select the instantiation.  For G_MROWS the
-// caller has already built the tile table (launch_tile_table) with the BM the
-// chosen tile shape uses (tile_bm()).  `name` labels the kernel for the timer.
-moe_status_t launch_gemm(bool is_bf16, int amode, int bmode, int gmode, int b2, int epi,
-                         TileCfg cfg, const GemmParams& p, int max_m_tiles,
-                         hipStream_t s, const char* name);
+// The GEMMs of the layer.  Each role fixes the operand layouts, the grouping
+// and the epilogue, and is its own kernel instance (so profilers tell them apart).
+enum GemmRole {
+  R_ROUTE_LOGITS = 0,   // logits = x Wr (+ b)
+  R_GATEUP_FWD = 1,     // [Hg | Hu] = Xp [Wg | Wu], A = silu(Hg) Hu
+  R_DOWN_FWD = 2,       // Yp = A Wd
+  R_DOWN_DGRAD = 3,     // dA = dYp Wd^T, then dSwiGLU -> [dHg | dHu]
+  R_GATEUP_DGRAD = 4,   // dXp = dHg Wg^T + dHu Wu^T
+  R_DOWN_WGRAD = 5,     // dWd = A^T dYp
+  R_GATEUP_WGRAD = 6,   // [dWg | dWu] = Xp^T [dHg | dHu]
+  R_ROUTE_DW = 7,       // dWr = x^T dL
+  R_ROUTE_DX = 8        // dX += dL Wr^T
+};
 
+// Tile shape each role runs with (bf16).
+TileCfg role_tile(GemmRole role);
 int tile_bm(TileCfg cfg);
 int tile_bn(TileCfg cfg);
+const char* role_name(GemmRole role);
+
+// Launch one GEMM: the bf16 MFMA kernel of the role, or the fp32 kernel.  For
+// G_MROWS the caller has built the tile table (launch_tile_table) for
+// tile_bm(role_tile(role)); max_m_tiles bounds its entries (fp32: the row count).
+moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
+                         hipStream_t s);
 
 // Tile table for G_MROWS: tiles[0] = number of M tiles, then for each tile
-// (expert, first row) in expert order; at most max_tiles entries.
+// (expert, first row) in expert order.
 moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* tiles,
                                hipStream_t s);
 

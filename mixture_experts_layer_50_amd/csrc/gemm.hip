@@ -76,8 +76,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
+// CPOL: cache-policy bits of the load (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
+template <int CPOL>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CPOL));
 }
 
 // Loader of a KC tile: row r of the tile is src[(row0 + r) * ld + k], rows
@@ -85,7 +87,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
 // k >= ksplit from s1 at k - ksplit (ksplit is a multiple of 64, so one K
 // slice never straddles it).  The per-lane address state is kept once; the
 // loaded data lives in a separate register array per pipeline stage.
-template <int ROWS, bool TWO, int NT>
+template <int ROWS, bool TWO, int NT, int CPOL>
 struct LoaderKC {
   static constexpr int CH = ROWS * 8;
   static constexpr int NR = (CH + NT - 1) / NT;
@@ -117,7 +119,7 @@ struct LoaderKC {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int kc = ((tid + NT * i) & 7) * 8;
-      d.r[i] = buf_load16(rs, kc < lim ? voff[i] : OOB, k0 * 2);
+      d.r[i] = buf_load16<CPOL>(rs, kc < lim ? voff[i] : OOB, k0 * 2);
     }
   }
   __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
@@ -137,7 +139,7 @@ struct LoaderKC {
 // zeros.  HALF: tile columns [0, COLS/2) come from s0 at col0 + c, columns
 // [COLS/2, COLS) from s1 at col0 + c - COLS/2 (the gate | up halves); each
 // load instruction reads one half only, so its buffer descriptor is uniform.
-template <int COLS, bool HALF, int NT>
+template <int COLS, bool HALF, int NT, int CPOL>
 struct LoaderKN {
   static constexpr int CPR = HALF ? COLS / 16 : COLS / 8;  // chunks per row and source
   static constexpr int CH = BK * CPR;                        // chunks per source
@@ -169,8 +171,8 @@ struct LoaderKN {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int v = (tid + NT * i) / CPR < lim ? voff[i] : OOB;
-      d.r[i] = buf_load16(rs0, v, soff);
-      if (HALF) d.r[NS + i] = buf_load16(rs1, v, soff);
+      d.r[i] = buf_load16<CPOL>(rs0, v, soff);
+      if (HALF) d.r[NS + i] = buf_load16<CPOL>(rs1, v, soff);
     }
   }
   __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
@@ -188,9 +190,9 @@ struct LoaderKN {
   }
 };
 
-template <bool KC, int ROWS, bool TWO, int NT> struct PickLoader;
-template <int ROWS, bool TWO, int NT> struct PickLoader<true, ROWS, TWO, NT> { typedef LoaderKC<ROWS, TWO, NT> type; };
-template <int ROWS, bool TWO, int NT> struct PickLoader<false, ROWS, TWO, NT> { typedef LoaderKN<ROWS, TWO, NT> type; };
+template <bool KC, int ROWS, bool TWO, int NT, int CPOL> struct PickLoader;
+template <int ROWS, bool TWO, int NT, int CPOL> struct PickLoader<true, ROWS, TWO, NT, CPOL> { typedef LoaderKC<ROWS, TWO, NT, CPOL> type; };
+template <int ROWS, bool TWO, int NT, int CPOL> struct PickLoader<false, ROWS, TWO, NT, CPOL> { typedef LoaderKN<ROWS, TWO, NT, CPOL> type; };
 
 // MFMA operand fragment (32 rows x 16 k): lane l holds row base + (l & 31),
 // k = 16 ks + 8 (l >> 5) + 0..7.
@@ -304,6 +306,54 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
   }
 }
 
+// Plain-store epilogue staged through LDS: the wave tiles are written to LDS
+// as bf16, then every store instruction writes whole 16-byte chunks of
+// consecutive columns (full cache lines per row) instead of 8-byte pieces
+// scattered over 32 rows.  16-byte chunk c of LDS row r sits at c ^ (r & 15).
+template <int BM, int BN, int FM, int FN, int WTM, int WTN, int NT, int GMD>
+__device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x16 (&acc)[FM][FN],
+                                                      bf16_t* lds, int m_lo, int m_hi, int n0,
+                                                      int e, int wm, int wn, int lane, int tid) {
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  static_assert(CPR >= 16, "swizzle needs 16 chunks per row");
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
+        const int c = (n >> 3) ^ (r & 15);
+        *reinterpret_cast<uint2*>(lds + r * BN + c * 8 + (n & 7)) =
+            make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                       pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+      }
+    }
+  }
+  __syncthreads();
+  bf16_t* C0 = static_cast<bf16_t*>(p.C0);
+  bf16_t* C1 = static_cast<bf16_t*>(p.C1);
+  if (GMD == G_KROWS) {
+    C0 += (int64_t)e * p.c_estride;
+    if (C1) C1 += (int64_t)e * p.c_estride;
+  }
+#pragma unroll
+  for (int q0 = 0; q0 < BM * CPR; q0 += NT) {
+    const int q = q0 + tid;
+    const int r = q / CPR, c = q % CPR;
+    const int m = m_lo + r;
+    int n = n0 + c * 8;
+    if (m < m_hi && n < p.N) {
+      bf16_t* C = C0;
+      if (p.n_split > 0 && n >= p.n_split) { C = C1; n -= p.n_split; }
+      *reinterpret_cast<uint4*>(C + (int64_t)m * p.ldc + n) =
+          *reinterpret_cast<const uint4*>(lds + r * BN + (c ^ (r & 15)) * 8);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM.  WGM x WGN waves, each owning a (BM/WGM) x
 // (BN/WGN) block of 32x32 MFMA tiles.  P register stages: while the
@@ -312,7 +362,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
 // With the gate|up halves (B2_NHALF) the first FN/2 column blocks of a wave
 // are gate columns and the last FN/2 the matching up columns.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI>
+template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -358,8 +408,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
     if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
   }
 
-  typedef typename PickLoader<AM == A_KC, BM, false, NT>::type LA;
-  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT>::type LB;
+#ifndef MOE_WEIGHT_CPOL
+#define MOE_WEIGHT_CPOL 2
+#endif
+  // expert weights (B of the row-grouped GEMMs) stream through once; the
+  // activation rows (A) are re-read by every column tile of the expert
+  constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
+  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0>::type LA;
+  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL>::type LB;
   LA la;
   LB lb;
   typename LA::Data da[P];
@@ -452,7 +508,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
      ...);
   }(std::make_integer_sequence<int, 2 * P - 1>{});
 
-  epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
+#ifndef MOE_STAGED_STORE
+#define MOE_STAGED_STORE 1
+#endif
+  if constexpr (EPI == EPI_STORE && MOE_STAGED_STORE && BN / 8 >= 16 && BM * BN <= (BM + BN) * BK * 2)
+    epilogue_store_staged<BM, BN, FM, FN, WTM, WTN, NT, GMD>(p, acc, smem, m_lo, m_hi, n0, e, wm,
+                                                             wn, lane, tid);
+  else
+    epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
 }
 
 // ===========================================================================
@@ -561,7 +624,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int WGM, int WGN, int S, int AM, int BMD, int GMD, int B2, int EPI>
+template <int BM, int BN, int WGM, int WGN, int S, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(GemmParams p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -729,7 +792,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(GemmParam
 // ---------------------------------------------------------------------------
 // fp32 kernel: one output (or one gate/up pair) per thread, fp32 FMA.
 // ---------------------------------------------------------------------------
-template <int AM, int BMD, int GMD, int B2, int EPI>
+template <int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   const int n = blockIdx.x * 16 + (threadIdx.x & 15);
   const int m = blockIdx.y * 16 + (threadIdx.x >> 4);
@@ -851,128 +914,129 @@ int tile_bn(TileCfg cfg) {
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-#define MOE_KEY(am, bm, gm, b2, epi) ((am) | ((bm) << 1) | ((gm) << 2) | ((b2) << 4) | ((epi) << 6))
-
+// Tile shape of each expert GEMM (build-time tunable).
+#ifndef MOE_TILE_GATEUP_FWD
+#define MOE_TILE_GATEUP_FWD TILE_256x256
+#endif
+#ifndef MOE_TILE_DOWN_FWD
+#define MOE_TILE_DOWN_FWD TILE_256x256
+#endif
+#ifndef MOE_TILE_DOWN_DGRAD
+#define MOE_TILE_DOWN_DGRAD TILE_256x128
+#endif
+#ifndef MOE_TILE_GATEUP_DGRAD
+#define MOE_TILE_GATEUP_DGRAD TILE_256x256
+#endif
+#ifndef MOE_WGRAD_TILE
+#define MOE_WGRAD_TILE TILE_128x128
+#endif
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 2
 #endif
-
 #ifndef MOE_WIDE_WAVES
 #define MOE_WIDE_WAVES 8
 #endif
-
 #ifndef MOE_GEMM_DMA
 #define MOE_GEMM_DMA 0
 #endif
 
-template <int BMt, int BNt, int AM, int BMD, int GMD, int B2, int EPI>
+// role, name, tile, A layout, B layout, grouping, two-source B, epilogue
+#define MOE_GEMM_ROLES(X)                                                                          \
+  X(R_ROUTE_LOGITS, "route_logits", TILE_64x64, A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)        \
+  X(R_GATEUP_FWD, "ffn_gateup_fwd", MOE_TILE_GATEUP_FWD, A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU) \
+  X(R_DOWN_FWD, "ffn_down_fwd", MOE_TILE_DOWN_FWD, A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)         \
+  X(R_DOWN_DGRAD, "ffn_down_dgrad", MOE_TILE_DOWN_DGRAD, A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU) \
+  X(R_GATEUP_DGRAD, "ffn_gateup_dgrad", MOE_TILE_GATEUP_DGRAD, A_KC, B_KC, G_MROWS, B2_KSPLIT,      \
+    EPI_STORE)                                                                                     \
+  X(R_DOWN_WGRAD, "ffn_down_wgrad", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)        \
+  X(R_GATEUP_WGRAD, "ffn_gateup_wgrad", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)    \
+  X(R_ROUTE_DW, "route_bwd_dw", TILE_64x64, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)               \
+  X(R_ROUTE_DX, "route_bwd_dx", TILE_64x64, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
+
+TileCfg role_tile(GemmRole role) {
+  switch (role) {
+#define X(r, n, t, a, b, g, t2, e) \
+  case r: return t;
+    MOE_GEMM_ROLES(X)
+#undef X
+  }
+  return TILE_64x64;
+}
+
+const char* role_name(GemmRole role) {
+  switch (role) {
+#define X(r, n, t, a, b, g, t2, e) \
+  case r: return n;
+    MOE_GEMM_ROLES(X)
+#undef X
+  }
+  return "gemm";
+}
+
+template <int CFG> struct TileDims;
+template <> struct TileDims<TILE_256x256> { static constexpr int BM = 256, BN = 256; };
+template <> struct TileDims<TILE_256x128> { static constexpr int BM = 256, BN = 128; };
+template <> struct TileDims<TILE_128x128> { static constexpr int BM = 128, BN = 128; };
+template <> struct TileDims<TILE_64x64> { static constexpr int BM = 64, BN = 64; };
+
+template <int CFG, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
+  constexpr int BMt = TileDims<CFG>::BM, BNt = TileDims<CFG>::BN;
   constexpr int P = (BMt >= 128) ? MOE_GEMM_STAGES : 2;  // register stages in flight
   // 256x256 tiles: MOE_WIDE_WAVES = 8 runs two waves per SIMD (2 x 4 grid)
   constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
   if constexpr (MOE_GEMM_DMA) {
-    // LDS stages: three when they fit in 160 KB next to nothing else
     constexpr int S = ((BMt + BNt) * BK * 2 * 3 <= 160 * 1024 && !(BMt == 128 && BNt == 128)) ? 3 : 2;
-    gemm_bf16_dma_kernel<BMt, BNt, 2, WGN, S, AM, BMD, GMD, B2, EPI><<<grid, 64 * 2 * WGN, 0, s>>>(p);
+    gemm_bf16_dma_kernel<BMt, BNt, 2, WGN, S, AM, BMD, GMD, B2, EPI, ROLE>
+        <<<grid, 64 * 2 * WGN, 0, s>>>(p);
   } else {
-    gemm_bf16_kernel<BMt, BNt, 2, WGN, P, AM, BMD, GMD, B2, EPI><<<grid, 64 * 2 * WGN, 0, s>>>(p);
+    gemm_bf16_kernel<BMt, BNt, 2, WGN, P, AM, BMD, GMD, B2, EPI, ROLE><<<grid, 64 * 2 * WGN, 0, s>>>(p);
   }
 }
 
-template <int AM, int BMD, int GMD, int B2, int EPI>
+template <int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 static void launch_f32(const GemmParams& p, int max_rows, hipStream_t s) {
   int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? p.I : p.N;
   dim3 grid((unsigned)ceil_div(ncols, 16), (unsigned)ceil_div(max_rows, 16),
             GMD == G_KROWS ? (unsigned)p.groups : 1u);
-  gemm_f32_kernel<AM, BMD, GMD, B2, EPI><<<grid, 256, 0, s>>>(p);
+  gemm_f32_kernel<AM, BMD, GMD, B2, EPI, ROLE><<<grid, 256, 0, s>>>(p);
 }
 
-moe_status_t launch_gemm(bool is_bf16, int am, int bmd, int gmd, int b2, int epi, TileCfg cfg,
-                         const GemmParams& p, int max_m_tiles, hipStream_t s, const char* name) {
-  const int key = MOE_KEY(am, bmd, gmd, b2, epi);
+moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
+                         hipStream_t s) {
+  const char* name = role_name(role);
   ProfScope prof(name, s);
   if (!is_bf16) {
-    // rows to cover: G_MROWS row capacity (max_m_tiles is then the row count), else M
-    int rows = (gmd == G_MROWS) ? max_m_tiles : p.M;
-    if (rows <= 0) return MOE_OK;
-    switch (key) {
-#define F32CASE(a, b, g, t, e) \
-  case MOE_KEY(a, b, g, t, e): launch_f32<a, b, g, t, e>(p, rows, s); break;
-      F32CASE(A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)
-      F32CASE(A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU)
-      F32CASE(A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)
-      F32CASE(A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU)
-      F32CASE(A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE)
-      F32CASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
-      F32CASE(A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
-#undef F32CASE
-      default:
-        set_error("internal: no fp32 GEMM variant for key %d (%s)", key, name);
-        return MOE_ERR_UNSUPPORTED;
+    // rows to cover: G_MROWS row capacity (passed as max_m_tiles), else M
+    switch (role) {
+#define X(r, n, t, a, b, g, t2, e)                        \
+  case r: {                                               \
+    const int rows = (g == G_MROWS) ? max_m_tiles : p.M;  \
+    if (rows <= 0) return MOE_OK;                         \
+    launch_f32<a, b, g, t2, e, r>(p, rows, s);            \
+    break;                                                \
+  }
+      MOE_GEMM_ROLES(X)
+#undef X
     }
     return check_launch(name);
   }
-  int tiles_per_group = max_m_tiles * p.n_tiles;
-  int64_t grid = (gmd == G_KROWS) ? (int64_t)tiles_per_group * p.groups : tiles_per_group;
-  if (grid <= 0) return MOE_OK;
-  if (grid > 0x7fffffff) {
-    set_error("GEMM %s: grid too large", name);
-    return MOE_ERR_UNSUPPORTED;
+  switch (role) {
+#define X(r, n, t, a, b, g, t2, e)                                                        \
+  case r: {                                                                               \
+    const int64_t per = (int64_t)max_m_tiles * p.n_tiles;                                 \
+    const int64_t grid = (g == G_KROWS) ? per * p.groups : per;                           \
+    if (grid <= 0) return MOE_OK;                                                         \
+    if (grid > 0x7fffffff) {                                                              \
+      set_error("GEMM %s: grid too large", name);                                         \
+      return MOE_ERR_UNSUPPORTED;                                                         \
+    }                                                                                     \
+    launch_bf16<t, a, b, g, t2, e, r>(p, (int)grid, s);                                   \
+    break;                                                                                \
   }
-#define MOE_ROW_GEMMS(X)                          \
-  X(A_KC, B_NC, G_MROWS, B2_NHALF, EPI_SWIGLU)     \
-  X(A_KC, B_NC, G_MROWS, B2_NONE, EPI_STORE)       \
-  X(A_KC, B_KC, G_MROWS, B2_NONE, EPI_DSWIGLU)     \
-  X(A_KC, B_KC, G_MROWS, B2_KSPLIT, EPI_STORE)     \
-  X(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
-  switch (cfg) {
-    case TILE_256x256:
-      switch (key) {
-#define BFCASE(a, b, g, t, e) \
-  case MOE_KEY(a, b, g, t, e): launch_bf16<256, 256, a, b, g, t, e>(p, (int)grid, s); break;
-        MOE_ROW_GEMMS(BFCASE)
-#undef BFCASE
-        default:
-          set_error("internal: no bf16 256x256 GEMM variant for key %d (%s)", key, name);
-          return MOE_ERR_UNSUPPORTED;
-      }
-      break;
-    case TILE_256x128:
-      switch (key) {
-#define BFCASE(a, b, g, t, e) \
-  case MOE_KEY(a, b, g, t, e): launch_bf16<256, 128, a, b, g, t, e>(p, (int)grid, s); break;
-        MOE_ROW_GEMMS(BFCASE)
-#undef BFCASE
-        default:
-          set_error("internal: no bf16 256x128 GEMM variant for key %d (%s)", key, name);
-          return MOE_ERR_UNSUPPORTED;
-      }
-      break;
-    case TILE_128x128:
-      switch (key) {
-#define BFCASE(a, b, g, t, e) \
-  case MOE_KEY(a, b, g, t, e): launch_bf16<128, 128, a, b, g, t, e>(p, (int)grid, s); break;
-        MOE_ROW_GEMMS(BFCASE)
-#undef BFCASE
-        default:
-          set_error("internal: no bf16 128x128 GEMM variant for key %d (%s)", key, name);
-          return MOE_ERR_UNSUPPORTED;
-      }
-      break;
-    default:
-      switch (key) {
-#define BFCASE(a, b, g, t, e) \
-  case MOE_KEY(a, b, g, t, e): launch_bf16<64, 64, a, b, g, t, e>(p, (int)grid, s); break;
-        BFCASE(A_KC, B_NC, G_DENSE, B2_NONE, EPI_F32_BIAS)
-        BFCASE(A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)
-        BFCASE(A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
-#undef BFCASE
-        default:
-          set_error("internal: no bf16 64x64 GEMM variant for key %d (%s)", key, name);
-          return MOE_ERR_UNSUPPORTED;
-      }
+    MOE_GEMM_ROLES(X)
+#undef X
   }
-#undef MOE_ROW_GEMMS
   return check_launch(name);
 }
 
