@@ -61,7 +61,7 @@ struct GemmParams {
 };
 
 // Tile shapes of the bf16 MFMA kernels.
-enum TileCfg { TILE_256x256 = 0, TILE_256x128 = 1, TILE_64x64 = 2, TILE_128x128 = 3 };
+enum TileCfg { TILE_256x256 = 0, TILE_256x128 = 1, TILE_64x64 = 2, TILE_128x128 = 3, TILE_128x256 = 4 };
 
 // The GEMMs of the layer.  Each role fixes the operand layouts, the grouping
 // and the epilogue, and is its own kernel instance (so profilers tell them apart).

@@ -1,16 +1,23 @@
 // Grouped GEMM kernels of the MoE layer for gfx950.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 (fp32 accumulation) on LDS-staged
-// 64-deep K slices in two LDS buffers, with several further slices in flight
-// in registers, four waves per workgroup.  Operands stored k-contiguous sit in
-// LDS the same way (16-byte chunks XOR-swizzled by row); operands stored
-// n-contiguous (weights [K][N], activations read transposed) are copied as is
-// and read back with the gfx950 LDS transpose read.  Workgroup ids are remapped
-// so that consecutive tiles land on the same XCD (its own L2), and tiles that
-// share an A row block or a weight column block run together (GROUP_M order).
+// 64-deep K slices in two LDS buffers, with further slices in flight in
+// registers.  Operands stored k-contiguous sit in LDS the same way (16-byte
+// chunks XOR-swizzled by row); operands stored n-contiguous (weights [K][N],
+// activations read transposed) are copied as is and read back with the gfx950
+// LDS transpose read.  Tiles are ordered so that consecutive tiles land on the
+// same XCD (its own L2) and tiles that share an A row block or a weight column
+// block run together (GROUP_M order).  Three kernel forms:
+//  * gemm_bf16_kernel: one workgroup per tile;
+//  * gemm_bf16_persistent_kernel: one workgroup per CU running a list of
+//    tiles with the K-slice pipeline running on across tile boundaries;
+//  * gemm_bf16_ws_kernel: persistent and warp-specialised (producer waves
+//    load, compute waves multiply and store), for plain-store epilogues with
+//    much output per unit of work (the weight gradients, the down projection).
 //
 // fp32 path: a plain fp32 kernel (one output per thread, fp32 FMA) used for
 // fp32 layers, which are small parity workloads.
+#include <algorithm>
 #include <utility>
 
 #include "gemm.h"
@@ -215,6 +222,133 @@ __device__ __forceinline__ bf16x8 frag_kn(const bf16_t* lds, int base, int ks, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---------------------------------------------------------------------------
+// Tiles.  Tile ids run over (expert for G_KROWS) x m tiles x n tiles; for
+// G_MROWS the m tiles come from the device-built tile table.
+// ---------------------------------------------------------------------------
+struct TileDesc {
+  int e;           // local expert (0 for G_DENSE)
+  int m_lo, m_hi;  // output rows [m_lo, m_hi)
+  int n0;          // first output column (gate|up: first column of each half)
+  int k_lo, k_hi;  // K range
+};
+
+// The group offsets and the tile table are read-only for the GEMM kernels;
+// reading them through the constant address space with a uniform index makes
+// them scalar loads, which do not wait behind the vector loads in flight.
+typedef __attribute__((address_space(4))) const int32_t cint32_t;
+__device__ __forceinline__ int ld_table(const int32_t* tab, int i) { return ((cint32_t*)tab)[i]; }
+
+template <int GMD>
+__device__ __forceinline__ int tile_count(const GemmParams& p) {
+  const int mt_count = (GMD == G_MROWS) ? ld_table(p.tiles, 0) : p.m_tiles;
+  const int per_group = mt_count * p.n_tiles;
+  return (GMD == G_KROWS) ? per_group * p.groups : per_group;
+}
+
+// The tile id is the same in every lane; the integer divisions below run on
+// the vector unit, so the indices are moved back to scalar registers before
+// they address the tables.
+template <int BM, int BN, int GMD, int B2>
+__device__ __forceinline__ TileDesc tile_desc(const GemmParams& p, int L) {
+  TileDesc t;
+  const int mt_count = (GMD == G_MROWS) ? ld_table(p.tiles, 0) : p.m_tiles;
+  t.e = 0;
+  if (GMD == G_KROWS) {
+    const int per_group = mt_count * p.n_tiles;
+    t.e = __builtin_amdgcn_readfirstlane(L / per_group);
+    L -= t.e * per_group;
+  }
+  int mt, nt;
+  group_order(L, mt_count, p.n_tiles, mt, nt);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  if (GMD == G_MROWS) {
+    t.e = ld_table(p.tiles, 1 + 2 * mt);
+    t.m_lo = ld_table(p.tiles, 2 + 2 * mt);
+    t.m_hi = min(t.m_lo + BM, ld_table(p.off, t.e + 1));
+    t.k_lo = 0;
+    t.k_hi = p.K;
+  } else {
+    t.m_lo = mt * BM;
+    t.m_hi = min(t.m_lo + BM, p.M);
+    if (GMD == G_KROWS && p.off) { t.k_lo = ld_table(p.off, t.e); t.k_hi = ld_table(p.off, t.e + 1); }
+    else { t.k_lo = 0; t.k_hi = p.K; }
+  }
+  t.n0 = nt * ((B2 == B2_NHALF) ? BN / 2 : BN);
+  return t;
+}
+
+#ifndef MOE_WEIGHT_CPOL
+#define MOE_WEIGHT_CPOL 2
+#endif
+// Cache policy of the warp-specialised kernel's result stores (2 = nt).
+#ifndef MOE_OUT_CPOL
+#define MOE_OUT_CPOL 2
+#endif
+
+// Loader types of a GEMM.  The expert weights (B of the row-grouped GEMMs)
+// stream through once and are loaded non-temporal; the activation rows (A)
+// are re-read by every column tile of the expert and stay cached.
+template <int BM, int BN, int NT, int AM, int BMD, int GMD, int B2>
+struct Loaders {
+  static constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
+  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0>::type LA;
+  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL>::type LB;
+};
+
+template <int GMD, int B2, typename LA, typename LB>
+__device__ __forceinline__ void init_loaders(const GemmParams& p, const TileDesc& t, LA& la, LB& lb,
+                                             int tid) {
+  const bf16_t* A = static_cast<const bf16_t*>(p.A);
+  const bf16_t* B0 = static_cast<const bf16_t*>(p.B0);
+  const bf16_t* B1 = static_cast<const bf16_t*>(p.B1);
+  if (GMD == G_MROWS) {
+    B0 += (int64_t)t.e * p.b_estride;
+    if (B2 != B2_NONE) B1 += (int64_t)t.e * p.b_estride;
+  }
+  la.init(A, A, p.lda, t.m_lo, t.m_hi, t.k_lo, t.k_hi, 0, tid);
+  // columns are bounded in the B source's column space
+  lb.init(B0, B1, p.ldb, t.n0, p.N, t.k_lo, t.k_hi, p.k_split, tid);
+}
+
+// The MFMAs of one K slice: A tile at `as` ([BM] rows), B tile right after it.
+// Wave (wm, wn) owns a (BM/WGM) x (BN/WGN) block of 32x32 accumulators; with
+// the gate|up halves (B2_NHALF) its first FN/2 column blocks are gate columns
+// and the last FN/2 the matching up columns.
+template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, int FM, int FN>
+__device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* as, int wm, int wn,
+                                          int lane) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static_assert(FM == WTM / 32 && FN == WTN / 32, "accumulator blocks match the wave tile");
+  const bf16_t* bs = as + BM * BK;
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    bf16x8 af[FM], bfg[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int base = wm * WTM + i * 32;
+      if constexpr (AM == A_KC) af[i] = frag_kc(as, base, ks, lane);
+      else af[i] = frag_kn<BM>(as, base, ks, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      int base;
+      if constexpr (B2 == B2_NHALF)
+        base = (j < FN / 2) ? (wn * (WTN / 2) + j * 32) : (BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 32);
+      else
+        base = wn * WTN + j * 32;
+      if constexpr (BMD == B_KC) bfg[j] = frag_kc(bs, base, ks, lane);
+      else bfg[j] = frag_kn<BN>(bs, base, ks, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
+  }
+}
+
 // Epilogue shared by the bf16 kernels.  Lane holds C[m][n..n+3] of every
 // 32x32 block of its wave tile: m = row (lane & 31), n = 8q + 4 (lane >> 5).
 template <int FM, int FN, int WTM, int WTN, int GMD, int EPI>
@@ -306,33 +440,57 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
   }
 }
 
+// 16-byte result chunks of a block whose rows start at element offset `row0`
+// of C0 / C1 and whose columns are [n_lo, n_hi): columns >= n_split go to C1
+// at column - n_split.  A block on one side of n_split (the usual case) takes
+// one buffer store per chunk; a block across it takes two masked ones.  A
+// masked lane gets an out-of-range offset and its store is dropped.
+struct BlockOut {
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  int shift;      // column shift of a one-sided block
+  bool straddle;  // columns on both sides of n_split
+  __device__ __forceinline__ BlockOut(const GemmParams& p, bf16_t* C0, bf16_t* C1, int64_t row0,
+                                      int n_lo, int n_hi) {
+    const bool split = p.n_split > 0;
+    straddle = split && n_lo < p.n_split && n_hi > p.n_split;
+    const bool upper = split && n_lo >= p.n_split;
+    shift = upper ? p.n_split : 0;
+    rs0 = make_rsrc((upper ? C1 : C0) + row0);
+    rs1 = make_rsrc((C1 ? C1 : C0) + row0);
+    if (straddle) rs0 = make_rsrc(C0 + row0);
+  }
+  template <int CPOL>
+  __device__ __forceinline__ void store(const GemmParams& p, uint4 v, int r, int n, bool ok) const {
+    const u32x4 d = __builtin_bit_cast(u32x4, v);
+    if (!straddle) {
+      const int off = (int)(((int64_t)r * p.ldc + n - shift) * 2);
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs0, ok ? off : OOB, 0, CPOL);
+    } else {
+      const bool hi = n >= p.n_split;
+      const int off = (int)(((int64_t)r * p.ldc + n - (hi ? p.n_split : 0)) * 2);
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs0, ok && !hi ? off : OOB, 0, CPOL);
+      __builtin_amdgcn_raw_buffer_store_b128(d, rs1, ok && hi ? off : OOB, 0, CPOL);
+    }
+  }
+};
+
 // Plain-store epilogue staged through LDS: the wave tiles are written to LDS
 // as bf16, then every store instruction writes whole 16-byte chunks of
 // consecutive columns (full cache lines per row) instead of 8-byte pieces
 // scattered over 32 rows.  16-byte chunk c of LDS row r sits at c ^ (r & 15).
-template <int BM, int BN, int FM, int FN, int WTM, int WTN, int NT, int GMD>
+// `lds` holds BM * BN / ROUNDS bf16: the tile passes through it in ROUNDS
+// bands of rows (WGM / ROUNDS wave rows each).  The caller synchronises before
+// it reuses `lds`.
+template <int BM, int BN, int WGM, int FM, int FN, int WTM, int WTN, int NT, int GMD, int ROUNDS>
 __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x16 (&acc)[FM][FN],
                                                       bf16_t* lds, int m_lo, int m_hi, int n0,
                                                       int e, int wm, int wn, int lane, int tid) {
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   static_assert(CPR >= 16, "swizzle needs 16 chunks per row");
+  static_assert(WGM % ROUNDS == 0, "bands of whole wave rows");
+  constexpr int WPR = WGM / ROUNDS;  // wave rows per band
+  constexpr int RB = WPR * WTM;      // tile rows per band
   const int half = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = wm * WTM + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
-        const int c = (n >> 3) ^ (r & 15);
-        *reinterpret_cast<uint2*>(lds + r * BN + c * 8 + (n & 7)) =
-            make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                       pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-      }
-    }
-  }
-  __syncthreads();
   bf16_t* C0 = static_cast<bf16_t*>(p.C0);
   bf16_t* C1 = static_cast<bf16_t*>(p.C1);
   if (GMD == G_KROWS) {
@@ -340,16 +498,46 @@ __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x1
     if (C1) C1 += (int64_t)e * p.c_estride;
   }
 #pragma unroll
-  for (int q0 = 0; q0 < BM * CPR; q0 += NT) {
-    const int q = q0 + tid;
-    const int r = q / CPR, c = q % CPR;
-    const int m = m_lo + r;
-    int n = n0 + c * 8;
-    if (m < m_hi && n < p.N) {
-      bf16_t* C = C0;
-      if (p.n_split > 0 && n >= p.n_split) { C = C1; n -= p.n_split; }
-      *reinterpret_cast<uint4*>(C + (int64_t)m * p.ldc + n) =
-          *reinterpret_cast<const uint4*>(lds + r * BN + (c ^ (r & 15)) * 8);
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) __syncthreads();  // the previous band has been read back
+    if (wm / WPR == rd) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = (wm - rd * WPR) * WTM + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
+            const int c = (n >> 3) ^ (r & 15);
+            *reinterpret_cast<uint2*>(lds + r * BN + c * 8 + (n & 7)) =
+                make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                           pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // all LDS reads first (every lane's address is inside the band), then
+    // the masked stores
+    constexpr int NQ = (RB * CPR + NT - 1) / NT;
+    uint4 v[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = min(i * NT + tid, RB * CPR - 1);
+      const int r = q / CPR, c = q % CPR;
+      v[i] = *reinterpret_cast<const uint4*>(lds + r * BN + (c ^ (r & 15)) * 8);
+    }
+    // buffer stores relative to the band's first row: a masked lane gets an
+    // out-of-range offset and its store is dropped, so no lane branches
+    const BlockOut bo(p, C0, C1, (int64_t)(m_lo + rd * RB) * p.ldc, n0, n0 + BN);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = i * NT + tid;
+      const int r = q / CPR, c = q % CPR;
+      const int n = n0 + c * 8;
+      const bool ok = (RB * CPR % NT == 0 || q < RB * CPR) && m_lo + rd * RB + r < m_hi && n < p.N;
+      bo.store<0>(p, v[i], r, n, ok);
     }
   }
 }
@@ -375,53 +563,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- which tile
-  int mt_count = (GMD == G_MROWS) ? p.tiles[0] : p.m_tiles;
-  int per_group = mt_count * p.n_tiles;
-  int count = (GMD == G_KROWS) ? per_group * p.groups : per_group;
+  const int count = tile_count<GMD>(p);
   if ((int)blockIdx.x >= count) return;
-  int L = remap_xcd(blockIdx.x, count);
-  int e = 0;
-  if (GMD == G_KROWS) { e = L / per_group; L -= e * per_group; }
-  int mt, nt;
-  group_order(L, mt_count, p.n_tiles, mt, nt);
-  int m_lo, m_hi, k_lo, k_hi;
-  if (GMD == G_MROWS) {
-    e = p.tiles[1 + 2 * mt];
-    m_lo = p.tiles[2 + 2 * mt];
-    m_hi = min(m_lo + BM, p.off[e + 1]);
-    k_lo = 0;
-    k_hi = p.K;
-  } else {
-    m_lo = mt * BM;
-    m_hi = min(m_lo + BM, p.M);
-    if (GMD == G_KROWS && p.off) { k_lo = p.off[e]; k_hi = p.off[e + 1]; }
-    else { k_lo = 0; k_hi = p.K; }
-  }
-  const int n0 = nt * ((B2 == B2_NHALF) ? BN / 2 : BN);
-  const int n_hi = p.N;  // column bound in the B source's column space
+  const TileDesc t = tile_desc<BM, BN, GMD, B2>(p, remap_xcd(blockIdx.x, count));
+  const int e = t.e, m_lo = t.m_lo, m_hi = t.m_hi, n0 = t.n0, k_lo = t.k_lo, k_hi = t.k_hi;
 
-  const bf16_t* A = static_cast<const bf16_t*>(p.A);
-  const bf16_t* B0 = static_cast<const bf16_t*>(p.B0);
-  const bf16_t* B1 = static_cast<const bf16_t*>(p.B1);
-  if (GMD == G_MROWS) {
-    B0 += (int64_t)e * p.b_estride;
-    if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
-  }
-
-#ifndef MOE_WEIGHT_CPOL
-#define MOE_WEIGHT_CPOL 2
-#endif
-  // expert weights (B of the row-grouped GEMMs) stream through once; the
-  // activation rows (A) are re-read by every column tile of the expert
-  constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
-  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0>::type LA;
-  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL>::type LB;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LA LA;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[P];
   typename LB::Data db[P];
-  la.init(A, A, p.lda, m_lo, m_hi, k_lo, k_hi, 0, tid);
-  lb.init(B0, B1, p.ldb, n0, n_hi, k_lo, k_hi, p.k_split, tid);
+  init_loaders<GMD, B2>(p, t, la, lb, tid);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -457,33 +610,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
     // keep the refill loads at the top of the step: the scheduler would
     // otherwise sink them below the MFMAs and expose their latency
     __builtin_amdgcn_sched_barrier(0);
-    const bf16_t* as = smem + (kt & 1) * (BM + BN) * BK;
-    const bf16_t* bs = as + BM * BK;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[FM], bfg[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int base = wm * WTM + i * 32;
-        if constexpr (AM == A_KC) af[i] = frag_kc(as, base, ks, lane);
-        else af[i] = frag_kn<BM>(as, base, ks, lane);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int base;
-        if constexpr (B2 == B2_NHALF)
-          base = (j < FN / 2) ? (wn * (WTN / 2) + j * 32) : (BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 32);
-        else
-          base = wn * WTN + j * 32;
-        if constexpr (BMD == B_KC) bfg[j] = frag_kc(bs, base, ks, lane);
-        else bfg[j] = frag_kn<BN>(bs, base, ks, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
-    }
+    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn, lane);
     __builtin_amdgcn_sched_barrier(0);
     if (do_store) {
       bf16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BK;
@@ -512,281 +639,384 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
 #define MOE_STAGED_STORE 1
 #endif
   if constexpr (EPI == EPI_STORE && MOE_STAGED_STORE && BN / 8 >= 16 && BM * BN <= (BM + BN) * BK * 2)
-    epilogue_store_staged<BM, BN, FM, FN, WTM, WTN, NT, GMD>(p, acc, smem, m_lo, m_hi, n0, e, wm,
-                                                             wn, lane, tid);
+    epilogue_store_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT, GMD, 1>(p, acc, smem, m_lo, m_hi, n0, e,
+                                                                    wm, wn, lane, tid);
   else
     epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
 }
 
-// ===========================================================================
-// Direct-to-LDS variant.  Every K slice goes from HBM/L2 straight into LDS
-// with the 16-byte buffer-load-to-LDS instruction (no register staging, no
-// LDS store instructions).  Lane l of a load lands at LDS base + 16 l, so the
-// swizzled layouts are produced by choosing each lane's source address.  Each
-// pipeline stage is a separate __shared__ array so the compiler can tell that
-// fragment reads of one stage do not alias loads into another.
-// ===========================================================================
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, bf16_t* lds_dst, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 16, voff, soff, 0, 0);
-}
-
-// KC tile [ROWS][64]: slot s (16 bytes) holds row s >> 3, physical chunk s & 7,
-// i.e. logical chunk (s & 7) ^ swz(row).
-template <int ROWS, bool TWO, int NT>
-struct DmaKC {
-  static constexpr int CH = ROWS * 8;
-  static constexpr int NR = CH / NT;
-  static_assert(CH % NT == 0, "whole load instructions");
-  int voff[NR];
-  int kcol[NR];
-  __amdgpu_buffer_rsrc_t rs0, rs1;
-  int ksplit, k_lo, k_hi;
-  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
-                                       int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid) {
-    rs0 = make_rsrc(s0 + (int64_t)row0 * ld);
-    rs1 = make_rsrc(TWO ? s1 + (int64_t)row0 * ld : s0);
-    ksplit = ksplit_;
-    k_lo = k_lo_;
-    k_hi = k_hi_;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int slot = tid + NT * i;
-      const int row = slot >> 3;
-      const int c = (slot & 7) ^ (row & 7) ^ ((row >> 3) & 1);  // inverse of swz
-      kcol[i] = c * 8;
-      voff[i] = row0 + row < row_hi ? (int)(((int64_t)row * ld + c * 8) * 2) : OOB;
-    }
-  }
-  __device__ __forceinline__ void issue(bf16_t* tile, int kofs, int tid) const {
-    int k0 = k_lo + kofs;
-    __amdgpu_buffer_rsrc_t rs = rs0;
-    int lim = k_hi - k0;
-    if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
-    bf16_t* dst = tile + (tid >> 6) * 64 * 8;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) dma16(rs, dst + i * NT * 8, kcol[i] < lim ? voff[i] : OOB, k0 * 2);
-  }
-};
-
-// KN tile [64][COLS] (HALF: two sub-tiles [64][COLS/2], gate then up): slot s
-// of a (sub-)tile of width W holds row s / (W/8), physical chunk s % (W/8).
-template <int COLS, bool HALF, int NT>
-struct DmaKN {
-  static constexpr int W = HALF ? COLS / 2 : COLS;  // width of one (sub-)tile
-  static constexpr int CPR = W / 8;
-  static constexpr int CH = BK * CPR;
-  static constexpr int NR = CH / NT;
-  static_assert(CH % NT == 0, "whole load instructions");
-  int voff[NR];
-  int krow[NR];
-  __amdgpu_buffer_rsrc_t rs0, rs1;
-  int64_t ld;
-  int k_lo, k_hi;
-  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld_, int col0,
-                                       int col_hi, int k_lo_, int k_hi_, int, int tid) {
-    ld = ld_;
-    k_lo = k_lo_;
-    k_hi = k_hi_;
-    rs0 = make_rsrc(s0 + (int64_t)k_lo * ld + col0);
-    rs1 = make_rsrc((HALF ? s1 : s0) + (int64_t)k_lo * ld + col0);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int slot = tid + NT * i;
-      const int k = slot / CPR;
-      const int col = kn_swz<W>(k, slot % CPR) * 8;  // the swizzle is its own inverse
-      krow[i] = k;
-      voff[i] = col0 + col < col_hi ? (int)(((int64_t)k * ld + col) * 2) : OOB;
-    }
-  }
-  __device__ __forceinline__ void issue(bf16_t* tile, int kofs, int tid) const {
-    const int lim = k_hi - k_lo - kofs;
-    const int soff = (int)((int64_t)kofs * ld * 2);
-    bf16_t* dst = tile + (tid >> 6) * 64 * 8;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int v = krow[i] < lim ? voff[i] : OOB;
-      dma16(rs0, dst + i * NT * 8, v, soff);
-      if (HALF) dma16(rs1, dst + BK * W + i * NT * 8, v, soff);
-    }
-  }
-};
-
-template <bool KC, int ROWS, bool TWO, int NT> struct PickDma;
-template <int ROWS, bool TWO, int NT> struct PickDma<true, ROWS, TWO, NT> { typedef DmaKC<ROWS, TWO, NT> type; };
-template <int ROWS, bool TWO, int NT> struct PickDma<false, ROWS, TWO, NT> { typedef DmaKN<ROWS, TWO, NT> type; };
-
-// s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int BM, int BN, int WGM, int WGN, int S, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(GemmParams p) {
+// ---------------------------------------------------------------------------
+// Persistent bf16 MFMA grouped GEMM.  About as many workgroups as fit on the
+// chip at once each run a fixed list of tiles back to back, and the K-slice
+// pipeline of gemm_bf16_kernel (two register stages, two LDS buffers) runs on
+// across tile boundaries: the first slices of the next tile are in flight
+// while the current tile finishes its MFMAs and writes its result, so neither
+// the pipeline fill nor the epilogue leaves the matrix cores idle.  This
+// matters where a tile has few K slices (the weight gradients: K is the rows
+// of one expert).
+// Workgroup w runs on XCD w % 8 (the hardware's round-robin dispatch) and
+// takes every (gridDim.x / 8)-th tile of the contiguous range of tile ids that
+// its XCD owns, so tiles that share operands stay in one L2.  gridDim.x is a
+// multiple of 8.  Tiles with no K slices (an expert with no rows in the weight
+// gradients) are written as zeros.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(GemmParams p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int SZ = (BM + BN) * BK;  // elements per stage
+  constexpr int BUF = (BM + BN) * BK;  // one LDS buffer (A slice, then B slice)
   static_assert(FM >= 1 && FN >= 1, "wave tile of at least 32x32");
   static_assert(B2 != B2_NHALF || FN % 2 == 0, "gate|up halves need an even block count");
-  static_assert(S == 2 || S == 3, "two or three LDS stages");
-  __shared__ __attribute__((aligned(16))) bf16_t st0[SZ];
-  __shared__ __attribute__((aligned(16))) bf16_t st1[SZ];
-  __shared__ __attribute__((aligned(16))) bf16_t st2[S > 2 ? SZ : 8];
+  // plain stores are staged through the LDS buffer that the finished slice
+  // frees, in bands of rows that fit into it
+  constexpr bool STAGED = EPI == EPI_STORE && BN / 8 >= 16;
+  constexpr int ROUNDS = (BM * BN + BUF - 1) / BUF;
+  static_assert(!STAGED || (WGM % ROUNDS == 0 && BM * BN / ROUNDS <= BUF), "staging bands");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // ---- which tile
-  int mt_count = (GMD == G_MROWS) ? p.tiles[0] : p.m_tiles;
-  int per_group = mt_count * p.n_tiles;
-  int count = (GMD == G_KROWS) ? per_group * p.groups : per_group;
-  if ((int)blockIdx.x >= count) return;
-  int L = remap_xcd(blockIdx.x, count);
-  int e = 0;
-  if (GMD == G_KROWS) { e = L / per_group; L -= e * per_group; }
-  int mt, nt;
-  group_order(L, mt_count, p.n_tiles, mt, nt);
-  int m_lo, m_hi, k_lo, k_hi;
-  if (GMD == G_MROWS) {
-    e = p.tiles[1 + 2 * mt];
-    m_lo = p.tiles[2 + 2 * mt];
-    m_hi = min(m_lo + BM, p.off[e + 1]);
-    k_lo = 0;
-    k_hi = p.K;
-  } else {
-    m_lo = mt * BM;
-    m_hi = min(m_lo + BM, p.M);
-    if (GMD == G_KROWS && p.off) { k_lo = p.off[e]; k_hi = p.off[e + 1]; }
-    else { k_lo = 0; k_hi = p.K; }
-  }
-  const int n0 = nt * ((B2 == B2_NHALF) ? BN / 2 : BN);
-  const int n_hi = p.N;
+  // ---- this workgroup's tiles: x_lo + pos for pos = slot, slot + S, ... < x_n
+  const int count = tile_count<GMD>(p);
+  const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD, S = gridDim.x / NXCD;
+  const int per = count / NXCD, rem = count % NXCD;
+  const int x_lo = xcd * per + min(xcd, rem);
+  const int x_n = per + (xcd < rem ? 1 : 0);
+  if (slot >= x_n) return;
 
-  const bf16_t* A = static_cast<const bf16_t*>(p.A);
-  const bf16_t* B0 = static_cast<const bf16_t*>(p.B0);
-  const bf16_t* B1 = static_cast<const bf16_t*>(p.B1);
-  if (GMD == G_MROWS) {
-    B0 += (int64_t)e * p.b_estride;
-    if (B2 != B2_NONE) B1 += (int64_t)e * p.b_estride;
-  }
-
-  typedef typename PickDma<AM == A_KC, BM, false, NT>::type LA;
-  typedef typename PickDma<BMD == B_KC, BN, B2 != B2_NONE, NT>::type LB;
-  constexpr int LPS = LA::NR + LB::NR * ((B2 == B2_NHALF) ? 2 : 1);  // loads per thread per stage
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LA LA;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LB LB;
   LA la;
   LB lb;
-  la.init(A, A, p.lda, m_lo, m_hi, k_lo, k_hi, 0, tid);
-  lb.init(B0, B1, p.ldb, n0, n_hi, k_lo, k_hi, p.k_split, tid);
-
-  auto buf = [&](auto Ic) __attribute__((always_inline)) -> bf16_t* {
-    constexpr int I = decltype(Ic)::value;
-    if constexpr (I == 0) return st0;
-    else if constexpr (I == 1) return st1;
-    else return st2;
-  };
-  auto issue = [&](bf16_t* b, int s) __attribute__((always_inline)) {
-    la.issue(b, s * BK, tid);
-    lb.issue(b + BM * BK, s * BK, tid);
-  };
+  typename LA::Data da[2];
+  typename LB::Data db[2];
 
   f32x16 acc[FM][FN];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  auto slices = [](const TileDesc& t) { return (t.k_hi - t.k_lo + BK - 1) / BK; };
 
-  const int nk = (k_hi - k_lo + BK - 1) / BK;
-  if (nk > 0) issue(st0, 0);
-  if (S > 2 && nk > 1) {
-    issue(st1, 1);
-    wait_vmcnt<LPS>();  // slice 0 landed, slice 1 may still be in flight
-  } else {
-    wait_vmcnt<0>();
-  }
-  __syncthreads();
-
-  // Fragment reads of operands in the k-major layout use the LDS transpose
-  // read, which the compiler cannot tie to one stage buffer: it would wait for
-  // every load in flight before such a read.  So a step reads all of them
-  // first, then issues the next slice's loads, then runs the MFMAs (with the
-  // plain reads of k-contiguous operands interleaved).
-  constexpr bool A_TR = AM != A_KC, B_TR = BMD != B_KC;
-  auto step = [&](auto Uc, int kt) __attribute__((always_inline)) {
-    constexpr int U = decltype(Uc)::value;
-    const bf16_t* as = buf(std::integral_constant<int, U>{});
-    const bf16_t* bs = as + BM * BK;
-    auto a_frag = [&](int i, int ks) __attribute__((always_inline)) -> bf16x8 {
-      const int base = wm * WTM + i * 32;
-      if constexpr (AM == A_KC) return frag_kc(as, base, ks, lane);
-      else return frag_kn<BM>(as, base, ks, lane);
-    };
-    auto b_frag = [&](int j, int ks) __attribute__((always_inline)) -> bf16x8 {
-      if constexpr (B2 == B2_NHALF) {
-        const int h = j < FN / 2 ? 0 : 1;
-        const int base = wn * (WTN / 2) + (j - h * (FN / 2)) * 32;
-        return frag_kn<BN / 2>(bs + h * BK * (BN / 2), base, ks, lane);
-      } else {
-        const int base = wn * WTN + j * 32;
-        if constexpr (BMD == B_KC) return frag_kc(bs, base, ks, lane);
-        else return frag_kn<BN>(bs, base, ks, lane);
+  // Load cursor: the tile (position l_pos) and slice (l_ks of l_nk) whose
+  // loads go out next.  Moves to the next tile with K slices and points the
+  // loaders at it.
+  int l_pos = slot, l_ks = 0, l_nk = 0;
+  // Past the end, the cursor stays on the last slice index of the last tile
+  // with slices (l_ks == l_nk), where the loads read nothing.
+  auto load_seek = [&]() __attribute__((always_inline)) {
+    for (; l_pos < x_n; l_pos += S) {
+      const TileDesc t = tile_desc<BM, BN, GMD, B2>(p, x_lo + l_pos);
+      const int nk = slices(t);
+      if (nk > 0) {
+        l_nk = nk;
+        l_ks = 0;
+        init_loaders<GMD, B2>(p, t, la, lb, tid);
+        break;
       }
-    };
-    bf16x8 apre[A_TR ? BK / 16 : 1][A_TR ? FM : 1];
-    bf16x8 bpre[B_TR ? BK / 16 : 1][B_TR ? FN : 1];
-    if constexpr (A_TR) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) apre[ks][i] = a_frag(i, ks);
     }
-    if constexpr (B_TR) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bpre[ks][j] = b_frag(j, ks);
+  };
+  int issued = 0;  // slices whose loads have gone out
+  // Loads of the slice at the load cursor into register stage U.  Inside the
+  // loop the loads go out unconditionally: past the last slice the loaders
+  // still point at the last tile, and a slice beyond its K range reads zeros
+  // through the range check without touching memory.  (A load under a branch
+  // would make the compiler wait for every load in flight at the join.)
+  auto issue = [&](auto Uc, bool first) __attribute__((always_inline)) {
+    constexpr int U = decltype(Uc)::value;
+    if (!first || l_pos < x_n) {
+      la.load(da[U], l_ks * BK, tid);
+      lb.load(db[U], l_ks * BK, tid);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + S - 1 < nk) issue(buf(std::integral_constant<int, (U + S - 1) % S>{}), kt + S - 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[FM], bfg[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = A_TR ? apre[A_TR ? ks : 0][A_TR ? i : 0] : a_frag(i, ks);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfg[j] = B_TR ? bpre[B_TR ? ks : 0][B_TR ? j : 0] : b_frag(j, ks);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      // slice kt+1 must have landed; slices after it may stay in flight
-      if (S > 2 && kt + 2 < nk) wait_vmcnt<LPS>();
-      else wait_vmcnt<0>();
-      __syncthreads();
+    if (l_pos < x_n) {
+      ++issued;
+      if (++l_ks == l_nk) {
+        l_pos += S;
+        load_seek();
+      }
     }
   };
 
-  int kt0 = 0;
-  for (; kt0 + S <= nk; kt0 += S) {
-    [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
-      (step(std::integral_constant<int, Us>{}, kt0 + Us), ...);
-    }(std::make_integer_sequence<int, S>{});
-  }
-  [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
-    ((kt0 + Us < nk ? step(std::integral_constant<int, Us>{}, kt0 + Us) : void()), ...);
-  }(std::make_integer_sequence<int, S - 1>{});
+  // Compute cursor: the tile being accumulated (ct, position c_pos) and its
+  // slice count.
+  int c_pos = slot, c_ks = 0, c_nk = 0;
+  TileDesc ct;
+  auto finish = [&](bf16_t* stage) __attribute__((always_inline)) {
+    if constexpr (STAGED) {
+      epilogue_store_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT, GMD, ROUNDS>(
+          p, acc, stage, ct.m_lo, ct.m_hi, ct.n0, ct.e, wm, wn, lane, tid);
+      __syncthreads();  // `stage` is read back before anyone refills it
+    } else {
+      epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, ct.m_lo, ct.m_hi, ct.n0, ct.e, wm, wn, lane);
+    }
+  };
+  // Move to the next tile with K slices; tiles without any are written as
+  // zeros on the way (acc is zero here).
+  auto compute_seek = [&](bf16_t* stage) __attribute__((always_inline)) {
+    for (; c_pos < x_n; c_pos += S) {
+      ct = tile_desc<BM, BN, GMD, B2>(p, x_lo + c_pos);
+      c_nk = slices(ct);
+      c_ks = 0;
+      if (c_nk > 0) break;
+      finish(stage);
+    }
+  };
 
-  epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
+  zero_acc();
+  load_seek();
+  issue(std::integral_constant<int, 0>{}, true);
+  issue(std::integral_constant<int, 1>{}, true);
+  compute_seek(smem);
+  if (issued == 0) return;  // every tile of this workgroup was empty
+  LA::store(da[0], smem, tid);
+  LB::store(db[0], smem + BM * BK, tid);
+  __syncthreads();
+
+  // One K slice g (U = g mod 2 is both its register stage and its LDS
+  // buffer): send the loads of slice g+2 into stage U, multiply slice g from
+  // buffer U, write slice g+1 (stage 1-U) into buffer 1-U, barrier.  After the
+  // last slice of a tile, write the tile out, staging through buffer U.
+  // Returns false once every tile is done.
+  int g = 0;
+  auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
+    constexpr int U = decltype(Uc)::value;
+    issue(Uc, false);
+    // keep the loads at the top of the step (the scheduler would sink them)
+    __builtin_amdgcn_sched_barrier(0);
+    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + U * BUF, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < issued) {
+      LA::store(da[1 - U], smem + (1 - U) * BUF, tid);
+      LB::store(db[1 - U], smem + (1 - U) * BUF + BM * BK, tid);
+    }
+    __syncthreads();
+    ++g;
+    if (++c_ks < c_nk) return true;
+    finish(smem + U * BUF);
+    zero_acc();
+    c_pos += S;
+    compute_seek(smem + U * BUF);
+    return c_pos < x_n;
+  };
+  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Warp-specialised persistent bf16 MFMA GEMM for plain-store epilogues.
+// Compute waves (WGM x WGN) only read LDS and run the MFMAs; producer waves
+// (NPW) only load K slices from memory into LDS.  On this hardware a wave's
+// loads and stores retire in one in-order queue, so a wave that stores its
+// result and then waits for its next slice also waits for the stores: here
+// the compute waves write their finished blocks (staged through a private
+// LDS area, whole 16-byte chunks of consecutive columns) while the producer
+// waves, which never store, keep the next slices coming.  Tile order and
+// the K-slice pipeline across tiles are those of gemm_bf16_persistent_kernel.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int NPW, int PD, int AM, int BMD, int GMD, int B2, int EPI,
+          int ROLE>
+__global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(GemmParams p) {
+  static_assert(EPI == EPI_STORE && B2 != B2_NHALF, "plain-store epilogue, contiguous wave columns");
+  constexpr int NC = WGM * WGN;       // compute waves
+  constexpr int NTP = 64 * NPW;       // producer threads
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int BUF = (BM + BN) * BK;
+  constexpr int SCPR = WTN / 8;       // 16-byte chunks per staged row
+  static_assert(SCPR == 8 || SCPR == 16, "staged rows of 64 or 128 columns");
+  constexpr int WST = WTM * WTN;      // staging elements per compute wave
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * BUF + NC * WST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= NC;
+  const int wm = wave / WGN, wn = wave % WGN;  // compute waves only
+  const int ptid = tid - NC * 64;              // producer waves only
+
+  const int count = tile_count<GMD>(p);
+  const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD, S = gridDim.x / NXCD;
+  const int per = count / NXCD, rem = count % NXCD;
+  const int x_lo = xcd * per + min(xcd, rem);
+  const int x_n = per + (xcd < rem ? 1 : 0);
+  if (slot >= x_n) return;
+  auto slices = [](const TileDesc& t) { return (t.k_hi - t.k_lo + BK - 1) / BK; };
+
+  // ---- producer state: loaders, PD register stages, load cursor
+  static_assert(PD >= 2, "at least two register stages");
+  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2>::LA LA;
+  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2>::LB LB;
+  LA la;
+  LB lb;
+  typename LA::Data da[PD];
+  typename LB::Data db[PD];
+  int l_pos = slot, l_ks = 0, l_nk = 0, issued = 0;
+  auto load_seek = [&]() __attribute__((always_inline)) {
+    for (; l_pos < x_n; l_pos += S) {
+      const TileDesc t = tile_desc<BM, BN, GMD, B2>(p, x_lo + l_pos);
+      const int nk = slices(t);
+      if (nk > 0) {
+        l_nk = nk;
+        l_ks = 0;
+        init_loaders<GMD, B2>(p, t, la, lb, ptid);
+        break;
+      }
+    }
+  };
+  // see gemm_bf16_persistent_kernel: loads in the loop go out unconditionally
+  auto issue = [&](auto Uc, bool first) __attribute__((always_inline)) {
+    constexpr int U = decltype(Uc)::value;
+    if (!first || l_pos < x_n) {
+      la.load(da[U], l_ks * BK, ptid);
+      lb.load(db[U], l_ks * BK, ptid);
+    }
+    if (l_pos < x_n) {
+      ++issued;
+      if (++l_ks == l_nk) {
+        l_pos += S;
+        load_seek();
+      }
+    }
+  };
+
+  // ---- compute state: accumulators and the wave's block of the tile
+  f32x16 acc[FM][FN];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  bf16_t* stage = smem + 2 * BUF + (producer ? 0 : wave) * WST;
+  // Write the wave's WTM x WTN block: accumulators -> private LDS area
+  // (16-byte chunk c of row r at c ^ (r mod SCPR)) -> whole chunks to memory
+  // with buffer stores (masked lanes get an out-of-range offset).
+  auto store_block = [&](const TileDesc& t) __attribute__((always_inline)) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = j * 32 + 8 * q + 4 * half;
+          const int c = (n >> 3) ^ (r & (SCPR - 1));
+          *reinterpret_cast<uint2*>(stage + r * WTN + c * 8 + (n & 7)) =
+              make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+        }
+    }
+    // the wave's own LDS writes and reads execute in order; keep the compiler
+    // from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int NQ = WTM * SCPR / 64;
+    uint4 v[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = i * 64 + lane;
+      const int r = q / SCPR, c = q % SCPR;
+      v[i] = *reinterpret_cast<const uint4*>(stage + r * WTN + (c ^ (r & (SCPR - 1))) * 8);
+    }
+    bf16_t* C0 = static_cast<bf16_t*>(p.C0);
+    bf16_t* C1 = static_cast<bf16_t*>(p.C1);
+    if (GMD == G_KROWS) {
+      C0 += (int64_t)t.e * p.c_estride;
+      if (C1) C1 += (int64_t)t.e * p.c_estride;
+    }
+    const int mb = t.m_lo + wm * WTM;
+    const int nb = t.n0 + wn * WTN;
+    const BlockOut bo(p, C0, C1, (int64_t)mb * p.ldc, nb, nb + WTN);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = i * 64 + lane;
+      const int r = q / SCPR, c = q % SCPR;
+      const int n = nb + c * 8;
+      bo.store<MOE_OUT_CPOL>(p, v[i], r, n, mb + r < t.m_hi && n < p.N);
+    }
+  };
+
+  // ---- compute cursor (every wave keeps it; it decides when the loop ends)
+  int c_pos = slot, c_ks = 0, c_nk = 0;
+  TileDesc ct;
+  auto compute_seek = [&]() __attribute__((always_inline)) {
+    for (; c_pos < x_n; c_pos += S) {
+      ct = tile_desc<BM, BN, GMD, B2>(p, x_lo + c_pos);
+      c_nk = slices(ct);
+      c_ks = 0;
+      if (c_nk > 0) break;
+      if (!producer) store_block(ct);  // a tile without K slices is zero
+    }
+  };
+  // after a step: true while slices are left
+  auto advance = [&]() __attribute__((always_inline)) -> bool {
+    if (++c_ks < c_nk) return true;
+    if (!producer) {
+      store_block(ct);
+      zero_acc();
+    }
+    c_pos += S;
+    compute_seek();
+    return c_pos < x_n;
+  };
+
+  // The two roles run separate loops (so that neither keeps the other's
+  // registers live) with one barrier per K slice each.  Step g: producers
+  // send the loads of slice g+PD into register stage g mod PD and write
+  // slice g+1 (stage (g+1) mod PD) into LDS buffer (g+1) mod 2; compute waves
+  // multiply slice g from buffer g mod 2 and, after a tile's last slice,
+  // write the tile out.
+  if (producer) {
+    load_seek();
+    [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+      (issue(std::integral_constant<int, Us>{}, true), ...);
+    }(std::make_integer_sequence<int, PD>{});
+    compute_seek();
+    if (c_pos >= x_n) return;  // every tile of this workgroup was empty
+    LA::store(da[0], smem, ptid);
+    LB::store(db[0], smem + BM * BK, ptid);
+    __syncthreads();
+    int g = 0;
+    auto step = [&](auto Vc) __attribute__((always_inline)) -> bool {
+      constexpr int V = decltype(Vc)::value;  // g mod (PD * 2 / gcd)
+      issue(std::integral_constant<int, V % PD>{}, false);
+      if (g + 1 < issued) {
+        bf16_t* nxt = smem + ((V + 1) & 1) * BUF;
+        LA::store(da[(V + 1) % PD], nxt, ptid);
+        LB::store(db[(V + 1) % PD], nxt + BM * BK, ptid);
+      }
+      __syncthreads();
+      ++g;
+      return advance();
+    };
+    constexpr int UN = (PD % 2 == 0) ? PD : 2 * PD;  // steps until stage and buffer repeat
+    while ([&]<int... Vs>(std::integer_sequence<int, Vs...>) __attribute__((always_inline)) {
+      return (step(std::integral_constant<int, Vs>{}) && ...);
+    }(std::make_integer_sequence<int, UN>{})) {
+    }
+  } else {
+    zero_acc();
+    compute_seek();
+    if (c_pos >= x_n) return;
+    __syncthreads();
+    int g = 0;
+    auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
+      constexpr int U = decltype(Uc)::value;
+      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + U * BUF, wm, wn, lane);
+      __syncthreads();
+      ++g;
+      return advance();
+    };
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -906,9 +1136,13 @@ moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* 
   return check_launch("tile_table_kernel");
 }
 
-int tile_bm(TileCfg cfg) { return cfg == TILE_64x64 ? 64 : cfg == TILE_128x128 ? 128 : 256; }
+int tile_bm(TileCfg cfg) {
+  return cfg == TILE_64x64 ? 64 : (cfg == TILE_128x128 || cfg == TILE_128x256) ? 128 : 256;
+}
 int tile_bn(TileCfg cfg) {
-  return cfg == TILE_256x256 ? 256 : (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128 : 64;
+  return (cfg == TILE_256x256 || cfg == TILE_128x256) ? 256
+         : (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128
+                                                         : 64;
 }
 
 // ---------------------------------------------------------------------------
@@ -919,7 +1153,7 @@ int tile_bn(TileCfg cfg) {
 #define MOE_TILE_GATEUP_FWD TILE_256x256
 #endif
 #ifndef MOE_TILE_DOWN_FWD
-#define MOE_TILE_DOWN_FWD TILE_256x256
+#define MOE_TILE_DOWN_FWD TILE_128x256
 #endif
 #ifndef MOE_TILE_DOWN_DGRAD
 #define MOE_TILE_DOWN_DGRAD TILE_256x128
@@ -928,16 +1162,13 @@ int tile_bn(TileCfg cfg) {
 #define MOE_TILE_GATEUP_DGRAD TILE_256x256
 #endif
 #ifndef MOE_WGRAD_TILE
-#define MOE_WGRAD_TILE TILE_128x128
+#define MOE_WGRAD_TILE TILE_256x128
 #endif
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 2
 #endif
 #ifndef MOE_WIDE_WAVES
 #define MOE_WIDE_WAVES 8
-#endif
-#ifndef MOE_GEMM_DMA
-#define MOE_GEMM_DMA 0
 #endif
 
 // role, name, tile, A layout, B layout, grouping, two-source B, epilogue
@@ -978,6 +1209,36 @@ template <> struct TileDims<TILE_256x256> { static constexpr int BM = 256, BN = 
 template <> struct TileDims<TILE_256x128> { static constexpr int BM = 256, BN = 128; };
 template <> struct TileDims<TILE_128x128> { static constexpr int BM = 128, BN = 128; };
 template <> struct TileDims<TILE_64x64> { static constexpr int BM = 64, BN = 64; };
+template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 256; };
+
+// Roles that run the warp-specialised kernel, and roles that run the
+// persistent kernel (bit r = role r; build-time tunable).
+#ifndef MOE_WS_ROLES
+#define MOE_WS_ROLES ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD))
+#endif
+#ifndef MOE_PERSIST_ROLES
+#define MOE_PERSIST_ROLES 0
+#endif
+// Register stages of the warp-specialised kernel's producer waves.
+#ifndef MOE_WS_STAGES
+#define MOE_WS_STAGES 2
+#endif
+
+// Workgroups of a persistent launch: as many as fit on the device at once,
+// at most one per tile, a multiple of the XCD count.
+static int persistent_grid(int occupancy, int max_tiles) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  int64_t g = std::min<int64_t>((int64_t)std::max(occupancy, 1) * cus[dev], max_tiles);
+  return (int)std::max<int64_t>(NXCD, g / NXCD * NXCD);
+}
 
 template <int CFG, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
@@ -985,12 +1246,24 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   constexpr int P = (BMt >= 128) ? MOE_GEMM_STAGES : 2;  // register stages in flight
   // 256x256 tiles: MOE_WIDE_WAVES = 8 runs two waves per SIMD (2 x 4 grid)
   constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
-  if constexpr (MOE_GEMM_DMA) {
-    constexpr int S = ((BMt + BNt) * BK * 2 * 3 <= 160 * 1024 && !(BMt == 128 && BNt == 128)) ? 3 : 2;
-    gemm_bf16_dma_kernel<BMt, BNt, 2, WGN, S, AM, BMD, GMD, B2, EPI, ROLE>
-        <<<grid, 64 * 2 * WGN, 0, s>>>(p);
+  constexpr int NT = 64 * 2 * WGN;
+  if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && EPI == EPI_STORE && B2 != B2_NHALF) {
+    // 2 x 2 compute waves and 4 producer waves
+    const auto kern = gemm_bf16_ws_kernel<BMt, BNt, 2, 2, 4, MOE_WS_STAGES, AM, BMD, GMD, B2, EPI, ROLE>;
+    static int occupancy = 0;
+    if (occupancy <= 0 &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, kern, 512, 0) != hipSuccess)
+      occupancy = 1;
+    kern<<<persistent_grid(occupancy, grid), 512, 0, s>>>(p);
+  } else if constexpr ((MOE_PERSIST_ROLES >> ROLE) & 1) {
+    const auto kern = gemm_bf16_persistent_kernel<BMt, BNt, 2, WGN, AM, BMD, GMD, B2, EPI, ROLE>;
+    static int occupancy = 0;  // per kernel instance; the same on every gfx950 device
+    if (occupancy <= 0 &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, kern, NT, 0) != hipSuccess)
+      occupancy = 1;
+    kern<<<persistent_grid(occupancy, grid), NT, 0, s>>>(p);
   } else {
-    gemm_bf16_kernel<BMt, BNt, 2, WGN, P, AM, BMD, GMD, B2, EPI, ROLE><<<grid, 64 * 2 * WGN, 0, s>>>(p);
+    gemm_bf16_kernel<BMt, BNt, 2, WGN, P, AM, BMD, GMD, B2, EPI, ROLE><<<grid, NT, 0, s>>>(p);
   }
 }
 
