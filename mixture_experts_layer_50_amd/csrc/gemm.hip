@@ -315,37 +315,68 @@ __device__ __forceinline__ void init_loaders(const GemmParams& p, const TileDesc
 // The MFMAs of one K slice: A tile at `as` ([BM] rows), B tile right after it.
 // Wave (wm, wn) owns a (BM/WGM) x (BN/WGN) block of 32x32 accumulators; with
 // the gate|up halves (B2_NHALF) its first FN/2 column blocks are gate columns
-// and the last FN/2 the matching up columns.
+// and the last FN/2 the matching up columns.  The operand fragments of step
+// ks+1 are read from LDS before the MFMAs of step ks are issued, so the LDS
+// latency is hidden behind the matrix cores even with one wave per SIMD.
 template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, int FM, int FN>
+__device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfg)[FN], const bf16_t* as,
+                                           int ks, int wm, int wn, int lane) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  const bf16_t* bs = as + BM * BK;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int base = wm * WTM + i * 32;
+    if constexpr (AM == A_KC) af[i] = frag_kc(as, base, ks, lane);
+    else af[i] = frag_kn<BM>(as, base, ks, lane);
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    int base;
+    if constexpr (B2 == B2_NHALF)
+      base = (j < FN / 2) ? (wn * (WTN / 2) + j * 32) : (BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 32);
+    else
+      base = wn * WTN + j * 32;
+    if constexpr (BMD == B_KC) bfg[j] = frag_kc(bs, base, ks, lane);
+    else bfg[j] = frag_kn<BN>(bs, base, ks, lane);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, bool PIPE = false, int FM,
+          int FN>
 __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* as, int wm, int wn,
                                           int lane) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static_assert(FM == WTM / 32 && FN == WTN / 32, "accumulator blocks match the wave tile");
-  const bf16_t* bs = as + BM * BK;
+  constexpr int KS = BK / 16;
+  if constexpr (PIPE) {
+    bf16x8 af[2][FM], bfg[2][FN];
+    load_frags<BM, BN, WGM, WGN, AM, BMD, B2>(af[0], bfg[0], as, 0, wm, wn, lane);
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8 af[FM], bfg[FN];
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS)
+        load_frags<BM, BN, WGM, WGN, AM, BMD, B2>(af[(ks + 1) & 1], bfg[(ks + 1) & 1], as, ks + 1,
+                                                  wm, wn, lane);
+      // keep the next step's reads above this step's MFMAs (the scheduler
+      // would otherwise move each read down to its first use)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int base = wm * WTM + i * 32;
-      if constexpr (AM == A_KC) af[i] = frag_kc(as, base, ks, lane);
-      else af[i] = frag_kn<BM>(as, base, ks, lane);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[ks & 1][j], af[ks & 1][i],
+                                                             acc[i][j], 0, 0, 0);
     }
+  } else {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      int base;
-      if constexpr (B2 == B2_NHALF)
-        base = (j < FN / 2) ? (wn * (WTN / 2) + j * 32) : (BN / 2 + wn * (WTN / 2) + (j - FN / 2) * 32);
-      else
-        base = wn * WTN + j * 32;
-      if constexpr (BMD == B_KC) bfg[j] = frag_kc(bs, base, ks, lane);
-      else bfg[j] = frag_kn<BN>(bs, base, ks, lane);
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 af[FM], bfg[FN];
+      load_frags<BM, BN, WGM, WGN, AM, BMD, B2>(af, bfg, as, ks, wm, wn, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
   }
 }
 
@@ -809,28 +840,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(Ge
 }
 
 // ---------------------------------------------------------------------------
-// Warp-specialised persistent bf16 MFMA GEMM for plain-store epilogues.
-// Compute waves (WGM x WGN) only read LDS and run the MFMAs; producer waves
-// (NPW) only load K slices from memory into LDS.  On this hardware a wave's
-// loads and stores retire in one in-order queue, so a wave that stores its
-// result and then waits for its next slice also waits for the stores: here
-// the compute waves write their finished blocks (staged through a private
-// LDS area, whole 16-byte chunks of consecutive columns) while the producer
-// waves, which never store, keep the next slices coming.  Tile order and
-// the K-slice pipeline across tiles are those of gemm_bf16_persistent_kernel.
+// Warp-specialised persistent bf16 MFMA GEMM.  Compute waves (WGM x WGN)
+// only read LDS, run the MFMAs and write results; producer waves (NPW) only
+// load K slices from memory into LDS, with PD slices in flight in their own
+// registers.  On this hardware a wave's loads and stores retire in one
+// in-order queue, so a wave that stores its result and then waits for its
+// next slice also waits for the stores: here the compute waves write their
+// finished blocks while the producer waves, which never store, keep the next
+// slices coming.  Plain stores are staged through a private LDS area per
+// compute wave (whole 16-byte chunks of consecutive columns); the other
+// epilogues write from registers.  Tile order and the K-slice pipeline across
+// tiles are those of gemm_bf16_persistent_kernel.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WGM, int WGN, int NPW, int PD, int AM, int BMD, int GMD, int B2, int EPI,
           int ROLE>
 __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(GemmParams p) {
-  static_assert(EPI == EPI_STORE && B2 != B2_NHALF, "plain-store epilogue, contiguous wave columns");
+  static_assert(EPI != EPI_STORE || B2 != B2_NHALF, "plain stores need contiguous wave columns");
   constexpr int NC = WGM * WGN;       // compute waves
   constexpr int NTP = 64 * NPW;       // producer threads
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int BUF = (BM + BN) * BK;
   constexpr int SCPR = WTN / 8;       // 16-byte chunks per staged row
-  static_assert(SCPR == 8 || SCPR == 16, "staged rows of 64 or 128 columns");
-  constexpr int WST = WTM * WTN;      // staging elements per compute wave
+  static_assert(EPI != EPI_STORE || SCPR == 8 || SCPR == 16, "staged rows of 64 or 128 columns");
+  constexpr int WST = EPI == EPI_STORE ? WTM * WTN : 0;  // staging elements per compute wave
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * BUF + NC * WST];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -899,6 +932,10 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
   // (16-byte chunk c of row r at c ^ (r mod SCPR)) -> whole chunks to memory
   // with buffer stores (masked lanes get an out-of-range offset).
   auto store_block = [&](const TileDesc& t) __attribute__((always_inline)) {
+    if constexpr (EPI != EPI_STORE) {
+      epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, t.m_lo, t.m_hi, t.n0, t.e, wm, wn, lane);
+      return;
+    }
     const int half = lane >> 5;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -1009,7 +1046,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     int g = 0;
     auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
       constexpr int U = decltype(Uc)::value;
-      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + U * BUF, wm, wn, lane);
+      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2, true>(acc, smem + U * BUF, wm, wn, lane);
       __syncthreads();
       ++g;
       return advance();
@@ -1219,9 +1256,14 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 #ifndef MOE_PERSIST_ROLES
 #define MOE_PERSIST_ROLES 0
 #endif
-// Register stages of the warp-specialised kernel's producer waves.
+// Register stages of the warp-specialised kernel's producer waves; its
+// compute waves each own a 64 x 64 block of the tile.
 #ifndef MOE_WS_STAGES
 #define MOE_WS_STAGES 2
+#endif
+#define MOE_WS_COMPUTE_WAVES 8
+#ifndef MOE_WS_PRODUCER_WAVES
+#define MOE_WS_PRODUCER_WAVES 4
 #endif
 
 // Workgroups of a persistent launch: as many as fit on the device at once,
@@ -1247,14 +1289,19 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   // 256x256 tiles: MOE_WIDE_WAVES = 8 runs two waves per SIMD (2 x 4 grid)
   constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
   constexpr int NT = 64 * 2 * WGN;
-  if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && EPI == EPI_STORE && B2 != B2_NHALF) {
-    // 2 x 2 compute waves and 4 producer waves
-    const auto kern = gemm_bf16_ws_kernel<BMt, BNt, 2, 2, 4, MOE_WS_STAGES, AM, BMD, GMD, B2, EPI, ROLE>;
+  if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && (EPI != EPI_STORE || B2 != B2_NHALF)) {
+    // eight compute waves with 64 x 64 blocks (two per SIMD) and the
+    // producer waves
+    constexpr int CWM = BMt / 64, CWN = BNt / 64;
+    static_assert(CWM * CWN == MOE_WS_COMPUTE_WAVES, "compute wave grid");
+    constexpr int WS_NT = 64 * (CWM * CWN + MOE_WS_PRODUCER_WAVES);
+    const auto kern = gemm_bf16_ws_kernel<BMt, BNt, CWM, CWN, MOE_WS_PRODUCER_WAVES, MOE_WS_STAGES,
+                                          AM, BMD, GMD, B2, EPI, ROLE>;
     static int occupancy = 0;
     if (occupancy <= 0 &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, kern, 512, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, kern, WS_NT, 0) != hipSuccess)
       occupancy = 1;
-    kern<<<persistent_grid(occupancy, grid), 512, 0, s>>>(p);
+    kern<<<persistent_grid(occupancy, grid), WS_NT, 0, s>>>(p);
   } else if constexpr ((MOE_PERSIST_ROLES >> ROLE) & 1) {
     const auto kern = gemm_bf16_persistent_kernel<BMt, BNt, 2, WGN, AM, BMD, GMD, B2, EPI, ROLE>;
     static int occupancy = 0;  // per kernel instance; the same on every gfx950 device
