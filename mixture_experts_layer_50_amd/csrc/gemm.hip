@@ -573,6 +573,172 @@ __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x1
   }
 }
 
+// Staged activation epilogues.  The tile passes through LDS in bands of one
+// wave row (WTM rows); each band array is [WTM][128] bf16 with 16-byte chunk
+// c of row r at c ^ (r & 15), so that memory is read and written in whole
+// 16-byte chunks of consecutive columns (full cache lines per row) instead
+// of 8-byte pieces spread over 32 rows.
+__device__ __forceinline__ int band_off(int r, int n) { return r * 128 + (((n >> 3) ^ (r & 15)) << 3) + (n & 7); }
+
+// SwiGLU: gate columns n0 .. n0+127 and the matching up columns of the tile
+// give H = [Hg | Hu] (optional) and A = silu(Hg) * Hu.
+template <int BM, int BN, int WGM, int FM, int FN, int WTM, int WTN, int NT>
+__device__ __forceinline__ void epilogue_swiglu_staged(const GemmParams& p, f32x16 (&acc)[FM][FN],
+                                                       bf16_t* lds, int m_lo, int m_hi, int n0,
+                                                       int wm, int wn, int lane, int tid) {
+  constexpr int HC = BN / 2;  // columns per half (128)
+  constexpr int BAND = WTM * HC;
+  bf16_t* Gs = lds;
+  bf16_t* Us = lds + BAND;
+  bf16_t* As = lds + 2 * BAND;
+  bf16_t* H = static_cast<bf16_t*>(p.C0);
+  bf16_t* Aout = static_cast<bf16_t*>(p.C2);
+  const int64_t I = p.I;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int rd = 0; rd < WGM; ++rd) {
+    if (rd > 0) __syncthreads();  // the previous band has been read back
+    if (wm == rd) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = i * 32 + (lane & 31);
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = wn * (WTN / 2) + jp * 32 + 8 * q + 4 * half;
+            float g[4], u[4], a[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              g[t] = acc[i][jp][4 * q + t];
+              u[t] = acc[i][jp + FN / 2][4 * q + t];
+              a[t] = g[t] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[t])) * u[t];
+            }
+            const int o = band_off(r, n);
+            *reinterpret_cast<uint2*>(Gs + o) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+            *reinterpret_cast<uint2*>(Us + o) = make_uint2(pack_bf2(u[0], u[1]), pack_bf2(u[2], u[3]));
+            *reinterpret_cast<uint2*>(As + o) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+          }
+      }
+    }
+    __syncthreads();
+    const int mb = m_lo + rd * WTM;
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(Aout + (int64_t)mb * I + n0);
+    const __amdgpu_buffer_rsrc_t rsg = make_rsrc((H ? H : Aout) + (int64_t)mb * 2 * I + n0);
+    const __amdgpu_buffer_rsrc_t rsu = make_rsrc((H ? H : Aout) + (int64_t)mb * 2 * I + I + n0);
+#pragma unroll
+    for (int q0 = 0; q0 < WTM * (HC / 8); q0 += NT) {
+      const int q = q0 + tid;
+      const int r = q / (HC / 8), c = q % (HC / 8);
+      const bool ok = mb + r < m_hi && n0 + c * 8 < I;
+      const int o = band_off(r, c * 8);
+      const u32x4 va = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(As + o));
+      __builtin_amdgcn_raw_buffer_store_b128(va, rsa, ok ? (int)(((int64_t)r * I + c * 8) * 2) : OOB, 0, 0);
+      if (H) {
+        const u32x4 vg = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Gs + o));
+        const u32x4 vu = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Us + o));
+        const int oh = ok ? (int)(((int64_t)r * 2 * I + c * 8) * 2) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(vg, rsg, oh, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(vu, rsu, oh, 0, 0);
+      }
+    }
+  }
+}
+
+// dSwiGLU: acc = dA for columns n0 .. n0+127; reads H = [Hg | Hu] of those
+// columns and writes dH = [dHg | dHu].
+template <int BM, int BN, int WGM, int FM, int FN, int WTM, int WTN, int NT>
+__device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32x16 (&acc)[FM][FN],
+                                                        bf16_t* lds, int m_lo, int m_hi, int n0,
+                                                        int wm, int wn, int lane, int tid) {
+  constexpr int BAND = WTM * BN;
+  constexpr int CPR = BN / 8;
+  bf16_t* Gs = lds;
+  bf16_t* Us = lds + BAND;
+  const bf16_t* H = static_cast<const bf16_t*>(p.aux);
+  bf16_t* dH = static_cast<bf16_t*>(p.C0);
+  const int64_t I = p.I;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int rd = 0; rd < WGM; ++rd) {
+    const int mb = m_lo + rd * WTM;
+    const int64_t hrow = (int64_t)mb * 2 * I + n0;
+    // 1. the band's Hg and Hu into LDS (rows past m_hi and columns past I read zeros)
+    {
+      const __amdgpu_buffer_rsrc_t rsg = make_rsrc(H + hrow);
+      const __amdgpu_buffer_rsrc_t rsu = make_rsrc(H + hrow + I);
+      constexpr int NQ = (WTM * CPR + NT - 1) / NT;
+      uint4 vg[NQ], vu[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int q = i * NT + tid;
+        const int r = q / CPR, c = q % CPR;
+        const bool ok = (WTM * CPR % NT == 0 || q < WTM * CPR) && mb + r < m_hi && n0 + c * 8 < I;
+        const int off = ok ? (int)(((int64_t)r * 2 * I + c * 8) * 2) : OOB;
+        vg[i] = buf_load16<0>(rsg, off, 0);
+        vu[i] = buf_load16<0>(rsu, off, 0);
+      }
+      if (rd > 0) __syncthreads();  // the previous band has been read back
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int q = i * NT + tid;
+        if (WTM * CPR % NT == 0 || q < WTM * CPR) {
+          const int r = q / CPR, c = q % CPR;
+          *reinterpret_cast<uint4*>(Gs + band_off(r, c * 8)) = vg[i];
+          *reinterpret_cast<uint4*>(Us + band_off(r, c * 8)) = vu[i];
+        }
+      }
+    }
+    __syncthreads();
+    // 2. the band's waves turn (dA, Hg, Hu) into (dHg, dHu) in place
+    if (wm == rd) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
+            const int o = band_off(r, n);
+            const uint2 hg = *reinterpret_cast<const uint2*>(Gs + o);
+            const uint2 hu = *reinterpret_cast<const uint2*>(Us + o);
+            const float g[4] = {bf2f((bf16_t)(hg.x & 0xffff)), bf2f((bf16_t)(hg.x >> 16)),
+                                bf2f((bf16_t)(hg.y & 0xffff)), bf2f((bf16_t)(hg.y >> 16))};
+            const float u[4] = {bf2f((bf16_t)(hu.x & 0xffff)), bf2f((bf16_t)(hu.x >> 16)),
+                                bf2f((bf16_t)(hu.y & 0xffff)), bf2f((bf16_t)(hu.y >> 16))};
+            float dg[4], du[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float v = acc[i][j][4 * q + t];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[t]));
+              dg[t] = v * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
+              du[t] = v * g[t] * sg;
+            }
+            *reinterpret_cast<uint2*>(Gs + o) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(Us + o) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+          }
+      }
+    }
+    __syncthreads();
+    // 3. whole chunks out
+    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(dH + hrow);
+    const __amdgpu_buffer_rsrc_t rsu = make_rsrc(dH + hrow + I);
+#pragma unroll
+    for (int q0 = 0; q0 < WTM * CPR; q0 += NT) {
+      const int q = q0 + tid;
+      const int r = q / CPR, c = q % CPR;
+      const bool ok = (WTM * CPR % NT == 0 || q < WTM * CPR) && mb + r < m_hi && n0 + c * 8 < I;
+      const int off = ok ? (int)(((int64_t)r * 2 * I + c * 8) * 2) : OOB;
+      const int o = band_off(r, c * 8);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Gs + o)), rsg, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Us + o)), rsu, off, 0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM.  WGM x WGN waves, each owning a (BM/WGM) x
 // (BN/WGN) block of 32x32 MFMA tiles.  P register stages: while the
@@ -669,9 +835,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
 #ifndef MOE_STAGED_STORE
 #define MOE_STAGED_STORE 1
 #endif
-  if constexpr (EPI == EPI_STORE && MOE_STAGED_STORE && BN / 8 >= 16 && BM * BN <= (BM + BN) * BK * 2)
+  // the two LDS buffers are free here (the last step ended with a barrier)
+  constexpr int LDS_ELEMS = (BM + BN) * BK * 2;
+  if constexpr (EPI == EPI_STORE && MOE_STAGED_STORE && BN / 8 >= 16 && BM * BN <= LDS_ELEMS)
     epilogue_store_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT, GMD, 1>(p, acc, smem, m_lo, m_hi, n0, e,
                                                                     wm, wn, lane, tid);
+  else if constexpr (EPI == EPI_SWIGLU && MOE_STAGED_STORE && BN / 16 == 16 &&
+                     3 * WTM * (BN / 2) <= LDS_ELEMS)
+    epilogue_swiglu_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT>(p, acc, smem, m_lo, m_hi, n0, wm, wn,
+                                                            lane, tid);
+  else if constexpr (EPI == EPI_DSWIGLU && MOE_STAGED_STORE && BN / 8 == 16 &&
+                     2 * WTM * BN <= LDS_ELEMS)
+    epilogue_dswiglu_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT>(p, acc, smem, m_lo, m_hi, n0, wm, wn,
+                                                             lane, tid);
   else
     epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
 }
