@@ -425,29 +425,10 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
                 group_offsets, s};
   auto rows_or_tiles = [&](GemmRole r) { return D.bf16 ? max_m_tiles(D, tile_bm(role_tile(r))) : D.R_cap; };
 
-  {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
-    GemmParams p{};
-    p.A = dyp; p.lda = D.d;
-    p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
-    p.N = D.I; p.K = D.d;
-    p.off = group_offsets; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_DOWN_DGRAD)));
-    p.C0 = dH; p.aux = h_save; p.I = D.I;
-    if (D.bf16) MOE_TRY(tt.get(R_DOWN_DGRAD, &p.tiles));
-    MOE_TRY(launch_gemm(D.bf16, R_DOWN_DGRAD, p, rows_or_tiles(R_DOWN_DGRAD), s));
-  }
-  {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
-    GemmParams p{};
-    p.A = dH; p.lda = 2 * (int64_t)D.I;
-    p.B0 = w_gate; p.B1 = w_up; p.ldb = D.I; p.b_estride = (int64_t)D.d * D.I;
-    p.k_split = D.I;
-    p.N = D.d; p.K = 2 * D.I;
-    p.off = group_offsets; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.d, tile_bn(role_tile(R_GATEUP_DGRAD)));
-    p.C0 = dxp; p.ldc = D.d;
-    if (D.bf16) MOE_TRY(tt.get(R_GATEUP_DGRAD, &p.tiles));
-    MOE_TRY(launch_gemm(D.bf16, R_GATEUP_DGRAD, p, rows_or_tiles(R_GATEUP_DGRAD), s));
-  }
+  // Order: the weight gradient of the down projection and the dSwiGLU GEMM
+  // read dYp while it is fresh in the memory-side cache, the gate/up weight
+  // gradient reads dH right after it is written, and dXp is written last, so
+  // that the permute backward that follows reads it back from that cache.
   {  // a8: dWd[e] = A_e^T dYp_e
     GemmParams p{};
     p.A = a_save; p.lda = D.I;
@@ -458,6 +439,17 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.m_tiles = (int)ceil_div(D.I, tile_bm(t)); p.n_tiles = (int)ceil_div(D.d, tile_bn(t));
     p.C0 = dw_down; p.ldc = D.d; p.c_estride = (int64_t)D.I * D.d;
     MOE_TRY(launch_gemm(D.bf16, R_DOWN_WGRAD, p, p.m_tiles, s));
+  }
+  {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
+    GemmParams p{};
+    p.A = dyp; p.lda = D.d;
+    p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
+    p.N = D.I; p.K = D.d;
+    p.off = group_offsets; p.groups = D.E_loc;
+    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_DOWN_DGRAD)));
+    p.C0 = dH; p.aux = h_save; p.I = D.I;
+    if (D.bf16) MOE_TRY(tt.get(R_DOWN_DGRAD, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, R_DOWN_DGRAD, p, rows_or_tiles(R_DOWN_DGRAD), s));
   }
   {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
     GemmParams p{};
@@ -470,6 +462,18 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.C0 = dw_gate; p.C1 = dw_up; p.n_split = D.I; p.ldc = D.I;
     p.c_estride = (int64_t)D.d * D.I;
     MOE_TRY(launch_gemm(D.bf16, R_GATEUP_WGRAD, p, p.m_tiles, s));
+  }
+  {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
+    GemmParams p{};
+    p.A = dH; p.lda = 2 * (int64_t)D.I;
+    p.B0 = w_gate; p.B1 = w_up; p.ldb = D.I; p.b_estride = (int64_t)D.d * D.I;
+    p.k_split = D.I;
+    p.N = D.d; p.K = 2 * D.I;
+    p.off = group_offsets; p.groups = D.E_loc;
+    p.n_tiles = (int)ceil_div(D.d, tile_bn(role_tile(R_GATEUP_DGRAD)));
+    p.C0 = dxp; p.ldc = D.d;
+    if (D.bf16) MOE_TRY(tt.get(R_GATEUP_DGRAD, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, R_GATEUP_DGRAD, p, rows_or_tiles(R_GATEUP_DGRAD), s));
   }
   return MOE_OK;
 }

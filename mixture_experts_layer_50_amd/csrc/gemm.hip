@@ -282,7 +282,7 @@ __device__ __forceinline__ TileDesc tile_desc(const GemmParams& p, int L) {
 #ifndef MOE_WEIGHT_CPOL
 #define MOE_WEIGHT_CPOL 2
 #endif
-// Cache policy of the warp-specialised kernel's result stores (2 = nt).
+// Cache policy of the weight-gradient result stores (2 = nt).
 #ifndef MOE_OUT_CPOL
 #define MOE_OUT_CPOL 2
 #endif
@@ -1152,7 +1152,9 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
       const int q = i * 64 + lane;
       const int r = q / SCPR, c = q % SCPR;
       const int n = nb + c * 8;
-      bo.store<MOE_OUT_CPOL>(p, v[i], r, n, mb + r < t.m_hi && n < p.N);
+      // weight gradients are not read again soon: stream them past the
+      // caches; other results (read by the next kernel) stay cacheable
+      bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, v[i], r, n, mb + r < t.m_hi && n < p.N);
     }
   };
 
