@@ -261,16 +261,15 @@ struct TileTables {
   int32_t* base;
   const int32_t* off;
   hipStream_t s;
-  bool built256 = false, built128 = false;
+  bool built = false;
   moe_status_t get(GemmRole role, const int32_t** out) {
-    const int bm = tile_bm(role_tile(role));
-    int32_t* t = bm == 256 ? base : base + one_table_bytes(D, 256) / 4;
-    bool& built = bm == 256 ? built256 : built128;
-    if (!built) {
-      MOE_TRY(launch_tile_table(off, D.E_loc, bm, t, s));
+    int32_t* t256 = base;
+    int32_t* t128 = base + one_table_bytes(D, 256) / 4;
+    if (!built) {  // both tables in one launch, on first use
+      MOE_TRY(launch_tile_tables(off, D.E_loc, t256, t128, s));
       built = true;
     }
-    *out = t;
+    *out = tile_bm(role_tile(role)) == 256 ? t256 : t128;
     return MOE_OK;
   }
 };
@@ -498,10 +497,8 @@ extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, c
   hipStream_t s = S(stream);
   if (D.balanced) {
     MOE_TRY(opt(fn, {{"dlogits", dlogits}, {"dw_router", dw_router}, {"dbias", dbias}}));
-    if (dlogits) MOE_TRY(launch_fill_zero(dlogits, (int64_t)D.T * D.E * 4, s));
-    if (dw_router) MOE_TRY(launch_fill_zero(dw_router, (int64_t)D.d * D.E * D.eb, s));
-    if (dbias) MOE_TRY(launch_fill_zero(dbias, (int64_t)D.E * 4, s));
-    return MOE_OK;
+    return launch_fill_zero(dlogits, (int64_t)D.T * D.E * 4, dw_router, (int64_t)D.d * D.E * D.eb,
+                            dbias, (int64_t)D.E * 4, s);
   }
   MOE_TRY(need(fn, {{"x", x}, {"w_router", w_router}, {"topk_idx", topk_idx}, {"topk_w", topk_w},
                     {"dtopk_w", dtopk_w}, {"dlogits", dlogits}, {"dw_router", dw_router}, {"dx", dx}}));

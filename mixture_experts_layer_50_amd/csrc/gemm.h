@@ -84,14 +84,15 @@ int tile_bn(TileCfg cfg);
 const char* role_name(GemmRole role);
 
 // Launch one GEMM: the bf16 MFMA kernel of the role, or the fp32 kernel.  For
-// G_MROWS the caller has built the tile table (launch_tile_table) for
+// G_MROWS the caller has built the tile table (launch_tile_tables) for
 // tile_bm(role_tile(role)); max_m_tiles bounds its entries (fp32: the row count).
 moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
                          hipStream_t s);
 
-// Tile table for G_MROWS: tiles[0] = number of M tiles, then for each tile
-// (expert, first row) in expert order.
-moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* tiles,
-                               hipStream_t s);
+// Tile tables for G_MROWS, for 256-row and for 128-row tiles (one launch):
+// tiles[0] = number of M tiles, then for each tile (expert, first row) in
+// expert order.
+moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
+                                int32_t* tiles128, hipStream_t s);
 
 }  // namespace moe

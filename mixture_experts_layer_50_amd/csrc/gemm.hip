@@ -1311,8 +1311,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Tile table for row-grouped GEMMs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups, int bm,
-                                                          int32_t* tiles) {
+// Workgroup 0 builds the table for 256-row tiles, workgroup 1 the one for
+// 128-row tiles.
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups,
+                                                          int32_t* tiles256, int32_t* tiles128) {
+  const int bm = blockIdx.x == 0 ? 256 : 128;
+  int32_t* tiles = blockIdx.x == 0 ? tiles256 : tiles128;
   __shared__ int32_t scan[1024];
   __shared__ int32_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -1344,10 +1348,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
   if (threadIdx.x == 0) tiles[0] = carry;
 }
 
-moe_status_t launch_tile_table(const int32_t* off, int groups, int bm, int32_t* tiles,
-                               hipStream_t s) {
+moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
+                                int32_t* tiles128, hipStream_t s) {
   ProfScope prof("tile_table", s);
-  tile_table_kernel<<<1, 1024, 0, s>>>(off, groups, bm, tiles);
+  tile_table_kernel<<<2, 1024, 0, s>>>(off, groups, tiles256, tiles128);
   return check_launch("tile_table_kernel");
 }
 

@@ -16,7 +16,9 @@ moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32
 moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
                                  int k, float* dl, bf16_t* dl_bf16, hipStream_t s);
 moe_status_t launch_col_sum(const float* dl, int T, int E, float* db, hipStream_t s);
-moe_status_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
+// Zeroes up to three buffers (null ones are skipped) in one launch.
+moe_status_t launch_fill_zero(void* p0, int64_t bytes0, void* p1, int64_t bytes1, void* p2,
+                              int64_t bytes2, hipStream_t s);
 
 // permute.hip
 constexpr int PERM_TOKENS = 256;  // tokens per block of the counting sort

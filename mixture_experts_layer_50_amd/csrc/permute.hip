@@ -27,17 +27,25 @@ int64_t permute_ws_bytes(int T, int E_loc) {
   return ceil_div(T, PERM_TOKENS) * (int64_t)E_loc * 4;
 }
 
-__device__ __forceinline__ void build_masks(uint32_t* mask, const int32_t* idx, int T, int k, int e_lo,
-                                            int e_hi, int E_loc) {
+constexpr int MAXK = 32;
+
+// The expert ids of this thread's token (slots >= k, and tokens >= T, get -1),
+// all loads in flight together.
+__device__ __forceinline__ void load_ids(int (&ids)[MAXK], const int32_t* idx, int T, int k) {
+  const int t = blockIdx.x * PERM_TOKENS + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) ids[j] = (t < T && j < k) ? idx[(int64_t)t * k + j] : -1;
+}
+
+__device__ __forceinline__ void build_masks(uint32_t* mask, const int (&ids)[MAXK], int e_lo, int e_hi,
+                                            int E_loc) {
   for (int i = threadIdx.x; i < E_loc * MASK_WORDS; i += blockDim.x) mask[i] = 0u;
   __syncthreads();
-  const int t = blockIdx.x * PERM_TOKENS + threadIdx.x;
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      int e = idx[(int64_t)t * k + j];
-      if (e >= e_lo && e < e_hi)
-        atomicOr(&mask[(e - e_lo) * MASK_WORDS + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
-    }
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    const int e = ids[j];
+    if (e >= e_lo && e < e_hi)
+      atomicOr(&mask[(e - e_lo) * MASK_WORDS + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
   }
   __syncthreads();
 }
@@ -47,7 +55,9 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_count_kernel(const int32_t* 
                                                                  int32_t* counts) {
   extern __shared__ uint32_t mask[];
   const int E_loc = e_hi - e_lo;
-  build_masks(mask, idx, T, k, e_lo, e_hi, E_loc);
+  int ids[MAXK];
+  load_ids(ids, idx, T, k);
+  build_masks(mask, ids, e_lo, e_hi, E_loc);
   for (int e = threadIdx.x; e < E_loc; e += blockDim.x) {
     int c = 0;
 #pragma unroll
@@ -62,12 +72,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* counts, int nb
                                                          int32_t* offsets) {
   __shared__ int32_t scan[1024];
   const int e = threadIdx.x;
+  constexpr int U = 8;  // block counts in flight per thread
   int total = 0;
   if (e < E_loc) {
-    for (int b = 0; b < nb; ++b) {
-      int c = counts[(int64_t)b * E_loc + e];
-      counts[(int64_t)b * E_loc + e] = total;
-      total += c;
+    for (int b0 = 0; b0 < nb; b0 += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b0 + u < nb ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u < nb) counts[(int64_t)(b0 + u) * E_loc + e] = total;
+        total += c[u];
+      }
     }
   }
   scan[e] = total;
@@ -92,17 +108,22 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_scatter_kernel(const int32_t
                                                                    int32_t* perm, int32_t* inv) {
   extern __shared__ uint32_t mask[];
   const int E_loc = e_hi - e_lo;
-  build_masks(mask, idx, T, k, e_lo, e_hi, E_loc);
+  int ids[MAXK];
+  load_ids(ids, idx, T, k);
+  build_masks(mask, ids, e_lo, e_hi, E_loc);
   const int t = blockIdx.x * PERM_TOKENS + threadIdx.x;
   if (t >= T) return;
   const int w = threadIdx.x >> 5;
   const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
-  for (int j = 0; j < k; ++j) {
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    if (j >= k) continue;
     const int64_t r = (int64_t)t * k + j;
-    const int e = idx[r];
+    const int e = ids[j];
     bool keep = e >= e_lo && e < e_hi;
-    for (int jj = 0; keep && jj < j; ++jj)  // a repeated expert keeps its first slot only
-      if (idx[(int64_t)t * k + jj] == e) keep = false;
+#pragma unroll
+    for (int jj = 0; jj < j; ++jj)  // a repeated expert keeps its first slot only
+      if (ids[jj] == e) keep = false;
     int pos = -1;
     if (keep) {
       const uint32_t* m = mask + (e - e_lo) * MASK_WORDS;
@@ -256,7 +277,6 @@ moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float*
 
 // dyp[inv[t,j]] = w[t,j] * dy[t];  dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when dropped).
 // One wavefront per token, slot data broadcast from lane j as above.
-constexpr int MAXK = 32;
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const uint4* yp,
                                                           const int32_t* inv, const float* w,

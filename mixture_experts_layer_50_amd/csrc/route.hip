@@ -164,18 +164,35 @@ moe_status_t launch_col_sum(const float* dl, int T, int E, float* db, hipStream_
 }
 
 // ---------------------------------------------------------------- fill
-__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) p[i] = 0u;
+// Zeroes up to three buffers in one launch.
+struct ZeroList {
+  uint32_t* p[3];
+  int64_t n[3];  // 4-byte words
+};
+
+__global__ void fill_zero_kernel(ZeroList z) {
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+    for (int64_t i = i0; i < z.n[b]; i += stride) z.p[b][i] = 0u;
 }
 
-moe_status_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
-  if (bytes <= 0) return MOE_OK;
+moe_status_t launch_fill_zero(void* p0, int64_t bytes0, void* p1, int64_t bytes1, void* p2,
+                              int64_t bytes2, hipStream_t s) {
+  ZeroList z{};
+  void* ps[3] = {p0, p1, p2};
+  const int64_t bs[3] = {bytes0, bytes1, bytes2};
+  int64_t most = 0;
+  for (int b = 0; b < 3; ++b) {
+    z.p[b] = static_cast<uint32_t*>(ps[b]);
+    z.n[b] = ps[b] ? bs[b] / 4 : 0;  // every buffer here is a multiple of 4 bytes
+    most = std::max(most, z.n[b]);
+  }
+  if (most <= 0) return MOE_OK;
   ProfScope prof("fill_zero", s);
-  int64_t words = bytes / 4;  // every buffer here is a multiple of 4 bytes
-  unsigned grid = (unsigned)std::min<int64_t>(ceil_div(words, 256), 4096);
-  fill_zero_kernel<<<grid, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(most, 256), 4096);
+  fill_zero_kernel<<<grid, 256, 0, s>>>(z);
   return check_launch("fill_zero_kernel");
 }
 
