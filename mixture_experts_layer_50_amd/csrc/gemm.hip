@@ -1130,14 +1130,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     // the wave's own LDS writes and reads execute in order; keep the compiler
     // from moving the reads above the writes
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    constexpr int NQ = WTM * SCPR / 64;
-    uint4 v[NQ];
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int q = i * 64 + lane;
-      const int r = q / SCPR, c = q % SCPR;
-      v[i] = *reinterpret_cast<const uint4*>(stage + r * WTN + (c ^ (r & (SCPR - 1))) * 8);
-    }
+    constexpr int NQ = WTM * SCPR / 64;  // chunks per lane
+    constexpr int QB = NQ < 8 ? NQ : 8;   // chunks per batch (bounds the registers)
     bf16_t* C0 = static_cast<bf16_t*>(p.C0);
     bf16_t* C1 = static_cast<bf16_t*>(p.C1);
     if (GMD == G_KROWS) {
@@ -1148,13 +1142,23 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     const int nb = t.n0 + wn * WTN;
     const BlockOut bo(p, C0, C1, (int64_t)mb * p.ldc, nb, nb + WTN);
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int q = i * 64 + lane;
-      const int r = q / SCPR, c = q % SCPR;
-      const int n = nb + c * 8;
-      // weight gradients are not read again soon: stream them past the
-      // caches; other results (read by the next kernel) stay cacheable
-      bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, v[i], r, n, mb + r < t.m_hi && n < p.N);
+    for (int i0 = 0; i0 < NQ; i0 += QB) {
+      uint4 v[QB];
+#pragma unroll
+      for (int i = 0; i < QB; ++i) {
+        const int q = (i0 + i) * 64 + lane;
+        const int r = q / SCPR, c = q % SCPR;
+        v[i] = *reinterpret_cast<const uint4*>(stage + r * WTN + (c ^ (r & (SCPR - 1))) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < QB; ++i) {
+        const int q = (i0 + i) * 64 + lane;
+        const int r = q / SCPR, c = q % SCPR;
+        const int n = nb + c * 8;
+        // weight gradients are not read again soon: stream them past the
+        // caches; other results (read by the next kernel) stay cacheable
+        bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, v[i], r, n, mb + r < t.m_hi && n < p.N);
+      }
     }
   };
 
@@ -1443,7 +1447,9 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 #ifndef MOE_WS_STAGES
 #define MOE_WS_STAGES 2
 #endif
-#define MOE_WS_COMPUTE_WAVES 8
+#ifndef MOE_WS_WAVE_ROWS
+#define MOE_WS_WAVE_ROWS 64
+#endif
 #ifndef MOE_WS_PRODUCER_WAVES
 #define MOE_WS_PRODUCER_WAVES 4
 #endif
@@ -1472,10 +1478,8 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
   constexpr int NT = 64 * 2 * WGN;
   if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && (EPI != EPI_STORE || B2 != B2_NHALF)) {
-    // eight compute waves with 64 x 64 blocks (two per SIMD) and the
-    // producer waves
-    constexpr int CWM = BMt / 64, CWN = BNt / 64;
-    static_assert(CWM * CWN == MOE_WS_COMPUTE_WAVES, "compute wave grid");
+    // compute waves with MOE_WS_WAVE_ROWS x 64 blocks, and the producer waves
+    constexpr int CWM = BMt / MOE_WS_WAVE_ROWS, CWN = BNt / 64;
     constexpr int WS_NT = 64 * (CWM * CWN + MOE_WS_PRODUCER_WAVES);
     const auto kern = gemm_bf16_ws_kernel<BMt, BNt, CWM, CWN, MOE_WS_PRODUCER_WAVES, MOE_WS_STAGES,
                                           AM, BMD, GMD, B2, EPI, ROLE>;
