@@ -256,8 +256,19 @@ def main():
                          "gbs": round(b / us / 1e3, 1), "mfma_frac": round(f / us / 1e6 / PEAK_BF16_TFLOPS, 3),
                          "hbm_frac": round(b / us / 1e3 / PEAK_HBM_GBS, 3)}
     fl, by = GEMMS[dom]
-    flops = fl(R, w.d, w.I, El)
-    achieved = flops / kernels[dom]["us_avg"] / 1e6
+    flops, nbytes = fl(R, w.d, w.I, El), by(R, w.d, w.I, El)
+    # the dominant kernel's bound by the roofline model: HBM when its
+    # algorithmic bytes take longer at peak bandwidth than its flops at peak
+    # MFMA rate (intensity below the ridge point), else MFMA
+    hbm_bound = nbytes / PEAK_HBM_GBS > flops / PEAK_BF16_TFLOPS / 1e3
+    dom_us = kernels[dom]["us_avg"]
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(nbytes / dom_us / 1e3, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / dom_us / 1e6, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
@@ -283,9 +294,9 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "I": w.I,
                    "gate": w.gate, "pass": "fwd+bwd" if w.backward else "fwd",
                    "routed_rows": R, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": dom},
+        "roofline": {**roof, "traffic": traffic, "kernel": dom,
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                     "mfma_tflops": round(flops / dom_us / 1e6, 1)},
         "grouped_gemm": {"tflops_all_six": round(gemm_flops / gemm_total_us / 1e6, 1),
                          "mfma_frac_all_six": round(gemm_flops / gemm_total_us / 1e6 / PEAK_BF16_TFLOPS, 4),
                          "kernels": gem},
