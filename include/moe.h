@@ -203,7 +203,10 @@ moe_status_t moe_permute_bwd(const moe_shape_t* shape, const void* dxp, const in
  *   and dbias (if non-NULL) are set to 0 and dx is not touched.
  * x [T,d]; w_router [d,E]; topk_idx, topk_w, dtopk_w [T,k]; dlogits [T,E] fp32
  * (required for softmax_topk); dw_router [d,E] (dtype); dbias [E] fp32;
- * dx [T,d].  ws: moe_workspace_size(MOE_OP_ROUTE_BWD). */
+ * dx [T,d].  ws: moe_workspace_size(MOE_OP_ROUTE_BWD) (0 for balanced; it
+ * holds the bf16 copy of dlogits, column sums of dlogits per 32 tokens and,
+ * for bf16, fp32 partials of dw_router over token ranges; every sum runs in a
+ * fixed order, so results are deterministic). */
 moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* w_router,
                            const int32_t* topk_idx, const float* topk_w,
                            const float* dtopk_w, float* dlogits, void* dw_router,

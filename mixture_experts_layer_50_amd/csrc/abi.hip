@@ -252,7 +252,10 @@ moe_status_t opt(const char* fn, std::initializer_list<std::pair<const char*, co
 int64_t one_table_bytes(const Dims& D, int bm) {
   return round_up((1 + 2 * ((int64_t)D.R_cap / bm + D.E_loc)) * 4, 256);
 }
-int64_t tile_table_bytes(const Dims& D) { return one_table_bytes(D, 256) + one_table_bytes(D, 128); }
+int64_t kcost_bytes(const Dims& D) { return round_up((int64_t)(D.E_loc + 1) * 4, 256); }
+int64_t tile_table_bytes(const Dims& D) {
+  return one_table_bytes(D, 256) + one_table_bytes(D, 128) + kcost_bytes(D);
+}
 int max_m_tiles(const Dims& D, int bm) { return D.R_cap / bm + D.E_loc; }
 
 // Builds the tile tables a call needs, once each, in its workspace.
@@ -262,15 +265,43 @@ struct TileTables {
   const int32_t* off;
   hipStream_t s;
   bool built = false;
-  moe_status_t get(GemmRole role, const int32_t** out) {
-    int32_t* t256 = base;
-    int32_t* t128 = base + one_table_bytes(D, 256) / 4;
-    if (!built) {  // both tables in one launch, on first use
-      MOE_TRY(launch_tile_tables(off, D.E_loc, t256, t128, s));
+  int32_t* t256() const { return base; }
+  int32_t* t128() const { return base + one_table_bytes(D, 256) / 4; }
+  int32_t* kcost() const { return t128() + one_table_bytes(D, 128) / 4; }
+  moe_status_t ensure() {  // all tables in one launch, on first use
+    if (!built) {
+      MOE_TRY(launch_tile_tables(off, D.E_loc, t256(), t128(), kcost(), s));
       built = true;
     }
-    *out = tile_bm(role_tile(role)) == 256 ? t256 : t128;
     return MOE_OK;
+  }
+  moe_status_t get(GemmRole role, const int32_t** out) {
+    MOE_TRY(ensure());
+    *out = tile_bm(role_tile(role)) == 256 ? t256() : t128();
+    return MOE_OK;
+  }
+};
+
+// Router-backward workspace: the bf16 copy of dL (bf16 layers), per-workgroup
+// column sums of dL, and the split-K partials of x^T dL (bf16 layers).
+struct RouteBwdWs {
+  int64_t dl16 = 0, dbp = 0, dwp = 0, total = 0;
+  int nblk = 0, nsplit = 0, k_chunk = 0;
+  explicit RouteBwdWs(const Dims& D) {
+    nblk = (int)ceil_div(D.T, ROUTE_BWD_TOKENS);
+    if (D.bf16) {
+      // about 512 token rows per split, at most 16 splits, whole 64-row K slices
+      nsplit = (int)std::min<int64_t>(16, std::max<int64_t>(1, ceil_div(D.T, 512)));
+      k_chunk = (int)round_up(ceil_div(D.T, nsplit), 64);
+      nsplit = (int)ceil_div(D.T, k_chunk);
+    }
+    const int64_t a = D.bf16 ? round_up((int64_t)D.T * D.E * 2, 256) : 0;
+    const int64_t b = round_up((int64_t)nblk * D.E * 4, 256);
+    const int64_t c = D.bf16 ? round_up((int64_t)nsplit * D.d * D.E * 4, 256) : 0;
+    dl16 = 0;
+    dbp = a;
+    dwp = a + b;
+    total = a + b + c;
   }
 };
 
@@ -281,8 +312,11 @@ int64_t ws_bytes(const Dims& D, int op) {
     case MOE_OP_FFN_BWD:
       return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
              (D.bf16 ? tile_table_bytes(D) : 0);
-    case MOE_OP_ROUTE_BWD:
-      return (D.bf16 && !D.balanced) ? round_up((int64_t)D.T * D.E * 2, 256) : 0;
+    case MOE_OP_ROUTE_BWD: {
+      if (D.balanced) return 0;
+      const RouteBwdWs r(D);
+      return r.total;
+    }
     default: return 0;
   }
 }
@@ -428,6 +462,7 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
   // read dYp while it is fresh in the memory-side cache, the gate/up weight
   // gradient reads dH right after it is written, and dXp is written last, so
   // that the permute backward that follows reads it back from that cache.
+  if (D.bf16) MOE_TRY(tt.ensure());
   {  // a8: dWd[e] = A_e^T dYp_e
     GemmParams p{};
     p.A = a_save; p.lda = D.I;
@@ -437,6 +472,7 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     const TileCfg t = role_tile(R_DOWN_WGRAD);
     p.m_tiles = (int)ceil_div(D.I, tile_bm(t)); p.n_tiles = (int)ceil_div(D.d, tile_bn(t));
     p.C0 = dw_down; p.ldc = D.d; p.c_estride = (int64_t)D.I * D.d;
+    if (D.bf16) p.kcost = tt.kcost();
     MOE_TRY(launch_gemm(D.bf16, R_DOWN_WGRAD, p, p.m_tiles, s));
   }
   {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
@@ -460,6 +496,7 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.m_tiles = (int)ceil_div(D.d, tile_bm(t)); p.n_tiles = (int)ceil_div(2 * D.I, tile_bn(t));
     p.C0 = dw_gate; p.C1 = dw_up; p.n_split = D.I; p.ldc = D.I;
     p.c_estride = (int64_t)D.d * D.I;
+    if (D.bf16) p.kcost = tt.kcost();
     MOE_TRY(launch_gemm(D.bf16, R_GATEUP_WGRAD, p, p.m_tiles, s));
   }
   {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
@@ -504,20 +541,29 @@ extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, c
                     {"dtopk_w", dtopk_w}, {"dlogits", dlogits}, {"dw_router", dw_router}, {"dx", dx}}));
   MOE_TRY(opt(fn, {{"dbias", dbias}}));
   MOE_TRY(check_ws(fn, D, MOE_OP_ROUTE_BWD, ws, ws_bytes_));
-  bf16_t* dl16 = D.bf16 ? static_cast<bf16_t*>(ws) : nullptr;
-  MOE_TRY(launch_route_bwd_dl(topk_idx, topk_w, dtopk_w, D.T, D.E, D.k, dlogits, dl16, s));
+  const RouteBwdWs rw(D);
+  char* wsb = static_cast<char*>(ws);
+  bf16_t* dl16 = D.bf16 ? reinterpret_cast<bf16_t*>(wsb + rw.dl16) : nullptr;
+  float* db_part = reinterpret_cast<float*>(wsb + rw.dbp);
+  float* dw_part = D.bf16 ? reinterpret_cast<float*>(wsb + rw.dwp) : nullptr;
+  MOE_TRY(launch_route_bwd_dl(topk_idx, topk_w, dtopk_w, D.T, D.E, D.k, dlogits, dl16, db_part, s));
   const void* dl = D.bf16 ? static_cast<const void*>(dl16) : static_cast<const void*>(dlogits);
-  {  // dWr = x^T dL
+  {  // dWr = x^T dL: bf16 layers as fp32 partials over nsplit K (token) ranges
     GemmParams p{};
     p.A = x; p.lda = D.d;
     p.B0 = dl; p.ldb = D.E;
     p.M = D.d; p.N = D.E; p.K = D.T;
-    p.off = nullptr; p.groups = 1;
+    p.off = nullptr;
+    p.groups = D.bf16 ? rw.nsplit : 1;
+    p.k_chunk = D.bf16 ? rw.k_chunk : 0;
     p.m_tiles = (int)ceil_div(D.d, 64); p.n_tiles = (int)ceil_div(D.E, 64);
-    p.C0 = dw_router; p.ldc = D.E;
+    p.C0 = D.bf16 ? static_cast<void*>(dw_part) : dw_router; p.ldc = D.E;
+    p.c_estride = (int64_t)D.d * D.E;
     MOE_TRY(launch_gemm(D.bf16, R_ROUTE_DW, p, p.m_tiles, s));
   }
-  if (dbias) MOE_TRY(launch_col_sum(dlogits, D.T, D.E, dbias, s));
+  // fixed-order sums: the split partials into dWr (bf16), the column sums into db
+  MOE_TRY(launch_route_bwd_reduce(dw_part, D.bf16 ? rw.nsplit : 0, (int64_t)D.d * D.E,
+                                  static_cast<bf16_t*>(dw_router), db_part, rw.nblk, D.E, dbias, s));
   {  // dX += dL Wr^T
     GemmParams p{};
     p.A = dl; p.lda = D.E;

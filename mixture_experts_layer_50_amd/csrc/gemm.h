@@ -45,8 +45,12 @@ struct GemmParams {
   int64_t b_estride;   // element stride between experts' B (G_MROWS)
   int M, N, K;         // G_DENSE: all; G_MROWS: N, K (M = row capacity); G_KROWS: M, N
   int k_split;         // B2_KSPLIT: k < k_split from B0, else B1 at k - k_split
-  const int32_t* off;  // group offsets [groups+1] (G_MROWS, G_KROWS); NULL in G_KROWS = one group [0,K)
+  const int32_t* off;  // group offsets [groups+1] (G_MROWS, G_KROWS); NULL in G_KROWS: see k_chunk
+  int k_chunk;         // G_KROWS without offsets: group g sums K rows [g*k_chunk, (g+1)*k_chunk)
+                       // (a split of K into partial results); 0 = one group [0, K)
   const int32_t* tiles;// G_MROWS tile table: tiles[0] = count, then (expert, first row) pairs
+  const int32_t* kcost;// G_KROWS (optional): prefix sums [groups+1] of the per-expert tile cost
+                       // (K slices + a fixed part), for balancing the persistent kernels
   int groups;          // number of local experts
   int m_tiles, n_tiles;
   void* C0;
@@ -91,8 +95,10 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
 
 // Tile tables for G_MROWS, for 256-row and for 128-row tiles (one launch):
 // tiles[0] = number of M tiles, then for each tile (expert, first row) in
-// expert order.
+// expert order; and the K-cost prefix of the weight gradients (kcost above).
 moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
-                                int32_t* tiles128, hipStream_t s);
+                                int32_t* tiles128, int32_t* kcost, hipStream_t s);
+// Per-tile cost of a weight-gradient tile beyond its K slices (its epilogue).
+constexpr int KCOST_FIXED = 2;
 
 }  // namespace moe

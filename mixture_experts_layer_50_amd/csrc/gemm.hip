@@ -273,10 +273,48 @@ __device__ __forceinline__ TileDesc tile_desc(const GemmParams& p, int L) {
     t.m_lo = mt * BM;
     t.m_hi = min(t.m_lo + BM, p.M);
     if (GMD == G_KROWS && p.off) { t.k_lo = ld_table(p.off, t.e); t.k_hi = ld_table(p.off, t.e + 1); }
-    else { t.k_lo = 0; t.k_hi = p.K; }
+    else if (GMD == G_KROWS && p.k_chunk > 0) {
+      t.k_lo = min(p.K, t.e * p.k_chunk);
+      t.k_hi = min(p.K, t.k_lo + p.k_chunk);
+    } else { t.k_lo = 0; t.k_hi = p.K; }
   }
   t.n0 = nt * ((B2 == B2_NHALF) ? BN / 2 : BN);
   return t;
+}
+
+// The contiguous range [x_lo, x_lo + x_n) of tile ids a persistent kernel's
+// XCD takes.  Tiles of the row-grouped and dense GEMMs cost the same, so the
+// XCDs get equal counts.  Weight-gradient tiles cost their expert's K slices
+// (plus a fixed part for the epilogue), which differ widely under natural
+// routing: there the split is by cost, so that no XCD is left with the
+// largest experts.
+template <int GMD>
+__device__ __forceinline__ void xcd_tile_range(const GemmParams& p, int count, int xcd, int& x_lo,
+                                               int& x_n) {
+  if (GMD != G_KROWS || p.kcost == nullptr) {
+    const int per = count / NXCD, rem = count % NXCD;
+    x_lo = xcd * per + min(xcd, rem);
+    x_n = per + (xcd < rem ? 1 : 0);
+    return;
+  }
+  const int per_group = count / p.groups;  // tiles per expert, all of the same cost
+  const int64_t total = (int64_t)ld_table(p.kcost, p.groups) * per_group;
+  // first tile whose cost prefix reaches c
+  auto first_at = [&](int64_t c) -> int {
+    if (c <= 0) return 0;
+    if (c >= total) return count;
+    int lo = 0, hi = p.groups - 1;  // last expert whose tiles start below c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)ld_table(p.kcost, mid) * per_group < c) lo = mid;
+      else hi = mid - 1;
+    }
+    const int64_t before = (int64_t)ld_table(p.kcost, lo) * per_group;
+    const int tc = ld_table(p.kcost, lo + 1) - ld_table(p.kcost, lo);
+    return lo * per_group + (int)min<int64_t>(per_group, (c - before + tc - 1) / tc);
+  };
+  x_lo = first_at(total * xcd / NXCD);
+  x_n = first_at(total * (xcd + 1) / NXCD) - x_lo;
 }
 
 #ifndef MOE_WEIGHT_CPOL
@@ -318,14 +356,15 @@ __device__ __forceinline__ void init_loaders(const GemmParams& p, const TileDesc
 // and the last FN/2 the matching up columns.  The operand fragments of step
 // ks+1 are read from LDS before the MFMAs of step ks are issued, so the LDS
 // latency is hidden behind the matrix cores even with one wave per SIMD.
-template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, int FM, int FN>
+template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, bool SKIP, int FM, int FN>
 __device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfg)[FN], const bf16_t* as,
-                                           int ks, int wm, int wn, int lane) {
+                                           int ks, int wm, int wn, int lane, int rows) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   const bf16_t* bs = as + BM * BK;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int base = wm * WTM + i * 32;
+    if (SKIP && base >= rows) continue;  // a block of padding rows: no reads, no MFMAs
     if constexpr (AM == A_KC) af[i] = frag_kc(as, base, ks, lane);
     else af[i] = frag_kn<BM>(as, base, ks, lane);
   }
@@ -341,36 +380,41 @@ __device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfg)[FN], 
   }
 }
 
+// `rows`: the tile's valid rows.  With PIPE, 32-row blocks at or past it are
+// skipped (the other form computes padding rows too: testing for them there
+// cost more registers than it saved).
 template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, bool PIPE = false, int FM,
           int FN>
 __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* as, int wm, int wn,
-                                          int lane) {
+                                          int lane, int rows) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static_assert(FM == WTM / 32 && FN == WTN / 32, "accumulator blocks match the wave tile");
   constexpr int KS = BK / 16;
   if constexpr (PIPE) {
     bf16x8 af[2][FM], bfg[2][FN];
-    load_frags<BM, BN, WGM, WGN, AM, BMD, B2>(af[0], bfg[0], as, 0, wm, wn, lane);
+    load_frags<BM, BN, WGM, WGN, AM, BMD, B2, true>(af[0], bfg[0], as, 0, wm, wn, lane, rows);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS)
-        load_frags<BM, BN, WGM, WGN, AM, BMD, B2>(af[(ks + 1) & 1], bfg[(ks + 1) & 1], as, ks + 1,
-                                                  wm, wn, lane);
+        load_frags<BM, BN, WGM, WGN, AM, BMD, B2, true>(af[(ks + 1) & 1], bfg[(ks + 1) & 1], as,
+                                                        ks + 1, wm, wn, lane, rows);
       // keep the next step's reads above this step's MFMAs (the scheduler
       // would otherwise move each read down to its first use)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        if (wm * WTM + i * 32 >= rows) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[ks & 1][j], af[ks & 1][i],
                                                              acc[i][j], 0, 0, 0);
+      }
     }
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 af[FM], bfg[FN];
-      load_frags<BM, BN, WGM, WGN, AM, BMD, B2>(af, bfg, as, ks, wm, wn, lane);
+      load_frags<BM, BN, WGM, WGN, AM, BMD, B2, false>(af, bfg, as, ks, wm, wn, lane, BM);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -438,6 +482,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
             *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf2(w0, w1), pack_bf2(w2, w3));
           } else if constexpr (EPI == EPI_F32_BIAS) {
             float* C = static_cast<float*>(p.C0) + (int64_t)m * p.ldc + n;
+            if (GMD == G_KROWS) C += (int64_t)e * p.c_estride;
             if (p.bias) {
 #pragma unroll
               for (int s = 0; s < 4; ++s) v[s] += p.bias[n + s];
@@ -807,7 +852,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
     // keep the refill loads at the top of the step: the scheduler would
     // otherwise sink them below the MFMAs and expose their latency
     __builtin_amdgcn_sched_barrier(0);
-    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn, lane);
+    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn, lane,
+                                             m_hi - m_lo);
     __builtin_amdgcn_sched_barrier(0);
     if (do_store) {
       bf16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BK;
@@ -888,9 +934,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(Ge
   // ---- this workgroup's tiles: x_lo + pos for pos = slot, slot + S, ... < x_n
   const int count = tile_count<GMD>(p);
   const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD, S = gridDim.x / NXCD;
-  const int per = count / NXCD, rem = count % NXCD;
-  const int x_lo = xcd * per + min(xcd, rem);
-  const int x_n = per + (xcd < rem ? 1 : 0);
+  int x_lo, x_n;
+  xcd_tile_range<GMD>(p, count, xcd, x_lo, x_n);
   if (slot >= x_n) return;
 
   typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LA LA;
@@ -996,7 +1041,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(Ge
     issue(Uc, false);
     // keep the loads at the top of the step (the scheduler would sink them)
     __builtin_amdgcn_sched_barrier(0);
-    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + U * BUF, wm, wn, lane);
+    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + U * BUF, wm, wn, lane, ct.m_hi - ct.m_lo);
     __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < issued) {
       LA::store(da[1 - U], smem + (1 - U) * BUF, tid);
@@ -1050,9 +1095,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
 
   const int count = tile_count<GMD>(p);
   const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD, S = gridDim.x / NXCD;
-  const int per = count / NXCD, rem = count % NXCD;
-  const int x_lo = xcd * per + min(xcd, rem);
-  const int x_n = per + (xcd < rem ? 1 : 0);
+  int x_lo, x_n;
+  xcd_tile_range<GMD>(p, count, xcd, x_lo, x_n);
   if (slot >= x_n) return;
   auto slices = [](const TileDesc& t) { return (t.k_hi - t.k_lo + BK - 1) / BK; };
 
@@ -1228,7 +1272,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     int g = 0;
     auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
       constexpr int U = decltype(Uc)::value;
-      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2, true>(acc, smem + U * BUF, wm, wn, lane);
+      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2, true>(acc, smem + U * BUF, wm, wn, lane,
+                                                     ct.m_hi - ct.m_lo);
       __syncthreads();
       ++g;
       return advance();
@@ -1266,6 +1311,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     if (GMD == G_KROWS) {
       e = blockIdx.z;
       if (p.off) { k_lo = p.off[e]; k_hi = p.off[e + 1]; }
+      else if (p.k_chunk > 0) { k_lo = min(p.K, e * p.k_chunk); k_hi = min(p.K, k_lo + p.k_chunk); }
     }
   }
   auto a_at = [&](int k) -> float {
@@ -1295,7 +1341,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   } else if constexpr (EPI == EPI_ACCUM) {
     static_cast<float*>(p.C0)[(int64_t)m * p.ldc + n] += acc;
   } else if constexpr (EPI == EPI_F32_BIAS) {
-    static_cast<float*>(p.C0)[(int64_t)m * p.ldc + n] = acc + (p.bias ? p.bias[n] : 0.f);
+    static_cast<float*>(p.C0)[(GMD == G_KROWS ? (int64_t)e * p.c_estride : 0) + (int64_t)m * p.ldc + n] =
+        acc + (p.bias ? p.bias[n] : 0.f);
   } else if constexpr (EPI == EPI_SWIGLU) {
     const int64_t I = p.I;
     float* H = static_cast<float*>(p.C0);
@@ -1318,7 +1365,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // Workgroup 0 builds the table for 256-row tiles, workgroup 1 the one for
 // 128-row tiles.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups,
-                                                          int32_t* tiles256, int32_t* tiles128) {
+                                                          int32_t* tiles256, int32_t* tiles128,
+                                                          int32_t* kcost) {
+  const bool cost = blockIdx.x == 2;  // workgroup 2: the weight-gradient cost prefix
+  if (cost && kcost == nullptr) return;
   const int bm = blockIdx.x == 0 ? 256 : 128;
   int32_t* tiles = blockIdx.x == 0 ? tiles256 : tiles128;
   __shared__ int32_t scan[1024];
@@ -1330,7 +1380,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
     int cnt = 0, o = 0;
     if (e < groups) {
       o = off[e];
-      cnt = (off[e + 1] - o + bm - 1) / bm;
+      cnt = cost ? (off[e + 1] - o + BK - 1) / BK + KCOST_FIXED : (off[e + 1] - o + bm - 1) / bm;
     }
     scan[threadIdx.x] = cnt;
     __syncthreads();
@@ -1341,21 +1391,28 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
       __syncthreads();
     }
     int first = carry + scan[threadIdx.x] - cnt;
-    for (int t = 0; t < cnt; ++t) {
-      tiles[1 + 2 * (first + t)] = e;
-      tiles[2 + 2 * (first + t)] = o + t * bm;
+    if (cost) {
+      if (e < groups) kcost[e + 1] = first + cnt;
+    } else {
+      for (int t = 0; t < cnt; ++t) {
+        tiles[1 + 2 * (first + t)] = e;
+        tiles[2 + 2 * (first + t)] = o + t * bm;
+      }
     }
     __syncthreads();
     if (threadIdx.x == 1023) carry += scan[1023];
     __syncthreads();
   }
-  if (threadIdx.x == 0) tiles[0] = carry;
+  if (threadIdx.x == 0) {
+    if (cost) kcost[0] = 0;
+    else tiles[0] = carry;
+  }
 }
 
 moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
-                                int32_t* tiles128, hipStream_t s) {
+                                int32_t* tiles128, int32_t* kcost, hipStream_t s) {
   ProfScope prof("tile_table", s);
-  tile_table_kernel<<<2, 1024, 0, s>>>(off, groups, tiles256, tiles128);
+  tile_table_kernel<<<3, 1024, 0, s>>>(off, groups, tiles256, tiles128, kcost);
   return check_launch("tile_table_kernel");
 }
 
@@ -1404,7 +1461,7 @@ int tile_bn(TileCfg cfg) {
     EPI_STORE)                                                                                     \
   X(R_DOWN_WGRAD, "ffn_down_wgrad", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)        \
   X(R_GATEUP_WGRAD, "ffn_gateup_wgrad", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)    \
-  X(R_ROUTE_DW, "route_bwd_dw", TILE_64x64, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)               \
+  X(R_ROUTE_DW, "route_bwd_dw", TILE_64x64, A_MC, B_NC, G_KROWS, B2_NONE, EPI_F32_BIAS)            \
   X(R_ROUTE_DX, "route_bwd_dx", TILE_64x64, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
 
 TileCfg role_tile(GemmRole role) {

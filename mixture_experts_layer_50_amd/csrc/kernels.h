@@ -13,9 +13,13 @@ namespace moe {
 moe_status_t launch_balanced_gate(int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
 moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                  hipStream_t s);
+// Tokens per workgroup of the router backward (one bias-gradient partial each).
+constexpr int ROUTE_BWD_TOKENS = 32;
 moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
-                                 int k, float* dl, bf16_t* dl_bf16, hipStream_t s);
-moe_status_t launch_col_sum(const float* dl, int T, int E, float* db, hipStream_t s);
+                                 int k, float* dl, bf16_t* dl_bf16, float* db_part, hipStream_t s);
+moe_status_t launch_route_bwd_reduce(const float* dw_part, int nsplit, int64_t n_dw, bf16_t* dw,
+                                     const float* db_part, int nblk, int E, float* db,
+                                     hipStream_t s);
 // Zeroes up to three buffers (null ones are skipped) in one launch.
 moe_status_t launch_fill_zero(void* p0, int64_t bytes0, void* p1, int64_t bytes1, void* p2,
                               int64_t bytes2, hipStream_t s);

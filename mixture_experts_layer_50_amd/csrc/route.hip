@@ -97,70 +97,108 @@ moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32
 
 // ---------------------------------------------------------------- backward
 // dL[t, idx[t,j]] = g_j (dg_j - sum_i g_i dg_i); all other logits get 0.
-// One wavefront per token; lane l writes experts l + 64 v.  The optional bf16
-// copy feeds the bf16 router-gradient GEMMs.
+// One workgroup per 64 tokens, one wavefront per 16 of them in token order;
+// lane l owns experts l + 64 q.  The optional bf16 copy feeds the bf16
+// router-gradient GEMMs.  Each workgroup also writes its column sums of dL
+// (tokens in order, then its four waves in order) to db_part[block][E].
+template <int VPL>
 __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, const float* g,
                                                            const float* dg, int T, int E, int k,
-                                                           float* dl, bf16_t* dl_bf16) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float gj = 0.f, dgj = 0.f;
-  int ij = -1;
-  if (lane < k) {
-    gj = g[(int64_t)t * k + lane];
-    dgj = dg[(int64_t)t * k + lane];
-    ij = idx[(int64_t)t * k + lane];
-  }
-  float s = gj * dgj;
+                                                           float* dl, bf16_t* dl_bf16,
+                                                           float* db_part) {
+  __shared__ float part[4][64 * VPL];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float col[VPL];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  const float val = gj * (dgj - s);
-  for (int base = 0; base < E; base += 64) {
-    int e = base + lane;
-    float out = 0.f;
-    for (int j = 0; j < k; ++j) {
-      int ej = __shfl(ij, j, 64);
-      float vj = __shfl(val, j, 64);
-      if (ej == e) out = vj;
+  for (int q = 0; q < VPL; ++q) col[q] = 0.f;
+  for (int i = 0; i < ROUTE_BWD_TOKENS / 4; ++i) {
+    const int t = blockIdx.x * ROUTE_BWD_TOKENS + wave * (ROUTE_BWD_TOKENS / 4) + i;
+    if (t >= T) break;  // uniform per wave
+    float gj = 0.f, dgj = 0.f;
+    int ij = -1;
+    if (lane < k) {
+      gj = g[(int64_t)t * k + lane];
+      dgj = dg[(int64_t)t * k + lane];
+      ij = idx[(int64_t)t * k + lane];
     }
-    if (e < E) {
-      dl[(int64_t)t * E + e] = out;
-      if (dl_bf16) dl_bf16[(int64_t)t * E + e] = f2bf(out);
+    float sum = gj * dgj;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const float val = gj * (dgj - sum);
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      const int e = q * 64 + lane;
+      float out = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int ej = __shfl(ij, j, 64);
+        const float vj = __shfl(val, j, 64);
+        if (ej == e) out = vj;
+      }
+      if (e < E) {
+        dl[(int64_t)t * E + e] = out;
+        if (dl_bf16) dl_bf16[(int64_t)t * E + e] = f2bf(out);
+        col[q] += out;
+      }
     }
   }
-}
-
-// db[e] = sum_t dL[t,e]: 4 fixed row strides per column, combined in order.
-__global__ __launch_bounds__(256) void col_sum_kernel(const float* dl, int T, int E, float* db) {
-  __shared__ float part[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int s = threadIdx.x >> 6;
-  float acc = 0.f;
-  if (c < E)
-    for (int t = s; t < T; t += 4) acc += dl[(int64_t)t * E + c];
-  part[s][threadIdx.x & 63] = acc;
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) part[wave][q * 64 + lane] = col[q];
   __syncthreads();
-  if (s == 0 && c < E) {
-    float v = part[0][threadIdx.x];
-    v += part[1][threadIdx.x];
-    v += part[2][threadIdx.x];
-    v += part[3][threadIdx.x];
-    db[c] = v;
-  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    db_part[(int64_t)blockIdx.x * E + e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
 }
 
 moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
-                                 int k, float* dl, bf16_t* dl_bf16, hipStream_t s) {
+                                 int k, float* dl, bf16_t* dl_bf16, float* db_part, hipStream_t s) {
   ProfScope prof("route_bwd_dlogits", s);
-  route_bwd_dl_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16);
+  const unsigned grid = (unsigned)ceil_div(T, ROUTE_BWD_TOKENS);
+  if (E <= 64) route_bwd_dl_kernel<1><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
+  else if (E <= 128) route_bwd_dl_kernel<2><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
+  else if (E <= 256) route_bwd_dl_kernel<4><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
+  else route_bwd_dl_kernel<8><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
   return check_launch("route_bwd_dl_kernel");
 }
 
-moe_status_t launch_col_sum(const float* dl, int T, int E, float* db, hipStream_t s) {
-  ProfScope prof("route_bwd_dbias", s);
-  col_sum_kernel<<<(unsigned)ceil_div(E, 64), 256, 0, s>>>(dl, T, E, db);
-  return check_launch("col_sum_kernel");
+// Final sums of the router backward, each in a fixed order:
+// dw[i] = sum_s dw_part[s][i] (split-K partials of x^T dL, when nsplit > 0),
+// db[e] = sum_b db_part[b][e] (per-workgroup column sums of dL, when db).
+__global__ __launch_bounds__(256) void route_bwd_reduce_kernel(const float* dw_part, int nsplit,
+                                                               int64_t n_dw, bf16_t* dw,
+                                                               const float* db_part, int nblk,
+                                                               int E, float* db) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nw = nsplit > 0 ? n_dw : 0;  // dw outputs, then the E bias outputs
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nw + (db ? E : 0);
+       i += stride) {
+    if (i < nw) {
+      float v = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) v += dw_part[(int64_t)sp * n_dw + i];
+      dw[i] = f2bf(v);
+    } else {
+      const int e = (int)(i - nw);
+      constexpr int U = 8;  // partial rows in flight
+      float v = 0.f;
+      for (int b0 = 0; b0 < nblk; b0 += U) {
+        float c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) c[u] = b0 + u < nblk ? db_part[(int64_t)(b0 + u) * E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v += c[u];
+      }
+      db[e] = v;
+    }
+  }
+}
+
+moe_status_t launch_route_bwd_reduce(const float* dw_part, int nsplit, int64_t n_dw, bf16_t* dw,
+                                     const float* db_part, int nblk, int E, float* db,
+                                     hipStream_t s) {
+  const int64_t n = (nsplit > 0 ? n_dw : 0) + (db ? E : 0);
+  if (n == 0) return MOE_OK;
+  ProfScope prof("route_bwd_reduce", s);
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n, 256), 2048);
+  route_bwd_reduce_kernel<<<grid, 256, 0, s>>>(dw_part, nsplit, n_dw, dw, db_part, nblk, E, db);
+  return check_launch("route_bwd_reduce_kernel");
 }
 
 // ---------------------------------------------------------------- fill

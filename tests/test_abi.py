@@ -104,12 +104,13 @@ def test_workspace_sizes_and_short_workspace(lib):
     assert B.workspace_size(s, "permute") == 16 * 128 * 4          # 16 blocks of 256 tokens
     def table(bm):  # one tile table per M-tile height, 256-byte aligned
         return -(-(1 + 2 * (R // bm + 128)) * 4 // 256) * 256
-    tiles = table(256) + table(128)
+    tiles = table(256) + table(128) + 768   # + weight-gradient cost prefix [E_loc + 1]
     assert B.workspace_size(s, "ffn_fwd") == tiles
     assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + tiles
     assert B.workspace_size(s, "route_bwd") == 0                    # balanced gate: no dL copy
     n = B.workspace_size(shape(T=4096, d=2048, E=128, k=8, I=768), "route_bwd")
-    assert n == 4096 * 128 * 2
+    # bf16 copy of dL, column sums per 32 tokens, 8 split-K partials of x^T dL (fp32)
+    assert n == 4096 * 128 * 2 + 128 * 128 * 4 + 8 * 2048 * 128 * 4
     with pytest.raises(B.MoEError) as ei:
         B.workspace_size(s, 99)
     assert ei.value.status_name == "MOE_ERR_ARG"
