@@ -140,6 +140,109 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int) -> dict:
     return out
 
 
+def timed_steps(step, steps: int, warmup: int):
+    """Median / min / p90 / mean of per-step times (HIP events around each step)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return {"median": round(t[len(t) // 2], 4), "min": round(t[0], 4),
+            "p90": round(t[min(len(t) - 1, int(0.9 * len(t)))], 4),
+            "mean": round(sum(t) / len(t), 4)}
+
+
+def kernel_averages(step, B, n: int):
+    """Per-kernel averages (us) over n instrumented steps."""
+    import torch
+    B.prof_select(None)
+    B.prof_enable(True)
+    B.prof_reset()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    res = {}
+    for name in B.prof_names():
+        tot, cnt = B.prof_read(name)
+        res[name] = round(1000.0 * tot / max(cnt, 1), 2)
+    B.prof_enable(False)
+    return res
+
+
+def secondary_workloads(B, dev, w_main):
+    """fwd+bwd of the natural softmax top-k router at the Qwen3 shape (same
+    tokens and expert weights as the main workload, router weights and bias
+    from the natural workload's recipe), and of one rank's share of the
+    DeepSeek-V3 shape (expert weights drawn on the GPU with the same
+    distribution as the recipe)."""
+    import numpy as np
+    import torch
+    import moe_inputs as MI
+    from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward
+
+    out = {}
+    # -- natural router, Qwen3 shape
+    wn = MI.WORKLOADS["qwen3_natural_fwd_T4096_d2048_E128_k8_I768"]
+    r = MI.generate(wn, parts=["Wr", "b"])
+    Wr = torch.from_numpy(r["Wr"]).to(torch.bfloat16).cuda()
+    bias = torch.from_numpy(r["b"]).cuda()
+    shape = B.MoEShape.make(wn.T, wn.d, wn.E, wn.k, wn.I, dtype="bf16", gate="softmax_topk")
+    buf = LayerBuffers(shape, training=True)
+
+    def step_nat():
+        forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
+        backward(shape, buf, dev["dY"], dev["x"], Wr, dev["Wg"], dev["Wu"], dev["Wd"])
+
+    st = timed_steps(step_nat, 10, 3)
+    counts = np.diff(buf["offsets"].cpu().numpy())
+    out["natural_router_fwdbwd"] = {
+        "workload": "qwen3_natural_fwdbwd_T4096_d2048_E128_k8_I768 (router bias N(0,1.5))",
+        "tokens_per_s": round(wn.T / (st["median"] / 1e3), 1), "step_ms": st,
+        "max_group_rows": int(counts.max()), "empty_experts": int((counts == 0).sum()),
+        "kernels_us_avg": kernel_averages(step_nat, B, 3)}
+    del buf
+    # -- one rank of eight at the DeepSeek-V3 shape, balanced gate
+    wd = MI.WORKLOADS["dsv3_ep8_rank_fwdbwd_T32768_d7168_E256_loc32_k8_I2048"]
+    g = torch.Generator(device="cuda").manual_seed(wd.seed)
+    El = wd.E_loc
+
+    def rnd(*sh, sigma):
+        return (torch.randn(*sh, device="cuda", generator=g) * sigma).to(torch.bfloat16)
+
+    d5 = {"x": rnd(wd.T, wd.d, sigma=wd.x_sigma), "Wg": rnd(El, wd.d, wd.I, sigma=wd.w_sigma),
+          "Wu": rnd(El, wd.d, wd.I, sigma=wd.w_sigma), "Wd": rnd(El, wd.I, wd.d, sigma=wd.w_sigma),
+          "dY": rnd(wd.T, wd.d, sigma=wd.dy_sigma)}
+    shape = B.MoEShape.make(wd.T, wd.d, wd.E, wd.k, wd.I, dtype="bf16", gate="balanced",
+                            e_lo=wd.e_lo, e_hi=wd.e_end)
+    buf = LayerBuffers(shape, training=True)
+
+    def step_ds():
+        forward(shape, buf, d5["x"], None, None, d5["Wg"], d5["Wu"], d5["Wd"])
+        backward(shape, buf, d5["dY"], d5["x"], None, d5["Wg"], d5["Wu"], d5["Wd"])
+
+    st = timed_steps(step_ds, 5, 2)
+    ker = kernel_averages(step_ds, B, 2)
+    R = int(buf["offsets"][-1].item())
+    gem_us = sum(ker[n] for n in GEMMS if n in ker)
+    gem_fl = sum(GEMMS[n][0](R, wd.d, wd.I, El) for n in GEMMS if n in ker)
+    out["dsv3_rank_share_fwdbwd"] = {
+        "workload": wd.name, "routed_rows": R,
+        "tokens_per_s": round(wd.T / (st["median"] / 1e3), 1), "step_ms": st,
+        "grouped_gemm_tflops": round(gem_fl / gem_us / 1e6, 1),
+        "grouped_gemm_mfma_frac": round(gem_fl / gem_us / 1e6 / PEAK_BF16_TFLOPS, 4),
+        "kernels_us_avg": ker}
+    del buf, d5
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +250,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the natural-router and DeepSeek-V3 rank-share timings")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="also run a fill and a sum of this size (HBM counter calibration)")
@@ -303,6 +408,10 @@ def main():
         "wall_s_timed": round(wall, 3),
         "kernels_us_avg": {k: round(v["us_avg"], 2) for k, v in kernels.items()},
     }
+    out["step_ms_stats"] = timed_steps(step, max(5, args.steps), 2)
+    if not args.no_secondary and w.name == WORKLOAD:
+        log("[bench] natural-router and DeepSeek-V3 rank-share timings")
+        out["secondary"] = secondary_workloads(B, dev, w)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
