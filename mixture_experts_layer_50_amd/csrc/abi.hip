@@ -481,7 +481,7 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
     p.N = D.I; p.K = D.d;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_DOWN_DGRAD)));
+    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_DOWN_DGRAD, D.I)));
     p.C0 = dH; p.aux = h_save; p.I = D.I;
     if (D.bf16) MOE_TRY(tt.get(R_DOWN_DGRAD, &p.tiles));
     MOE_TRY(launch_gemm(D.bf16, R_DOWN_DGRAD, p, rows_or_tiles(R_DOWN_DGRAD), s));

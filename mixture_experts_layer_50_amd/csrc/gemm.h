@@ -81,8 +81,9 @@ enum GemmRole {
   R_ROUTE_DX = 8        // dX += dL Wr^T
 };
 
-// Tile shape each role runs with (bf16).
-TileCfg role_tile(GemmRole role);
+// Tile shape each role runs with (bf16), for a GEMM with n output columns
+// (n = 0: the role's usual shape).
+TileCfg role_tile(GemmRole role, int n = 0);
 int tile_bm(TileCfg cfg);
 int tile_bn(TileCfg cfg);
 const char* role_name(GemmRole role);

@@ -619,11 +619,12 @@ __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x1
 }
 
 // Staged activation epilogues.  The tile passes through LDS in bands of one
-// wave row (WTM rows); each band array is [WTM][128] bf16 with 16-byte chunk
+// wave row (WTM rows); each band array is [WTM][W] bf16 (W = 128 or 256) with 16-byte chunk
 // c of row r at c ^ (r & 15), so that memory is read and written in whole
 // 16-byte chunks of consecutive columns (full cache lines per row) instead
 // of 8-byte pieces spread over 32 rows.
-__device__ __forceinline__ int band_off(int r, int n) { return r * 128 + (((n >> 3) ^ (r & 15)) << 3) + (n & 7); }
+template <int W = 128>
+__device__ __forceinline__ int band_off(int r, int n) { return r * W + (((n >> 3) ^ (r & 15)) << 3) + (n & 7); }
 
 // SwiGLU: gate columns n0 .. n0+127 and the matching up columns of the tile
 // give H = [Hg | Hu] (optional) and A = silu(Hg) * Hu.
@@ -690,7 +691,7 @@ __device__ __forceinline__ void epilogue_swiglu_staged(const GemmParams& p, f32x
   }
 }
 
-// dSwiGLU: acc = dA for columns n0 .. n0+127; reads H = [Hg | Hu] of those
+// dSwiGLU: acc = dA for columns n0 .. n0+BN-1; reads H = [Hg | Hu] of those
 // columns and writes dH = [dHg | dHu].
 template <int BM, int BN, int WGM, int FM, int FN, int WTM, int WTN, int NT>
 __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32x16 (&acc)[FM][FN],
@@ -729,8 +730,8 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
         const int q = i * NT + tid;
         if (WTM * CPR % NT == 0 || q < WTM * CPR) {
           const int r = q / CPR, c = q % CPR;
-          *reinterpret_cast<uint4*>(Gs + band_off(r, c * 8)) = vg[i];
-          *reinterpret_cast<uint4*>(Us + band_off(r, c * 8)) = vu[i];
+          *reinterpret_cast<uint4*>(Gs + band_off<BN>(r, c * 8)) = vg[i];
+          *reinterpret_cast<uint4*>(Us + band_off<BN>(r, c * 8)) = vu[i];
         }
       }
     }
@@ -745,7 +746,7 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
-            const int o = band_off(r, n);
+            const int o = band_off<BN>(r, n);
             const uint2 hg = *reinterpret_cast<const uint2*>(Gs + o);
             const uint2 hu = *reinterpret_cast<const uint2*>(Us + o);
             const float g[4] = {bf2f((bf16_t)(hg.x & 0xffff)), bf2f((bf16_t)(hg.x >> 16)),
@@ -775,7 +776,7 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
       const int r = q / CPR, c = q % CPR;
       const bool ok = (WTM * CPR % NT == 0 || q < WTM * CPR) && mb + r < m_hi && n0 + c * 8 < I;
       const int off = ok ? (int)(((int64_t)r * 2 * I + c * 8) * 2) : OOB;
-      const int o = band_off(r, c * 8);
+      const int o = band_off<BN>(r, c * 8);
       __builtin_amdgcn_raw_buffer_store_b128(
           __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Gs + o)), rsg, off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(
@@ -890,7 +891,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
                      3 * WTM * (BN / 2) <= LDS_ELEMS)
     epilogue_swiglu_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT>(p, acc, smem, m_lo, m_hi, n0, wm, wn,
                                                             lane, tid);
-  else if constexpr (EPI == EPI_DSWIGLU && MOE_STAGED_STORE && BN / 8 == 16 &&
+  else if constexpr (EPI == EPI_DSWIGLU && MOE_STAGED_STORE && (BN == 128 || BN == 256) &&
                      2 * WTM * BN <= LDS_ELEMS)
     epilogue_dswiglu_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT>(p, acc, smem, m_lo, m_hi, n0, wm, wn,
                                                              lane, tid);
@@ -1464,7 +1465,23 @@ int tile_bn(TileCfg cfg) {
   X(R_ROUTE_DW, "route_bwd_dw", TILE_64x64, A_MC, B_NC, G_KROWS, B2_NONE, EPI_F32_BIAS)            \
   X(R_ROUTE_DX, "route_bwd_dx", TILE_64x64, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
 
-TileCfg role_tile(GemmRole role) {
+// A role may take a second tile shape when its N (output columns) is large:
+// role, tile, smallest N (build-time tunable).
+#define MOE_GEMM_ALT_TILES(X) X(R_DOWN_DGRAD, TILE_256x256, 1536)
+
+constexpr int role_alt_tile(GemmRole role) {
+#define X(r, t, nmin) \
+  if (role == r) return t;
+  MOE_GEMM_ALT_TILES(X)
+#undef X
+  return -1;
+}
+
+TileCfg role_tile(GemmRole role, int n) {
+#define X(r, t, nmin) \
+  if (role == r && n >= nmin) return t;
+  MOE_GEMM_ALT_TILES(X)
+#undef X
   switch (role) {
 #define X(r, n, t, a, b, g, t2, e) \
   case r: return t;
@@ -1557,6 +1574,18 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   }
 }
 
+// The role's usual tile, or its alternate tile (ALT >= 0) when `alt`.
+template <int ALT, int CFG, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
+static void launch_bf16_role(const GemmParams& p, int grid, hipStream_t s, bool alt) {
+  if constexpr (ALT >= 0) {
+    if (alt) {
+      launch_bf16<ALT, AM, BMD, GMD, B2, EPI, ROLE>(p, grid, s);
+      return;
+    }
+  }
+  launch_bf16<CFG, AM, BMD, GMD, B2, EPI, ROLE>(p, grid, s);
+}
+
 template <int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 static void launch_f32(const GemmParams& p, int max_rows, hipStream_t s) {
   int ncols = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU) ? p.I : p.N;
@@ -1594,7 +1623,8 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
       set_error("GEMM %s: grid too large", name);                                         \
       return MOE_ERR_UNSUPPORTED;                                                         \
     }                                                                                     \
-    launch_bf16<t, a, b, g, t2, e, r>(p, (int)grid, s);                                   \
+    launch_bf16_role<role_alt_tile(r), t, a, b, g, t2, e, r>(                               \
+        p, (int)grid, s, role_tile(r, p.N) != t);                                          \
     break;                                                                                \
   }
     MOE_GEMM_ROLES(X)
