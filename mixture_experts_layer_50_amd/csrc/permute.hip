@@ -67,38 +67,65 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_count_kernel(const int32_t* 
 }
 
 // One workgroup; E_loc <= 1024.  counts[b][e] becomes the first sorted
-// position of block b's rows of expert e.
+// position of block b's rows of expert e.  TPE = 1024 / E_loc (rounded down
+// to a power of two) threads share an expert, each summing a contiguous run
+// of blocks; the runs and then the experts are scanned in order.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* counts, int nb, int E_loc, int R_cap,
                                                          int32_t* offsets) {
+  __shared__ int32_t part[1024];
   __shared__ int32_t scan[1024];
-  const int e = threadIdx.x;
+  int tpe = 1;
+  while (tpe * 2 * E_loc <= 1024) tpe *= 2;
+  const int e = threadIdx.x / tpe, c = threadIdx.x % tpe;
+  const int run = (nb + tpe - 1) / tpe;
+  const int b_lo = min(nb, c * run), b_hi = min(nb, b_lo + run);
   constexpr int U = 8;  // block counts in flight per thread
-  int total = 0;
+  int sum = 0;
   if (e < E_loc) {
-    for (int b0 = 0; b0 < nb; b0 += U) {
-      int c[U];
+    for (int b0 = b_lo; b0 < b_hi; b0 += U) {
+      int v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) c[u] = b0 + u < nb ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
+      for (int u = 0; u < U; ++u) v[u] = b0 + u < b_hi ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (b0 + u < nb) counts[(int64_t)(b0 + u) * E_loc + e] = total;
-        total += c[u];
-      }
+      for (int u = 0; u < U; ++u) sum += v[u];
     }
   }
-  scan[e] = total;
+  part[threadIdx.x] = sum;
   __syncthreads();
-  for (int s = 1; s < 1024; s <<= 1) {
-    int v = e >= s ? scan[e - s] : 0;
+  int before = 0, total = 0;  // this run's start within its expert; the expert's total
+  if (e < E_loc) {
+    for (int cc = 0; cc < tpe; ++cc) {
+      const int v = part[e * tpe + cc];
+      if (cc < c) before += v;
+      total += v;
+    }
+  }
+  scan[threadIdx.x] = (e < E_loc && c == 0) ? total : 0;  // one entry per expert, at its first thread
+  __syncthreads();
+  for (int s = 1; s < 1024; s <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = threadIdx.x >= s ? scan[threadIdx.x - s] : 0;
     __syncthreads();
-    scan[e] += v;
+    scan[threadIdx.x] += v;
     __syncthreads();
   }
   if (e < E_loc) {
-    int o = scan[e] - total;  // exclusive
-    for (int b = 0; b < nb; ++b) counts[(int64_t)b * E_loc + e] += o;
-    offsets[e] = min(o, R_cap);
-    if (e == E_loc - 1) offsets[E_loc] = min(o + total, R_cap);
+    const int o = scan[e * tpe] - total;  // exclusive prefix over experts
+    int pos = o + before;
+    for (int b0 = b_lo; b0 < b_hi; b0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = b0 + u < b_hi ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (b0 + u < b_hi) {
+          counts[(int64_t)(b0 + u) * E_loc + e] = pos;
+          pos += v[u];
+        }
+    }
+    if (c == 0) {
+      offsets[e] = min(o, R_cap);
+      if (e == E_loc - 1) offsets[E_loc] = min(o + total, R_cap);
+    }
   }
 }
 
