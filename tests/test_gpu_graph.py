@@ -1,0 +1,58 @@
+"""The layer's calls can be captured in a HIP graph: they allocate nothing,
+issue no memset and never synchronise with the host.  Replays of the graph,
+with eager work between them, must give the eager results bit for bit (every
+sum in the library runs in a fixed order)."""
+import sys
+
+import pytest
+import torch
+
+import moe_inputs as MI
+import gpu_util as U
+from mixture_experts_layer_50_amd import binding as B
+from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ["logits", "topk_idx", "topk_w", "y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w",
+        "dw_router", "dbias"]
+
+
+@pytest.mark.parametrize("gate", ["softmax_topk", "balanced"])
+def test_graph_replay_matches_eager(gate):
+    w = MI.small_workload(f"graph_{gate}_T384_d256_E16_k4_I256", 384, 256, 16, 4, 256, gate=gate,
+                          bias_sigma=1.0 if gate == "softmax_topk" else None, seed=31)
+    print(f"\n[gpu case] {w.name}", flush=True)
+    sys.stdout.flush()
+    dev = U.upload(w, MI.generate(w))
+    shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate)
+    buf = LayerBuffers(shape, training=True)
+
+    def step():
+        forward(shape, buf, dev["x"], dev.get("Wr"), dev.get("b"), dev["Wg"], dev["Wu"], dev["Wd"])
+        backward(shape, buf, dev["dY"], dev["x"], dev.get("Wr"), dev["Wg"], dev["Wu"], dev["Wd"])
+
+    # outputs the gate writes (the balanced gate computes no logits)
+    outs = [k for k in OUTS if buf.t.get(k) is not None and not (gate == "balanced" and k == "logits")]
+    step()
+    torch.cuda.synchronize()
+    ref = {k: buf[k].clone() for k in outs}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in outs:
+            buf[k].fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(buf[k], ref[k]), f"replay {rep}: {k} differs from the eager run"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
