@@ -4,7 +4,9 @@ One step = one forward and one backward of the whole layer (route, permute,
 grouped SwiGLU FFN, combine and the backward of each) on the Qwen3-30B-A3B
 shaped workload with the balanced gate: T=4096 tokens, d=2048, E=128 experts,
 k=8, I=768, bf16 storage with fp32 accumulation, seeded synthetic inputs that
-are resident in HBM before the timed region.
+are resident in HBM before the timed region.  By default the expert FFN runs
+in its gathered form (the GEMMs read the permuted rows from x through the
+token table; outputs bit-identical to the form with the Xp copy).
 
 Prints ONE JSON line (rank 0) with tokens/s, the roofline of the dominant
 kernel (timed with HIP events on its launch stream during the timed region)
@@ -30,21 +32,28 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["gemm.hip", "gemm.h", "common.h"]
 
 # Algorithmic work per launch of each GEMM kernel: (flops, bytes) as functions
-# of R routed rows, d, I, E_loc.  Bytes: every operand read once, every output
-# written once, bf16 (2 bytes).
+# of R routed rows, d, I, E_loc and T tokens.  Bytes: every operand read once,
+# every output written once, bf16 (2 bytes).  The gathered forms read the
+# rows of Xp from x, so their A operand is x itself (T rows, not R).
 GEMMS = {
-    "ffn_gateup_fwd":   (lambda R, d, I, El: 4 * R * d * I,
-                         lambda R, d, I, El: 2 * (R * d + 2 * El * d * I + 2 * R * I + R * I)),
-    "ffn_down_fwd":     (lambda R, d, I, El: 2 * R * I * d,
-                         lambda R, d, I, El: 2 * (R * I + El * I * d + R * d)),
-    "ffn_down_dgrad":   (lambda R, d, I, El: 2 * R * d * I,
-                         lambda R, d, I, El: 2 * (R * d + El * I * d + 2 * R * I + 2 * R * I)),
-    "ffn_gateup_dgrad": (lambda R, d, I, El: 4 * R * d * I,
-                         lambda R, d, I, El: 2 * (2 * R * I + 2 * El * d * I + R * d)),
-    "ffn_down_wgrad":   (lambda R, d, I, El: 2 * R * I * d,
-                         lambda R, d, I, El: 2 * (R * I + R * d + El * I * d)),
-    "ffn_gateup_wgrad": (lambda R, d, I, El: 4 * R * d * I,
-                         lambda R, d, I, El: 2 * (R * d + 2 * R * I + 2 * El * d * I)),
+    "ffn_gateup_fwd":   (lambda R, d, I, El, T: 4 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (R * d + 2 * El * d * I + 2 * R * I + R * I)),
+    "ffn_gateup_fwd_gather":
+                        (lambda R, d, I, El, T: 4 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (T * d + 2 * El * d * I + 2 * R * I + R * I)),
+    "ffn_down_fwd":     (lambda R, d, I, El, T: 2 * R * I * d,
+                         lambda R, d, I, El, T: 2 * (R * I + El * I * d + R * d)),
+    "ffn_down_dgrad":   (lambda R, d, I, El, T: 2 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (R * d + El * I * d + 2 * R * I + 2 * R * I)),
+    "ffn_gateup_dgrad": (lambda R, d, I, El, T: 4 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (2 * R * I + 2 * El * d * I + R * d)),
+    "ffn_down_wgrad":   (lambda R, d, I, El, T: 2 * R * I * d,
+                         lambda R, d, I, El, T: 2 * (R * I + R * d + El * I * d)),
+    "ffn_gateup_wgrad": (lambda R, d, I, El, T: 4 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (R * d + 2 * R * I + 2 * El * d * I)),
+    "ffn_gateup_wgrad_gather":
+                        (lambda R, d, I, El, T: 4 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (T * d + 2 * R * I + 2 * El * d * I)),
 }
 
 
@@ -94,7 +103,7 @@ def cpu_baseline(budget_s: float):
 # GEMM roles: the last template argument of the GEMM kernels
 ROLE_NAMES = {0: "route_logits", 1: "ffn_gateup_fwd", 2: "ffn_down_fwd", 3: "ffn_down_dgrad",
               4: "ffn_gateup_dgrad", 5: "ffn_down_wgrad", 6: "ffn_gateup_wgrad", 7: "route_bwd_dw",
-              8: "route_bwd_dx"}
+              8: "route_bwd_dx", 9: "ffn_gateup_fwd_gather", 10: "ffn_gateup_wgrad_gather"}
 
 
 def gemm_role_of(kernel_name: str):
@@ -176,25 +185,41 @@ def kernel_averages(step, B, n: int):
     return res
 
 
-def secondary_workloads(B, dev, w_main):
-    """fwd+bwd of the natural softmax top-k router at the Qwen3 shape (same
-    tokens and expert weights as the main workload, router weights and bias
-    from the natural workload's recipe), and of one rank's share of the
-    DeepSeek-V3 shape (expert weights drawn on the GPU with the same
-    distribution as the recipe)."""
+def secondary_workloads(B, dev, w_main, gather):
+    """The main workload with the other FFN form (Xp materialised by the
+    permute, or read from x through the token table); fwd+bwd of the natural
+    softmax top-k router at the Qwen3 shape (same tokens and expert weights as
+    the main workload, router weights and bias from the natural workload's
+    recipe); and of one rank's share of the DeepSeek-V3 shape (expert weights
+    drawn on the GPU with the same distribution as the recipe)."""
     import numpy as np
     import torch
     import moe_inputs as MI
     from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward
 
     out = {}
+    # -- the main workload, other FFN form
+    shape = B.MoEShape.make(w_main.T, w_main.d, w_main.E, w_main.k, w_main.I, dtype=w_main.dtype,
+                            gate=w_main.gate)
+    buf = LayerBuffers(shape, training=True, gather=not gather)
+
+    def step_other():
+        forward(shape, buf, dev["x"], None, None, dev["Wg"], dev["Wu"], dev["Wd"])
+        backward(shape, buf, dev["dY"], dev["x"], None, dev["Wg"], dev["Wu"], dev["Wd"])
+
+    st = timed_steps(step_other, 10, 3)
+    out["plain_ffn_fwdbwd" if gather else "gathered_ffn_fwdbwd"] = {
+        "workload": w_main.name, "ffn": "plain" if gather else "gather",
+        "tokens_per_s": round(w_main.T / (st["median"] / 1e3), 1), "step_ms": st,
+        "kernels_us_avg": kernel_averages(step_other, B, 3)}
+    del buf
     # -- natural router, Qwen3 shape
     wn = MI.WORKLOADS["qwen3_natural_fwd_T4096_d2048_E128_k8_I768"]
     r = MI.generate(wn, parts=["Wr", "b"])
     Wr = torch.from_numpy(r["Wr"]).to(torch.bfloat16).cuda()
     bias = torch.from_numpy(r["b"]).cuda()
     shape = B.MoEShape.make(wn.T, wn.d, wn.E, wn.k, wn.I, dtype="bf16", gate="softmax_topk")
-    buf = LayerBuffers(shape, training=True)
+    buf = LayerBuffers(shape, training=True, gather=gather)
 
     def step_nat():
         forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
@@ -221,7 +246,7 @@ def secondary_workloads(B, dev, w_main):
           "dY": rnd(wd.T, wd.d, sigma=wd.dy_sigma)}
     shape = B.MoEShape.make(wd.T, wd.d, wd.E, wd.k, wd.I, dtype="bf16", gate="balanced",
                             e_lo=wd.e_lo, e_hi=wd.e_end)
-    buf = LayerBuffers(shape, training=True)
+    buf = LayerBuffers(shape, training=True, gather=gather)
 
     def step_ds():
         forward(shape, buf, d5["x"], None, None, d5["Wg"], d5["Wu"], d5["Wd"])
@@ -231,7 +256,7 @@ def secondary_workloads(B, dev, w_main):
     ker = kernel_averages(step_ds, B, 2)
     R = int(buf["offsets"][-1].item())
     gem_us = sum(ker[n] for n in GEMMS if n in ker)
-    gem_fl = sum(GEMMS[n][0](R, wd.d, wd.I, El) for n in GEMMS if n in ker)
+    gem_fl = sum(GEMMS[n][0](R, wd.d, wd.I, El, wd.T) for n in GEMMS if n in ker)
     out["dsv3_rank_share_fwdbwd"] = {
         "workload": wd.name, "routed_rows": R,
         "tokens_per_s": round(wd.T / (st["median"] / 1e3), 1), "step_ms": st,
@@ -249,6 +274,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--ffn", choices=("gather", "plain"), default="gather",
+                    help="gather: the FFN reads the rows of Xp from x through the token table "
+                         "(no Xp buffer); plain: the permute writes Xp")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the natural-router and DeepSeek-V3 rank-share timings")
@@ -290,7 +318,8 @@ def main():
     del a
     shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate, e_lo=w.e_lo,
                             e_hi=w.e_end)
-    buf = LayerBuffers(shape, training=w.backward)
+    gather = args.ffn == "gather"
+    buf = LayerBuffers(shape, training=w.backward, gather=gather)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -356,12 +385,12 @@ def main():
     for name, (fl, by) in GEMMS.items():
         if name in kernels:
             us = kernels[name]["us_avg"]
-            f, b = fl(R, w.d, w.I, El), by(R, w.d, w.I, El)
+            f, b = fl(R, w.d, w.I, El, w.T), by(R, w.d, w.I, El, w.T)
             gem[name] = {"us": round(us, 2), "tflops": round(f / us / 1e6, 1),
                          "gbs": round(b / us / 1e3, 1), "mfma_frac": round(f / us / 1e6 / PEAK_BF16_TFLOPS, 3),
                          "hbm_frac": round(b / us / 1e3 / PEAK_HBM_GBS, 3)}
     fl, by = GEMMS[dom]
-    flops, nbytes = fl(R, w.d, w.I, El), by(R, w.d, w.I, El)
+    flops, nbytes = fl(R, w.d, w.I, El, w.T), by(R, w.d, w.I, El, w.T)
     # the dominant kernel's bound by the roofline model: HBM when its
     # algorithmic bytes take longer at peak bandwidth than its flops at peak
     # MFMA rate (intensity below the ridge point), else MFMA
@@ -381,7 +410,7 @@ def main():
         if ent and tr.get("source_hash") == kernel_source_hash():
             traffic = ent["bytes_per_launch"]
     gemm_total_us = sum(g["us"] for g in gem.values())
-    gemm_flops = sum(GEMMS[n][0](R, w.d, w.I, El) for n in gem)
+    gemm_flops = sum(GEMMS[n][0](R, w.d, w.I, El, w.T) for n in gem)
 
     out = {
         "metric": METRIC,
@@ -398,7 +427,7 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, N(0,1) upstream grad)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "I": w.I,
                    "gate": w.gate, "pass": "fwd+bwd" if w.backward else "fwd",
-                   "routed_rows": R, "parallelism": "single GPU"},
+                   "routed_rows": R, "ffn": args.ffn, "parallelism": "single GPU"},
         "roofline": {**roof, "traffic": traffic, "kernel": dom,
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_tflops": round(flops / dom_us / 1e6, 1)},
@@ -411,7 +440,7 @@ def main():
     out["step_ms_stats"] = timed_steps(step, max(5, args.steps), 2)
     if not args.no_secondary and w.name == WORKLOAD:
         log("[bench] natural-router and DeepSeek-V3 rank-share timings")
-        out["secondary"] = secondary_workloads(B, dev, w)
+        out["secondary"] = secondary_workloads(B, dev, w, gather)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)

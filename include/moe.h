@@ -130,6 +130,8 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
  *     dropped by the capacity, or repeats an expert id an earlier slot of the
  *     same token already holds (routing never produces repeats);
  *   xp [R_cap, d] (dtype): xp[p] = x[perm[p] / k] (rows past the end untouched).
+ *     xp may be NULL (then x may be NULL too): only the sort runs, for the
+ *     _gather forms of the FFN calls below, which read x through perm.
  * ws/ws_bytes: workspace of moe_workspace_size(MOE_OP_PERMUTE). */
 moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, const void* x,
                          int32_t* group_offsets, int32_t* perm, int32_t* inv, void* xp,
@@ -152,6 +154,21 @@ moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void* xp,
                                  const void* w_up, const void* w_down, void* h_save,
                                  void* a_save, void* yp, void* ws, size_t ws_bytes,
                                  moe_stream_t stream);
+
+/* a2 + a3 + a4 fused -- the same FFN with the dispatch copy folded into the
+ * gate/up GEMM's operand loads (the one-GPU counterpart of dispatch fused with
+ * the expert computation, [P3] section 加速来源, DeepEP item): row p of Xp is
+ * read as x[perm[p] / k] and Xp is never written.  Results are bit-identical
+ * to moe_permute(xp) followed by moe_grouped_ffn_fwd.  x [T,d]; perm [R_cap]
+ * as written by moe_permute (which may then skip xp); the other arguments and
+ * the workspace as for moe_grouped_ffn_fwd.  Needs T*d*element bytes < 2^31
+ * (else MOE_ERR_UNSUPPORTED). */
+moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, const void* x,
+                                        const int32_t* perm, const int32_t* group_offsets,
+                                        const void* w_gate, const void* w_up,
+                                        const void* w_down, void* h_save, void* a_save,
+                                        void* yp, void* ws, size_t ws_bytes,
+                                        moe_stream_t stream);
 
 /* a5 -- combine (the "combine" half of dispatch/combine, [P3] section 加速来源):
  * y[t] = sum_j topk_w[t,j] * yp[inv[t*k+j]] over the slots with inv >= 0, in
@@ -187,6 +204,19 @@ moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void* xp,
                                  const void* a_save, const void* dyp, void* dxp,
                                  void* dw_gate, void* dw_up, void* dw_down, void* ws,
                                  size_t ws_bytes, moe_stream_t stream);
+
+/* a7..a10 with the Xp rows of the gate/up weight gradient read as
+ * x[perm[p] / k] (the backward of moe_grouped_ffn_fwd_gather; no Xp buffer).
+ * Bit-identical to moe_grouped_ffn_bwd on the Xp that moe_permute writes.
+ * x [T,d]; perm [R_cap]; the rest as for moe_grouped_ffn_bwd.  Needs
+ * T*d*element bytes < 2^31 (else MOE_ERR_UNSUPPORTED). */
+moe_status_t moe_grouped_ffn_bwd_gather(const moe_shape_t* shape, const void* x,
+                                        const int32_t* perm, const int32_t* group_offsets,
+                                        const void* w_gate, const void* w_up,
+                                        const void* w_down, const void* h_save,
+                                        const void* a_save, const void* dyp, void* dxp,
+                                        void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                                        size_t ws_bytes, moe_stream_t stream);
 
 /* a11 -- permute backward: dx[t] = sum_j dxp[inv[t*k+j]] over slots with
  * inv >= 0, ascending j, fp32 accumulation (tokens with no slot get 0).

@@ -25,7 +25,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
 EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_size",
            "moe_route", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine", "moe_combine_bwd",
            "moe_grouped_ffn_bwd", "moe_permute_bwd", "moe_route_bwd", "moe_prof_enable",
-           "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names"]
+           "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names",
+           "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather"]
 
 
 class MoEError(RuntimeError):
@@ -87,6 +88,8 @@ def load_library() -> ctypes.CDLL:
         "moe_combine": [S, P, P, P, P, P],
         "moe_combine_bwd": [S, P, P, P, P, P, P, P],
         "moe_grouped_ffn_bwd": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_grouped_ffn_fwd_gather": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
         "moe_route_bwd": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_prof_enable": [I32],
@@ -153,6 +156,14 @@ def moe_grouped_ffn_fwd(shape, xp, group_offsets, w_gate, w_up, w_down, h_save, 
         _stream(stream)))
 
 
+def moe_grouped_ffn_fwd_gather(shape, x, perm, group_offsets, w_gate, w_up, w_down, h_save,
+                               a_save, yp, ws, stream=None):
+    _check("moe_grouped_ffn_fwd_gather", load_library().moe_grouped_ffn_fwd_gather(
+        ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(group_offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(yp), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
 def moe_combine(shape, yp, inv, topk_w, y, stream=None):
     _check("moe_combine", load_library().moe_combine(
         ctypes.byref(shape), _ptr(yp), _ptr(inv), _ptr(topk_w), _ptr(y), _stream(stream)))
@@ -168,6 +179,14 @@ def moe_grouped_ffn_bwd(shape, xp, group_offsets, w_gate, w_up, w_down, h_save, 
                         dxp, dw_gate, dw_up, dw_down, ws, stream=None):
     _check("moe_grouped_ffn_bwd", load_library().moe_grouped_ffn_bwd(
         ctypes.byref(shape), _ptr(xp), _ptr(group_offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(dyp), _ptr(dxp), _ptr(dw_gate),
+        _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_grouped_ffn_bwd_gather(shape, x, perm, group_offsets, w_gate, w_up, w_down, h_save,
+                               a_save, dyp, dxp, dw_gate, dw_up, dw_down, ws, stream=None):
+    _check("moe_grouped_ffn_bwd_gather", load_library().moe_grouped_ffn_bwd_gather(
+        ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(group_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(dyp), _ptr(dxp), _ptr(dw_gate),
         _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _stream(stream)))
 

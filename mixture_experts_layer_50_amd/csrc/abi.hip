@@ -253,25 +253,42 @@ int64_t one_table_bytes(const Dims& D, int bm) {
   return round_up((1 + 2 * ((int64_t)D.R_cap / bm + D.E_loc)) * 4, 256);
 }
 int64_t kcost_bytes(const Dims& D) { return round_up((int64_t)(D.E_loc + 1) * 4, 256); }
+int64_t tok_bytes(const Dims& D) { return round_up((int64_t)D.R_cap * 4, 256); }
 int64_t tile_table_bytes(const Dims& D) {
-  return one_table_bytes(D, 256) + one_table_bytes(D, 128) + kcost_bytes(D);
+  return one_table_bytes(D, 256) + one_table_bytes(D, 128) + kcost_bytes(D) + tok_bytes(D);
 }
 int max_m_tiles(const Dims& D, int bm) { return D.R_cap / bm + D.E_loc; }
 
 // Builds the tile tables a call needs, once each, in its workspace.
+// With perm (the gathered calls) also the token row of every routed row.
 struct TileTables {
   const Dims& D;
   int32_t* base;
   const int32_t* off;
   hipStream_t s;
+  const int32_t* perm = nullptr;
   bool built = false;
   int32_t* t256() const { return base; }
   int32_t* t128() const { return base + one_table_bytes(D, 256) / 4; }
   int32_t* kcost() const { return t128() + one_table_bytes(D, 128) / 4; }
+  int32_t* tok() const { return kcost() + kcost_bytes(D) / 4; }
   moe_status_t ensure() {  // all tables in one launch, on first use
     if (!built) {
-      MOE_TRY(launch_tile_tables(off, D.E_loc, t256(), t128(), kcost(), s));
+      MOE_TRY(launch_tile_tables(off, D.E_loc, t256(), t128(), kcost(), s, perm, D.k, tok(),
+                                 D.R_cap));
       built = true;
+    }
+    return MOE_OK;
+  }
+  // A rows of a gather role: the token table (bf16 kernels) or perm with k (fp32)
+  moe_status_t rows(GemmParams* p) {
+    if (D.bf16) {
+      MOE_TRY(ensure());
+      p->a_rows = tok();
+      p->a_rows_div = 1;
+    } else {
+      p->a_rows = perm;
+      p->a_rows_div = D.k;
     }
     return MOE_OK;
   }
@@ -371,38 +388,56 @@ extern "C" moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* top
   const char* fn = "moe_permute";
   Dims D;
   MOE_TRY(check_shape(shape, fn, &D));
-  MOE_TRY(need(fn, {{"topk_idx", topk_idx}, {"x", x}, {"group_offsets", group_offsets},
-                    {"perm", perm}, {"inv", inv}, {"xp", xp}}));
+  MOE_TRY(need(fn, {{"topk_idx", topk_idx}, {"group_offsets", group_offsets}, {"perm", perm},
+                    {"inv", inv}}));
+  if (xp) MOE_TRY(need(fn, {{"x", x}, {"xp", xp}}));
   MOE_TRY(check_ws(fn, D, MOE_OP_PERMUTE, ws, ws_bytes_));
   return launch_permute(topk_idx, x, D.T, D.d, D.k, D.e_lo, D.e_hi, D.R_cap, D.eb, group_offsets,
                         perm, inv, xp, ws, S(stream));
 }
 
-extern "C" moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void* xp,
-                                            const int32_t* group_offsets, const void* w_gate,
-                                            const void* w_up, const void* w_down, void* h_save,
-                                            void* a_save, void* yp, void* ws, size_t ws_bytes_,
-                                            moe_stream_t stream) {
-  const char* fn = "moe_grouped_ffn_fwd";
+namespace {
+
+// The gathered forms read row p of Xp as row perm[p] / k of x; their A byte
+// offsets are 32-bit.
+moe_status_t check_gather(const char* fn, const Dims& D) {
+  if ((int64_t)D.T * D.d * D.eb >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: x of %lld bytes; the gathered form needs < 2^31", fn,
+                (long long)D.T * D.d * D.eb);
+  return MOE_OK;
+}
+
+// Forward FFN over Xp rows: xp itself, or (gather) x read through perm.
+moe_status_t ffn_fwd(const char* fn, bool gather, const moe_shape_t* shape, const void* a_src,
+                     const int32_t* perm, const int32_t* group_offsets, const void* w_gate,
+                     const void* w_up, const void* w_down, void* h_save, void* a_save, void* yp,
+                     void* ws, size_t ws_bytes_, moe_stream_t stream) {
   Dims D;
   MOE_TRY(check_shape(shape, fn, &D));
-  MOE_TRY(need(fn, {{"xp", xp}, {"group_offsets", group_offsets}, {"w_gate", w_gate},
-                    {"w_up", w_up}, {"w_down", w_down}, {"a_save", a_save}, {"yp", yp}}));
+  MOE_TRY(need(fn, {{gather ? "x" : "xp", a_src}, {"group_offsets", group_offsets},
+                    {"w_gate", w_gate}, {"w_up", w_up}, {"w_down", w_down}, {"a_save", a_save}, {"yp", yp}}));
+  if (!gather) perm = nullptr;
+  if (gather) {
+    MOE_TRY(need(fn, {{"perm", perm}}));
+    MOE_TRY(check_gather(fn, D));
+  }
   MOE_TRY(opt(fn, {{"h_save", h_save}}));
   MOE_TRY(check_ws(fn, D, MOE_OP_FFN_FWD, ws, ws_bytes_));
-  TileTables tt{D, static_cast<int32_t*>(ws), group_offsets, S(stream)};
+  TileTables tt{D, static_cast<int32_t*>(ws), group_offsets, S(stream), perm};
   // fp32: the row count; bf16: the most M tiles the tile table can hold
   auto rows_or_tiles = [&](GemmRole r) { return D.bf16 ? max_m_tiles(D, tile_bm(role_tile(r))) : D.R_cap; };
 
+  const GemmRole gu = perm ? R_GATEUP_FWD_GATHER : R_GATEUP_FWD;
   GemmParams g{};
-  g.A = xp; g.lda = D.d;
+  g.A = a_src; g.lda = D.d;
+  if (perm) MOE_TRY(tt.rows(&g));
   g.B0 = w_gate; g.B1 = w_up; g.ldb = D.I; g.b_estride = (int64_t)D.d * D.I;
   g.N = D.I; g.K = D.d;
   g.off = group_offsets; g.groups = D.E_loc;
-  g.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_GATEUP_FWD)) / 2);
+  g.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(gu)) / 2);
   g.C0 = h_save; g.C2 = a_save; g.I = D.I;
-  if (D.bf16) MOE_TRY(tt.get(R_GATEUP_FWD, &g.tiles));
-  MOE_TRY(launch_gemm(D.bf16, R_GATEUP_FWD, g, rows_or_tiles(R_GATEUP_FWD), S(stream)));
+  if (D.bf16) MOE_TRY(tt.get(gu, &g.tiles));
+  MOE_TRY(launch_gemm(D.bf16, gu, g, rows_or_tiles(gu), S(stream)));
 
   GemmParams p{};
   p.A = a_save; p.lda = D.I;
@@ -413,6 +448,28 @@ extern "C" moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void
   p.C0 = yp; p.ldc = D.d;
   if (D.bf16) MOE_TRY(tt.get(R_DOWN_FWD, &p.tiles));
   return launch_gemm(D.bf16, R_DOWN_FWD, p, rows_or_tiles(R_DOWN_FWD), S(stream));
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_grouped_ffn_fwd(const moe_shape_t* shape, const void* xp,
+                                            const int32_t* group_offsets, const void* w_gate,
+                                            const void* w_up, const void* w_down, void* h_save,
+                                            void* a_save, void* yp, void* ws, size_t ws_bytes_,
+                                            moe_stream_t stream) {
+  return ffn_fwd("moe_grouped_ffn_fwd", false, shape, xp, nullptr, group_offsets, w_gate, w_up,
+                 w_down, h_save, a_save, yp, ws, ws_bytes_, stream);
+}
+
+extern "C" moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, const void* x,
+                                                   const int32_t* perm,
+                                                   const int32_t* group_offsets,
+                                                   const void* w_gate, const void* w_up,
+                                                   const void* w_down, void* h_save, void* a_save,
+                                                   void* yp, void* ws, size_t ws_bytes_,
+                                                   moe_stream_t stream) {
+  return ffn_fwd("moe_grouped_ffn_fwd_gather", true, shape, x, perm, group_offsets, w_gate, w_up,
+                 w_down, h_save, a_save, yp, ws, ws_bytes_, stream);
 }
 
 extern "C" moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,
@@ -436,18 +493,23 @@ extern "C" moe_status_t moe_combine_bwd(const moe_shape_t* shape, const void* dy
   return launch_combine_bwd(dy, yp, inv, topk_w, D.T, D.d, D.k, D.eb, dyp, dtopk_w, S(stream));
 }
 
-extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void* xp,
-                                            const int32_t* group_offsets, const void* w_gate,
-                                            const void* w_up, const void* w_down,
-                                            const void* h_save, const void* a_save,
-                                            const void* dyp, void* dxp, void* dw_gate,
-                                            void* dw_up, void* dw_down, void* ws,
-                                            size_t ws_bytes_, moe_stream_t stream) {
-  const char* fn = "moe_grouped_ffn_bwd";
+namespace {
+
+// Backward FFN over Xp rows: xp itself, or (gather) x read through perm.
+moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, const void* xp,
+                     const int32_t* perm, const int32_t* group_offsets, const void* w_gate,
+                     const void* w_up, const void* w_down, const void* h_save,
+                     const void* a_save, const void* dyp, void* dxp, void* dw_gate, void* dw_up,
+                     void* dw_down, void* ws, size_t ws_bytes_, moe_stream_t stream) {
   Dims D;
   MOE_TRY(check_shape(shape, fn, &D));
-  MOE_TRY(need(fn, {{"xp", xp}, {"group_offsets", group_offsets}, {"w_gate", w_gate},
-                    {"w_up", w_up}, {"w_down", w_down}, {"h_save", h_save}, {"a_save", a_save},
+  if (!gather) perm = nullptr;
+  if (gather) {
+    MOE_TRY(need(fn, {{"perm", perm}}));
+    MOE_TRY(check_gather(fn, D));
+  }
+  MOE_TRY(need(fn, {{gather ? "x" : "xp", xp}, {"group_offsets", group_offsets},
+                    {"w_gate", w_gate}, {"w_up", w_up}, {"w_down", w_down}, {"h_save", h_save}, {"a_save", a_save},
                     {"dyp", dyp}, {"dxp", dxp}, {"dw_gate", dw_gate}, {"dw_up", dw_up},
                     {"dw_down", dw_down}}));
   MOE_TRY(check_ws(fn, D, MOE_OP_FFN_BWD, ws, ws_bytes_));
@@ -455,7 +517,7 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
   void* dH = wsb;
   hipStream_t s = S(stream);
   TileTables tt{D, reinterpret_cast<int32_t*>(wsb + round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256)),
-                group_offsets, s};
+                group_offsets, s, perm};
   auto rows_or_tiles = [&](GemmRole r) { return D.bf16 ? max_m_tiles(D, tile_bm(role_tile(r))) : D.R_cap; };
 
   // Order: the weight gradient of the down projection and the dSwiGLU GEMM
@@ -487,17 +549,19 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     MOE_TRY(launch_gemm(D.bf16, R_DOWN_DGRAD, p, rows_or_tiles(R_DOWN_DGRAD), s));
   }
   {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
+    const GemmRole gw = perm ? R_GATEUP_WGRAD_GATHER : R_GATEUP_WGRAD;
     GemmParams p{};
     p.A = xp; p.lda = D.d;
+    if (perm) MOE_TRY(tt.rows(&p));
     p.B0 = dH; p.ldb = 2 * (int64_t)D.I;
     p.M = D.d; p.N = 2 * D.I;
     p.off = group_offsets; p.groups = D.E_loc;
-    const TileCfg t = role_tile(R_GATEUP_WGRAD);
+    const TileCfg t = role_tile(gw);
     p.m_tiles = (int)ceil_div(D.d, tile_bm(t)); p.n_tiles = (int)ceil_div(2 * D.I, tile_bn(t));
     p.C0 = dw_gate; p.C1 = dw_up; p.n_split = D.I; p.ldc = D.I;
     p.c_estride = (int64_t)D.d * D.I;
     if (D.bf16) p.kcost = tt.kcost();
-    MOE_TRY(launch_gemm(D.bf16, R_GATEUP_WGRAD, p, p.m_tiles, s));
+    MOE_TRY(launch_gemm(D.bf16, gw, p, p.m_tiles, s));
   }
   {  // a9: dXp = dHg Wg^T + dHu Wu^T (one K loop over [dHg | dHu])
     GemmParams p{};
@@ -512,6 +576,32 @@ extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void
     MOE_TRY(launch_gemm(D.bf16, R_GATEUP_DGRAD, p, rows_or_tiles(R_GATEUP_DGRAD), s));
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_grouped_ffn_bwd(const moe_shape_t* shape, const void* xp,
+                                            const int32_t* group_offsets, const void* w_gate,
+                                            const void* w_up, const void* w_down,
+                                            const void* h_save, const void* a_save,
+                                            const void* dyp, void* dxp, void* dw_gate,
+                                            void* dw_up, void* dw_down, void* ws,
+                                            size_t ws_bytes_, moe_stream_t stream) {
+  return ffn_bwd("moe_grouped_ffn_bwd", false, shape, xp, nullptr, group_offsets, w_gate, w_up,
+                 w_down, h_save, a_save, dyp, dxp, dw_gate, dw_up, dw_down, ws, ws_bytes_, stream);
+}
+
+extern "C" moe_status_t moe_grouped_ffn_bwd_gather(const moe_shape_t* shape, const void* x,
+                                                   const int32_t* perm,
+                                                   const int32_t* group_offsets,
+                                                   const void* w_gate, const void* w_up,
+                                                   const void* w_down, const void* h_save,
+                                                   const void* a_save, const void* dyp, void* dxp,
+                                                   void* dw_gate, void* dw_up, void* dw_down,
+                                                   void* ws, size_t ws_bytes_,
+                                                   moe_stream_t stream) {
+  return ffn_bwd("moe_grouped_ffn_bwd_gather", true, shape, x, perm, group_offsets, w_gate, w_up,
+                 w_down, h_save, a_save, dyp, dxp, dw_gate, dw_up, dw_down, ws, ws_bytes_, stream);
 }
 
 extern "C" moe_status_t moe_permute_bwd(const moe_shape_t* shape, const void* dxp, const int32_t* inv,

@@ -62,6 +62,9 @@ struct GemmParams {
   int I;               // EPI_SWIGLU / EPI_DSWIGLU: expert width (H row stride is 2I)
   const void* aux;     // EPI_DSWIGLU: saved H
   const float* bias;   // EPI_F32_BIAS (may be NULL)
+  const int32_t* a_rows;  // gather roles: A row p (the M index for G_MROWS, the K index for
+  int a_rows_div;         // G_KROWS) is row a_rows[p] / a_rows_div of the matrix at A (the
+                          // bf16 kernels take a table of rows: a_rows_div must be 1)
 };
 
 // Tile shapes of the bf16 MFMA kernels.
@@ -78,7 +81,11 @@ enum GemmRole {
   R_DOWN_WGRAD = 5,     // dWd = A^T dYp
   R_GATEUP_WGRAD = 6,   // [dWg | dWu] = Xp^T [dHg | dHu]
   R_ROUTE_DW = 7,       // dWr = x^T dL
-  R_ROUTE_DX = 8        // dX += dL Wr^T
+  R_ROUTE_DX = 8,       // dX += dL Wr^T
+  // R_GATEUP_FWD and R_GATEUP_WGRAD with the rows of Xp read from x through
+  // perm (Xp is never written): a_rows = perm, a_rows_div = k
+  R_GATEUP_FWD_GATHER = 9,
+  R_GATEUP_WGRAD_GATHER = 10
 };
 
 // Tile shape each role runs with (bf16), for a GEMM with n output columns
@@ -97,8 +104,12 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
 // Tile tables for G_MROWS, for 256-row and for 128-row tiles (one launch):
 // tiles[0] = number of M tiles, then for each tile (expert, first row) in
 // expert order; and the K-cost prefix of the weight gradients (kcost above).
+// With perm, the same launch also writes the token row of every routed row,
+// tok[p] = perm[p] / k for p < off[groups] (the A rows of the gather roles).
 moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
-                                int32_t* tiles128, int32_t* kcost, hipStream_t s);
+                                int32_t* tiles128, int32_t* kcost, hipStream_t s,
+                                const int32_t* perm = nullptr, int k = 1, int32_t* tok = nullptr,
+                                int rows_cap = 0);
 // Per-tile cost of a weight-gradient tile beyond its K slices (its epilogue).
 constexpr int KCOST_FIXED = 2;
 

@@ -14,6 +14,10 @@
 //  * gemm_bf16_ws_kernel: persistent and warp-specialised (producer waves
 //    load, compute waves multiply and store), for plain-store epilogues with
 //    much output per unit of work (the weight gradients, the down projection).
+// The gather roles read the rows of their A operand through a table of row
+// numbers (the permuted rows Xp read from x: the dispatch copy folded into
+// the GEMM's operand loads, page "Accelerating Transformers fine-tuning with
+// NVIDIA NeMo AutoModel", section 加速来源, DeepEP item).
 //
 // fp32 path: a plain fp32 kernel (one output per thread, fp32 FMA) used for
 // fp32 layers, which are small parity workloads.
@@ -89,13 +93,24 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CPOL));
 }
 
+// The group offsets, the tile table and the gather rows are read-only for the GEMM kernels;
+// reading them through the constant address space with a uniform index makes
+// them scalar loads, which do not wait behind the vector loads in flight.
+typedef __attribute__((address_space(4))) const int32_t cint32_t;
+__device__ __forceinline__ int ld_table(const int32_t* tab, int i) { return ((cint32_t*)tab)[i]; }
+
 // Loader of a KC tile: row r of the tile is src[(row0 + r) * ld + k], rows
 // r >= row_hi - row0 read as zeros.  With TWO, k < ksplit comes from s0 and
 // k >= ksplit from s1 at k - ksplit (ksplit is a multiple of 64, so one K
 // slice never straddles it).  The per-lane address state is kept once; the
 // loaded data lives in a separate register array per pipeline stage.
-template <int ROWS, bool TWO, int NT, int CPOL>
+//
+// GATHER: tile row r is row rows[row0 + r] of the source (the rows of Xp
+// read from x through the token table); the row numbers are loaded once per
+// tile.
+template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER>
 struct LoaderKC {
+  static_assert(!(GATHER && TWO), "a gathered operand has one source");
   static constexpr int CH = ROWS * 8;
   static constexpr int NR = (CH + NT - 1) / NT;
   struct Data { uint4 r[NR]; };
@@ -103,8 +118,9 @@ struct LoaderKC {
   __amdgpu_buffer_rsrc_t rs0, rs1;
   int ksplit, k_lo, k_hi;
   __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
-                                       int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid) {
-    rs0 = make_rsrc(s0 + (int64_t)row0 * ld);
+                                       int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid,
+                                       const int32_t* rows) {
+    rs0 = make_rsrc(GATHER ? s0 : s0 + (int64_t)row0 * ld);
     rs1 = make_rsrc(TWO ? s1 + (int64_t)row0 * ld : s0);
     ksplit = ksplit_;
     k_lo = k_lo_;
@@ -114,6 +130,7 @@ struct LoaderKC {
       int q = tid + NT * i;
       int row = q >> 3;
       bool ok = (CH % NT == 0 || q < CH) && row0 + row < row_hi;
+      if (GATHER) row = ok ? rows[row0 + row] : 0;
       voff[i] = ok ? (int)(((int64_t)row * ld + (q & 7) * 8) * 2) : OOB;
     }
   }
@@ -146,34 +163,76 @@ struct LoaderKC {
 // zeros.  HALF: tile columns [0, COLS/2) come from s0 at col0 + c, columns
 // [COLS/2, COLS) from s1 at col0 + c - COLS/2 (the gate | up halves); each
 // load instruction reads one half only, so its buffer descriptor is uniform.
-template <int COLS, bool HALF, int NT, int CPOL>
+//
+// GATHER: row k of the K range is row rows[k] of the source.  The lanes
+// of one wave cover 64 / CPR consecutive rows per load, so each wave reads
+// its row numbers with scalar loads, one K slice ahead of the data loads
+// (scalar loads retire through their own counter, so waiting for them never
+// waits for data loads in flight).
+template <int COLS, bool HALF, int NT, int CPOL, bool GATHER>
 struct LoaderKN {
   static constexpr int CPR = HALF ? COLS / 16 : COLS / 8;  // chunks per row and source
   static constexpr int CH = BK * CPR;                        // chunks per source
   static constexpr int NS = (CH + NT - 1) / NT;              // loads per source
   static constexpr int NR = HALF ? 2 * NS : NS;
+  static constexpr int RW = GATHER ? 64 / CPR : 1;           // rows per wave and load (GATHER)
+  static_assert(!GATHER || (!HALF && 64 % CPR == 0 && NT % 64 == 0 && CH % NT == 0),
+                "gathered rows: whole rows per wave");
   struct Data { uint4 r[NR]; };
   int voff[NS];
   __amdgpu_buffer_rsrc_t rs0, rs1;
   int64_t ld;
   int k_lo, k_hi;
+  const int32_t* rows;
+  int wrow;         // GATHER: the wave's first row of load 0
+  int nxt[NS][RW];  // GATHER: row numbers of the next slice (wave-uniform)
+  __device__ __forceinline__ void prefetch(int kofs) {
+    // the pointer is the same in every lane; say so, or the loads stay vector loads
+    const uint64_t a = (uint64_t)rows;
+    const int32_t* tab = (const int32_t*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                                          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int j = 0; j < RW; ++j)
+        nxt[i][j] = ld_table(tab, min(k_lo + kofs + wrow + i * (NT / CPR) + j, k_hi - 1));
+  }
   __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld_, int col0,
-                                       int col_hi, int k_lo_, int k_hi_, int, int tid) {
+                                       int col_hi, int k_lo_, int k_hi_, int, int tid,
+                                       const int32_t* rows_) {
     ld = ld_;
     k_lo = k_lo_;
     k_hi = k_hi_;
-    rs0 = make_rsrc(s0 + (int64_t)k_lo * ld + col0);
+    rs0 = make_rsrc(s0 + (GATHER ? 0 : (int64_t)k_lo * ld) + col0);
     rs1 = make_rsrc((HALF ? s1 : s0) + (int64_t)k_lo * ld + col0);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       int q = tid + NT * i;
       int col = (q % CPR) * 8;
       bool ok = (CH % NT == 0 || q < CH) && col0 + col < col_hi;
-      voff[i] = ok ? (int)(((int64_t)(q / CPR) * ld + col) * 2) : OOB;
+      voff[i] = ok ? (int)(((GATHER ? 0 : (int64_t)(q / CPR) * ld) + col) * 2) : OOB;
+    }
+    if constexpr (GATHER) {
+      rows = rows_;
+      wrow = __builtin_amdgcn_readfirstlane((tid >> 6) * (64 / CPR));
+      prefetch(0);
     }
   }
-  __device__ __forceinline__ void load(Data& d, int kofs, int tid) const {
+  __device__ __forceinline__ void load(Data& d, int kofs, int tid) {
     const int lim = k_hi - k_lo - kofs;
+    if constexpr (GATHER) {
+      const int sub = (tid & 63) / CPR;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        int r = nxt[i][0];
+#pragma unroll
+        for (int j = 1; j < RW; ++j) r = sub == j ? nxt[i][j] : r;
+        const bool ok = (tid + NT * i) / CPR < lim && voff[i] != OOB;
+        d.r[i] = buf_load16<CPOL>(rs0, ok ? (int)(r * ld * 2) + voff[i] : OOB, 0);
+      }
+      if (kofs + BK < k_hi - k_lo) prefetch(kofs + BK);
+      return;
+    }
     const int soff = (int)((int64_t)kofs * ld * 2);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -197,9 +256,11 @@ struct LoaderKN {
   }
 };
 
-template <bool KC, int ROWS, bool TWO, int NT, int CPOL> struct PickLoader;
-template <int ROWS, bool TWO, int NT, int CPOL> struct PickLoader<true, ROWS, TWO, NT, CPOL> { typedef LoaderKC<ROWS, TWO, NT, CPOL> type; };
-template <int ROWS, bool TWO, int NT, int CPOL> struct PickLoader<false, ROWS, TWO, NT, CPOL> { typedef LoaderKN<ROWS, TWO, NT, CPOL> type; };
+template <bool KC, int ROWS, bool TWO, int NT, int CPOL, bool GATHER> struct PickLoader;
+template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER>
+struct PickLoader<true, ROWS, TWO, NT, CPOL, GATHER> { typedef LoaderKC<ROWS, TWO, NT, CPOL, GATHER> type; };
+template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER>
+struct PickLoader<false, ROWS, TWO, NT, CPOL, GATHER> { typedef LoaderKN<ROWS, TWO, NT, CPOL, GATHER> type; };
 
 // MFMA operand fragment (32 rows x 16 k): lane l holds row base + (l & 31),
 // k = 16 ks + 8 (l >> 5) + 0..7.
@@ -233,11 +294,6 @@ struct TileDesc {
   int k_lo, k_hi;  // K range
 };
 
-// The group offsets and the tile table are read-only for the GEMM kernels;
-// reading them through the constant address space with a uniform index makes
-// them scalar loads, which do not wait behind the vector loads in flight.
-typedef __attribute__((address_space(4))) const int32_t cint32_t;
-__device__ __forceinline__ int ld_table(const int32_t* tab, int i) { return ((cint32_t*)tab)[i]; }
 
 template <int GMD>
 __device__ __forceinline__ int tile_count(const GemmParams& p) {
@@ -328,11 +384,14 @@ __device__ __forceinline__ void xcd_tile_range(const GemmParams& p, int count, i
 // Loader types of a GEMM.  The expert weights (B of the row-grouped GEMMs)
 // stream through once and are loaded non-temporal; the activation rows (A)
 // are re-read by every column tile of the expert and stay cached.
-template <int BM, int BN, int NT, int AM, int BMD, int GMD, int B2>
+// The gather roles read the rows of A through a_rows.
+constexpr bool gathers_a(int role) { return role == R_GATEUP_FWD_GATHER || role == R_GATEUP_WGRAD_GATHER; }
+
+template <int BM, int BN, int NT, int AM, int BMD, int GMD, int B2, bool AG>
 struct Loaders {
   static constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
-  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0>::type LA;
-  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL>::type LB;
+  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0, AG>::type LA;
+  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL, false>::type LB;
 };
 
 template <int GMD, int B2, typename LA, typename LB>
@@ -345,9 +404,9 @@ __device__ __forceinline__ void init_loaders(const GemmParams& p, const TileDesc
     B0 += (int64_t)t.e * p.b_estride;
     if (B2 != B2_NONE) B1 += (int64_t)t.e * p.b_estride;
   }
-  la.init(A, A, p.lda, t.m_lo, t.m_hi, t.k_lo, t.k_hi, 0, tid);
+  la.init(A, A, p.lda, t.m_lo, t.m_hi, t.k_lo, t.k_hi, 0, tid, p.a_rows);
   // columns are bounded in the B source's column space
-  lb.init(B0, B1, p.ldb, t.n0, p.N, t.k_lo, t.k_hi, p.k_split, tid);
+  lb.init(B0, B1, p.ldb, t.n0, p.N, t.k_lo, t.k_hi, p.k_split, tid, nullptr);
 }
 
 // The MFMAs of one K slice: A tile at `as` ([BM] rows), B tile right after it.
@@ -811,8 +870,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
   const TileDesc t = tile_desc<BM, BN, GMD, B2>(p, remap_xcd(blockIdx.x, count));
   const int e = t.e, m_lo = t.m_lo, m_hi = t.m_hi, n0 = t.n0, k_lo = t.k_lo, k_hi = t.k_hi;
 
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LA LA;
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LB LB;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[P];
@@ -939,8 +998,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(Ge
   xcd_tile_range<GMD>(p, count, xcd, x_lo, x_n);
   if (slot >= x_n) return;
 
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LA LA;
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2>::LB LB;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[2];
@@ -1103,8 +1162,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
 
   // ---- producer state: loaders, PD register stages, load cursor
   static_assert(PD >= 2, "at least two register stages");
-  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2>::LA LA;
-  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2>::LB LB;
+  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
+  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[PD];
@@ -1315,8 +1374,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
       else if (p.k_chunk > 0) { k_lo = min(p.K, e * p.k_chunk); k_hi = min(p.K, k_lo + p.k_chunk); }
     }
   }
+  // gather roles: logical A row j is row a_rows[j] / a_rows_div
+  auto a_row = [&](int j) -> int64_t {
+    return gathers_a(ROLE) ? (int64_t)((uint32_t)p.a_rows[j] / (uint32_t)p.a_rows_div) : j;
+  };
   auto a_at = [&](int k) -> float {
-    return AM == A_KC ? A[(int64_t)m * p.lda + k] : A[(int64_t)k * p.lda + m];
+    return AM == A_KC ? A[a_row(m) * p.lda + k] : A[a_row(k) * p.lda + m];
   };
   auto b_at = [&](const float* B, int k, int col) -> float {
     return BMD == B_NC ? B[(int64_t)k * p.ldb + col] : B[(int64_t)col * p.ldb + k];
@@ -1365,9 +1428,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Workgroup 0 builds the table for 256-row tiles, workgroup 1 the one for
 // 128-row tiles.
+// Workgroups 3 and up (launched with a token table only) write the token
+// rows of the routed rows.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups,
                                                           int32_t* tiles256, int32_t* tiles128,
-                                                          int32_t* kcost) {
+                                                          int32_t* kcost, const int32_t* perm,
+                                                          int k, int32_t* tok) {
+  if (blockIdx.x >= 3) {
+    const int R = off[groups];
+    for (int p = (blockIdx.x - 3) * 1024 + threadIdx.x; p < R; p += (gridDim.x - 3) * 1024)
+      tok[p] = (int)((uint32_t)perm[p] / (uint32_t)k);
+    return;
+  }
   const bool cost = blockIdx.x == 2;  // workgroup 2: the weight-gradient cost prefix
   if (cost && kcost == nullptr) return;
   const int bm = blockIdx.x == 0 ? 256 : 128;
@@ -1411,9 +1483,12 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
 }
 
 moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
-                                int32_t* tiles128, int32_t* kcost, hipStream_t s) {
+                                int32_t* tiles128, int32_t* kcost, hipStream_t s,
+                                const int32_t* perm, int k, int32_t* tok, int rows_cap) {
   ProfScope prof("tile_table", s);
-  tile_table_kernel<<<3, 1024, 0, s>>>(off, groups, tiles256, tiles128, kcost);
+  const int extra =
+      perm ? (int)std::min<int64_t>(64, std::max<int64_t>(1, ceil_div(rows_cap, 1024))) : 0;
+  tile_table_kernel<<<3 + extra, 1024, 0, s>>>(off, groups, tiles256, tiles128, kcost, perm, k, tok);
   return check_launch("tile_table_kernel");
 }
 
@@ -1463,7 +1538,11 @@ int tile_bn(TileCfg cfg) {
   X(R_DOWN_WGRAD, "ffn_down_wgrad", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)        \
   X(R_GATEUP_WGRAD, "ffn_gateup_wgrad", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, EPI_STORE)    \
   X(R_ROUTE_DW, "route_bwd_dw", TILE_64x64, A_MC, B_NC, G_KROWS, B2_NONE, EPI_F32_BIAS)            \
-  X(R_ROUTE_DX, "route_bwd_dx", TILE_64x64, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)
+  X(R_ROUTE_DX, "route_bwd_dx", TILE_64x64, A_KC, B_KC, G_DENSE, B2_NONE, EPI_ACCUM)                \
+  X(R_GATEUP_FWD_GATHER, "ffn_gateup_fwd_gather", MOE_TILE_GATEUP_FWD, A_KC, B_NC, G_MROWS, B2_NHALF, \
+    EPI_SWIGLU)                                                                                    \
+  X(R_GATEUP_WGRAD_GATHER, "ffn_gateup_wgrad_gather", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, \
+    EPI_STORE)
 
 // A role may take a second tile shape when its N (output columns) is large:
 // role, tile, smallest N (build-time tunable).
@@ -1511,7 +1590,8 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 // Roles that run the warp-specialised kernel, and roles that run the
 // persistent kernel (bit r = role r; build-time tunable).
 #ifndef MOE_WS_ROLES
-#define MOE_WS_ROLES ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD))
+#define MOE_WS_ROLES \
+  ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD) | (1 << R_GATEUP_WGRAD_GATHER))
 #endif
 #ifndef MOE_PERSIST_ROLES
 #define MOE_PERSIST_ROLES 0

@@ -205,7 +205,7 @@ moe_status_t launch_permute(const int32_t* idx, const void* x, int T, int d, int
     perm_scatter_kernel<<<nb, PERM_TOKENS, lds, s>>>(idx, T, k, e_lo, e_hi, R_cap, counts, perm, inv);
     if ((st = check_launch("perm_scatter_kernel")) != MOE_OK) return st;
   }
-  {
+  if (xp) {  // without xp only the sort runs (the gathered GEMMs read x through perm)
     ProfScope prof("permute_gather", s);
     const int chunks = d * elt_bytes / 16;
     perm_gather_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(

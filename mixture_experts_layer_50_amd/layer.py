@@ -22,6 +22,7 @@ class LayerBuffers:
     shape: B.MoEShape
     device: str = "cuda"
     training: bool = True
+    gather: bool = False  # FFN reads x through perm (the _gather calls); no Xp buffer
     t: Dict[str, torch.Tensor] = field(default_factory=dict)
 
     def __post_init__(self):
@@ -40,7 +41,7 @@ class LayerBuffers:
         t["offsets"] = e(El + 1, dtype=i32)
         t["perm"] = e(R, dtype=i32)
         t["inv"] = e(T * k, dtype=i32)
-        t["xp"] = e(R, d)
+        t["xp"] = None if self.gather else e(R, d)
         t["h"] = e(R, 2 * I) if self.training else None
         t["a"] = e(R, I)
         t["yp"] = e(R, d)
@@ -71,13 +72,18 @@ class LayerBuffers:
 
 def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
             stream=None):
-    """route -> permute -> grouped SwiGLU FFN -> combine; y lands in buf['y']."""
+    """route -> permute -> grouped SwiGLU FFN -> combine; y lands in buf['y'].
+    With buf.gather the permute only sorts and the FFN reads x through perm."""
     t = buf.t
     B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
     B.moe_permute(shape, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"],
                   t["ws_permute"], stream)
-    B.moe_grouped_ffn_fwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
-                          t["yp"], t["ws_ffn_fwd"], stream)
+    if buf.gather:
+        B.moe_grouped_ffn_fwd_gather(shape, x, t["perm"], t["offsets"], w_gate, w_up, w_down,
+                                     t["h"], t["a"], t["yp"], t["ws_ffn_fwd"], stream)
+    else:
+        B.moe_grouped_ffn_fwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
+                              t["yp"], t["ws_ffn_fwd"], stream)
     B.moe_combine(shape, t["yp"], t["inv"], t["topk_w"], t["y"], stream)
 
 
@@ -86,9 +92,14 @@ def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up
     """combine_bwd -> grouped FFN bwd -> permute_bwd -> route_bwd."""
     t = buf.t
     B.moe_combine_bwd(shape, dy, t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"], stream)
-    B.moe_grouped_ffn_bwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
-                          t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"],
-                          t["ws_ffn_bwd"], stream)
+    if buf.gather:
+        B.moe_grouped_ffn_bwd_gather(shape, x, t["perm"], t["offsets"], w_gate, w_up, w_down,
+                                     t["h"], t["a"], t["dyp"], t["dxp"], t["dw_gate"],
+                                     t["dw_up"], t["dw_down"], t["ws_ffn_bwd"], stream)
+    else:
+        B.moe_grouped_ffn_bwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
+                              t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"],
+                              t["ws_ffn_bwd"], stream)
     B.moe_permute_bwd(shape, t["dxp"], t["inv"], t["dx"], stream)
     B.moe_route_bwd(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"], t["dlogits"],
                     t["dw_router"], t["dbias"], t["dx"], t["ws_route_bwd"], stream)

@@ -104,7 +104,8 @@ def test_workspace_sizes_and_short_workspace(lib):
     assert B.workspace_size(s, "permute") == 16 * 128 * 4          # 16 blocks of 256 tokens
     def table(bm):  # one tile table per M-tile height, 256-byte aligned
         return -(-(1 + 2 * (R // bm + 128)) * 4 // 256) * 256
-    tiles = table(256) + table(128) + 768   # + weight-gradient cost prefix [E_loc + 1]
+    # + weight-gradient cost prefix [E_loc + 1] + token row of each routed row (gathered calls)
+    tiles = table(256) + table(128) + 768 + R * 4
     assert B.workspace_size(s, "ffn_fwd") == tiles
     assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + tiles
     assert B.workspace_size(s, "route_bwd") == 0                    # balanced gate: no dL copy
@@ -130,6 +131,10 @@ def test_every_entry_point_validates_before_launch(lib):
         lambda: lib.moe_grouped_ffn_bwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, P, P, P,
                                         1 << 30, None),
         lambda: lib.moe_permute_bwd(ctypes.byref(s), P, P, P, None),
+        lambda: lib.moe_grouped_ffn_fwd_gather(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P,
+                                               1 << 20, None),
+        lambda: lib.moe_grouped_ffn_bwd_gather(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, P,
+                                               P, P, P, 1 << 30, None),
         lambda: lib.moe_route_bwd(ctypes.byref(s), P, P, P, P, P, P, P, P, P, P, 1 << 20, None),
     ]
     for c in calls:
@@ -147,3 +152,33 @@ def test_profiler_api_without_gpu(lib):
     B.prof_reset()
     assert B.prof_read("ffn_gateup_fwd") == (0.0, 0)
     assert B.prof_names() == []
+
+
+def test_gathered_ffn_validation(lib):
+    """The gathered FFN calls need perm, check the 32-bit offsets of x, and
+    moe_permute runs without xp (the sort alone)."""
+    P = FAKE
+    good = shape()
+    st = lib.moe_grouped_ffn_fwd_gather(ctypes.byref(good), P, None, P, P, P, P, P, P, P, P,
+                                        1 << 20, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "perm" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_ffn_fwd_gather(ctypes.byref(good), None, P, P, P, P, P, P, P, P, P,
+                                        1 << 20, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "x is NULL" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_ffn_bwd_gather(ctypes.byref(good), P, None, P, P, P, P, P, P, P, P, P,
+                                        P, P, P, 1 << 30, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "perm" in lib.moe_last_error().decode()
+    # x of 2^31 bytes or more: the gathered form is refused, the plain one is not limited
+    big = shape(T=65536, d=16384, E=8, k=2, I=64)
+    st = lib.moe_grouped_ffn_fwd_gather(ctypes.byref(big), P, P, P, P, P, P, P, P, P, P,
+                                        1 << 40, None)
+    assert B.STATUS[st] == "MOE_ERR_UNSUPPORTED" and "2^31" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_ffn_bwd_gather(ctypes.byref(big), P, P, P, P, P, P, P, P, P, P, P, P,
+                                        P, P, 1 << 40, None)
+    assert B.STATUS[st] == "MOE_ERR_UNSUPPORTED"
+    # permute: xp NULL is the sort alone (x may then be NULL); validation still runs
+    s = shape(k=9)
+    assert B.STATUS[lib.moe_permute(ctypes.byref(s), P, None, P, P, P, None, P, 1 << 20,
+                                    None)] == "MOE_ERR_ARG"
+    st = lib.moe_permute(ctypes.byref(good), P, None, P, P, P, P, P, 1 << 20, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "x is NULL" in lib.moe_last_error().decode()
