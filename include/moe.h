@@ -76,7 +76,8 @@ typedef enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_BALANCED = 1 } moe_gate_t;
 /* Which call a workspace size is asked for. */
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
-  MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7
+  MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7,
+  MOE_OP_SMALL_FWD = 8
 } moe_op_t;
 
 typedef void* moe_stream_t; /* hipStream_t */
@@ -176,6 +177,26 @@ moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, const void* x,
  * yp [R_cap,d]; inv [T*k]; topk_w [T,k] fp32; y [T,d].  No workspace. */
 moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,
                          const float* topk_w, void* y, moe_stream_t stream);
+
+/* a3 + a4 + a5 for a few tokens -- the batched_mm expert backend ([P3] section
+ * 专家后端, backend table: each routed pair multiplies by its own expert's
+ * weights in one batched product, for small inputs).  No sort and no grouped
+ * GEMM: every (token, slot) pair with a local, first-occurrence expert
+ * e = topk_idx[t,j] reads that expert's weights directly, and
+ *   y[t] = sum_j topk_w[t,j] * (silu(x[t] Wg[e]) * (x[t] Wu[e])) Wd[e]
+ * in ascending j with fp32 accumulation (A rounded to the dtype, as in
+ * moe_grouped_ffn_fwd); tokens with no local slot get y[t] = 0.  The same
+ * result as moe_permute + moe_grouped_ffn_fwd + moe_combine within rounding
+ * (the sums run in another order).  x [T,d]; topk_idx, topk_w [T,k];
+ * weights as for moe_grouped_ffn_fwd; y [T,d].  ws:
+ * moe_workspace_size(MOE_OP_SMALL_FWD) (A, the per-slot outputs and the slot
+ * map).  Every pair re-reads its expert's weights, so it pays for T*k up to
+ * about E_loc.  Needs T*k <= 65535, d and I <= 12288 and no row capacity
+ * (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
+moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const int32_t* topk_idx,
+                               const float* topk_w, const void* w_gate, const void* w_up,
+                               const void* w_down, void* y, void* ws, size_t ws_bytes,
+                               moe_stream_t stream);
 
 /* ------------------------------------------------------------ backward */
 /* Full-parameter fine-tuning needs every gradient ([P3] Qwen3 and Nemotron

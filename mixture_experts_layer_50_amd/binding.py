@@ -17,7 +17,7 @@ LIB_NAME = "libmoe.so"
 DTYPES = {"f32": 0, "bf16": 1}
 GATES = {"softmax_topk": 0, "balanced": 1}
 OPS = {"route": 0, "permute": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4, "ffn_bwd": 5,
-       "permute_bwd": 6, "route_bwd": 7}
+       "permute_bwd": 6, "route_bwd": 7, "small_fwd": 8}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED"}
 
@@ -26,7 +26,7 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_
            "moe_route", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine", "moe_combine_bwd",
            "moe_grouped_ffn_bwd", "moe_permute_bwd", "moe_route_bwd", "moe_prof_enable",
            "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names",
-           "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather"]
+           "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd"]
 
 
 class MoEError(RuntimeError):
@@ -89,6 +89,7 @@ def load_library() -> ctypes.CDLL:
         "moe_combine_bwd": [S, P, P, P, P, P, P, P],
         "moe_grouped_ffn_bwd": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_grouped_ffn_fwd_gather": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_ffn_small_fwd": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
         "moe_route_bwd": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -162,6 +163,12 @@ def moe_grouped_ffn_fwd_gather(shape, x, perm, group_offsets, w_gate, w_up, w_do
         ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(group_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(yp), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def moe_ffn_small_fwd(shape, x, topk_idx, topk_w, w_gate, w_up, w_down, y, ws, stream=None):
+    _check("moe_ffn_small_fwd", load_library().moe_ffn_small_fwd(
+        ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_combine(shape, yp, inv, topk_w, y, stream=None):

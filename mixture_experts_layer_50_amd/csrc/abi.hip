@@ -329,6 +329,7 @@ int64_t ws_bytes(const Dims& D, int op) {
     case MOE_OP_FFN_BWD:
       return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
              (D.bf16 ? tile_table_bytes(D) : 0);
+    case MOE_OP_SMALL_FWD: return small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.eb);
     case MOE_OP_ROUTE_BWD: {
       if (D.balanced) return 0;
       const RouteBwdWs r(D);
@@ -355,7 +356,8 @@ extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, siz
   Dims D;
   if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
   MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
-  if (op < MOE_OP_ROUTE || op > MOE_OP_ROUTE_BWD) return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
+  if (op < MOE_OP_ROUTE || op > MOE_OP_SMALL_FWD)
+    return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
   *bytes = (size_t)ws_bytes(D, op);
   return MOE_OK;
 }
@@ -470,6 +472,28 @@ extern "C" moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, con
                                                    moe_stream_t stream) {
   return ffn_fwd("moe_grouped_ffn_fwd_gather", true, shape, x, perm, group_offsets, w_gate, w_up,
                  w_down, h_save, a_save, yp, ws, ws_bytes_, stream);
+}
+
+extern "C" moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x,
+                                          const int32_t* topk_idx, const float* topk_w,
+                                          const void* w_gate, const void* w_up,
+                                          const void* w_down, void* y, void* ws,
+                                          size_t ws_bytes_, moe_stream_t stream) {
+  const char* fn = "moe_ffn_small_fwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"x", x}, {"topk_idx", topk_idx}, {"topk_w", topk_w}, {"w_gate", w_gate},
+                    {"w_up", w_up}, {"w_down", w_down}, {"y", y}}));
+  if ((int64_t)D.T * D.k > SMALL_MAX_PAIRS)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld > %lld (use the grouped FFN)", fn,
+                (long long)D.T * D.k, (long long)SMALL_MAX_PAIRS);
+  if (D.d > SMALL_MAX_WIDTH || D.I > SMALL_MAX_WIDTH)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d and I must be <= %d", fn, SMALL_MAX_WIDTH);
+  if (D.R_cap != D.T * D.k)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: no row capacity (R_cap must be 0 or T*k)", fn);
+  MOE_TRY(check_ws(fn, D, MOE_OP_SMALL_FWD, ws, ws_bytes_));
+  return launch_small_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, D.T, D.d, D.k, D.I, D.e_lo,
+                          D.e_hi, D.eb, y, ws, S(stream));
 }
 
 extern "C" moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,

@@ -37,4 +37,15 @@ moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* i
                                 int T, int d, int k, int elt_bytes, void* dyp, float* dw,
                                 hipStream_t s);
 
+// small.hip: the small-batch FFN (no sort): y[t] = sum_j w[t,j] FFN_e(x[t]) over
+// the local, first-occurrence slots.  Workspace: A [T*k, I], Yp [T*k, d], the
+// slot map [T*k].  Needs T*k <= SMALL_MAX_PAIRS, d and I <= SMALL_MAX_WIDTH.
+constexpr int64_t SMALL_MAX_PAIRS = 65535;
+constexpr int SMALL_MAX_WIDTH = 12288;
+int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int elt_bytes);
+moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_topk,
+                              const void* wg, const void* wu, const void* wd, int T, int d, int k,
+                              int I, int e_lo, int e_hi, int elt_bytes, void* y, void* ws,
+                              hipStream_t s);
+
 }  // namespace moe

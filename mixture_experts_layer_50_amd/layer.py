@@ -87,6 +87,18 @@ def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_u
     B.moe_combine(shape, t["yp"], t["inv"], t["topk_w"], t["y"], stream)
 
 
+def forward_small(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
+                  stream=None):
+    """route -> small-batch FFN with the combine (no sort; for a few tokens);
+    y lands in buf['y']."""
+    t = buf.t
+    if t.get("ws_small_fwd") is None:
+        t["ws_small_fwd"] = buf._ws("small_fwd")
+    B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
+    B.moe_ffn_small_fwd(shape, x, t["topk_idx"], t["topk_w"], w_gate, w_up, w_down, t["y"],
+                        t["ws_small_fwd"], stream)
+
+
 def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up, w_down,
              stream=None):
     """combine_bwd -> grouped FFN bwd -> permute_bwd -> route_bwd."""

@@ -182,3 +182,28 @@ def test_gathered_ffn_validation(lib):
                                     None)] == "MOE_ERR_ARG"
     st = lib.moe_permute(ctypes.byref(good), P, None, P, P, P, P, P, 1 << 20, None)
     assert B.STATUS[st] == "MOE_ERR_ARG" and "x is NULL" in lib.moe_last_error().decode()
+
+
+def test_small_batch_ffn_validation(lib):
+    """moe_ffn_small_fwd: its size limits, no row capacity, its workspace."""
+    P = FAKE
+    s = shape(T=64, d=128, E=8, k=2, I=256)
+    n = B.workspace_size(s, "small_fwd")
+    # A [T*k, I] and the slot outputs [T*k, d] in bf16, the slot map [T*k] int32
+    assert n == 128 * 256 * 2 + 128 * 128 * 2 + 512
+
+    def call(sh, ws_bytes=1 << 30, y=P):
+        return B.STATUS[lib.moe_ffn_small_fwd(ctypes.byref(sh), P, P, P, P, P, P, y, P, ws_bytes,
+                                               None)], lib.moe_last_error().decode()
+
+    assert call(s, y=None) == ("MOE_ERR_ARG", "moe_ffn_small_fwd: y is NULL")
+    st, msg = call(shape(T=40000, d=128, E=8, k=2, I=256))
+    assert st == "MOE_ERR_UNSUPPORTED" and "T*k" in msg
+    st, msg = call(shape(T=4, d=16384, E=8, k=2, I=256))
+    assert st == "MOE_ERR_UNSUPPORTED" and "<=" in msg
+    st, msg = call(shape(T=64, d=128, E=8, k=2, I=256, R_cap=100))
+    assert st == "MOE_ERR_UNSUPPORTED" and "capacity" in msg
+    st, msg = call(s, ws_bytes=n - 1)
+    assert st == "MOE_ERR_WORKSPACE"
+    assert B.STATUS[lib.moe_ffn_small_fwd(ctypes.byref(shape(k=9)), P, P, P, P, P, P, P, P,
+                                          1 << 20, None)] == "MOE_ERR_ARG"

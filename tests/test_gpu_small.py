@@ -1,0 +1,114 @@
+"""GPU parity of the small-batch FFN (moe_ffn_small_fwd, the batched_mm
+backend's counterpart: no sort, every (token, slot) pair reads its expert's
+weights): y against the CPU oracle, and against the grouped path, on the
+parity workloads, at decode sizes of the Qwen3 shape, and with routing tables
+that hold non-local and repeated expert ids."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as MI
+import gpu_util as U
+from mixture_experts_layer_50_amd import binding as B
+from mixture_experts_layer_50_amd.layer import LayerBuffers, forward_small
+from oracle import moe_oracle as O
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"\n[gpu case] small-batch {name}", flush=True)
+    sys.stdout.flush()
+
+
+def run_small(w, dev, R_cap=0):
+    s = U.shape_of(w, R_cap)
+    buf = LayerBuffers(s, training=False)
+    forward_small(s, buf, dev["x"], dev.get("Wr"), dev.get("b"), dev["Wg"], dev["Wu"], dev["Wd"])
+    torch.cuda.synchronize()
+    return s, buf
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_batch_matches_oracle(w):
+    _announce(w.name)
+    a = MI.generate(w, parts=("x", "Wr", "b", "Wg", "Wu", "Wd"))
+    f, _ = U.oracle_full(w, a)
+    dev = U.upload(w, a)
+    _, sb = run_small(w, dev)
+    tol = U.TOL[w.dtype]
+    assert np.array_equal(sb["topk_idx"].cpu().numpy(), f["idx"])
+    e = U.check("y(small)", U.np64(sb["y"]), f["y"], tol)
+    # the grouped path on the same inputs agrees to the same tolerance
+    _, gb = U.run_layer(w, dev, training=False)
+    U.check("y(small) vs y(grouped)", U.np64(sb["y"]), U.np64(gb["y"]), tol)
+    print(f"y rel err {e:.2e}")
+
+
+def _oracle_y(x, idx, g, Wg, Wu, Wd, e_lo, e_hi):
+    """y[t] = sum over the local first-occurrence slots of g * FFN_e(x[t]),
+    one (token, slot) pair at a time with the oracle's expert FFN."""
+    T, k = idx.shape
+    y = np.zeros((T, x.shape[1]))
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if not (e_lo <= e < e_hi) or e in seen:
+                continue
+            seen.add(e)
+            le = e - e_lo
+            f = O.expert_ffn_fwd(x[t:t + 1].astype(np.float64), np.array([0, 1]),
+                                 Wg[le:le + 1], Wu[le:le + 1], Wd[le:le + 1])
+            y[t] += g[t, j] * f["Yp"][0]
+    return y
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_sizes_qwen3_shape(T):
+    """Natural router at the Qwen3 shape on the first T tokens of its workload."""
+    w0 = MI.WORKLOADS["qwen3_natural_fwd_T4096_d2048_E128_k8_I768"]
+    w = MI.Workload(**{**w0.__dict__, "name": f"qwen3_natural_decode_T{T}", "T": T})
+    _announce(w.name)
+    a = MI.generate(w0, parts=("x", "Wr", "b", "Wg", "Wu", "Wd"))
+    a["x"] = a["x"][:T]
+    dev = U.upload(w, a)
+    _, sb = run_small(w, dev)
+    L, idx, g = O.route(a["x"], a["Wr"], a["b"], w.k, w.gate)
+    assert np.array_equal(sb["topk_idx"].cpu().numpy(), idx)
+    ref = _oracle_y(a["x"], idx, g, a["Wg"], a["Wu"], a["Wd"], 0, w.E)
+    U.check("y(small)", U.np64(sb["y"]), ref, U.TOL["bf16"])
+    _, gb = U.run_layer(w, dev, training=False)
+    U.check("y(small) vs y(grouped)", U.np64(sb["y"]), U.np64(gb["y"]), U.TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_routing_table_with_foreign_and_repeated_experts(dtype):
+    """A caller's routing table: slots outside the local range [4, 12) and
+    repeated ids (only the first occurrence counts, as in the permute)."""
+    T, d, E, k, I = 37, 128, 16, 4, 192
+    w = MI.small_workload("table", T, d, E, k, I, dtype=dtype, e_lo=4, e_hi=12, seed=41,
+                          backward=False)
+    _announce(f"routing table {dtype}")
+    a = MI.generate(w, parts=("x", "Wg", "Wu", "Wd"))
+    rng = np.random.default_rng(41)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[3] = [5, 5, 5, 5]
+    idx[4] = [0, 1, 2, 3]            # no local slot: y = 0
+    idx[5] = [11, 4, 11, 4]
+    g = rng.random((T, k)).astype(np.float32)
+    dev = U.upload(w, a)
+    s = U.shape_of(w)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = torch.full((T, d), float("nan"), dtype=dt, device="cuda")
+    ws = torch.empty(B.workspace_size(s, "small_fwd"), dtype=torch.uint8, device="cuda")
+    B.moe_ffn_small_fwd(s, dev["x"], torch.from_numpy(idx).cuda(), torch.from_numpy(g).cuda(),
+                        dev["Wg"], dev["Wu"], dev["Wd"], y, ws)
+    torch.cuda.synchronize()
+    ref = _oracle_y(a["x"], idx, g.astype(np.float64), a["Wg"], a["Wu"], a["Wd"], 4, 12)
+    got = U.np64(y)
+    assert np.all(got[4] == 0)
+    U.check("y", got, ref, U.TOL[dtype])
