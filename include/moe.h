@@ -189,8 +189,8 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t
  * result as moe_permute + moe_grouped_ffn_fwd + moe_combine within rounding
  * (the sums run in another order).  x [T,d]; topk_idx, topk_w [T,k];
  * weights as for moe_grouped_ffn_fwd; y [T,d].  ws:
- * moe_workspace_size(MOE_OP_SMALL_FWD) (A, the per-slot outputs and the slot
- * map).  Every pair re-reads its expert's weights, so it pays for T*k up to
+ * moe_workspace_size(MOE_OP_SMALL_FWD) (fp32 partial sums of [Hg | Hu] over
+ * up to 8 ranges of d, the per-slot outputs and the slot map).  Every pair re-reads its expert's weights, so it pays for T*k up to
  * about E_loc.  Needs T*k <= 65535, d and I <= 12288 and no row capacity
  * (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
 moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const int32_t* topk_idx,

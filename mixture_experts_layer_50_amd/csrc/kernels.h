@@ -38,8 +38,8 @@ moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* i
                                 hipStream_t s);
 
 // small.hip: the small-batch FFN (no sort): y[t] = sum_j w[t,j] FFN_e(x[t]) over
-// the local, first-occurrence slots.  Workspace: A [T*k, I], Yp [T*k, d], the
-// slot map [T*k].  Needs T*k <= SMALL_MAX_PAIRS, d and I <= SMALL_MAX_WIDTH.
+// the local, first-occurrence slots.  Workspace: fp32 gate/up partial sums
+// [T*k, KS, 2I] (KS splits of d), Yp [T*k, d], the slot map [T*k].  Needs T*k <= SMALL_MAX_PAIRS, d and I <= SMALL_MAX_WIDTH.
 constexpr int64_t SMALL_MAX_PAIRS = 65535;
 constexpr int SMALL_MAX_WIDTH = 12288;
 int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int elt_bytes);

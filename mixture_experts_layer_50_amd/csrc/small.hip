@@ -6,9 +6,12 @@
 // tokens the whole FFN is two memory-bound matrix-vector kernels and the
 // combine, instead of the sort, the tile tables and two grouped GEMMs.
 //
-// Kernel 1, one workgroup per (pair, column block of the expert width):
-//   Hg = x[t] Wg[e], Hu = x[t] Wu[e] over the block's columns, A = silu(Hg) Hu.
-// Kernel 2, one workgroup per (pair, column block of d):  Yp[pair] = A Wd[e].
+// Kernel 1, one workgroup per (pair, column block of the expert width, K
+// split): partial sums of Hg = x[t] Wg[e] and Hu = x[t] Wu[e] over the
+// block's columns and one of KS ranges of d (KS > 1 only when there are too
+// few pairs to fill the GPU).
+// Kernel 2, one workgroup per (pair, column block of d): adds the KS partials
+// in order, A = silu(Hg) Hu (rounded to the dtype), then Yp[pair] = A Wd[e].
 // Then the combine kernel sums Yp over each token's slots in ascending slot
 // order.  Inside a workgroup, lane (rs, c) of wave w accumulates the rows
 // r = 8w + rs (mod 32) for its 16-byte column chunk c; the 32 partial sums of
@@ -106,48 +109,46 @@ template <typename ELT>
 __global__ __launch_bounds__(256) void small_gateup_kernel(const ELT* x, const int32_t* idx,
                                                            const ELT* wg, const ELT* wu, int d,
                                                            int I, int k, int e_lo, int e_hi,
-                                                           ELT* a, int32_t* inv) {
+                                                           float* part, int32_t* inv) {
   constexpr int N = Vec16<ELT>::N, CB = 8 * N;
-  const int pair = blockIdx.y;
+  const int pair = blockIdx.y, ks = blockIdx.z, KS = gridDim.z;
   const int le = pair_expert(idx, pair, k, e_lo, e_hi);
-  if (blockIdx.x == 0 && threadIdx.x == 0) inv[pair] = le >= 0 ? pair : -1;
+  if (blockIdx.x == 0 && ks == 0 && threadIdx.x == 0) inv[pair] = le >= 0 ? pair : -1;
   if (le < 0) return;
-  extern __shared__ float smem[];  // x[t] as fp32 (d), then the partial sums
+  extern __shared__ float smem[];  // x[t] over the K range as fp32 (Kc), then the partial sums
+  const int Kc = d / KS, k0 = ks * Kc;
   float* sx = smem;
-  float* red = smem + d;
+  float* red = smem + Kc;
   const int t = pair / k;
-  for (int i = threadIdx.x; i < d; i += 256) sx[i] = Elt<ELT>::load(x + (int64_t)t * d + i);
+  for (int i = threadIdx.x; i < Kc; i += 256) sx[i] = Elt<ELT>::load(x + (int64_t)t * d + k0 + i);
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, rs = lane >> 3, c = lane & 7;
   const int n0 = blockIdx.x * CB;
-  const ELT* const m[2] = {wg + (int64_t)le * d * I + n0, wu + (int64_t)le * d * I + n0};
+  const int64_t base = ((int64_t)le * d + k0) * I + n0;
+  const ELT* const m[2] = {wg + base, wu + base};
   float acc[2][N];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[h][i] = 0.f;
-  gemv_rows<ELT, 2>(m, I, d, sx, w, rs, c, acc);
+  gemv_rows<ELT, 2>(m, I, Kc, sx, w, rs, c, acc);
   // partials: [w][rs][c][h][i]
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < N; ++i) red[(((w * 8 + rs) * 8 + c) * 2 + h) * N + i] = acc[h][i];
   __syncthreads();
-  if (threadIdx.x < CB) {
-    const int col = threadIdx.x;
-    const float g = column_sum<2, N>(red, 0, col);
-    const float u = column_sum<2, N>(red, 1, col);
-    float av;
-    if constexpr (sizeof(ELT) == 2) av = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-    else av = g / (1.0f + expf(-g)) * u;
-    Elt<ELT>::store(a + (int64_t)pair * I + n0 + col, av);
+  if (threadIdx.x < 2 * CB) {
+    const int h = threadIdx.x / CB, col = threadIdx.x % CB;
+    part[(((int64_t)pair * KS + ks) * 2 + h) * I + n0 + col] = column_sum<2, N>(red, h, col);
   }
 }
 
 template <typename ELT>
-__global__ __launch_bounds__(256) void small_down_kernel(const ELT* a, const int32_t* idx,
-                                                         const ELT* wd, int d, int I, int k,
-                                                         int e_lo, int e_hi, ELT* yp) {
+__global__ __launch_bounds__(256) void small_down_kernel(const float* part, int KS,
+                                                         const int32_t* idx, const ELT* wd, int d,
+                                                         int I, int k, int e_lo, int e_hi,
+                                                         ELT* yp) {
   constexpr int N = Vec16<ELT>::N, CB = 8 * N;
   const int pair = blockIdx.y;
   const int le = pair_expert(idx, pair, k, e_lo, e_hi);
@@ -155,7 +156,20 @@ __global__ __launch_bounds__(256) void small_down_kernel(const ELT* a, const int
   extern __shared__ float smem[];  // A[pair] as fp32 (I), then the partial sums
   float* sa = smem;
   float* red = smem + I;
-  for (int i = threadIdx.x; i < I; i += 256) sa[i] = Elt<ELT>::load(a + (int64_t)pair * I + i);
+  for (int i = threadIdx.x; i < I; i += 256) {
+    const float* p = part + (int64_t)pair * KS * 2 * I + i;
+    float g = 0.f, u = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      g += p[(int64_t)ks * 2 * I];
+      u += p[(int64_t)ks * 2 * I + I];
+    }
+    float av;
+    if constexpr (sizeof(ELT) == 2) av = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+    else av = g / (1.0f + expf(-g)) * u;
+    ELT q;
+    Elt<ELT>::store(&q, av);  // A is rounded to the dtype, as the grouped path stores it
+    sa[i] = Elt<ELT>::load(&q);
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, rs = lane >> 3, c = lane & 7;
   const int n0 = blockIdx.x * CB;
@@ -175,9 +189,20 @@ __global__ __launch_bounds__(256) void small_down_kernel(const ELT* a, const int
 
 }  // namespace
 
+// K splits of the gate/up kernel: only when there are too few pairs to give
+// every CU a workgroup (the split costs the down kernel a pass over the
+// partials), each split at least 128 rows of d.
+static int small_ks(int64_t pairs, int d, int I, int elt_bytes) {
+  const int64_t blocks = pairs * (I / (8 * (16 / elt_bytes)));
+  int ks = 1;
+  while (ks < 8 && blocks * ks < 256 && d % (2 * ks * 128) == 0) ks *= 2;
+  return ks;
+}
+
 int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int elt_bytes) {
   const int64_t pairs = (int64_t)T * k;
-  return round_up(pairs * I * elt_bytes, 256) + round_up(pairs * d * elt_bytes, 256) +
+  const int KS = small_ks(pairs, d, I, elt_bytes);
+  return round_up(pairs * KS * 2 * I * 4, 256) + round_up(pairs * d * elt_bytes, 256) +
          round_up(pairs * 4, 256);
 }
 
@@ -186,25 +211,26 @@ moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_
                               int I, int e_lo, int e_hi, int elt_bytes, void* y, void* ws,
                               hipStream_t s) {
   const int64_t pairs = (int64_t)T * k;
+  const int KS = small_ks(pairs, d, I, elt_bytes);
   char* base = static_cast<char*>(ws);
-  void* a = base;
-  void* yp = base + round_up(pairs * I * elt_bytes, 256);
-  int32_t* inv = reinterpret_cast<int32_t*>(base + round_up(pairs * I * elt_bytes, 256) +
-                                            round_up(pairs * d * elt_bytes, 256));
+  float* part = reinterpret_cast<float*>(base);
+  const int64_t part_bytes = round_up(pairs * KS * 2 * I * 4, 256);
+  void* yp = base + part_bytes;
+  int32_t* inv = reinterpret_cast<int32_t*>(base + part_bytes + round_up(pairs * d * elt_bytes, 256));
   const int N = 16 / elt_bytes, CB = 8 * N;
   moe_status_t st;
   {
     ProfScope prof("small_gateup", s);
-    const dim3 grid((unsigned)(I / CB), (unsigned)pairs);
-    const size_t lds = (size_t)(d + 4 * 8 * 8 * 2 * N) * 4;
+    const dim3 grid((unsigned)(I / CB), (unsigned)pairs, (unsigned)KS);
+    const size_t lds = (size_t)(d / KS + 4 * 8 * 8 * 2 * N) * 4;
     if (elt_bytes == 2)
       small_gateup_kernel<bf16_t><<<grid, 256, lds, s>>>(
           static_cast<const bf16_t*>(x), idx, static_cast<const bf16_t*>(wg),
-          static_cast<const bf16_t*>(wu), d, I, k, e_lo, e_hi, static_cast<bf16_t*>(a), inv);
+          static_cast<const bf16_t*>(wu), d, I, k, e_lo, e_hi, part, inv);
     else
       small_gateup_kernel<float><<<grid, 256, lds, s>>>(
           static_cast<const float*>(x), idx, static_cast<const float*>(wg),
-          static_cast<const float*>(wu), d, I, k, e_lo, e_hi, static_cast<float*>(a), inv);
+          static_cast<const float*>(wu), d, I, k, e_lo, e_hi, part, inv);
     if ((st = check_launch("small_gateup_kernel")) != MOE_OK) return st;
   }
   {
@@ -212,13 +238,13 @@ moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_
     const dim3 grid((unsigned)(d / CB), (unsigned)pairs);
     const size_t lds = (size_t)(I + 4 * 8 * 8 * N) * 4;
     if (elt_bytes == 2)
-      small_down_kernel<bf16_t><<<grid, 256, lds, s>>>(
-          static_cast<const bf16_t*>(a), idx, static_cast<const bf16_t*>(wd), d, I, k, e_lo,
-          e_hi, static_cast<bf16_t*>(yp));
+      small_down_kernel<bf16_t><<<grid, 256, lds, s>>>(part, KS, idx,
+                                                       static_cast<const bf16_t*>(wd), d, I, k,
+                                                       e_lo, e_hi, static_cast<bf16_t*>(yp));
     else
-      small_down_kernel<float><<<grid, 256, lds, s>>>(
-          static_cast<const float*>(a), idx, static_cast<const float*>(wd), d, I, k, e_lo, e_hi,
-          static_cast<float*>(yp));
+      small_down_kernel<float><<<grid, 256, lds, s>>>(part, KS, idx, static_cast<const float*>(wd),
+                                                      d, I, k, e_lo, e_hi,
+                                                      static_cast<float*>(yp));
     if ((st = check_launch("small_down_kernel")) != MOE_OK) return st;
   }
   return launch_gather_sum(yp, inv, w_topk, T, d, k, elt_bytes, y, s, "small_combine");

@@ -189,8 +189,12 @@ def test_small_batch_ffn_validation(lib):
     P = FAKE
     s = shape(T=64, d=128, E=8, k=2, I=256)
     n = B.workspace_size(s, "small_fwd")
-    # A [T*k, I] and the slot outputs [T*k, d] in bf16, the slot map [T*k] int32
-    assert n == 128 * 256 * 2 + 128 * 128 * 2 + 512
+    # fp32 [Hg | Hu] partials (one K range at d = 128), the slot outputs
+    # [T*k, d] in bf16, the slot map [T*k] int32
+    assert n == 128 * 2 * 256 * 4 + 128 * 128 * 2 + 512
+    # at T = 1 of the Qwen3 shape (96 column blocks) d splits in 4 ranges
+    n1 = B.workspace_size(shape(T=1, d=2048, E=128, k=8, I=768), "small_fwd")
+    assert n1 == 8 * 4 * 2 * 768 * 4 + 8 * 2048 * 2 + 256
 
     def call(sh, ws_bytes=1 << 30, y=P):
         return B.STATUS[lib.moe_ffn_small_fwd(ctypes.byref(sh), P, P, P, P, P, P, y, P, ws_bytes,
