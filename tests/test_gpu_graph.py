@@ -10,7 +10,7 @@ import torch
 import moe_inputs as MI
 import gpu_util as U
 from mixture_experts_layer_50_amd import binding as B
-from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward
+from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward, forward_small
 
 pytestmark = pytest.mark.gpu
 
@@ -18,22 +18,32 @@ OUTS = ["logits", "topk_idx", "topk_w", "y", "dx", "dw_gate", "dw_up", "dw_down"
         "dw_router", "dbias"]
 
 
-@pytest.mark.parametrize("gate", ["softmax_topk", "balanced"])
-def test_graph_replay_matches_eager(gate):
-    w = MI.small_workload(f"graph_{gate}_T384_d256_E16_k4_I256", 384, 256, 16, 4, 256, gate=gate,
-                          bias_sigma=1.0 if gate == "softmax_topk" else None, seed=31)
+@pytest.mark.parametrize("gate,path", [("softmax_topk", "plain"), ("balanced", "plain"),
+                                       ("softmax_topk", "gather"), ("balanced", "gather"),
+                                       ("softmax_topk", "small")])
+def test_graph_replay_matches_eager(gate, path):
+    """path: plain (permute writes Xp), gather (the FFN reads x through the
+    token table), small (the small-batch forward, no backward)."""
+    w = MI.small_workload(f"graph_{gate}_{path}_T384_d256_E16_k4_I256", 384, 256, 16, 4, 256,
+                          gate=gate, bias_sigma=1.0 if gate == "softmax_topk" else None, seed=31)
     print(f"\n[gpu case] {w.name}", flush=True)
     sys.stdout.flush()
     dev = U.upload(w, MI.generate(w))
     shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate)
-    buf = LayerBuffers(shape, training=True)
+    buf = LayerBuffers(shape, training=path != "small", gather=path == "gather")
 
     def step():
+        if path == "small":
+            forward_small(shape, buf, dev["x"], dev.get("Wr"), dev.get("b"), dev["Wg"], dev["Wu"],
+                          dev["Wd"])
+            return
         forward(shape, buf, dev["x"], dev.get("Wr"), dev.get("b"), dev["Wg"], dev["Wu"], dev["Wd"])
         backward(shape, buf, dev["dY"], dev["x"], dev.get("Wr"), dev["Wg"], dev["Wu"], dev["Wd"])
 
-    # outputs the gate writes (the balanced gate computes no logits)
+    # outputs the path writes (the balanced gate computes no logits)
     outs = [k for k in OUTS if buf.t.get(k) is not None and not (gate == "balanced" and k == "logits")]
+    if path == "small":
+        outs = ["logits", "topk_idx", "topk_w", "y"]
     step()
     torch.cuda.synchronize()
     ref = {k: buf[k].clone() for k in outs}
