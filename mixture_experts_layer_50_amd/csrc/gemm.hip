@@ -1546,7 +1546,12 @@ int tile_bn(TileCfg cfg) {
 
 // A role may take a second tile shape when its N (output columns) is large:
 // role, tile, smallest N (build-time tunable).
-#define MOE_GEMM_ALT_TILES(X) X(R_DOWN_DGRAD, TILE_256x256, 1536)
+// (down dgrad: the 256x256 tile from N = 768 on; at N = 768 it reads the dYp
+// rows three times instead of six)
+#ifndef MOE_DOWN_DGRAD_WIDE_N
+#define MOE_DOWN_DGRAD_WIDE_N 768
+#endif
+#define MOE_GEMM_ALT_TILES(X) X(R_DOWN_DGRAD, TILE_256x256, MOE_DOWN_DGRAD_WIDE_N)
 
 constexpr int role_alt_tile(GemmRole role) {
 #define X(r, t, nmin) \

@@ -34,8 +34,9 @@ SMALL = [
     MI.small_workload("skewed_T640_d192_E64_k6_I320", 640, 192, 64, 6, 320, bias_sigma=2.5, seed=26),
     MI.small_workload("f32_natural_T200_d128_E16_k3_I192", 200, 128, 16, 3, 192, dtype="f32",
                       bias_sigma=1.0, seed=27, x_sigma=0.5),
-    # expert width >= 1536: the wide tile of the dSwiGLU GEMM, ragged groups
+    # expert width >= 768: the wide tile of the dSwiGLU GEMM, ragged groups
     MI.small_workload("wide_I_T300_d128_E8_k2_I1536", 300, 128, 8, 2, 1536, bias_sigma=1.0, seed=28),
+    MI.small_workload("wide_I_T260_d192_E8_k2_I768", 260, 192, 8, 2, 768, bias_sigma=1.0, seed=41),
 ]
 
 
