@@ -108,19 +108,28 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
                                                            float* db_part) {
   __shared__ float part[4][64 * VPL];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int TPW = ROUTE_BWD_TOKENS / 4;  // tokens per wave
+  const int t0 = blockIdx.x * ROUTE_BWD_TOKENS + wave * TPW;
+  // every token's slot data first (the loads in flight together)
+  float gq[TPW], dgq[TPW];
+  int iq[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const bool ok = t0 + i < T && lane < k;
+    const int64_t o = (int64_t)(t0 + i) * k + lane;
+    gq[i] = ok ? g[o] : 0.f;
+    dgq[i] = ok ? dg[o] : 0.f;
+    iq[i] = ok ? idx[o] : -1;
+  }
   float col[VPL];
 #pragma unroll
   for (int q = 0; q < VPL; ++q) col[q] = 0.f;
-  for (int i = 0; i < ROUTE_BWD_TOKENS / 4; ++i) {
-    const int t = blockIdx.x * ROUTE_BWD_TOKENS + wave * (ROUTE_BWD_TOKENS / 4) + i;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = t0 + i;
     if (t >= T) break;  // uniform per wave
-    float gj = 0.f, dgj = 0.f;
-    int ij = -1;
-    if (lane < k) {
-      gj = g[(int64_t)t * k + lane];
-      dgj = dg[(int64_t)t * k + lane];
-      ij = idx[(int64_t)t * k + lane];
-    }
+    const float gj = gq[i], dgj = dgq[i];
+    const int ij = iq[i];
     float sum = gj * dgj;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
@@ -162,42 +171,42 @@ moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float
 // Final sums of the router backward, each in a fixed order:
 // dw[i] = sum_s dw_part[s][i] (split-K partials of x^T dL, when nsplit > 0),
 // db[e] = sum_b db_part[b][e] (per-workgroup column sums of dL, when db).
+// dw[i] = sum of the nsplit partials (in split order), for the first nb_dw
+// workgroups; db[e] = sum over the nblk block partials, one wavefront per
+// expert: lane l adds blocks l, l + 64, ... in order, then the lanes are
+// combined by a fixed butterfly.  Deterministic either way.
 __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(const float* dw_part, int nsplit,
                                                                int64_t n_dw, bf16_t* dw,
                                                                const float* db_part, int nblk,
-                                                               int E, float* db) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t nw = nsplit > 0 ? n_dw : 0;  // dw outputs, then the E bias outputs
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nw + (db ? E : 0);
-       i += stride) {
-    if (i < nw) {
+                                                               int E, float* db, int nb_dw) {
+  if ((int)blockIdx.x < nb_dw) {
+    const int64_t stride = (int64_t)nb_dw * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_dw; i += stride) {
       float v = 0.f;
       for (int sp = 0; sp < nsplit; ++sp) v += dw_part[(int64_t)sp * n_dw + i];
       dw[i] = f2bf(v);
-    } else {
-      const int e = (int)(i - nw);
-      constexpr int U = 8;  // partial rows in flight
-      float v = 0.f;
-      for (int b0 = 0; b0 < nblk; b0 += U) {
-        float c[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) c[u] = b0 + u < nblk ? db_part[(int64_t)(b0 + u) * E + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) v += c[u];
-      }
-      db[e] = v;
     }
+    return;
   }
+  const int lane = threadIdx.x & 63;
+  const int e = ((int)blockIdx.x - nb_dw) * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;  // uniform per wave
+  float v = 0.f;
+  for (int b = lane; b < nblk; b += 64) v += db_part[(int64_t)b * E + e];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) db[e] = v;
 }
 
 moe_status_t launch_route_bwd_reduce(const float* dw_part, int nsplit, int64_t n_dw, bf16_t* dw,
                                      const float* db_part, int nblk, int E, float* db,
                                      hipStream_t s) {
-  const int64_t n = (nsplit > 0 ? n_dw : 0) + (db ? E : 0);
-  if (n == 0) return MOE_OK;
+  const int nb_dw = nsplit > 0 ? (int)std::min<int64_t>(ceil_div(n_dw, 256), 2048) : 0;
+  const int nb_db = db ? (int)ceil_div(E, 4) : 0;
+  if (nb_dw + nb_db == 0) return MOE_OK;
   ProfScope prof("route_bwd_reduce", s);
-  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n, 256), 2048);
-  route_bwd_reduce_kernel<<<grid, 256, 0, s>>>(dw_part, nsplit, n_dw, dw, db_part, nblk, E, db);
+  route_bwd_reduce_kernel<<<nb_dw + nb_db, 256, 0, s>>>(dw_part, nsplit, n_dw, dw, db_part, nblk,
+                                                        E, db, nb_dw);
   return check_launch("route_bwd_reduce_kernel");
 }
 
