@@ -861,7 +861,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
   static_assert(B2 != B2_NHALF || FN % 2 == 0, "gate|up halves need an even block count");
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- which tile
@@ -869,6 +869,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
   if ((int)blockIdx.x >= count) return;
   const TileDesc t = tile_desc<BM, BN, GMD, B2>(p, remap_xcd(blockIdx.x, count));
   const int e = t.e, m_lo = t.m_lo, m_hi = t.m_hi, n0 = t.n0, k_lo = t.k_lo, k_hi = t.k_hi;
+  // A wave whose rows all lie at or past the tile's last valid row (the
+  // ragged last tile of a group) skips the MFMAs; it still loads and stores
+  // its share of each slice and takes part in every barrier.
+  const bool wave_rows = wm * WTM < m_hi - m_lo;
 
   typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
   typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
@@ -912,8 +916,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
     // keep the refill loads at the top of the step: the scheduler would
     // otherwise sink them below the MFMAs and expose their latency
     __builtin_amdgcn_sched_barrier(0);
-    mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn, lane,
-                                             m_hi - m_lo);
+    if (wave_rows)
+      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn, lane,
+                                               m_hi - m_lo);
     __builtin_amdgcn_sched_barrier(0);
     if (do_store) {
       bf16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BK;
