@@ -134,18 +134,21 @@ struct LoaderKC {
       voff[i] = ok ? (int)(((int64_t)row * ld + (q & 7) * 8) * 2) : OOB;
     }
   }
-  // K slice starting at k_lo + kofs
-  __device__ __forceinline__ void load(Data& d, int kofs, int tid) const {
+  // K slice starting at k_lo + kofs; load_part<J, NJ> sends the loads i
+  // with i mod NJ == J only (a slice in NJ parts)
+  template <int J, int NJ>
+  __device__ __forceinline__ void load_part(Data& d, int kofs, int tid) const {
     int k0 = k_lo + kofs;
     __amdgpu_buffer_rsrc_t rs = rs0;
     int lim = k_hi - k0;
     if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = J; i < NR; i += NJ) {
       const int kc = ((tid + NT * i) & 7) * 8;
       d.r[i] = buf_load16<CPOL>(rs, kc < lim ? voff[i] : OOB, k0 * 2);
     }
   }
+  __device__ __forceinline__ void load(Data& d, int kofs, int tid) const { load_part<0, 1>(d, kofs, tid); }
   __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -215,7 +218,7 @@ struct LoaderKN {
     if constexpr (GATHER) {
       rows = rows_;
       wrow = __builtin_amdgcn_readfirstlane((tid >> 6) * (64 / CPR));
-      prefetch(0);
+      if (k_hi > k_lo) prefetch(0);  // an empty K range has no row numbers
     }
   }
   __device__ __forceinline__ void load(Data& d, int kofs, int tid) {
@@ -233,9 +236,16 @@ struct LoaderKN {
       if (kofs + BK < k_hi - k_lo) prefetch(kofs + BK);
       return;
     }
+    load_part<0, 1>(d, kofs, tid);
+  }
+  // the loads i with i mod NJ == J only (not for GATHER)
+  template <int J, int NJ>
+  __device__ __forceinline__ void load_part(Data& d, int kofs, int tid) const {
+    static_assert(!GATHER || NJ == 1, "gathered rows load whole slices");
+    const int lim = k_hi - k_lo - kofs;
     const int soff = (int)((int64_t)kofs * ld * 2);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = J; i < NS; i += NJ) {
       const int v = (tid + NT * i) / CPR < lim ? voff[i] : OOB;
       d.r[i] = buf_load16<CPOL>(rs0, v, soff);
       if (HALF) d.r[NS + i] = buf_load16<CPOL>(rs1, v, soff);
@@ -442,10 +452,18 @@ __device__ __forceinline__ void load_frags(bf16x8 (&af)[FM], bf16x8 (&bfg)[FN], 
 // `rows`: the tile's valid rows.  With PIPE, 32-row blocks at or past it are
 // skipped (the other form computes padding rows too: testing for them there
 // cost more registers than it saved).
+struct NoHook {
+  template <typename K>
+  __device__ __forceinline__ void operator()(K) const {}
+};
+
+// `hook(integral_constant<ks>)` runs before MFMA step ks (the other form);
+// with `active` false only the hooks run.
 template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, bool PIPE = false, int FM,
-          int FN>
+          int FN, typename Hook = NoHook>
 __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* as, int wm, int wn,
-                                          int lane, int rows) {
+                                          int lane, int rows, Hook hook = Hook(),
+                                          bool active = true) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static_assert(FM == WTM / 32 && FN == WTN / 32, "accumulator blocks match the wave tile");
   constexpr int KS = BK / 16;
@@ -470,8 +488,10 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* a
       }
     }
   } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    auto kstep = [&](auto ksc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(ksc)::value;
+      hook(ksc);
+      if (!active) return;
       bf16x8 af[FM], bfg[FN];
       load_frags<BM, BN, WGM, WGN, AM, BMD, B2, false>(af, bfg, as, ks, wm, wn, lane, BM);
 #pragma unroll
@@ -479,7 +499,10 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* a
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
-    }
+    };
+    [&]<int... Ks>(std::integer_sequence<int, Ks...>) __attribute__((always_inline)) {
+      (kstep(std::integral_constant<int, Ks>{}), ...);
+    }(std::make_integer_sequence<int, KS>{});
   }
 }
 
@@ -852,6 +875,14 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
 // With the gate|up halves (B2_NHALF) the first FN/2 column blocks of a wave
 // are gate columns and the last FN/2 the matching up columns.
 // ---------------------------------------------------------------------------
+// Refill loads of gemm_bf16_kernel's steady state: 0 = all at the top of the
+// step; 1 = two parts, before MFMA steps 0 and 2; 2 = four parts, one per MFMA
+// step (build-time tunable).  Eight waves sending a whole slice of loads at
+// once fill the memory pipeline's address queue and stall their own MFMA
+// issue; parts spread the loads over the step.
+#ifndef MOE_LOAD_SPLIT
+#define MOE_LOAD_SPLIT 1
+#endif
 template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = 64 * WGM * WGN;
@@ -891,34 +922,54 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (k_hi - k_lo + BK - 1) / BK;
+  // The first P slices load (and slice 0 is stored) unconditionally: slices
+  // past the K range read as zeros without touching memory.  Guarding them
+  // would leave loads that are never waited for on the guarded path, and the
+  // compiler, merging that path into the loop, would then wait for the
+  // previous step's loads at the top of every step.
 #pragma unroll
   for (int s = 0; s < P; ++s) {
-    if (s < nk) {
-      la.load(da[s], s * BK, tid);
-      lb.load(db[s], s * BK, tid);
-    }
+    la.load(da[s], s * BK, tid);
+    lb.load(db[s], s * BK, tid);
   }
-  if (nk > 0) {
-    LA::store(da[0], smem, tid);
-    LB::store(db[0], smem + BM * BK, tid);
-  }
+  LA::store(da[0], smem, tid);
+  LB::store(db[0], smem + BM * BK, tid);
   __syncthreads();
 
   // One K slice: refill the register slot of slice kt with slice kt+P, multiply
   // slice kt from LDS, write slice kt+1 (loaded P-1 slices ago) to the other
   // LDS buffer, barrier.  U = kt mod P is a compile-time constant.
-  auto step = [&](auto Uc, int kt, bool do_load, bool do_store) __attribute__((always_inline)) {
+  auto step = [&](auto Uc, auto Sc, int kt, bool do_load, bool do_store)
+                  __attribute__((always_inline)) {
     constexpr int U = decltype(Uc)::value;
-    if (do_load) {
-      la.load(da[U], (kt + P) * BK, tid);
-      lb.load(db[U], (kt + P) * BK, tid);
-    }
-    // keep the refill loads at the top of the step: the scheduler would
-    // otherwise sink them below the MFMAs and expose their latency
-    __builtin_amdgcn_sched_barrier(0);
-    if (wave_rows)
+    if constexpr (!decltype(Sc)::value) {
+      if (do_load) {
+        la.load(da[U], (kt + P) * BK, tid);
+        lb.load(db[U], (kt + P) * BK, tid);
+      }
+      // keep the refill loads at the top of the step: the scheduler would
+      // otherwise sink them below the MFMAs and expose their latency
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave_rows)
+        mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn,
+                                                 lane, m_hi - m_lo);
+    } else {
+      // steady state (every step loads): the refill loads go out in parts
+      // between the MFMA steps, each part pinned in place
+      auto hook = [&](auto ksc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr int NJ = MOE_LOAD_SPLIT == 1 ? 2 : 4;
+        if constexpr (ks % (4 / NJ) == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          la.template load_part<ks / (4 / NJ), NJ>(da[U], (kt + P) * BK, tid);
+          lb.template load_part<ks / (4 / NJ), NJ>(db[U], (kt + P) * BK, tid);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      __builtin_amdgcn_sched_barrier(0);
       mma_slice<BM, BN, WGM, WGN, AM, BMD, B2>(acc, smem + (kt & 1) * (BM + BN) * BK, wm, wn, lane,
-                                               m_hi - m_lo);
+                                               m_hi - m_lo, hook, wave_rows);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (do_store) {
       bf16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BK;
@@ -932,13 +983,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
   // steady state: every step loads and stores
   for (; kt0 + 2 * P <= nk; kt0 += P) {
     [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
-      (step(std::integral_constant<int, Us>{}, kt0 + Us, true, true), ...);
+      (step(std::integral_constant<int, Us>{}, std::bool_constant<MOE_LOAD_SPLIT != 0>{}, kt0 + Us,
+            true, true),
+       ...);
     }(std::make_integer_sequence<int, P>{});
   }
   // drain: at most 2P-1 slices left
   [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
-    ((kt0 + Us < nk ? step(std::integral_constant<int, Us % P>{}, kt0 + Us, kt0 + Us + P < nk,
-                           kt0 + Us + 1 < nk)
+    ((kt0 + Us < nk ? step(std::integral_constant<int, Us % P>{}, std::false_type{}, kt0 + Us,
+                           kt0 + Us + P < nk, kt0 + Us + 1 < nk)
                     : void()),
      ...);
   }(std::make_integer_sequence<int, 2 * P - 1>{});
