@@ -83,8 +83,13 @@ __device__ __forceinline__ int kn_swz(int k, int c) {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int OOB = (int)0x80000000u;
 
+// A buffer descriptor over `nrec` bytes from `base` (the hardware range check
+// covers the vector offset; loads at or past nrec return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, int nrec) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  return make_rsrc_n(base, 0x7fffffff);
 }
 
 // CPOL: cache-policy bits of the load (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
@@ -108,7 +113,7 @@ __device__ __forceinline__ int ld_table(const int32_t* tab, int i) { return ((ci
 // GATHER: tile row r is row rows[row0 + r] of the source (the rows of Xp
 // read from x through the token table); the row numbers are loaded once per
 // tile.
-template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER>
+template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER, bool FULLK>
 struct LoaderKC {
   static_assert(!(GATHER && TWO), "a gathered operand has one source");
   static constexpr int CH = ROWS * 8;
@@ -116,12 +121,15 @@ struct LoaderKC {
   struct Data { uint4 r[NR]; };
   int voff[NR];
   __amdgpu_buffer_rsrc_t rs0, rs1;
+  const bf16_t *p0, *p1;  // FULLK: the sources at the tile's first row
   int ksplit, k_lo, k_hi;
   __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
                                        int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid,
                                        const int32_t* rows) {
-    rs0 = make_rsrc(GATHER ? s0 : s0 + (int64_t)row0 * ld);
-    rs1 = make_rsrc(TWO ? s1 + (int64_t)row0 * ld : s0);
+    p0 = GATHER ? s0 : s0 + (int64_t)row0 * ld;
+    p1 = TWO ? s1 + (int64_t)row0 * ld : p0;
+    rs0 = make_rsrc(p0);
+    rs1 = make_rsrc(p1);
     ksplit = ksplit_;
     k_lo = k_lo_;
     k_hi = k_hi_;
@@ -135,17 +143,29 @@ struct LoaderKC {
     }
   }
   // K slice starting at k_lo + kofs; load_part<J, NJ> sends the loads i
-  // with i mod NJ == J only (a slice in NJ parts)
+  // with i mod NJ == J only (a slice in NJ parts).  FULLK (K a multiple of
+  // 64): a slice lies wholly inside K or wholly past it, and one past it
+  // gets an empty descriptor, so each load takes its precomputed offset as
+  // is (a per-load select would write a temporary right before the load,
+  // which the compiler then orders behind every load in flight).
   template <int J, int NJ>
   __device__ __forceinline__ void load_part(Data& d, int kofs, int tid) const {
     int k0 = k_lo + kofs;
-    __amdgpu_buffer_rsrc_t rs = rs0;
     int lim = k_hi - k0;
-    if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
+    if constexpr (FULLK) {
+      const bf16_t* b = p0;
+      if (TWO && k0 >= ksplit) { b = p1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(b, lim > 0 ? 0x7fffffff : 0);
 #pragma unroll
-    for (int i = J; i < NR; i += NJ) {
-      const int kc = ((tid + NT * i) & 7) * 8;
-      d.r[i] = buf_load16<CPOL>(rs, kc < lim ? voff[i] : OOB, k0 * 2);
+      for (int i = J; i < NR; i += NJ) d.r[i] = buf_load16<CPOL>(rs, voff[i], k0 * 2);
+    } else {
+      __amdgpu_buffer_rsrc_t rs = rs0;
+      if (TWO && k0 >= ksplit) { rs = rs1; k0 -= ksplit; lim = k_hi - ksplit - k0; }
+#pragma unroll
+      for (int i = J; i < NR; i += NJ) {
+        const int kc = ((tid + NT * i) & 7) * 8;
+        d.r[i] = buf_load16<CPOL>(rs, kc < lim ? voff[i] : OOB, k0 * 2);
+      }
     }
   }
   __device__ __forceinline__ void load(Data& d, int kofs, int tid) const { load_part<0, 1>(d, kofs, tid); }
@@ -167,12 +187,18 @@ struct LoaderKC {
 // [COLS/2, COLS) from s1 at col0 + c - COLS/2 (the gate | up halves); each
 // load instruction reads one half only, so its buffer descriptor is uniform.
 //
+// Rows past k_hi: by default each K slice gets its own descriptor whose
+// record count ends at the last valid row, so a load takes its precomputed
+// offset as is.  SEL masks them with a per-load select instead (a temporary
+// written right before the load; the compiler then orders it behind loads
+// in flight, which measured faster where the A operand is gathered).
+//
 // GATHER: row k of the K range is row rows[k] of the source.  The lanes
 // of one wave cover 64 / CPR consecutive rows per load, so each wave reads
 // its row numbers with scalar loads, one K slice ahead of the data loads
 // (scalar loads retire through their own counter, so waiting for them never
 // waits for data loads in flight).
-template <int COLS, bool HALF, int NT, int CPOL, bool GATHER>
+template <int COLS, bool HALF, int NT, int CPOL, bool GATHER, bool SEL>
 struct LoaderKN {
   static constexpr int CPR = HALF ? COLS / 16 : COLS / 8;  // chunks per row and source
   static constexpr int CH = BK * CPR;                        // chunks per source
@@ -182,8 +208,9 @@ struct LoaderKN {
   static_assert(!GATHER || (!HALF && 64 % CPR == 0 && NT % 64 == 0 && CH % NT == 0),
                 "gathered rows: whole rows per wave");
   struct Data { uint4 r[NR]; };
-  int voff[NS];
-  __amdgpu_buffer_rsrc_t rs0, rs1;
+  int voff[NS];  // byte offset of the lane's chunk from the slice's first row (OOB: masked column)
+  __amdgpu_buffer_rsrc_t rs0, rs1;  // GATHER, SEL
+  const bf16_t *p0, *p1;            // the sources at (k_lo, col0)
   int64_t ld;
   int k_lo, k_hi;
   const int32_t* rows;
@@ -206,8 +233,10 @@ struct LoaderKN {
     ld = ld_;
     k_lo = k_lo_;
     k_hi = k_hi_;
-    rs0 = make_rsrc(s0 + (GATHER ? 0 : (int64_t)k_lo * ld) + col0);
-    rs1 = make_rsrc((HALF ? s1 : s0) + (int64_t)k_lo * ld + col0);
+    p0 = s0 + (int64_t)k_lo * ld + col0;
+    p1 = (HALF ? s1 : s0) + (int64_t)k_lo * ld + col0;
+    rs0 = make_rsrc(GATHER ? s0 + col0 : p0);
+    rs1 = make_rsrc(p1);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       int q = tid + NT * i;
@@ -221,9 +250,10 @@ struct LoaderKN {
       if (k_hi > k_lo) prefetch(0);  // an empty K range has no row numbers
     }
   }
+  // K slice starting at k_lo + kofs
   __device__ __forceinline__ void load(Data& d, int kofs, int tid) {
-    const int lim = k_hi - k_lo - kofs;
     if constexpr (GATHER) {
+      const int lim = k_hi - k_lo - kofs;
       const int sub = (tid & 63) / CPR;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -243,12 +273,23 @@ struct LoaderKN {
   __device__ __forceinline__ void load_part(Data& d, int kofs, int tid) const {
     static_assert(!GATHER || NJ == 1, "gathered rows load whole slices");
     const int lim = k_hi - k_lo - kofs;
-    const int soff = (int)((int64_t)kofs * ld * 2);
+    if constexpr (SEL) {
+      const int soff = (int)((int64_t)kofs * ld * 2);
 #pragma unroll
-    for (int i = J; i < NS; i += NJ) {
-      const int v = (tid + NT * i) / CPR < lim ? voff[i] : OOB;
-      d.r[i] = buf_load16<CPOL>(rs0, v, soff);
-      if (HALF) d.r[NS + i] = buf_load16<CPOL>(rs1, v, soff);
+      for (int i = J; i < NS; i += NJ) {
+        const int v = (tid + NT * i) / CPR < lim ? voff[i] : OOB;
+        d.r[i] = buf_load16<CPOL>(rs0, v, soff);
+        if (HALF) d.r[NS + i] = buf_load16<CPOL>(rs1, v, soff);
+      }
+    } else {
+      const int nrec = lim <= 0 ? 0 : lim >= BK ? 0x7fffffff : (int)((int64_t)lim * ld * 2);
+      const __amdgpu_buffer_rsrc_t r0 = make_rsrc_n(p0 + (int64_t)kofs * ld, nrec);
+      const __amdgpu_buffer_rsrc_t r1 = make_rsrc_n(p1 + (int64_t)kofs * ld, nrec);
+#pragma unroll
+      for (int i = J; i < NS; i += NJ) {
+        d.r[i] = buf_load16<CPOL>(r0, voff[i], 0);
+        if (HALF) d.r[NS + i] = buf_load16<CPOL>(r1, voff[i], 0);
+      }
     }
   }
   __device__ __forceinline__ static void store(const Data& d, bf16_t* lds, int tid) {
@@ -266,11 +307,17 @@ struct LoaderKN {
   }
 };
 
-template <bool KC, int ROWS, bool TWO, int NT, int CPOL, bool GATHER> struct PickLoader;
-template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER>
-struct PickLoader<true, ROWS, TWO, NT, CPOL, GATHER> { typedef LoaderKC<ROWS, TWO, NT, CPOL, GATHER> type; };
-template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER>
-struct PickLoader<false, ROWS, TWO, NT, CPOL, GATHER> { typedef LoaderKN<ROWS, TWO, NT, CPOL, GATHER> type; };
+// FULLK: K is a multiple of 64 (KC loaders); SEL: per-load row selects (KN)
+template <bool KC, int ROWS, bool TWO, int NT, int CPOL, bool GATHER, bool FULLK, bool SEL>
+struct PickLoader;
+template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER, bool FULLK, bool SEL>
+struct PickLoader<true, ROWS, TWO, NT, CPOL, GATHER, FULLK, SEL> {
+  typedef LoaderKC<ROWS, TWO, NT, CPOL, GATHER, FULLK> type;
+};
+template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER, bool FULLK, bool SEL>
+struct PickLoader<false, ROWS, TWO, NT, CPOL, GATHER, FULLK, SEL> {
+  typedef LoaderKN<ROWS, TWO, NT, CPOL, GATHER, SEL> type;
+};
 
 // MFMA operand fragment (32 rows x 16 k): lane l holds row base + (l & 31),
 // k = 16 ks + 8 (l >> 5) + 0..7.
@@ -396,12 +443,17 @@ __device__ __forceinline__ void xcd_tile_range(const GemmParams& p, int count, i
 // are re-read by every column tile of the expert and stay cached.
 // The gather roles read the rows of A through a_rows.
 constexpr bool gathers_a(int role) { return role == R_GATEUP_FWD_GATHER || role == R_GATEUP_WGRAD_GATHER; }
+// Roles whose k-contiguous operands have K a multiple of 64 (d or I, which
+// the entry points require to be); the router's input gradient runs over the
+// E expert logits instead.
+constexpr bool full_k(int role) { return role != R_ROUTE_DX; }
 
-template <int BM, int BN, int NT, int AM, int BMD, int GMD, int B2, bool AG>
+template <int BM, int BN, int NT, int AM, int BMD, int GMD, int B2, bool AG, bool FK>
 struct Loaders {
   static constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
-  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0, AG>::type LA;
-  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL, false>::type LB;
+  // next to a gathered A operand, B keeps per-load selects (measured faster)
+  typedef typename PickLoader<AM == A_KC, BM, false, NT, 0, AG, FK, AG>::type LA;
+  typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL, false, FK, AG>::type LB;
 };
 
 template <int GMD, int B2, typename LA, typename LB>
@@ -905,8 +957,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
   // its share of each slice and takes part in every barrier.
   const bool wave_rows = wm * WTM < m_hi - m_lo;
 
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE), full_k(ROLE)>::LA LA;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE), full_k(ROLE)>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[P];
@@ -1056,8 +1108,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(Ge
   xcd_tile_range<GMD>(p, count, xcd, x_lo, x_n);
   if (slot >= x_n) return;
 
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
-  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE), full_k(ROLE)>::LA LA;
+  typedef typename Loaders<BM, BN, NT, AM, BMD, GMD, B2, gathers_a(ROLE), full_k(ROLE)>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[2];
@@ -1220,8 +1272,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
 
   // ---- producer state: loaders, PD register stages, load cursor
   static_assert(PD >= 2, "at least two register stages");
-  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2, gathers_a(ROLE)>::LA LA;
-  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2, gathers_a(ROLE)>::LB LB;
+  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2, gathers_a(ROLE), full_k(ROLE)>::LA LA;
+  typedef typename Loaders<BM, BN, NTP, AM, BMD, GMD, B2, gathers_a(ROLE), full_k(ROLE)>::LB LB;
   LA la;
   LB lb;
   typename LA::Data da[PD];
