@@ -32,6 +32,9 @@ What the layer computes, with the passage each step follows:
 * Combine: dispatch and combine are the two token-movement steps that DeepEP
   fuses ([P3] section 加速来源, DeepEP item); combine is the gate-weighted sum
   of a token's expert outputs.
+* Auxiliary load-balancing loss (optional, natural gate): named by [P1]
+  section 延伸觀點 and the routing-gate note of [P3]; the formula is the
+  Switch Transformer balancing loss (see ``aux_loss``).
 * Backward: full-parameter fine-tuning reports a separate backward time
   ([P3] Qwen3 and Nemotron tables, row 平均反向); the gradients below are the
   exact derivatives of the forward definition.
@@ -251,15 +254,66 @@ def permute_bwd(dXp, inv, T, k):
 
 
 # ----------------------------------------------------------------------------
+# load-balancing auxiliary loss
+# ----------------------------------------------------------------------------
+def softmax_rows(L):
+    """Softmax of every row of L over all of its entries (max subtracted)."""
+    L = _f64(L)
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def aux_loss(L, idx, E, alpha):
+    """Load-balancing auxiliary loss of the router.
+
+    The pages name the practice but not a formula: an auxiliary loss keeps
+    the naturally uneven routing even while fine-tuning ([P1] section
+    延伸觀點), and a trained model's load-balancing loss drives expert
+    utilisation toward uniform ([P3] section 单节点30B MoE基准测试,
+    routing-gate note).  This oracle takes the differentiable balancing loss
+    of the Switch Transformer (Fedus, Zoph and Shazeer, 2021), the k routed
+    slots of a token counted as k dispatches:
+
+        f_e  = c_e / (T k)            share of the T*k routed rows on expert e
+                                      (c_e counted over all E experts),
+        P_e  = (1/T) sum_t p[t, e]    mean router probability, p = softmax of
+                                      the full logit row,
+        loss = alpha * E * sum_e f_e P_e.
+
+    The counts are piecewise constant in the logits, so the gradient flows
+    through P only; w_e = alpha * E * f_e / T is its weight per probability.
+    """
+    L = _f64(L)
+    T = L.shape[0]
+    k = idx.shape[1]
+    p = softmax_rows(L)
+    c = np.bincount(np.asarray(idx, dtype=np.int64).ravel(), minlength=E).astype(np.float64)
+    f = c / (T * k)
+    P = p.mean(axis=0)
+    return dict(loss=float(alpha * E * np.sum(f * P)), f=f, P=P, w=alpha * E * f / T, counts=c)
+
+
+def aux_loss_dlogits(L, w):
+    """Gradient of the auxiliary loss with respect to the logits:
+    d loss / d L[t, j] = sum_e w_e d p[t, e] / d L[t, j]
+                       = p[t, j] (w_j - sum_e w_e p[t, e])  (softmax Jacobian)."""
+    p = softmax_rows(L)
+    w = _f64(w)
+    return p * (w[None, :] - (p @ w)[:, None])
+
+
+# ----------------------------------------------------------------------------
 # router backward
 # ----------------------------------------------------------------------------
-def route_bwd(x, Wr, idx, g, dG, gate):
+def route_bwd(x, Wr, idx, g, dG, gate, dL_aux=None):
     """Gradients through the gate.
 
     softmax over the selected logits: dL[t, idx[t,j]] = g_j (dG_j - sum_i g_i dG_i),
     every other logit gets 0 (the selection is piecewise constant);
     dWr = x^T dL, db = sum_t dL, dX_router = dL Wr^T.
-    Balanced gate: the weights are constants, so dL, dWr, db and dX_router are 0."""
+    Balanced gate: the weights are constants, so dL, dWr, db and dX_router are 0.
+    dL_aux (optional): a further gradient on the logits (the auxiliary loss's),
+    added to dL before dWr, db and dX_router are formed."""
     T, k = idx.shape
     E = Wr.shape[1]
     if gate == GATE_BALANCED:
@@ -270,6 +324,8 @@ def route_bwd(x, Wr, idx, g, dG, gate):
     dsel = g * (dG - s)
     dL = np.zeros((T, E))
     np.put_along_axis(dL, idx.astype(np.int64), dsel, axis=1)
+    if dL_aux is not None:
+        dL = dL + _f64(dL_aux)
     return dict(dL=dL, dWr=_f64(x).T @ dL, db=dL.sum(axis=0), dX=dL @ _f64(Wr).T)
 
 

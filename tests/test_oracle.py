@@ -424,3 +424,118 @@ def test_gate_weights_stable_for_large_logits():
     g = O.topk_softmax_weights(L, idx)
     z = np.array([1.0, math.exp(-1.0), math.exp(-2.0)])
     np.testing.assert_allclose(g[0], z / z.sum(), rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# load-balancing auxiliary loss
+# --------------------------------------------------------------------------
+def test_aux_loss_hand_example():
+    """tests/golden/aux_loss_example.json: the loss re-derived by hand from
+    its definition, each softmax row written out term by term."""
+    g = json.load(open(os.path.join(GOLD, "aux_loss_example.json")))
+    e = math.e
+    Z0 = e + 2 * e ** 3 + 1
+    Z1 = 2 * e ** 2 + 1 + e ** 5
+    p0 = [e / Z0, e ** 3 / Z0, e ** 3 / Z0, 1 / Z0]
+    p1 = [e ** 2 / Z1, 1 / Z1, e ** 2 / Z1, e ** 5 / Z1]
+    P = [(a + b + 0.25) / 3 for a, b in zip(p0, p1)]
+    hand = 0.01 * 4 * (P[0] / 3 + P[1] / 3 + P[2] / 6 + P[3] / 6)
+    assert hand == pytest.approx(g["loss_closed_form_value"], rel=1e-13)
+    r = O.aux_loss(np.array(g["logits"], float), np.array(g["idx"]), g["E"], g["alpha"])
+    assert r["loss"] == pytest.approx(hand, rel=1e-13)
+    assert r["f"] == pytest.approx([1 / 3, 1 / 3, 1 / 6, 1 / 6], rel=1e-15)
+    assert r["counts"].tolist() == [2, 2, 1, 1]
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (60, 16, 4), (7, 4, 4)])
+def test_aux_loss_uniform_routing_is_alpha(T, E, k):
+    """Equal logits give P_e = 1/E; a routing that puts T*k/E rows on every
+    expert gives f_e = 1/E; then loss = alpha * E * E * (1/E)(1/E) = alpha."""
+    L = np.full((T, E), 0.37)
+    idx = np.array([[(t * k + j) % E for j in range(k)] for t in range(T)])
+    if (T * k) % E:
+        pytest.skip("rows do not divide evenly")
+    r = O.aux_loss(L, idx, E, 0.25)
+    assert r["loss"] == pytest.approx(0.25, rel=1e-14)
+    # the gradient vanishes: every w_e equal, softmax Jacobian rows sum to zero
+    assert np.abs(O.aux_loss_dlogits(L, r["w"])).max() < 1e-15
+
+
+def test_aux_loss_all_on_one_expert():
+    """Every token routed to expert 0 (k = 1), logits strongly favouring it:
+    f = (1, 0, ...), P_0 -> 1, so loss -> alpha * E (its largest value)."""
+    T, E = 16, 8
+    L = np.zeros((T, E))
+    L[:, 0] = 60.0
+    idx = np.zeros((T, 1), dtype=np.int32)
+    r = O.aux_loss(L, idx, E, 1.0)
+    assert r["loss"] == pytest.approx(E * (1.0 / (1.0 + (E - 1) * math.exp(-60.0))), rel=1e-14)
+
+
+def test_aux_loss_gradient_by_finite_differences():
+    """Central differences of loss(L) with the routing held fixed (the counts
+    are piecewise constant) against the closed-form gradient."""
+    r = _rng(41)
+    T, E, k = 6, 5, 2
+    L = r.standard_normal((T, E))
+    idx = O.topk_select(L, k)
+    w = O.aux_loss(L, idx, E, 0.7)["w"]
+    G = O.aux_loss_dlogits(L, w)
+    h = 1e-6
+    num = np.zeros_like(L)
+    for t in range(T):
+        for e in range(E):
+            Lp, Lm = L.copy(), L.copy()
+            Lp[t, e] += h
+            Lm[t, e] -= h
+            num[t, e] = (O.aux_loss(Lp, idx, E, 0.7)["loss"] - O.aux_loss(Lm, idx, E, 0.7)["loss"]) / (2 * h)
+    np.testing.assert_allclose(G, num, rtol=1e-7, atol=1e-10)
+
+
+def test_aux_loss_router_parameter_gradients_by_finite_differences():
+    """The auxiliary gradient pushed through the router (dWr = x^T dL,
+    db = column sums of dL, dX = dL Wr^T) against central differences of
+    loss(x Wr + b) in Wr, b and x, the routing held fixed."""
+    r = _rng(43)
+    T, d, E, k = 5, 3, 4, 2
+    x, Wr, b = r.standard_normal((T, d)), r.standard_normal((d, E)), r.standard_normal(E)
+    idx = O.topk_select(O.router_logits(x, Wr, b), k)
+    alpha = 0.3
+
+    def loss(x_, Wr_, b_):
+        return O.aux_loss(O.router_logits(x_, Wr_, b_), idx, E, alpha)["loss"]
+
+    L = O.router_logits(x, Wr, b)
+    dL = O.aux_loss_dlogits(L, O.aux_loss(L, idx, E, alpha)["w"])
+    zero_g = np.zeros((T, k))
+    rb = O.route_bwd(x, Wr, idx, zero_g, zero_g, O.GATE_SOFTMAX_TOPK, dL_aux=dL)
+    h = 1e-6
+    for name, arr, grad in (("Wr", Wr, rb["dWr"]), ("b", b, rb["db"]), ("x", x, rb["dX"])):
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[i] += h
+            am[i] -= h
+            args_p = dict(x_=x, Wr_=Wr, b_=b)
+            args_m = dict(x_=x, Wr_=Wr, b_=b)
+            key = {"Wr": "Wr_", "b": "b_", "x": "x_"}[name]
+            args_p[key], args_m[key] = ap, am
+            num[i] = (loss(**args_p) - loss(**args_m)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-10, err_msg=name)
+
+
+def test_aux_loss_invariant_under_expert_relabelling():
+    """Renaming the experts (permuting logit columns and routed ids alike)
+    changes neither the loss nor, relabelled, its gradient."""
+    r = _rng(47)
+    T, E, k = 9, 6, 3
+    L = r.standard_normal((T, E))
+    idx = O.topk_select(L, k)
+    perm = r.permutation(E)
+    inv = np.argsort(perm)
+    a = O.aux_loss(L, idx, E, 0.1)
+    b = O.aux_loss(L[:, perm], inv[idx], E, 0.1)
+    assert b["loss"] == pytest.approx(a["loss"], rel=1e-14)
+    ga = O.aux_loss_dlogits(L, a["w"])
+    gb = O.aux_loss_dlogits(L[:, perm], b["w"])
+    np.testing.assert_allclose(gb, ga[:, perm], rtol=1e-12, atol=1e-16)

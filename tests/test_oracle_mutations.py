@@ -50,6 +50,13 @@ MUTATIONS = [
     ("softmax Jacobian term dropped", "dsel = g * (dG - s)", "dsel = g * dG"),
     ("db averaged", "db=dL.sum(axis=0)", "db=dL.mean(axis=0)"),
     ("router dX dropped", "dX=dL @ _f64(Wr).T)", "dX=0 * dL @ _f64(Wr).T)"),
+    ("aux loss without the expert count factor", "loss=float(alpha * E * np.sum(f * P))",
+     "loss=float(alpha * np.sum(f * P))"),
+    ("aux shares over tokens not rows", "f = c / (T * k)", "f = c / T"),
+    ("aux mean probability not averaged", "P = p.mean(axis=0)", "P = p.sum(axis=0)"),
+    ("aux gradient Jacobian term dropped", "return p * (w[None, :] - (p @ w)[:, None])",
+     "return p * w[None, :]"),
+    ("aux gradient not added to the router", "dL = dL + _f64(dL_aux)", "dL = dL"),
 ]
 
 
