@@ -233,6 +233,21 @@ def secondary_workloads(B, dev, w_main, gather):
         "max_group_rows": int(counts.max()), "empty_experts": int((counts == 0).sum()),
         "kernels_us_avg": kernel_averages(step_nat, B, 3)}
     del buf
+    # -- the same with the router's load-balancing auxiliary loss (alpha 0.01)
+    buf = LayerBuffers(shape, training=True, gather=gather, aux_alpha=0.01)
+
+    def step_nat_aux():
+        forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
+        backward(shape, buf, dev["dY"], dev["x"], Wr, dev["Wg"], dev["Wu"], dev["Wd"])
+
+    st = timed_steps(step_nat_aux, 10, 3)
+    ka = kernel_averages(step_nat_aux, B, 3)
+    out["natural_router_aux_fwdbwd"] = {
+        "workload": "qwen3_natural_fwdbwd_T4096_d2048_E128_k8_I768 + balancing loss (alpha 0.01)",
+        "tokens_per_s": round(wn.T / (st["median"] / 1e3), 1), "step_ms": st,
+        "aux_loss": float(buf["aux_loss"].item()),
+        "kernels_us_avg": {k: v for k, v in ka.items() if k.startswith(("aux", "route"))}}
+    del buf
     # -- decode-sized batches, natural router: the small-batch FFN (no sort)
     #    against the grouped path, forward only
     out["small_batch_fwd"] = {}

@@ -77,7 +77,7 @@ typedef enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_BALANCED = 1 } moe_gate_t;
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7,
-  MOE_OP_SMALL_FWD = 8
+  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9
 } moe_op_t;
 
 typedef void* moe_stream_t; /* hipStream_t */
@@ -263,6 +263,41 @@ moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* 
                            const float* dtopk_w, float* dlogits, void* dw_router,
                            float* dbias, void* dx, void* ws, size_t ws_bytes,
                            moe_stream_t stream);
+
+/* Load-balancing auxiliary loss of the router (softmax_topk gate).  The pages
+ * name an auxiliary loss that keeps the naturally uneven routing even during
+ * fine-tuning (page "NVIDIA NeMo AutoModel MoE 微調的 3.7 倍加速突破", section
+ * 延伸觀點; [P3] section 单节点30B MoE基准测试, routing-gate note: a trained
+ * model's balancing loss drives expert utilisation toward uniform) without a
+ * formula; this is the Switch Transformer balancing loss with the k slots of
+ * a token counted as k dispatches:
+ *   f_e  = c_e / (T*k), c_e = routed slots on expert e (all E experts, from
+ *          topk_idx, whichever experts are local),
+ *   P_e  = (1/T) sum_t softmax(logits[t,:])_e (full softmax over E, fp32),
+ *   loss = alpha * E * sum_e f_e P_e.
+ * logits [T,E] fp32 (as moe_route wrote them); topk_idx [T,k]; loss [1] fp32
+ * (written); aux_w [E] fp32 (written): alpha*E*f_e/T, the weights
+ * moe_route_bwd_aux needs.  Every sum runs in a fixed order (deterministic).
+ * ws: moe_workspace_size(MOE_OP_AUX_LOSS) (per-32-token partial sums).
+ * MOE_ERR_ARG for the balanced gate (it has no router probabilities) or a
+ * non-finite alpha. */
+moe_status_t moe_aux_loss(const moe_shape_t* shape, const float* logits, const int32_t* topk_idx,
+                          float alpha, float* loss, float* aux_w, void* ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/* moe_route_bwd with the auxiliary loss's gradient added to dlogits before
+ * dw_router, dbias and dx are formed: the counts c_e are piecewise constant,
+ * so the gradient flows through P only:
+ *   dlogits[t,e] += p[t,e] (aux_w[e] - sum_e' aux_w[e'] p[t,e']),
+ * p = softmax(logits[t,:]).  logits [T,E] fp32 and aux_w [E] fp32 (from
+ * moe_aux_loss) are required; the other arguments, the workspace
+ * (MOE_OP_ROUTE_BWD) and the errors are those of moe_route_bwd, plus
+ * MOE_ERR_ARG for the balanced gate. */
+moe_status_t moe_route_bwd_aux(const moe_shape_t* shape, const void* x, const void* w_router,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const float* dtopk_w, const float* logits, const float* aux_w,
+                               float* dlogits, void* dw_router, float* dbias, void* dx, void* ws,
+                               size_t ws_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------- kernel timer */
 /* Optional per-kernel timing with HIP events recorded on the launch stream

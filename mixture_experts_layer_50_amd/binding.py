@@ -17,7 +17,7 @@ LIB_NAME = "libmoe.so"
 DTYPES = {"f32": 0, "bf16": 1}
 GATES = {"softmax_topk": 0, "balanced": 1}
 OPS = {"route": 0, "permute": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4, "ffn_bwd": 5,
-       "permute_bwd": 6, "route_bwd": 7, "small_fwd": 8}
+       "permute_bwd": 6, "route_bwd": 7, "small_fwd": 8, "aux_loss": 9}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED"}
 
@@ -26,7 +26,8 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_
            "moe_route", "moe_permute", "moe_grouped_ffn_fwd", "moe_combine", "moe_combine_bwd",
            "moe_grouped_ffn_bwd", "moe_permute_bwd", "moe_route_bwd", "moe_prof_enable",
            "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names",
-           "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd"]
+           "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd",
+           "moe_aux_loss", "moe_route_bwd_aux"]
 
 
 class MoEError(RuntimeError):
@@ -93,6 +94,8 @@ def load_library() -> ctypes.CDLL:
         "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
         "moe_route_bwd": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_aux_loss": [S, P, P, ctypes.c_float, P, P, P, SZ, P],
+        "moe_route_bwd_aux": [S, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_prof_enable": [I32],
         "moe_prof_select": [ctypes.c_char_p],
         "moe_prof_reset": [],
@@ -209,6 +212,20 @@ def moe_route_bwd(shape, x, w_router, topk_idx, topk_w, dtopk_w, dlogits, dw_rou
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_w),
         _ptr(dtopk_w), _ptr(dlogits), _ptr(dw_router), _ptr(dbias), _ptr(dx), _ptr(ws),
         _nbytes(ws), _stream(stream)))
+
+
+def moe_aux_loss(shape, logits, topk_idx, alpha, loss, aux_w, ws, stream=None):
+    _check("moe_aux_loss", load_library().moe_aux_loss(
+        ctypes.byref(shape), _ptr(logits), _ptr(topk_idx), float(alpha), _ptr(loss), _ptr(aux_w),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_route_bwd_aux(shape, x, w_router, topk_idx, topk_w, dtopk_w, logits, aux_w, dlogits,
+                      dw_router, dbias, dx, ws, stream=None):
+    _check("moe_route_bwd_aux", load_library().moe_route_bwd_aux(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(dtopk_w), _ptr(logits), _ptr(aux_w), _ptr(dlogits), _ptr(dw_router), _ptr(dbias),
+        _ptr(dx), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def prof_enable(on: bool = True):

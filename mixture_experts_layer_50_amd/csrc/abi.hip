@@ -1,5 +1,6 @@
 // C ABI of the MoE layer library: argument checks, workspace sizing, the
 // order of kernel launches of each call, and the optional kernel timer.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -330,6 +331,7 @@ int64_t ws_bytes(const Dims& D, int op) {
       return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
              (D.bf16 ? tile_table_bytes(D) : 0);
     case MOE_OP_SMALL_FWD: return small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.eb);
+    case MOE_OP_AUX_LOSS: return D.balanced ? 0 : aux_loss_ws_bytes(D.T, D.E);
     case MOE_OP_ROUTE_BWD: {
       if (D.balanced) return 0;
       const RouteBwdWs r(D);
@@ -356,7 +358,7 @@ extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, siz
   Dims D;
   if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
   MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
-  if (op < MOE_OP_ROUTE || op > MOE_OP_SMALL_FWD)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_AUX_LOSS)
     return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
   *bytes = (size_t)ws_bytes(D, op);
   return MOE_OK;
@@ -637,15 +639,18 @@ extern "C" moe_status_t moe_permute_bwd(const moe_shape_t* shape, const void* dx
   return launch_gather_sum(dxp, inv, nullptr, D.T, D.d, D.k, D.eb, dx, S(stream), "permute_bwd");
 }
 
-extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* w_router,
-                                      const int32_t* topk_idx, const float* topk_w,
-                                      const float* dtopk_w, float* dlogits, void* dw_router,
-                                      float* dbias, void* dx, void* ws, size_t ws_bytes_,
-                                      moe_stream_t stream) {
-  const char* fn = "moe_route_bwd";
+namespace {
+moe_status_t route_bwd(const char* fn, const moe_shape_t* shape, const void* x, const void* w_router,
+                       const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
+                       const float* logits, const float* aux_w, float* dlogits, void* dw_router,
+                       float* dbias, void* dx, void* ws, size_t ws_bytes_, moe_stream_t stream) {
   Dims D;
   MOE_TRY(check_shape(shape, fn, &D));
   hipStream_t s = S(stream);
+  if (aux_w) {
+    if (D.balanced) return fail(MOE_ERR_ARG, "%s: the balanced gate has no router probabilities", fn);
+    MOE_TRY(need(fn, {{"logits", logits}}));
+  }
   if (D.balanced) {
     MOE_TRY(opt(fn, {{"dlogits", dlogits}, {"dw_router", dw_router}, {"dbias", dbias}}));
     return launch_fill_zero(dlogits, (int64_t)D.T * D.E * 4, dw_router, (int64_t)D.d * D.E * D.eb,
@@ -660,7 +665,8 @@ extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, c
   bf16_t* dl16 = D.bf16 ? reinterpret_cast<bf16_t*>(wsb + rw.dl16) : nullptr;
   float* db_part = reinterpret_cast<float*>(wsb + rw.dbp);
   float* dw_part = D.bf16 ? reinterpret_cast<float*>(wsb + rw.dwp) : nullptr;
-  MOE_TRY(launch_route_bwd_dl(topk_idx, topk_w, dtopk_w, D.T, D.E, D.k, dlogits, dl16, db_part, s));
+  MOE_TRY(launch_route_bwd_dl(topk_idx, topk_w, dtopk_w, D.T, D.E, D.k, dlogits, dl16, db_part,
+                              aux_w ? logits : nullptr, aux_w, s));
   const void* dl = D.bf16 ? static_cast<const void*>(dl16) : static_cast<const void*>(dlogits);
   {  // dWr = x^T dL: bf16 layers as fp32 partials over nsplit K (token) ranges
     GemmParams p{};
@@ -689,4 +695,40 @@ extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, c
     MOE_TRY(launch_gemm(D.bf16, R_ROUTE_DX, p, p.m_tiles, s));
   }
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status_t moe_route_bwd(const moe_shape_t* shape, const void* x, const void* w_router,
+                                      const int32_t* topk_idx, const float* topk_w,
+                                      const float* dtopk_w, float* dlogits, void* dw_router,
+                                      float* dbias, void* dx, void* ws, size_t ws_bytes_,
+                                      moe_stream_t stream) {
+  return route_bwd("moe_route_bwd", shape, x, w_router, topk_idx, topk_w, dtopk_w, nullptr, nullptr,
+                   dlogits, dw_router, dbias, dx, ws, ws_bytes_, stream);
+}
+
+extern "C" moe_status_t moe_route_bwd_aux(const moe_shape_t* shape, const void* x,
+                                          const void* w_router, const int32_t* topk_idx,
+                                          const float* topk_w, const float* dtopk_w,
+                                          const float* logits, const float* aux_w, float* dlogits,
+                                          void* dw_router, float* dbias, void* dx, void* ws,
+                                          size_t ws_bytes_, moe_stream_t stream) {
+  const char* fn = "moe_route_bwd_aux";
+  MOE_TRY(need(fn, {{"aux_w", aux_w}}));
+  return route_bwd(fn, shape, x, w_router, topk_idx, topk_w, dtopk_w, logits, aux_w, dlogits,
+                   dw_router, dbias, dx, ws, ws_bytes_, stream);
+}
+
+extern "C" moe_status_t moe_aux_loss(const moe_shape_t* shape, const float* logits,
+                                     const int32_t* topk_idx, float alpha, float* loss,
+                                     float* aux_w, void* ws, size_t ws_bytes_,
+                                     moe_stream_t stream) {
+  const char* fn = "moe_aux_loss";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  if (D.balanced) return fail(MOE_ERR_ARG, "%s: the balanced gate has no router probabilities", fn);
+  if (!std::isfinite(alpha)) return fail(MOE_ERR_ARG, "%s: alpha must be finite", fn);
+  MOE_TRY(need(fn, {{"logits", logits}, {"topk_idx", topk_idx}, {"loss", loss}, {"aux_w", aux_w}}));
+  MOE_TRY(check_ws(fn, D, MOE_OP_AUX_LOSS, ws, ws_bytes_));
+  return launch_aux_loss(logits, topk_idx, D.T, D.E, D.k, alpha, loss, aux_w, ws, S(stream));
 }

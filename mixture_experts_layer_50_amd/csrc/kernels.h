@@ -15,8 +15,14 @@ moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32
                                  hipStream_t s);
 // Tokens per workgroup of the router backward (one bias-gradient partial each).
 constexpr int ROUTE_BWD_TOKENS = 32;
+// logits / aux_w (both or neither): add the auxiliary loss's logit gradient.
 moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
-                                 int k, float* dl, bf16_t* dl_bf16, float* db_part, hipStream_t s);
+                                 int k, float* dl, bf16_t* dl_bf16, float* db_part,
+                                 const float* logits, const float* aux_w, hipStream_t s);
+// Load-balancing auxiliary loss: loss[0] and aux_w[E] (the backward's weights).
+int64_t aux_loss_ws_bytes(int T, int E);
+moe_status_t launch_aux_loss(const float* logits, const int32_t* idx, int T, int E, int k,
+                             float alpha, float* loss, float* aux_w, void* ws, hipStream_t s);
 moe_status_t launch_route_bwd_reduce(const float* dw_part, int nsplit, int64_t n_dw, bf16_t* dw,
                                      const float* db_part, int nblk, int E, float* db,
                                      hipStream_t s);

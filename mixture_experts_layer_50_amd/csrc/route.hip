@@ -101,15 +101,23 @@ moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32
 // lane l owns experts l + 64 q.  The optional bf16 copy feeds the bf16
 // router-gradient GEMMs.  Each workgroup also writes its column sums of dL
 // (tokens in order, then its four waves in order) to db_part[block][E].
-template <int VPL>
+//
+// AUX adds the gradient of the load-balancing auxiliary loss:
+// dL[t, e] += p[t, e] (w[e] - sum_e' w[e'] p[t, e']), p = softmax of the
+// token's full logit row (fp32, max subtracted), w = aux_w.
+template <int VPL, bool AUX>
 __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, const float* g,
                                                            const float* dg, int T, int E, int k,
                                                            float* dl, bf16_t* dl_bf16,
-                                                           float* db_part) {
+                                                           float* db_part, const float* logits,
+                                                           const float* aux_w) {
   __shared__ float part[4][64 * VPL];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int TPW = ROUTE_BWD_TOKENS / 4;  // tokens per wave
   const int t0 = blockIdx.x * ROUTE_BWD_TOKENS + wave * TPW;
+  float aw[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) aw[q] = AUX && q * 64 + lane < E ? aux_w[q * 64 + lane] : 0.f;
   // every token's slot data first (the loads in flight together)
   float gq[TPW], dgq[TPW];
   int iq[TPW];
@@ -134,6 +142,32 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
     const float val = gj * (dgj - sum);
+    float pa[VPL], pdot = 0.f;  // AUX: the token's probabilities and sum_e w_e p_e
+    if constexpr (AUX) {
+      float lv[VPL], m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        lv[q] = q * 64 + lane < E ? logits[(int64_t)t * E + q * 64 + lane] : -INFINITY;
+        m = fmaxf(m, lv[q]);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      float z = 0.f;
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        pa[q] = q * 64 + lane < E ? expf(lv[q] - m) : 0.f;
+        z += pa[q];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) {
+        pa[q] = pa[q] / z;
+        pdot += aw[q] * pa[q];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) pdot += __shfl_xor(pdot, off, 64);
+    }
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
       const int e = q * 64 + lane;
@@ -143,6 +177,7 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
         const float vj = __shfl(val, j, 64);
         if (ej == e) out = vj;
       }
+      if constexpr (AUX) out += pa[q] * (aw[q] - pdot);
       if (e < E) {
         dl[(int64_t)t * E + e] = out;
         if (dl_bf16) dl_bf16[(int64_t)t * E + e] = f2bf(out);
@@ -157,15 +192,147 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
     db_part[(int64_t)blockIdx.x * E + e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
 }
 
-moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
-                                 int k, float* dl, bf16_t* dl_bf16, float* db_part, hipStream_t s) {
-  ProfScope prof("route_bwd_dlogits", s);
+template <bool AUX>
+static void route_bwd_dl_launch(const int32_t* idx, const float* g, const float* dg, int T, int E,
+                                int k, float* dl, bf16_t* dl_bf16, float* db_part,
+                                const float* logits, const float* aux_w, hipStream_t s) {
   const unsigned grid = (unsigned)ceil_div(T, ROUTE_BWD_TOKENS);
-  if (E <= 64) route_bwd_dl_kernel<1><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
-  else if (E <= 128) route_bwd_dl_kernel<2><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
-  else if (E <= 256) route_bwd_dl_kernel<4><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
-  else route_bwd_dl_kernel<8><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part);
+#define L_(V) route_bwd_dl_kernel<V, AUX><<<grid, 256, 0, s>>>(idx, g, dg, T, E, k, dl, dl_bf16, db_part, logits, aux_w)
+  if (E <= 64) L_(1);
+  else if (E <= 128) L_(2);
+  else if (E <= 256) L_(4);
+  else L_(8);
+#undef L_
+}
+
+moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float* dg, int T, int E,
+                                 int k, float* dl, bf16_t* dl_bf16, float* db_part,
+                                 const float* logits, const float* aux_w, hipStream_t s) {
+  ProfScope prof(aux_w ? "route_bwd_dlogits_aux" : "route_bwd_dlogits", s);
+  if (aux_w) route_bwd_dl_launch<true>(idx, g, dg, T, E, k, dl, dl_bf16, db_part, logits, aux_w, s);
+  else route_bwd_dl_launch<false>(idx, g, dg, T, E, k, dl, dl_bf16, db_part, nullptr, nullptr, s);
   return check_launch("route_bwd_dl_kernel");
+}
+
+// ---------------------------------------------------------------- aux loss
+// Load-balancing auxiliary loss, loss = alpha E sum_e f_e P_e with
+// f_e = c_e / (T k) (routed rows on expert e) and P_e = mean_t softmax(L[t,:])_e
+// (the Switch Transformer balancing loss; the pages name an auxiliary
+// balancing loss without its formula).  Pass 1: one workgroup per
+// ROUTE_BWD_TOKENS tokens, one wavefront per quarter of them in token order,
+// lane l owns experts l + 64 q; writes the block's column sums of p and its
+// expert counts (waves added in a fixed order).  Pass 2, one workgroup: per
+// expert the block partials in order (lane l: blocks l, l + 64, ...; then a
+// fixed butterfly), then the loss over the experts in order.  fp32 throughout.
+template <int VPL>
+__global__ __launch_bounds__(256) void aux_loss_part_kernel(const float* logits, const int32_t* idx,
+                                                            int T, int E, int k, float* pp_part,
+                                                            int32_t* cnt_part) {
+  __shared__ float pp[4][64 * VPL];
+  __shared__ int cn[4][64 * VPL];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int TPW = ROUTE_BWD_TOKENS / 4;
+  const int t0 = blockIdx.x * ROUTE_BWD_TOKENS + wave * TPW;
+  float col[VPL];
+  int cnt[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) {
+    col[q] = 0.f;
+    cnt[q] = 0;
+  }
+  for (int i = 0; i < TPW; ++i) {
+    const int t = t0 + i;
+    if (t >= T) break;  // uniform per wave
+    float lv[VPL], m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      lv[q] = q * 64 + lane < E ? logits[(int64_t)t * E + q * 64 + lane] : -INFINITY;
+      m = fmaxf(m, lv[q]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    float z = 0.f;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      lv[q] = q * 64 + lane < E ? expf(lv[q] - m) : 0.f;
+      z += lv[q];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+    const int ij = lane < k ? idx[(int64_t)t * k + lane] : -1;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      col[q] += lv[q] / z;
+      for (int j = 0; j < k; ++j) cnt[q] += __shfl(ij, j, 64) == q * 64 + lane;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) {
+    pp[wave][q * 64 + lane] = col[q];
+    cn[wave][q * 64 + lane] = cnt[q];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    pp_part[(int64_t)blockIdx.x * E + e] = ((pp[0][e] + pp[1][e]) + pp[2][e]) + pp[3][e];
+    cnt_part[(int64_t)blockIdx.x * E + e] = cn[0][e] + cn[1][e] + cn[2][e] + cn[3][e];
+  }
+}
+
+__global__ __launch_bounds__(256) void aux_loss_final_kernel(const float* pp_part,
+                                                             const int32_t* cnt_part, int nblk,
+                                                             int T, int E, int k, float alpha,
+                                                             float* loss, float* aux_w) {
+  __shared__ float term[512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float rows = (float)T * (float)k;
+  for (int e = wave; e < E; e += 4) {  // uniform per wave
+    float ps = 0.f;
+    int c = 0;
+    for (int b = lane; b < nblk; b += 64) {
+      ps += pp_part[(int64_t)b * E + e];
+      c += cnt_part[(int64_t)b * E + e];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      ps += __shfl_xor(ps, off, 64);
+      c += __shfl_xor(c, off, 64);
+    }
+    const float f = (float)c / rows;
+    if (lane == 0) {
+      term[e] = f * (ps / (float)T);
+      aux_w[e] = alpha * (float)E * f / (float)T;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float v = 0.f;
+    for (int e = lane; e < E; e += 64) v += term[e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) loss[0] = alpha * (float)E * v;
+  }
+}
+
+int64_t aux_loss_ws_bytes(int T, int E) {
+  const int64_t nblk = ceil_div(T, ROUTE_BWD_TOKENS);
+  return 2 * round_up(nblk * E * 4, 256);
+}
+
+moe_status_t launch_aux_loss(const float* logits, const int32_t* idx, int T, int E, int k,
+                             float alpha, float* loss, float* aux_w, void* ws, hipStream_t s) {
+  ProfScope prof("aux_loss", s);
+  const int nblk = (int)ceil_div(T, ROUTE_BWD_TOKENS);
+  float* pp_part = static_cast<float*>(ws);
+  int32_t* cnt_part = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                 round_up((int64_t)nblk * E * 4, 256));
+  if (E <= 64) aux_loss_part_kernel<1><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
+  else if (E <= 128) aux_loss_part_kernel<2><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
+  else if (E <= 256) aux_loss_part_kernel<4><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
+  else aux_loss_part_kernel<8><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
+  const moe_status_t st = check_launch("aux_loss_part_kernel");
+  if (st != MOE_OK) return st;
+  aux_loss_final_kernel<<<1, 256, 0, s>>>(pp_part, cnt_part, nblk, T, E, k, alpha, loss, aux_w);
+  return check_launch("aux_loss_final_kernel");
 }
 
 // Final sums of the router backward, each in a fixed order:

@@ -23,6 +23,7 @@ class LayerBuffers:
     device: str = "cuda"
     training: bool = True
     gather: bool = False  # FFN reads x through perm (the _gather calls); no Xp buffer
+    aux_alpha: Optional[float] = None  # router balancing loss weight (softmax top-k gate)
     t: Dict[str, torch.Tensor] = field(default_factory=dict)
 
     def __post_init__(self):
@@ -48,6 +49,10 @@ class LayerBuffers:
         t["y"] = e(T, d)
         for op in ("permute", "ffn_fwd"):
             t["ws_" + op] = self._ws(op)
+        if self.aux_alpha is not None:
+            t["aux_loss"] = e(1, dtype=f32)
+            t["aux_w"] = e(E, dtype=f32)
+            t["ws_aux_loss"] = self._ws("aux_loss")
         if self.training:
             t["dyp"] = e(R, d)
             t["dtopk_w"] = e(T, k, dtype=f32)
@@ -73,9 +78,13 @@ class LayerBuffers:
 def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
             stream=None):
     """route -> permute -> grouped SwiGLU FFN -> combine; y lands in buf['y'].
-    With buf.gather the permute only sorts and the FFN reads x through perm."""
+    With buf.gather the permute only sorts and the FFN reads x through perm.
+    With buf.aux_alpha the router's balancing loss lands in buf['aux_loss']."""
     t = buf.t
     B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
+    if buf.aux_alpha is not None:
+        B.moe_aux_loss(shape, t["logits"], t["topk_idx"], buf.aux_alpha, t["aux_loss"], t["aux_w"],
+                       t["ws_aux_loss"], stream)
     B.moe_permute(shape, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"],
                   t["ws_permute"], stream)
     if buf.gather:
@@ -101,7 +110,8 @@ def forward_small(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gat
 
 def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up, w_down,
              stream=None):
-    """combine_bwd -> grouped FFN bwd -> permute_bwd -> route_bwd."""
+    """combine_bwd -> grouped FFN bwd -> permute_bwd -> route_bwd (with the
+    balancing loss's gradient when buf.aux_alpha is set)."""
     t = buf.t
     B.moe_combine_bwd(shape, dy, t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"], stream)
     if buf.gather:
@@ -113,5 +123,10 @@ def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up
                               t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"],
                               t["ws_ffn_bwd"], stream)
     B.moe_permute_bwd(shape, t["dxp"], t["inv"], t["dx"], stream)
+    if buf.aux_alpha is not None:
+        B.moe_route_bwd_aux(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"],
+                            t["logits"], t["aux_w"], t["dlogits"], t["dw_router"], t["dbias"],
+                            t["dx"], t["ws_route_bwd"], stream)
+        return
     B.moe_route_bwd(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"], t["dlogits"],
                     t["dw_router"], t["dbias"], t["dx"], t["ws_route_bwd"], stream)

@@ -211,3 +211,36 @@ def test_small_batch_ffn_validation(lib):
     assert st == "MOE_ERR_WORKSPACE"
     assert B.STATUS[lib.moe_ffn_small_fwd(ctypes.byref(shape(k=9)), P, P, P, P, P, P, P, P,
                                           1 << 20, None)] == "MOE_ERR_ARG"
+
+
+def test_aux_loss_validation(lib):
+    """moe_aux_loss / moe_route_bwd_aux: natural gate only, required buffers,
+    finite alpha, the workspace of per-32-token partials."""
+    P = FAKE
+    s = shape(T=100, d=128, E=16, k=2, I=256)
+    n = B.workspace_size(s, "aux_loss")
+    # column sums of the probabilities and expert counts per 32 tokens (4 blocks)
+    assert n == 2 * 256
+    assert B.workspace_size(shape(T=4096, d=2048, E=128, k=8, I=768), "aux_loss") == 2 * 128 * 128 * 4
+
+    def aux(sh, alpha=0.01, logits=P, loss=P, ws_bytes=1 << 20):
+        return B.STATUS[lib.moe_aux_loss(ctypes.byref(sh), logits, P, ctypes.c_float(alpha), loss, P,
+                                         P, ws_bytes, None)], lib.moe_last_error().decode()
+
+    assert aux(s, logits=None) == ("MOE_ERR_ARG", "moe_aux_loss: logits is NULL")
+    assert aux(s, loss=None) == ("MOE_ERR_ARG", "moe_aux_loss: loss is NULL")
+    st, msg = aux(s, alpha=float("nan"))
+    assert st == "MOE_ERR_ARG" and "alpha" in msg
+    st, msg = aux(shape(T=100, d=128, E=16, k=2, I=256, gate="balanced"))
+    assert st == "MOE_ERR_ARG" and "balanced" in msg
+    assert aux(s, ws_bytes=n - 1)[0] == "MOE_ERR_WORKSPACE"
+
+    def bwd(sh, logits=P, aux_w=P):
+        return B.STATUS[lib.moe_route_bwd_aux(ctypes.byref(sh), P, P, P, P, P, logits, aux_w, P, P,
+                                              None, P, P, 1 << 30, None)], \
+            lib.moe_last_error().decode()
+
+    assert bwd(s, aux_w=None) == ("MOE_ERR_ARG", "moe_route_bwd_aux: aux_w is NULL")
+    assert bwd(s, logits=None) == ("MOE_ERR_ARG", "moe_route_bwd_aux: logits is NULL")
+    st, msg = bwd(shape(T=100, d=128, E=16, k=2, I=256, gate="balanced"))
+    assert st == "MOE_ERR_ARG" and "balanced" in msg

@@ -15,22 +15,24 @@ from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward, 
 pytestmark = pytest.mark.gpu
 
 OUTS = ["logits", "topk_idx", "topk_w", "y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w",
-        "dw_router", "dbias"]
+        "dw_router", "dbias", "dlogits", "aux_loss", "aux_w"]
 
 
 @pytest.mark.parametrize("gate,path", [("softmax_topk", "plain"), ("balanced", "plain"),
                                        ("softmax_topk", "gather"), ("balanced", "gather"),
-                                       ("softmax_topk", "small")])
+                                       ("softmax_topk", "small"), ("softmax_topk", "aux")])
 def test_graph_replay_matches_eager(gate, path):
     """path: plain (permute writes Xp), gather (the FFN reads x through the
-    token table), small (the small-batch forward, no backward)."""
+    token table), small (the small-batch forward, no backward), aux (plain
+    with the router's balancing loss and its gradient)."""
     w = MI.small_workload(f"graph_{gate}_{path}_T384_d256_E16_k4_I256", 384, 256, 16, 4, 256,
                           gate=gate, bias_sigma=1.0 if gate == "softmax_topk" else None, seed=31)
     print(f"\n[gpu case] {w.name}", flush=True)
     sys.stdout.flush()
     dev = U.upload(w, MI.generate(w))
     shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate)
-    buf = LayerBuffers(shape, training=path != "small", gather=path == "gather")
+    buf = LayerBuffers(shape, training=path != "small", gather=path == "gather",
+                       aux_alpha=0.05 if path == "aux" else None)
 
     def step():
         if path == "small":
