@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
   // every token's slot data first (the loads in flight together)
   float gq[TPW], dgq[TPW];
   int iq[TPW];
+  float lq[AUX ? TPW : 1][VPL];  // AUX: the tokens' logit rows
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const bool ok = t0 + i < T && lane < k;
@@ -128,6 +129,12 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
     gq[i] = ok ? g[o] : 0.f;
     dgq[i] = ok ? dg[o] : 0.f;
     iq[i] = ok ? idx[o] : -1;
+    if constexpr (AUX) {
+#pragma unroll
+      for (int q = 0; q < VPL; ++q)
+        lq[i][q] = t0 + i < T && q * 64 + lane < E ? logits[(int64_t)(t0 + i) * E + q * 64 + lane]
+                                                   : -INFINITY;
+    }
   }
   float col[VPL];
 #pragma unroll
@@ -144,12 +151,10 @@ __global__ __launch_bounds__(256) void route_bwd_dl_kernel(const int32_t* idx, c
     const float val = gj * (dgj - sum);
     float pa[VPL], pdot = 0.f;  // AUX: the token's probabilities and sum_e w_e p_e
     if constexpr (AUX) {
-      float lv[VPL], m = -INFINITY;
+      float m = -INFINITY;
+      const float* lv = lq[i];
 #pragma unroll
-      for (int q = 0; q < VPL; ++q) {
-        lv[q] = q * 64 + lane < E ? logits[(int64_t)t * E + q * 64 + lane] : -INFINITY;
-        m = fmaxf(m, lv[q]);
-      }
+      for (int q = 0; q < VPL; ++q) m = fmaxf(m, lv[q]);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
       float z = 0.f;
@@ -222,91 +227,106 @@ moe_status_t launch_route_bwd_dl(const int32_t* idx, const float* g, const float
 // ROUTE_BWD_TOKENS tokens, one wavefront per quarter of them in token order,
 // lane l owns experts l + 64 q; writes the block's column sums of p and its
 // expert counts (waves added in a fixed order).  Pass 2, one workgroup: per
-// expert the block partials in order (lane l: blocks l, l + 64, ...; then a
-// fixed butterfly), then the loss over the experts in order.  fp32 throughout.
+// expert the block partials in block order, then the loss over the experts in
+// order.  fp32 throughout.
 template <int VPL>
 __global__ __launch_bounds__(256) void aux_loss_part_kernel(const float* logits, const int32_t* idx,
                                                             int T, int E, int k, float* pp_part,
                                                             int32_t* cnt_part) {
   __shared__ float pp[4][64 * VPL];
-  __shared__ int cn[4][64 * VPL];
+  __shared__ int cn[64 * VPL];  // the block's expert counts (integer adds: order-free)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int TPW = ROUTE_BWD_TOKENS / 4;
   const int t0 = blockIdx.x * ROUTE_BWD_TOKENS + wave * TPW;
-  float col[VPL];
-  int cnt[VPL];
+  for (int e = threadIdx.x; e < 64 * VPL; e += blockDim.x) cn[e] = 0;
+  __syncthreads();
+  // every token's logit row and slots first (the loads in flight together)
+  float lv[TPW][VPL];
+  int iq[TPW];
 #pragma unroll
-  for (int q = 0; q < VPL; ++q) {
-    col[q] = 0.f;
-    cnt[q] = 0;
-  }
   for (int i = 0; i < TPW; ++i) {
-    const int t = t0 + i;
-    if (t >= T) break;  // uniform per wave
-    float lv[VPL], m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      lv[q] = q * 64 + lane < E ? logits[(int64_t)t * E + q * 64 + lane] : -INFINITY;
-      m = fmaxf(m, lv[q]);
-    }
+    for (int q = 0; q < VPL; ++q)
+      lv[i][q] = t0 + i < T && q * 64 + lane < E ? logits[(int64_t)(t0 + i) * E + q * 64 + lane]
+                                                 : -INFINITY;
+    iq[i] = t0 + i < T && lane < k ? idx[(int64_t)(t0 + i) * k + lane] : -1;
+  }
+  float col[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) col[q] = 0.f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+    if (iq[i] >= 0 && iq[i] < E) atomicAdd(&cn[iq[i]], 1);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (t0 + i >= T) break;  // uniform per wave
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) m = fmaxf(m, lv[i][q]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    float z = 0.f;
+    float z = 0.f, ev[VPL];
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
-      lv[q] = q * 64 + lane < E ? expf(lv[q] - m) : 0.f;
-      z += lv[q];
+      ev[q] = q * 64 + lane < E ? expf(lv[i][q] - m) : 0.f;
+      z += ev[q];
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-    const int ij = lane < k ? idx[(int64_t)t * k + lane] : -1;
 #pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      col[q] += lv[q] / z;
-      for (int j = 0; j < k; ++j) cnt[q] += __shfl(ij, j, 64) == q * 64 + lane;
-    }
+    for (int q = 0; q < VPL; ++q) col[q] += ev[q] / z;
   }
 #pragma unroll
-  for (int q = 0; q < VPL; ++q) {
-    pp[wave][q * 64 + lane] = col[q];
-    cn[wave][q * 64 + lane] = cnt[q];
-  }
+  for (int q = 0; q < VPL; ++q) pp[wave][q * 64 + lane] = col[q];
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     pp_part[(int64_t)blockIdx.x * E + e] = ((pp[0][e] + pp[1][e]) + pp[2][e]) + pp[3][e];
-    cnt_part[(int64_t)blockIdx.x * E + e] = cn[0][e] + cn[1][e] + cn[2][e] + cn[3][e];
+    cnt_part[(int64_t)blockIdx.x * E + e] = cn[e];
   }
 }
 
-__global__ __launch_bounds__(256) void aux_loss_final_kernel(const float* pp_part,
+// One workgroup: thread e adds expert e's block partials in block order
+// (neighbouring threads read neighbouring words, so the loads of a block row
+// coalesce and stay in flight together), then wavefront 0 adds the experts'
+// terms in order.
+__global__ __launch_bounds__(512) void aux_loss_final_kernel(const float* pp_part,
                                                              const int32_t* cnt_part, int nblk,
                                                              int T, int E, int k, float alpha,
                                                              float* loss, float* aux_w) {
   __shared__ float term[512];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float rows = (float)T * (float)k;
-  for (int e = wave; e < E; e += 4) {  // uniform per wave
+  const int e = threadIdx.x;
+  if (e < E) {
     float ps = 0.f;
     int c = 0;
-    for (int b = lane; b < nblk; b += 64) {
+    constexpr int U = 32;  // block partials loaded together, then added in order
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      float pv[U];
+      int cv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        pv[u] = pp_part[(int64_t)(b + u) * E + e];
+        cv[u] = cnt_part[(int64_t)(b + u) * E + e];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ps += pv[u];
+        c += cv[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       ps += pp_part[(int64_t)b * E + e];
       c += cnt_part[(int64_t)b * E + e];
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      ps += __shfl_xor(ps, off, 64);
-      c += __shfl_xor(c, off, 64);
-    }
-    const float f = (float)c / rows;
-    if (lane == 0) {
-      term[e] = f * (ps / (float)T);
-      aux_w[e] = alpha * (float)E * f / (float)T;
-    }
+    const float f = (float)c / ((float)T * (float)k);
+    term[e] = f * (ps / (float)T);
+    aux_w[e] = alpha * (float)E * f / (float)T;
   }
   __syncthreads();
-  if (wave == 0) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     float v = 0.f;
-    for (int e = lane; e < E; e += 64) v += term[e];
+    for (int i = lane; i < E; i += 64) v += term[i];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     if (lane == 0) loss[0] = alpha * (float)E * v;
@@ -320,18 +340,21 @@ int64_t aux_loss_ws_bytes(int T, int E) {
 
 moe_status_t launch_aux_loss(const float* logits, const int32_t* idx, int T, int E, int k,
                              float alpha, float* loss, float* aux_w, void* ws, hipStream_t s) {
-  ProfScope prof("aux_loss", s);
   const int nblk = (int)ceil_div(T, ROUTE_BWD_TOKENS);
   float* pp_part = static_cast<float*>(ws);
   int32_t* cnt_part = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                  round_up((int64_t)nblk * E * 4, 256));
+  {
+  ProfScope prof("aux_loss_part", s);
   if (E <= 64) aux_loss_part_kernel<1><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
   else if (E <= 128) aux_loss_part_kernel<2><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
   else if (E <= 256) aux_loss_part_kernel<4><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
   else aux_loss_part_kernel<8><<<nblk, 256, 0, s>>>(logits, idx, T, E, k, pp_part, cnt_part);
   const moe_status_t st = check_launch("aux_loss_part_kernel");
   if (st != MOE_OK) return st;
-  aux_loss_final_kernel<<<1, 256, 0, s>>>(pp_part, cnt_part, nblk, T, E, k, alpha, loss, aux_w);
+  }
+  ProfScope prof("aux_loss_final", s);
+  aux_loss_final_kernel<<<1, 512, 0, s>>>(pp_part, cnt_part, nblk, T, E, k, alpha, loss, aux_w);
   return check_launch("aux_loss_final_kernel");
 }
 
