@@ -933,7 +933,7 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
 // once fill the memory pipeline's address queue and stall their own MFMA
 // issue; parts spread the loads over the step.
 #ifndef MOE_LOAD_SPLIT
-#define MOE_LOAD_SPLIT 1
+#define MOE_LOAD_SPLIT 2
 #endif
 template <int BM, int BN, int WGM, int WGN, int P, int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p) {
