@@ -1379,24 +1379,26 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
   // ---- compute cursor (every wave keeps it; it decides when the loop ends)
   int c_pos = slot, c_ks = 0, c_nk = 0;
   TileDesc ct;
-  auto compute_seek = [&]() __attribute__((always_inline)) {
+  // (the producer and compute forms are separate instances, so that the
+  // producer loop never holds the accumulators live)
+  auto compute_seek = [&](auto Cc) __attribute__((always_inline)) {
     for (; c_pos < x_n; c_pos += S) {
       ct = tile_desc<BM, BN, GMD, B2>(p, x_lo + c_pos);
       c_nk = slices(ct);
       c_ks = 0;
       if (c_nk > 0) break;
-      if (!producer) store_block(ct);  // a tile without K slices is zero
+      if constexpr (decltype(Cc)::value) store_block(ct);  // a tile without K slices is zero
     }
   };
   // after a step: true while slices are left
-  auto advance = [&]() __attribute__((always_inline)) -> bool {
+  auto advance = [&](auto Cc) __attribute__((always_inline)) -> bool {
     if (++c_ks < c_nk) return true;
-    if (!producer) {
+    if constexpr (decltype(Cc)::value) {
       store_block(ct);
       zero_acc();
     }
     c_pos += S;
-    compute_seek();
+    compute_seek(Cc);
     return c_pos < x_n;
   };
 
@@ -1411,7 +1413,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
       (issue(std::integral_constant<int, Us>{}, true), ...);
     }(std::make_integer_sequence<int, PD>{});
-    compute_seek();
+    compute_seek(std::false_type{});
     if (c_pos >= x_n) return;  // every tile of this workgroup was empty
     LA::store(da[0], smem, ptid);
     LB::store(db[0], smem + BM * BK, ptid);
@@ -1427,7 +1429,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
       }
       __syncthreads();
       ++g;
-      return advance();
+      return advance(std::false_type{});
     };
     constexpr int UN = (PD % 2 == 0) ? PD : 2 * PD;  // steps until stage and buffer repeat
     while ([&]<int... Vs>(std::integer_sequence<int, Vs...>) __attribute__((always_inline)) {
@@ -1436,7 +1438,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     }
   } else {
     zero_acc();
-    compute_seek();
+    compute_seek(std::true_type{});
     if (c_pos >= x_n) return;
     __syncthreads();
     int g = 0;
@@ -1446,7 +1448,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
                                                      ct.m_hi - ct.m_lo);
       __syncthreads();
       ++g;
-      return advance();
+      return advance(std::true_type{});
     };
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
