@@ -27,9 +27,10 @@ def upload(w: MI.Workload, arrays):
     return dev
 
 
-def run_layer(w: MI.Workload, dev, R_cap=0, training=True, poison=False, gather=False):
+def run_layer(w: MI.Workload, dev, R_cap=0, training=True, poison=False, gather=False,
+              aux_alpha=None):
     s = shape_of(w, R_cap)
-    buf = LayerBuffers(s, training=training, gather=gather)
+    buf = LayerBuffers(s, training=training, gather=gather, aux_alpha=aux_alpha)
     if poison:
         for v in buf.t.values():
             if v is not None and v.is_floating_point():
@@ -205,3 +206,22 @@ def assert_same_outputs(a, b, R, balanced=False):
         v1 = t1 if t1.dtype == torch.int32 else t1.view(torch.uint8)
         v2 = t2 if t2.dtype == torch.int32 else t2.view(torch.uint8)
         assert torch.equal(v1, v2), f"{name} differs"
+
+
+def compare_aux(w: MI.Workload, a, buf, f, bw, alpha):
+    """The balancing loss, its backward weights and the router gradients
+    that include its term, against the oracle (forward f, backward bw
+    without the loss)."""
+    t = buf.t
+    r = O.aux_loss(f["logits"], f["idx"], w.E, alpha)
+    got = t["aux_loss"].item()
+    assert abs(got - r["loss"]) <= 2e-5 * abs(r["loss"]), f"aux_loss {got} vs {r['loss']}"
+    check("aux_w", np64(t["aux_w"]), r["w"], 2e-5)
+    dLa = O.aux_loss_dlogits(f["logits"], r["w"])
+    zero = np.zeros(f["idx"].shape)
+    rb = O.route_bwd(a["x"], a["Wr"], f["idx"], zero, zero, O.GATE_SOFTMAX_TOPK, dL_aux=dLa)
+    tol = TOL[w.dtype]
+    check("dlogits(aux)", np64(t["dlogits"]), bw["dL"] + rb["dL"], tol)
+    check("dw_router(aux)", np64(t["dw_router"]), bw["dWr"] + rb["dWr"], tol)
+    check("dbias(aux)", np64(t["dbias"]), bw["db"] + rb["db"], tol)
+    check("dx(aux)", np64(t["dx"]), bw["dX"] + rb["dX"], tol)

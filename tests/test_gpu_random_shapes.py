@@ -2,7 +2,8 @@
 gate, the dtype, a local expert range and a row capacity drawn at random
 (within the supported shapes), so that ragged tails land differently in every
 tile shape the GEMMs pick.  Each case runs the plain and the gathered FFN
-(and, for the forward, the small-batch path) against the CPU oracle."""
+(and, for the forward, the small-batch path; for the natural gate, the
+router's balancing loss too) against the CPU oracle."""
 import sys
 
 import numpy as np
@@ -67,6 +68,9 @@ def test_random_shape(case):
     for gather in (False, True):
         _, buf = U.run_layer(w, dev, R_cap=R_cap, gather=gather)
         U.compare_full(w, a, buf, f, bw)
+    if w.gate == "softmax_topk":  # with the router's balancing loss
+        _, buf = U.run_layer(w, dev, R_cap=R_cap, aux_alpha=0.05)
+        U.compare_aux(w, a, buf, f, bw, 0.05)
     if not R_cap and w.T * w.k <= 65535:
         _, sb = run_small(w, dev)
         U.check("y(small)", U.np64(sb["y"]), f["y"], U.TOL[w.dtype])
