@@ -37,6 +37,10 @@ SMALL = [
     # expert width >= 768: the wide tile of the dSwiGLU GEMM, ragged groups
     MI.small_workload("wide_I_T300_d128_E8_k2_I1536", 300, 128, 8, 2, 1536, bias_sigma=1.0, seed=28),
     MI.small_workload("wide_I_T260_d192_E8_k2_I768", 260, 192, 8, 2, 768, bias_sigma=1.0, seed=41),
+    # 104 row tiles x 3 wide column tiles: more tiles than compute units, a
+    # partial second wave
+    MI.small_workload("tail_split_T3200_d64_E8_k8_I768", 3200, 64, 8, 8, 768, bias_sigma=1.0,
+                      seed=43),
 ]
 
 
