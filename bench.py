@@ -330,7 +330,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(expert parallelism across GPUs is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
