@@ -684,6 +684,14 @@ struct BlockOut {
   }
 };
 
+// Result staging in LDS: besides the chunk swizzle, the two 8-byte halves of
+// a 16-byte chunk are swapped in rows where stage_swap(r), so that the 32
+// lanes of an accumulator write (rows r..r+31, one 8-byte half each) hit 32
+// different 8-byte bank groups instead of 16; whole-chunk readers and writers
+// swap them back with swap_halves.
+__device__ __forceinline__ int stage_swap(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
+__device__ __forceinline__ uint4 swap_halves(uint4 v, int s) { return s ? make_uint4(v.z, v.w, v.x, v.y) : v; }
+
 // Plain-store epilogue staged through LDS: the wave tiles are written to LDS
 // as bf16, then every store instruction writes whole 16-byte chunks of
 // consecutive columns (full cache lines per row) instead of 8-byte pieces
@@ -720,7 +728,7 @@ __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x1
           for (int q = 0; q < 4; ++q) {
             const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
             const int c = (n >> 3) ^ (r & 15);
-            *reinterpret_cast<uint2*>(lds + r * BN + c * 8 + (n & 7)) =
+            *reinterpret_cast<uint2*>(lds + r * BN + c * 8 + ((n & 7) ^ (stage_swap(r) << 2))) =
                 make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                            pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
           }
@@ -736,7 +744,7 @@ __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x1
     for (int i = 0; i < NQ; ++i) {
       const int q = min(i * NT + tid, RB * CPR - 1);
       const int r = q / CPR, c = q % CPR;
-      v[i] = *reinterpret_cast<const uint4*>(lds + r * BN + (c ^ (r & 15)) * 8);
+      v[i] = swap_halves(*reinterpret_cast<const uint4*>(lds + r * BN + (c ^ (r & 15)) * 8), stage_swap(r));
     }
     // buffer stores relative to the band's first row: a masked lane gets an
     // out-of-range offset and its store is dropped, so no lane branches
@@ -757,8 +765,14 @@ __device__ __forceinline__ void epilogue_store_staged(const GemmParams& p, f32x1
 // c of row r at c ^ (r & 15), so that memory is read and written in whole
 // 16-byte chunks of consecutive columns (full cache lines per row) instead
 // of 8-byte pieces spread over 32 rows.
+// (halves swapped by stage_swap as in the plain staging).  band_off gives
+// element n of row r; band_chunk the start of whole chunk c.
 template <int W = 128>
-__device__ __forceinline__ int band_off(int r, int n) { return r * W + (((n >> 3) ^ (r & 15)) << 3) + (n & 7); }
+__device__ __forceinline__ int band_off(int r, int n) {
+  return r * W + (((n >> 3) ^ (r & 15)) << 3) + ((n & 7) ^ (stage_swap(r) << 2));
+}
+template <int W = 128>
+__device__ __forceinline__ int band_chunk(int r, int c) { return r * W + ((c ^ (r & 15)) << 3); }
 
 // SwiGLU: gate columns n0 .. n0+127 and the matching up columns of the tile
 // give H = [Hg | Hu] (optional) and A = silu(Hg) * Hu.
@@ -811,12 +825,12 @@ __device__ __forceinline__ void epilogue_swiglu_staged(const GemmParams& p, f32x
       const int q = q0 + tid;
       const int r = q / (HC / 8), c = q % (HC / 8);
       const bool ok = mb + r < m_hi && n0 + c * 8 < I;
-      const int o = band_off(r, c * 8);
-      const u32x4 va = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(As + o));
+      const int o = band_chunk(r, c), sw = stage_swap(r);
+      const u32x4 va = __builtin_bit_cast(u32x4, swap_halves(*reinterpret_cast<const uint4*>(As + o), sw));
       __builtin_amdgcn_raw_buffer_store_b128(va, rsa, ok ? (int)(((int64_t)r * I + c * 8) * 2) : OOB, 0, 0);
       if (H) {
-        const u32x4 vg = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Gs + o));
-        const u32x4 vu = __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Us + o));
+        const u32x4 vg = __builtin_bit_cast(u32x4, swap_halves(*reinterpret_cast<const uint4*>(Gs + o), sw));
+        const u32x4 vu = __builtin_bit_cast(u32x4, swap_halves(*reinterpret_cast<const uint4*>(Us + o), sw));
         const int oh = ok ? (int)(((int64_t)r * 2 * I + c * 8) * 2) : OOB;
         __builtin_amdgcn_raw_buffer_store_b128(vg, rsg, oh, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(vu, rsu, oh, 0, 0);
@@ -864,8 +878,8 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
         const int q = i * NT + tid;
         if (WTM * CPR % NT == 0 || q < WTM * CPR) {
           const int r = q / CPR, c = q % CPR;
-          *reinterpret_cast<uint4*>(Gs + band_off<BN>(r, c * 8)) = vg[i];
-          *reinterpret_cast<uint4*>(Us + band_off<BN>(r, c * 8)) = vu[i];
+          *reinterpret_cast<uint4*>(Gs + band_chunk<BN>(r, c)) = swap_halves(vg[i], stage_swap(r));
+          *reinterpret_cast<uint4*>(Us + band_chunk<BN>(r, c)) = swap_halves(vu[i], stage_swap(r));
         }
       }
     }
@@ -910,11 +924,11 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
       const int r = q / CPR, c = q % CPR;
       const bool ok = (WTM * CPR % NT == 0 || q < WTM * CPR) && mb + r < m_hi && n0 + c * 8 < I;
       const int off = ok ? (int)(((int64_t)r * 2 * I + c * 8) * 2) : OOB;
-      const int o = band_off<BN>(r, c * 8);
+      const int o = band_chunk<BN>(r, c), sw = stage_swap(r);
       __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Gs + o)), rsg, off, 0, 0);
+          __builtin_bit_cast(u32x4, swap_halves(*reinterpret_cast<const uint4*>(Gs + o), sw)), rsg, off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(Us + o)), rsu, off, 0, 0);
+          __builtin_bit_cast(u32x4, swap_halves(*reinterpret_cast<const uint4*>(Us + o), sw)), rsu, off, 0, 0);
     }
   }
 }
