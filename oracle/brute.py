@@ -107,7 +107,9 @@ def layer_forward(x, Wr, b, Wg, Wu, Wd, k, gate, E):
 
 def stable_groups(idx, E, e_lo=0, e_hi=None):
     """perm and group sizes by definition: for each expert in ascending order,
-    every flattened row t*k+j with that expert, in ascending row order."""
+    every flattened row t*k+j with that expert, in ascending row order; a
+    token that names one expert in several slots visits it once, through the
+    first of those slots."""
     e_hi = E if e_hi is None else e_hi
     T, k = len(idx), len(idx[0])
     perm, counts = [], []
@@ -118,6 +120,7 @@ def stable_groups(idx, E, e_lo=0, e_hi=None):
                 if int(idx[t][j]) == e:
                     perm.append(t * k + j)
                     c += 1
+                    break  # the token's later slots naming e are not visited
         counts.append(c)
     return perm, counts
 

@@ -130,12 +130,22 @@ def permute(idx, x, E, e_lo=0, e_hi=None, R_cap=None):
     Returns dict(counts [E_loc], offsets [E_loc+1], perm [R], inv [T*k], Xp [R,d]).
     Only rows whose expert lies in [e_lo, e_hi) are kept; ``inv`` is -1 for the
     others.  Rows whose sorted position is >= R_cap are dropped as well (their
-    ``inv`` is -1 and the offsets are clamped to R_cap)."""
+    ``inv`` is -1 and the offsets are clamped to R_cap).
+
+    A routing table handed in by a caller may name one expert in several
+    slots of a token (the router never does: its k experts are distinct).
+    The pages do not cover this; the reading taken is that a token visits an
+    expert once, through the first slot that names it, and its later slots
+    with the same id are dropped like non-local ones (``inv`` = -1)."""
     e_hi = E if e_hi is None else e_hi
     T, k = idx.shape
-    flat = idx.reshape(-1).astype(np.int64)
+    ids = np.asarray(idx, dtype=np.int64)
+    first = np.ones((T, k), dtype=bool)   # slot j names an id no earlier slot of its token names
+    for j in range(1, k):
+        first[:, j] = ~np.any(ids[:, :j] == ids[:, j:j + 1], axis=1)
+    flat = ids.reshape(-1)
     E_loc = e_hi - e_lo
-    local = (flat >= e_lo) & (flat < e_hi)
+    local = (flat >= e_lo) & (flat < e_hi) & first.reshape(-1)
     counts = np.bincount(flat[local] - e_lo, minlength=E_loc).astype(np.int64)
     offsets = np.concatenate([[0], np.cumsum(counts)])
     rows = np.nonzero(local)[0]                       # ascending flattened row

@@ -173,6 +173,72 @@ def test_balanced_closed_form(T, E, k):
         assert (got == want).all()
 
 
+def test_repeated_and_foreign_ids_hand_example():
+    """A caller's table with repeated and out-of-range ids (hand-worked)."""
+    gold = json.load(open(os.path.join(GOLD, "repeated_ids_example.json")))
+    idx = np.array(gold["idx"], dtype=np.int32)
+    E = gold["E"]
+    p = O.permute(idx, None, E)
+    assert p["counts"].tolist() == gold["counts"]
+    assert p["offsets"].tolist() == gold["offsets"]
+    assert p["perm"].tolist() == gold["perm"]
+    assert p["inv"].tolist() == gold["inv"]
+    kept = (p["inv"] >= 0).reshape(idx.shape)
+    assert kept.tolist() == gold["kept_slots"]
+    q = O.permute(idx, None, E, e_lo=2, e_hi=6)
+    loc = gold["local_2_6"]
+    assert q["counts"].tolist() == loc["counts"]
+    assert q["offsets"].tolist() == loc["offsets"]
+    assert q["perm"].tolist() == loc["perm"]
+    assert q["inv"].tolist() == loc["inv"]
+
+
+@pytest.mark.parametrize("seed,e_lo,e_hi", [(0, 0, 6), (1, 1, 4), (2, 5, 6)])
+def test_permute_with_repeated_ids_matches_definition(seed, e_lo, e_hi):
+    """Random tables drawn with replacement (repeats) and ids outside [0, E)."""
+    r = _rng(100 + seed)
+    T, E, k = 31, 6, 4
+    idx = r.integers(-1, E + 2, size=(T, k)).astype(np.int32)
+    p = O.permute(idx, None, E, e_lo, e_hi)
+    perm, counts = brute.stable_groups(idx.tolist(), E, e_lo, e_hi)
+    assert p["perm"].tolist() == perm
+    assert p["counts"].tolist() == counts
+    # every kept slot is the first of its token to name its (local) expert
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            keep = e_lo <= e < e_hi and e not in seen
+            seen.add(e)
+            assert (p["inv"][t * k + j] >= 0) == keep
+
+
+def test_forward_with_caller_table_vs_brute():
+    """y for a table with repeats: each token's distinct local experts, each
+    weighted by the gate weight of the first slot that names it."""
+    x, Wr, b, Wg, Wu, Wd = _tiny(77, T=6, d=3, E=4, k=3, I=2)
+    idx = np.array([[1, 1, 2], [3, 0, 3], [2, 2, 2], [0, 1, 3], [5, 1, -2], [0, 0, 1]],
+                   dtype=np.int32)
+    g = _rng(78).random(idx.shape)
+    T, k = idx.shape
+    p = O.permute(idx, x, 4)
+    f = O.expert_ffn_fwd(p["Xp"], p["offsets"], Wg, Wu, Wd)
+    y = O.combine(f["Yp"], p["inv"], g, T, k)
+    want = []
+    for t in range(T):
+        acc = [0.0] * x.shape[1]
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if e in seen or not 0 <= e < 4:
+                continue
+            seen.add(e)
+            out = brute.ffn(x[t].tolist(), Wg[e].tolist(), Wu[e].tolist(), Wd[e].tolist())
+            acc = [a + g[t, j] * o for a, o in zip(acc, out)]
+        want.append(acc)
+    np.testing.assert_allclose(y, np.array(want), rtol=1e-12, atol=1e-14)
+
+
 def test_capacity_drop_keeps_sorted_prefix():
     r = _rng(11)
     T, E, k = 30, 5, 2

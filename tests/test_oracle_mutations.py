@@ -28,7 +28,11 @@ MUTATIONS = [
     ("balanced gate index transposed", "idx = ((t % P) + i * P).astype(np.int32)",
      "idx = ((t % P) * k + i).astype(np.int32)"),
     ("balanced gate weight not 1/k", "g = np.full((T, k), 1.0 / k)", "g = np.full((T, k), 1.0)"),
-    ("unstable sort", 'perm = rows[np.argsort(flat[rows], kind="stable")]',
+    ("repeated expert ids all kept", "local = (flat >= e_lo) & (flat < e_hi) & first.reshape(-1)",
+     "local = (flat >= e_lo) & (flat < e_hi)"),
+    ("repeat test against slot 0 only", "first[:, j] = ~np.any(ids[:, :j] == ids[:, j:j + 1], axis=1)",
+     "first[:, j] = ~np.any(ids[:, :1] == ids[:, j:j + 1], axis=1)"),
+    ("unstable sort",'perm = rows[np.argsort(flat[rows], kind="stable")]',
      'perm = rows[np.argsort(flat[rows], kind="quicksort")]'),
     ("capacity keeps the tail", "perm = perm[:cap]", "perm = perm[-cap:]"),
     ("offsets not clamped to capacity", "offsets = np.minimum(offsets, cap)", "offsets = offsets"),
