@@ -119,7 +119,7 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
                        const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
                        moe_stream_t stream);
 
-/* a2 -- permute ("sort tokens by their assigned expert", [P3] section 专家后端).
+/* a2 -- permute: the rows sorted by their expert ([P3] section 专家后端, grouped_mm row).
  * Rows r = t*k + j whose expert e = topk_idx[t,j] is local (e_lo <= e < e_hi)
  * are ordered by expert and, inside an expert, by r (a stable sort; the
  * result is unique).  Outputs:
@@ -138,8 +138,8 @@ moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, cons
                          int32_t* group_offsets, int32_t* perm, int32_t* inv, void* xp,
                          void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* a3 + a4 -- expert FFN over the expert groups as grouped GEMMs ("a single
- * grouped GEMM", [P3] section 专家后端; experts are fused 3-D weight tensors,
+/* a3 + a4 -- expert FFN over the expert groups as grouped GEMMs (one grouped
+ * GEMM over all groups, [P3] section 专家后端; experts are fused 3-D weight tensors,
  * [P3] note under the Qwen3 table).  For each local expert i and every row p
  * in [o_i, o_{i+1}):
  *   Hg = xp[p] * w_gate[i], Hu = xp[p] * w_up[i]      (fp32 accumulation)
@@ -171,7 +171,7 @@ moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, const void* x,
                                         void* yp, void* ws, size_t ws_bytes,
                                         moe_stream_t stream);
 
-/* a5 -- combine (the "combine" half of dispatch/combine, [P3] section 加速来源):
+/* a5 -- combine (the second of the two token-movement kernels, [P3] section 加速来源, DeepEP item):
  * y[t] = sum_j topk_w[t,j] * yp[inv[t*k+j]] over the slots with inv >= 0, in
  * ascending j, fp32 accumulation; a token with no local slot gets y[t] = 0.
  * yp [R_cap,d]; inv [T*k]; topk_w [T,k] fp32; y [T,d].  No workspace. */
@@ -190,8 +190,11 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t
  * (the sums run in another order).  x [T,d]; topk_idx, topk_w [T,k];
  * weights as for moe_grouped_ffn_fwd; y [T,d].  ws:
  * moe_workspace_size(MOE_OP_SMALL_FWD) (fp32 partial sums of [Hg | Hu] over
- * up to 8 ranges of d, the per-slot outputs and the slot map).  Every pair re-reads its expert's weights, so it pays for T*k up to
- * about E_loc.  Needs T*k <= 65535, d and I <= 12288 and no row capacity
+ * up to 8 ranges of d, the per-slot outputs and the slot map).  Every pair
+ * re-reads its expert's weights (3*d*I elements), so the form is faster than
+ * the grouped path only while T*k is at most about E_loc: measured at the
+ * Qwen3-30B-A3B shape (E_loc = 128, k = 8), 50 vs 102 us at T = 1, about equal
+ * at T = 8, 3.6x slower at T = 64.  Needs T*k <= 65535, d and I <= 12288 and no row capacity
  * (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
 moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const int32_t* topk_idx,
                                const float* topk_w, const void* w_gate, const void* w_up,

@@ -11,9 +11,10 @@
 //   G_DENSE  one plain GEMM of M x N x K;
 //   G_MROWS  expert groups along M: the rows of local expert e are
 //            [off[e], off[e+1]) of A and C, and B is expert e's weight matrix
-//            (forward and input-gradient GEMMs; "sort tokens by expert, then
-//            one grouped GEMM", page "Accelerating Transformers fine-tuning
-//            with NVIDIA NeMo AutoModel", section 专家后端);
+//            (forward and input-gradient GEMMs: the rows sorted by expert
+//            and one grouped GEMM over the groups, page "Accelerating
+//            Transformers fine-tuning with NVIDIA NeMo AutoModel", section
+//            专家后端, grouped_mm row);
 //   G_KROWS  expert groups along K: C for expert e sums over the rows
 //            [off[e], off[e+1]) of A and B (weight gradients); an expert
 //            with no rows gets C = 0.

@@ -1,8 +1,8 @@
 // Token permutation and combine kernels of the MoE layer.
 //
-// The permutation sorts the (token, slot) rows by expert ("sort tokens by
-// their assigned expert, then one grouped GEMM": page "Accelerating
-// Transformers fine-tuning with NVIDIA NeMo AutoModel", section 专家后端).
+// The permutation sorts the (token, slot) rows by expert, so that one grouped
+// GEMM can run over the expert groups (page "Accelerating Transformers
+// fine-tuning with NVIDIA NeMo AutoModel", section 专家后端, grouped_mm row).
 // It is a deterministic counting sort in three passes:
 //   1. per block of 256 tokens, one 256-bit token mask per local expert is
 //      built in LDS (atomic OR: order-free), and its popcounts are the
@@ -11,10 +11,12 @@
 //      each block its first position per expert and the group offsets;
 //   3. each block rebuilds its masks and places row (t, j) of expert e at
 //      base[block][e] + popcount(mask_e below t): stable by token, and since
-//      a token's k experts are distinct, stable by row t*k + j.
+//      a token's kept experts are distinct, stable by row t*k + j (a slot
+//      repeating an earlier slot's expert is dropped).
 // A fourth kernel copies each token's x row to its k sorted positions.
 //
-// Combine ("dispatch and combine", section 加速来源) is a gather-weighted sum
+// Combine (the pages give token dispatch and combine kernels of their own:
+// section 加速来源, DeepEP item) is a gather-weighted sum
 // back to token order; its backward and the permutation's backward are the
 // matching gather/scatter kernels.  All sums run in a fixed order.
 #include "kernels.h"
@@ -166,18 +168,22 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_scatter_kernel(const int32_t
 
 // One wavefront per token: read x[t] once, write it to every sorted position.
 // Lane j < k holds the token's j-th sorted position; the chunk loop reads it
-// back with a lane broadcast instead of reloading it.
+// back with a lane broadcast instead of reloading it.  The loop runs over
+// whole wavefronts of chunks (lanes past the last chunk idle through it), so
+// every broadcast executes with all lanes active, also when k > chunks.
 __global__ __launch_bounds__(256) void perm_gather_kernel(const uint4* x, const int32_t* inv, int T,
                                                           int k, int chunks, uint4* xp) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
-  for (int c = lane; c < chunks; c += 64) {
-    const uint4 v = x[(int64_t)t * chunks + c];
+  for (int c0 = 0; c0 < chunks; c0 += 64) {
+    const int c = c0 + lane;
+    const bool ok = c < chunks;
+    const uint4 v = ok ? x[(int64_t)t * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
     for (int j = 0; j < k; ++j) {
       const int p = __builtin_amdgcn_readlane(myp, j);
-      if (p >= 0) xp[(int64_t)p * chunks + c] = v;
+      if (ok && p >= 0) xp[(int64_t)p * chunks + c] = v;
     }
   }
 }
@@ -248,7 +254,8 @@ template <> struct Chunk<float> {
 // y[t] = sum_j w[t,j] * src[inv[t,j]] in ascending j (w NULL: weight 1).
 // One wavefront per token; lane j < k holds slot j's position and weight,
 // broadcast to the wavefront in the chunk loop; the k row loads of a chunk are
-// all issued before the first is used.
+// all issued before the first is used.  The chunk loop runs over whole
+// wavefronts of chunks, so the broadcasts execute with all lanes active.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_sum_kernel(const uint4* src, const int32_t* inv,
                                                          const float* w, int Tn, int k, int chunks,
@@ -260,7 +267,9 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const uint4* src, const
   if (t >= Tn) return;
   const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
   const float myw = lane < k ? (w ? w[(int64_t)t * k + lane] : 1.0f) : 0.0f;
-  for (int c = lane; c < chunks; c += 64) {
+  for (int c0 = 0; c0 < chunks; c0 += 64) {
+    const int c = c0 + lane;
+    const bool ok = c < chunks;
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
@@ -270,13 +279,13 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const uint4* src, const
       for (int jj = 0; jj < G; ++jj) {
         const int j = j0 + jj;
         const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
-        v[jj] = p >= 0 ? src[(int64_t)p * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
+        v[jj] = (ok && p >= 0) ? src[(int64_t)p * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int jj = 0; jj < G; ++jj) {
         const int j = j0 + jj;
         const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
-        if (p < 0) continue;
+        if (p < 0) continue;  // uniform over the wavefront
         const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), j));
         float f[N];
         Chunk<T>::unpack(v[jj], f);
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const uint4* src, const
         for (int i = 0; i < N; ++i) acc[i] = fmaf(g, f[i], acc[i]);
       }
     }
-    y[(int64_t)t * chunks + c] = Chunk<T>::pack(acc);
+    if (ok) y[(int64_t)t * chunks + c] = Chunk<T>::pack(acc);
   }
 }
 
@@ -303,7 +312,8 @@ moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float*
 }
 
 // dyp[inv[t,j]] = w[t,j] * dy[t];  dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when dropped).
-// One wavefront per token, slot data broadcast from lane j as above.
+// One wavefront per token, slot data broadcast from lane j as above (the
+// chunk loop over whole wavefronts of chunks, all lanes active).
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const uint4* yp,
                                                           const int32_t* inv, const float* w,
@@ -318,9 +328,11 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
   float part[MAXK];
 #pragma unroll
   for (int j = 0; j < MAXK; ++j) part[j] = 0.f;
-  for (int c = lane; c < chunks; c += 64) {
+  for (int c0 = 0; c0 < chunks; c0 += 64) {
+    const int c = c0 + lane;
+    const bool ok = c < chunks;
     float fy[N];
-    Chunk<T>::unpack(dy[(int64_t)t * chunks + c], fy);
+    Chunk<T>::unpack(ok ? dy[(int64_t)t * chunks + c] : make_uint4(0u, 0u, 0u, 0u), fy);
 #pragma unroll
     for (int j0 = 0; j0 < MAXK; j0 += 8) {
       if (j0 >= k) break;  // uniform
@@ -329,13 +341,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
-        v[jj] = p >= 0 ? yp[(int64_t)p * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
+        v[jj] = (ok && p >= 0) ? yp[(int64_t)p * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int p = j < k ? __builtin_amdgcn_readlane(myp, j) : -1;
-        if (p < 0) continue;
+        if (p < 0) continue;  // uniform over the wavefront
         const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), j));
         float f[N], o[N];
         Chunk<T>::unpack(v[jj], f);
@@ -345,8 +357,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
           a = fmaf(fy[i], f[i], a);
           o[i] = g * fy[i];
         }
-        part[j] += a;
-        dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
+        part[j] += a;  // lanes past the last chunk add zeros
+        if (ok) dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
       }
     }
   }
@@ -356,7 +368,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
       float v = part[j];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) dw[(int64_t)t * k + j] = __builtin_amdgcn_readlane(myp, j) >= 0 ? v : 0.f;
+      const bool kept = __builtin_amdgcn_readlane(myp, j) >= 0;  // all lanes active here
+      if (lane == 0) dw[(int64_t)t * k + j] = kept ? v : 0.f;
     }
   }
 }

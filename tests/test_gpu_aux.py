@@ -24,8 +24,10 @@ CASES = [
     MI.small_workload("aux_T500_d256_E128_k8_I256", 500, 256, 128, 8, 256, bias_sigma=1.5, seed=63),
     MI.small_workload("aux_T70_d128_E320_k6_I128", 70, 128, 320, 6, 128, bias_sigma=1.0, seed=64),
 ]
-# the aux kernels sum in fp32 over T tokens; the oracle is fp64
-AUX_TOL = 2e-5
+# the loss, its backward weights and the router gradients are fp32 outputs
+# (fp32 softmax of fp32 logits, fp32 sums over the tokens), held to the fp32
+# bound max|err| / max|ref| <= 1e-5 against the fp64 oracle
+AUX_TOL = 1e-5
 
 
 def _run(w, a, alpha, zero_dy=False):
@@ -86,10 +88,10 @@ def test_aux_gradient_alone(w):
     L, idx = O.router_logits(a["x"], a["Wr"], a.get("b")), t["topk_idx"].cpu().numpy()
     r, rb = _aux_only_router_grads(w, a, L, idx, alpha)
     tol = U.TOL[w.dtype]
-    # dlogits: fp32 softmax of fp32 logits on the GPU
-    U.check("dlogits", U.np64(t["dlogits"]), rb["dL"], 1e-4)
+    # dlogits and dbias are fp32 outputs (fp32 softmax of fp32 logits)
+    U.check("dlogits", U.np64(t["dlogits"]), rb["dL"], AUX_TOL)
     U.check("dw_router", U.np64(t["dw_router"]), rb["dWr"], tol)
-    U.check("dbias", U.np64(t["dbias"]), rb["db"], 1e-4)
+    U.check("dbias", U.np64(t["dbias"]), rb["db"], AUX_TOL)
     U.check("dx", U.np64(t["dx"]), rb["dX"], tol)
 
 
@@ -117,7 +119,7 @@ def test_full_size_qwen3_natural_aux():
     assert abs(t["aux_loss"].item() - rg["loss"]) <= AUX_TOL * abs(rg["loss"])
     U.check("aux_w", U.np64(t["aux_w"]), rg["w"], AUX_TOL)
     r, rb = _aux_only_router_grads(w, a, Lg, idxg, alpha)
-    U.check("dlogits", U.np64(t["dlogits"]), rb["dL"], 1e-4)
+    U.check("dlogits", U.np64(t["dlogits"]), rb["dL"], AUX_TOL)
     U.check("dw_router", U.np64(t["dw_router"]), rb["dWr"], U.TOL["bf16"])
-    U.check("dbias", U.np64(t["dbias"]), rb["db"], 1e-4)
+    U.check("dbias", U.np64(t["dbias"]), rb["db"], AUX_TOL)
     U.check("dx", U.np64(t["dx"]), rb["dX"], U.TOL["bf16"])

@@ -48,23 +48,13 @@ def test_small_batch_matches_oracle(w):
     print(f"y rel err {e:.2e}")
 
 
-def _oracle_y(x, idx, g, Wg, Wu, Wd, e_lo, e_hi):
-    """y[t] = sum over the local first-occurrence slots of g * FFN_e(x[t]),
-    one (token, slot) pair at a time with the oracle's expert FFN."""
+def _oracle_y(x, idx, g, Wg, Wu, Wd, E, e_lo, e_hi):
+    """The oracle's layer output for a given routing table: permute (local,
+    first-occurrence slots), expert FFN, combine."""
     T, k = idx.shape
-    y = np.zeros((T, x.shape[1]))
-    for t in range(T):
-        seen = set()
-        for j in range(k):
-            e = int(idx[t, j])
-            if not (e_lo <= e < e_hi) or e in seen:
-                continue
-            seen.add(e)
-            le = e - e_lo
-            f = O.expert_ffn_fwd(x[t:t + 1].astype(np.float64), np.array([0, 1]),
-                                 Wg[le:le + 1], Wu[le:le + 1], Wd[le:le + 1])
-            y[t] += g[t, j] * f["Yp"][0]
-    return y
+    p = O.permute(idx, x, E, e_lo, e_hi)
+    f = O.expert_ffn_fwd(p["Xp"], p["offsets"], Wg, Wu, Wd)
+    return O.combine(f["Yp"], p["inv"], g, T, k)
 
 
 @pytest.mark.parametrize("T", [1, 8, 64])
@@ -79,7 +69,7 @@ def test_decode_sizes_qwen3_shape(T):
     _, sb = run_small(w, dev)
     L, idx, g = O.route(a["x"], a["Wr"], a["b"], w.k, w.gate)
     assert np.array_equal(sb["topk_idx"].cpu().numpy(), idx)
-    ref = _oracle_y(a["x"], idx, g, a["Wg"], a["Wu"], a["Wd"], 0, w.E)
+    ref = _oracle_y(a["x"], idx, g, a["Wg"], a["Wu"], a["Wd"], w.E, 0, w.E)
     U.check("y(small)", U.np64(sb["y"]), ref, U.TOL["bf16"])
     _, gb = U.run_layer(w, dev, training=False)
     U.check("y(small) vs y(grouped)", U.np64(sb["y"]), U.np64(gb["y"]), U.TOL["bf16"])
@@ -108,7 +98,7 @@ def test_routing_table_with_foreign_and_repeated_experts(dtype):
     B.moe_ffn_small_fwd(s, dev["x"], torch.from_numpy(idx).cuda(), torch.from_numpy(g).cuda(),
                         dev["Wg"], dev["Wu"], dev["Wd"], y, ws)
     torch.cuda.synchronize()
-    ref = _oracle_y(a["x"], idx, g.astype(np.float64), a["Wg"], a["Wu"], a["Wd"], 4, 12)
+    ref = _oracle_y(a["x"], idx, g.astype(np.float64), a["Wg"], a["Wu"], a["Wd"], E, 4, 12)
     got = U.np64(y)
     assert np.all(got[4] == 0)
     U.check("y", got, ref, U.TOL[dtype])
