@@ -23,7 +23,9 @@
  *   stated otherwise.  Matrices are row-major and dense (no padding).
  * - The caller owns every buffer.  The library never allocates, frees or keeps
  *   device memory; it keeps no state between calls except the optional kernel
- *   timer (moe_prof_*) and a thread-local error string.
+ *   timer (moe_prof_*), a thread-local error string, and the one static
+ *   scratch array of moe_grouped_ffn_fwd_gather_noalloc (4 MiB per device,
+ *   part of the library image, held until the process ends).
  * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the
  *   default stream) and returns without waiting for them.  Data-dependent sizes
  *   (group sizes, the routed row count R) stay on the device: buffers are sized
@@ -170,6 +172,27 @@ moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, const void* x,
                                         const void* w_down, void* h_save, void* a_save,
                                         void* yp, void* ws, size_t ws_bytes,
                                         moe_stream_t stream);
+
+/* moe_grouped_ffn_fwd_gather without a workspace, for callers that cannot
+ * allocate (code under HIP-graph capture, serving loops, harnesses that
+ * forbid allocation).  Same arguments, kernels and bit-identical results as
+ * moe_grouped_ffn_fwd_gather minus ws/ws_bytes: the tile tables and the token
+ * table live in a static device array of 4 MiB per device instead (enough
+ * for R_cap up to about 900,000 rows; a shape whose tables need more returns
+ * MOE_ERR_UNSUPPORTED before anything is launched).  The call allocates
+ * nothing: on its first call on a device it looks up that device's copy of
+ * the array (hipGetSymbolAddress, with the device current) and keeps the
+ * address.  Every call rewrites the part of the array it reads, so nothing
+ * needs clearing between calls; but every call on one device shares that
+ * device's array, so calls that may overlap on one device (different
+ * streams without ordering between them) race and give wrong results.  The
+ * stream must belong to the current device. */
+moe_status_t moe_grouped_ffn_fwd_gather_noalloc(const moe_shape_t* shape, const void* x,
+                                                const int32_t* perm,
+                                                const int32_t* group_offsets,
+                                                const void* w_gate, const void* w_up,
+                                                const void* w_down, void* h_save, void* a_save,
+                                                void* yp, moe_stream_t stream);
 
 /* a5 -- combine (the second of the two token-movement kernels, [P3] section 加速来源, DeepEP item):
  * y[t] = sum_j topk_w[t,j] * yp[inv[t*k+j]] over the slots with inv >= 0, in

@@ -27,7 +27,7 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_
            "moe_grouped_ffn_bwd", "moe_permute_bwd", "moe_route_bwd", "moe_prof_enable",
            "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names",
            "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd",
-           "moe_aux_loss", "moe_route_bwd_aux"]
+           "moe_aux_loss", "moe_route_bwd_aux", "moe_grouped_ffn_fwd_gather_noalloc"]
 
 
 class MoEError(RuntimeError):
@@ -90,6 +90,7 @@ def load_library() -> ctypes.CDLL:
         "moe_combine_bwd": [S, P, P, P, P, P, P, P],
         "moe_grouped_ffn_bwd": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_grouped_ffn_fwd_gather": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_grouped_ffn_fwd_gather_noalloc": [S, P, P, P, P, P, P, P, P, P, P],
         "moe_ffn_small_fwd": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
@@ -166,6 +167,14 @@ def moe_grouped_ffn_fwd_gather(shape, x, perm, group_offsets, w_gate, w_up, w_do
         ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(group_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(yp), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def moe_grouped_ffn_fwd_gather_noalloc(shape, x, perm, group_offsets, w_gate, w_up, w_down,
+                                       h_save, a_save, yp, stream=None):
+    _check("moe_grouped_ffn_fwd_gather_noalloc",
+           load_library().moe_grouped_ffn_fwd_gather_noalloc(
+               ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(group_offsets), _ptr(w_gate),
+               _ptr(w_up), _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(yp), _stream(stream)))
 
 
 def moe_ffn_small_fwd(shape, x, topk_idx, topk_w, w_gate, w_up, w_down, y, ws, stream=None):

@@ -476,6 +476,63 @@ extern "C" moe_status_t moe_grouped_ffn_fwd_gather(const moe_shape_t* shape, con
                  w_down, h_save, a_save, yp, ws, ws_bytes_, stream);
 }
 
+// ---------------------------------------------------------------- no allocation
+// The gathered FFN forward for callers that cannot allocate (code under
+// HIP-graph capture, serving loops, harnesses that forbid allocation): its
+// tile tables and token table live in this file-scope device array instead
+// of a caller workspace.  Each device holds its own copy until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (the array's name on the host is a
+// host-side stand-in, not a device address).
+constexpr int64_t MOE_NOALLOC_SCRATCH_BYTES = (int64_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MOE_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[MOE_MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+moe_status_t noalloc_scratch(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= MOE_MAX_DEVICES)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", fn, dev,
+                MOE_MAX_DEVICES);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status_t moe_grouped_ffn_fwd_gather_noalloc(
+    const moe_shape_t* shape, const void* x, const int32_t* perm, const int32_t* group_offsets,
+    const void* w_gate, const void* w_up, const void* w_down, void* h_save, void* a_save, void* yp,
+    moe_stream_t stream) {
+  const char* fn = "moe_grouped_ffn_fwd_gather_noalloc";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  const int64_t want = ws_bytes(D, MOE_OP_FFN_FWD);
+  if (want > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: this shape needs %lld bytes of scratch; the static scratch holds %lld "
+                "(use moe_grouped_ffn_fwd_gather with a workspace)",
+                fn, (long long)want, (long long)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(fn, &ws));
+  return ffn_fwd(fn, true, shape, x, perm, group_offsets, w_gate, w_up, w_down, h_save, a_save, yp,
+                 ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 extern "C" moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x,
                                           const int32_t* topk_idx, const float* topk_w,
                                           const void* w_gate, const void* w_up,

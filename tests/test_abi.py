@@ -244,3 +244,13 @@ def test_aux_loss_validation(lib):
     assert bwd(s, logits=None) == ("MOE_ERR_ARG", "moe_route_bwd_aux: logits is NULL")
     st, msg = bwd(shape(T=100, d=128, E=16, k=2, I=256, gate="balanced"))
     assert st == "MOE_ERR_ARG" and "balanced" in msg
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """The entry point without a workspace refuses a shape whose tile and
+    token tables exceed its static scratch, before any device work."""
+    s = shape(T=262144, d=128, E=8, k=8)        # R_cap = 2M rows: 8 MiB of token table
+    st = lib.moe_grouped_ffn_fwd_gather_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, None, FAKE, FAKE, None)
+    assert B.STATUS[st] == "MOE_ERR_UNSUPPORTED"
+    assert "static scratch" in lib.moe_last_error().decode()
