@@ -54,6 +54,11 @@ GEMMS = {
     "ffn_gateup_wgrad_gather":
                         (lambda R, d, I, El, T: 4 * R * d * I,
                          lambda R, d, I, El, T: 2 * (T * d + 2 * R * I + 2 * El * d * I)),
+    # the down projection with the combine in its epilogue: also reads the
+    # token's rows of Yp back and writes y
+    "ffn_down_fwd_combine":
+                        (lambda R, d, I, El, T: 2 * R * I * d,
+                         lambda R, d, I, El, T: 2 * (R * I + El * I * d + 2 * R * d + T * d)),
 }
 
 
@@ -69,10 +74,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(budget_s: float):
+def cpu_baseline(budget_s: float, dsv3_sample: bool = True):
     """The oracle (numpy fp64) timed on the host on a bounded sample of the
     workload: the same layer with the first T_s tokens (balanced gate, so every
-    expert keeps an equal share of rows)."""
+    expert keeps an equal share of rows), each step of the layer timed on its
+    own.  Also (dsv3_sample) the oracle's expert FFN, forward and backward, on
+    4 of the 32 local experts of the DeepSeek-V3 rank share (1,024 rows each),
+    extrapolated to all 32."""
     import numpy as np
     import moe_inputs as MI
     from oracle import moe_oracle as O
@@ -85,25 +93,68 @@ def cpu_baseline(budget_s: float):
     a = MI.generate(w)
 
     def step(Ts):
+        """One fwd+bwd in the oracle's own call order, each call timed."""
         x, dY = a["x"][:Ts], a["dY"][:Ts]
-        t0 = time.perf_counter()
-        f = O.layer_fwd(x, a["Wr"], None, a["Wg"], a["Wu"], a["Wd"], w.k, w.gate, w.E)
-        O.layer_bwd(f, dY, x, a["Wr"], a["Wg"], a["Wu"], a["Wd"], w.k, w.gate)
-        return time.perf_counter() - t0
+        t = {}
 
-    t_probe = step(512)
+        def timed(name, fn, *args):
+            t0 = time.perf_counter()
+            r = fn(*args)
+            t[name] = time.perf_counter() - t0
+            return r
+
+        L, idx, g = timed("route", O.route, x, a["Wr"], None, w.k, w.gate)
+        p = timed("permute", O.permute, idx, x, w.E)
+        f = timed("ffn_fwd", O.expert_ffn_fwd, p["Xp"], p["offsets"], a["Wg"], a["Wu"], a["Wd"])
+        timed("combine", O.combine, f["Yp"], p["inv"], g, Ts, w.k)
+        dYp, dG = timed("combine_bwd", O.combine_bwd, dY, f["Yp"], p["inv"], g, Ts, w.k)
+        fb = timed("ffn_bwd", O.expert_ffn_bwd, p["Xp"], p["offsets"], a["Wg"], a["Wu"], a["Wd"],
+                   f["Hg"], f["Hu"], f["A"], dYp)
+        timed("permute_bwd", O.permute_bwd, fb["dXp"], p["inv"], Ts, w.k)
+        timed("route_bwd", O.route_bwd, x, a["Wr"], idx, g, dG, w.gate)
+        return sum(t.values()), t
+
+    t_probe, _ = step(512)
     est_full = t_probe * w.T / 512  # overestimates: the probe carries fixed costs
     Ts = w.T if est_full <= 2 * budget_s else int(max(512, 512 * budget_s / t_probe)) // 256 * 256
-    dt = step(Ts)
-    return {"value": round(Ts / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one fwd+bwd of the layer on the first {Ts} of {w.T} tokens "
-                      f"(balanced gate, all {w.E} experts), numpy fp64, {dt:.1f} s"}
+    dt, steps = step(Ts)
+    out = {"value": round(Ts / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"one fwd+bwd of the layer on the first {Ts} of {w.T} tokens "
+                     f"(balanced gate, all {w.E} experts), numpy fp64, {dt:.1f} s",
+           "step_s": {k: round(v, 4) for k, v in steps.items()}}
+    del a
+    if dsv3_sample:
+        wd = MI.WORKLOADS["dsv3_ep8_rank_fwdbwd_T32768_d7168_E256_loc32_k8_I2048"]
+        experts = [0, 1, 17, 31]
+        ad = MI.generate(wd, parts=("x", "dY"))
+        P = wd.E // wd.k
+        t_ffn = 0.0
+        for e in experts:
+            tok = np.arange(e, wd.T, P)  # the balanced gate sends tokens t = e mod P to expert e
+            Xe = ad["x"][tok]
+            Wg, Wu, Wd = (MI.expert_weights(wd, n, [e]) for n in ("Wg", "Wu", "Wd"))
+            one = np.array([0, len(tok)])
+            t0 = time.perf_counter()
+            fe = O.expert_ffn_fwd(Xe, one, Wg, Wu, Wd)
+            O.expert_ffn_bwd(Xe, one, Wg, Wu, Wd, fe["Hg"], fe["Hu"], fe["A"],
+                             ad["dY"][tok] / wd.k)
+            t_ffn += time.perf_counter() - t0
+        scale = wd.E_loc / len(experts)
+        out["dsv3_rank_share_ffn"] = {
+            "kind": "oracle, extrapolated", "experts_timed": experts,
+            "rows_per_expert": wd.T * wd.k // wd.E, "seconds_timed": round(t_ffn, 2),
+            "extrapolation_factor": scale,
+            "ffn_fwdbwd_s_extrapolated": round(t_ffn * scale, 2),
+            "note": "expert FFN forward and backward only (the GEMMs: over 99% of the layer's "
+                    "flops) of 4 sampled local experts, times 8 for the 32 local experts"}
+    return out
 
 
 # GEMM roles: the last template argument of the GEMM kernels
 ROLE_NAMES = {0: "route_logits", 1: "ffn_gateup_fwd", 2: "ffn_down_fwd", 3: "ffn_down_dgrad",
               4: "ffn_gateup_dgrad", 5: "ffn_down_wgrad", 6: "ffn_gateup_wgrad", 7: "route_bwd_dw",
-              8: "route_bwd_dx", 9: "ffn_gateup_fwd_gather", 10: "ffn_gateup_wgrad_gather"}
+              8: "route_bwd_dx", 9: "ffn_gateup_fwd_gather", 10: "ffn_gateup_wgrad_gather",
+              11: "ffn_down_fwd_combine"}
 
 
 def gemm_role_of(kernel_name: str):
@@ -185,121 +236,177 @@ def kernel_averages(step, B, n: int):
     return res
 
 
-def secondary_workloads(B, dev, w_main, gather):
+def secondary_workloads(B, dev, w_main, gather, which="all"):
     """The main workload with the other FFN form (Xp materialised by the
     permute, or read from x through the token table); fwd+bwd of the natural
     softmax top-k router at the Qwen3 shape (same tokens and expert weights as
     the main workload, router weights and bias from the natural workload's
-    recipe); and of one rank's share of the DeepSeek-V3 shape (expert weights
-    drawn on the GPU with the same distribution as the recipe)."""
+    recipe), also with the router's balancing loss; decode-sized forwards of
+    the small-batch and grouped paths; and fwd+bwd of one rank's share of the
+    DeepSeek-V3 shape (expert weights drawn on the GPU with the same
+    distribution as the recipe).  `which`: a comma-separated subset of
+    other_ffn, natural, natural_aux, small, dsv3 (or 'all')."""
     import numpy as np
     import torch
     import moe_inputs as MI
     from mixture_experts_layer_50_amd.layer import LayerBuffers, backward, forward, forward_small
 
     out = {}
-    # -- the main workload, other FFN form
-    shape = B.MoEShape.make(w_main.T, w_main.d, w_main.E, w_main.k, w_main.I, dtype=w_main.dtype,
-                            gate=w_main.gate)
-    buf = LayerBuffers(shape, training=True, gather=not gather)
+    want = set(which.split(",")) if which != "all" else {"other_ffn", "fwd", "natural",
+                                                          "natural_aux", "small", "dsv3"}
+    if "fwd" in want:
+        # forward only, inference (no H saved for a backward pass): the balanced
+        # gate on the main workload's tensors (the work does not depend on the
+        # values: every expert gets T*k/E rows), and the natural router on the
+        # natural workload's own tokens, router weights and bias (its routing:
+        # 40 empty experts, largest group 3,275 rows)
+        shape_b = B.MoEShape.make(w_main.T, w_main.d, w_main.E, w_main.k, w_main.I,
+                                  dtype=w_main.dtype, gate="balanced")
+        buf = LayerBuffers(shape_b, training=False, gather=gather != "plain",
+                           fused=gather == "fused")
 
-    def step_other():
-        forward(shape, buf, dev["x"], None, None, dev["Wg"], dev["Wu"], dev["Wd"])
-        backward(shape, buf, dev["dY"], dev["x"], None, dev["Wg"], dev["Wu"], dev["Wd"])
+        def step_fwd_b():
+            forward(shape_b, buf, dev["x"], None, None, dev["Wg"], dev["Wu"], dev["Wd"])
 
-    st = timed_steps(step_other, 10, 3)
-    out["plain_ffn_fwdbwd" if gather else "gathered_ffn_fwdbwd"] = {
-        "workload": w_main.name, "ffn": "plain" if gather else "gather",
-        "tokens_per_s": round(w_main.T / (st["median"] / 1e3), 1), "step_ms": st,
-        "kernels_us_avg": kernel_averages(step_other, B, 3)}
-    del buf
-    # -- natural router, Qwen3 shape
+        st = timed_steps(step_fwd_b, 20, 3)
+        out["balanced_fwd_inference"] = {
+            "workload": "qwen3_balanced_fwd_T4096_d2048_E128_k8_I768 (shapes and routing; "
+                        "tensors of the main workload)",
+            "tokens_per_s": round(w_main.T / (st["median"] / 1e3), 1), "step_ms": st,
+            "kernels_us_avg": kernel_averages(step_fwd_b, B, 5)}
+        del buf
+        w3 = MI.WORKLOADS["qwen3_natural_fwd_T4096_d2048_E128_k8_I768"]
+        a3 = MI.generate(w3, parts=("x", "Wr", "b"))
+        x3 = torch.from_numpy(a3["x"]).to(torch.bfloat16).cuda()
+        Wr3 = torch.from_numpy(a3["Wr"]).to(torch.bfloat16).cuda()
+        b3 = torch.from_numpy(a3["b"]).cuda()
+        shape_n = B.MoEShape.make(w3.T, w3.d, w3.E, w3.k, w3.I, dtype="bf16", gate="softmax_topk")
+        buf = LayerBuffers(shape_n, training=False, gather=gather != "plain",
+                           fused=gather == "fused")
+
+        def step_fwd_n():
+            forward(shape_n, buf, x3, Wr3, b3, dev["Wg"], dev["Wu"], dev["Wd"])
+
+        st = timed_steps(step_fwd_n, 20, 3)
+        counts = np.diff(buf["offsets"].cpu().numpy())
+        out["natural_fwd_inference"] = {
+            "workload": "qwen3_natural_fwd_T4096_d2048_E128_k8_I768 (its tokens, router weights "
+                        "and bias; expert weights of the main workload)",
+            "tokens_per_s": round(w3.T / (st["median"] / 1e3), 1), "step_ms": st,
+            "max_group_rows": int(counts.max()), "empty_experts": int((counts == 0).sum()),
+            "kernels_us_avg": kernel_averages(step_fwd_n, B, 5)}
+        del buf, x3, Wr3, b3
+    if "other_ffn" in want:  # the main workload, the FFN forms the main run did not use
+        shape = B.MoEShape.make(w_main.T, w_main.d, w_main.E, w_main.k, w_main.I,
+                                dtype=w_main.dtype, gate=w_main.gate)
+        for form in ("plain", "gather", "fused"):
+            if form == gather:
+                continue
+            buf = LayerBuffers(shape, training=True, gather=form != "plain",
+                               fused=form == "fused")
+
+            def step_other():
+                forward(shape, buf, dev["x"], None, None, dev["Wg"], dev["Wu"], dev["Wd"])
+                backward(shape, buf, dev["dY"], dev["x"], None, dev["Wg"], dev["Wu"], dev["Wd"])
+
+            st = timed_steps(step_other, 10, 3)
+            key = {"plain": "plain", "gather": "gathered", "fused": "fused"}[form]
+            out[key + "_ffn_fwdbwd"] = {
+                "workload": w_main.name, "ffn": form,
+                "tokens_per_s": round(w_main.T / (st["median"] / 1e3), 1), "step_ms": st,
+                "kernels_us_avg": kernel_averages(step_other, B, 3)}
+            del buf
     wn = MI.WORKLOADS["qwen3_natural_fwd_T4096_d2048_E128_k8_I768"]
     r = MI.generate(wn, parts=["Wr", "b"])
     Wr = torch.from_numpy(r["Wr"]).to(torch.bfloat16).cuda()
     bias = torch.from_numpy(r["b"]).cuda()
     shape = B.MoEShape.make(wn.T, wn.d, wn.E, wn.k, wn.I, dtype="bf16", gate="softmax_topk")
-    buf = LayerBuffers(shape, training=True, gather=gather)
+    if "natural" in want:  # natural router, Qwen3 shape
+        buf = LayerBuffers(shape, training=True, gather=gather != "plain", fused=gather == "fused")
 
-    def step_nat():
-        forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
-        backward(shape, buf, dev["dY"], dev["x"], Wr, dev["Wg"], dev["Wu"], dev["Wd"])
+        def step_nat():
+            forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
+            backward(shape, buf, dev["dY"], dev["x"], Wr, dev["Wg"], dev["Wu"], dev["Wd"])
 
-    st = timed_steps(step_nat, 10, 3)
-    counts = np.diff(buf["offsets"].cpu().numpy())
-    out["natural_router_fwdbwd"] = {
-        "workload": "qwen3_natural_fwdbwd_T4096_d2048_E128_k8_I768 (router bias N(0,1.5))",
-        "tokens_per_s": round(wn.T / (st["median"] / 1e3), 1), "step_ms": st,
-        "max_group_rows": int(counts.max()), "empty_experts": int((counts == 0).sum()),
-        "kernels_us_avg": kernel_averages(step_nat, B, 3)}
-    del buf
-    # -- the same with the router's load-balancing auxiliary loss (alpha 0.01)
-    buf = LayerBuffers(shape, training=True, gather=gather, aux_alpha=0.01)
+        st = timed_steps(step_nat, 10, 3)
+        counts = np.diff(buf["offsets"].cpu().numpy())
+        out["natural_router_fwdbwd"] = {
+            "workload": "qwen3_natural_fwdbwd_T4096_d2048_E128_k8_I768 (router bias N(0,1.5))",
+            "tokens_per_s": round(wn.T / (st["median"] / 1e3), 1), "step_ms": st,
+            "max_group_rows": int(counts.max()), "empty_experts": int((counts == 0).sum()),
+            "kernels_us_avg": kernel_averages(step_nat, B, 3)}
+        del buf
+    if "natural_aux" in want:  # the same with the balancing loss (alpha 0.01)
+        buf = LayerBuffers(shape, training=True, gather=gather != "plain", fused=gather == "fused",
+                           aux_alpha=0.01)
 
-    def step_nat_aux():
-        forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
-        backward(shape, buf, dev["dY"], dev["x"], Wr, dev["Wg"], dev["Wu"], dev["Wd"])
+        def step_nat_aux():
+            forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
+            backward(shape, buf, dev["dY"], dev["x"], Wr, dev["Wg"], dev["Wu"], dev["Wd"])
 
-    st = timed_steps(step_nat_aux, 10, 3)
-    ka = kernel_averages(step_nat_aux, B, 3)
-    out["natural_router_aux_fwdbwd"] = {
-        "workload": "qwen3_natural_fwdbwd_T4096_d2048_E128_k8_I768 + balancing loss (alpha 0.01)",
-        "tokens_per_s": round(wn.T / (st["median"] / 1e3), 1), "step_ms": st,
-        "aux_loss": float(buf["aux_loss"].item()),
-        "kernels_us_avg": {k: v for k, v in ka.items() if k.startswith(("aux", "route"))}}
-    del buf
-    # -- decode-sized batches, natural router: the small-batch FFN (no sort)
-    #    against the grouped path, forward only
-    out["small_batch_fwd"] = {}
-    for Ts in (1, 8, 64):
-        shape = B.MoEShape.make(Ts, wn.d, wn.E, wn.k, wn.I, dtype="bf16", gate="softmax_topk")
-        xs = dev["x"][:Ts].contiguous()
-        bs = LayerBuffers(shape, training=False)
-        bg = LayerBuffers(shape, training=False, gather=True)
+        st = timed_steps(step_nat_aux, 10, 3)
+        ka = kernel_averages(step_nat_aux, B, 3)
+        out["natural_router_aux_fwdbwd"] = {
+            "workload": "qwen3_natural_fwdbwd_T4096_d2048_E128_k8_I768 + balancing loss (alpha 0.01)",
+            "tokens_per_s": round(wn.T / (st["median"] / 1e3), 1), "step_ms": st,
+            "aux_loss": float(buf["aux_loss"].item()),
+            "kernels_us_avg": {k: v for k, v in ka.items() if k.startswith(("aux", "route"))}}
+        del buf
+    if "small" in want:  # decode-sized batches, natural router, forward only
+        out["small_batch_fwd"] = {}
+        for Ts in (1, 8, 64):
+            shape_s = B.MoEShape.make(Ts, wn.d, wn.E, wn.k, wn.I, dtype="bf16",
+                                      gate="softmax_topk")
+            xs = dev["x"][:Ts].contiguous()
+            bs = LayerBuffers(shape_s, training=False)
+            bg = LayerBuffers(shape_s, training=False, gather=True)
 
-        def step_small():
-            forward_small(shape, bs, xs, Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
+            def step_small():
+                forward_small(shape_s, bs, xs, Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
 
-        def step_grouped():
-            forward(shape, bg, xs, Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
+            def step_grouped():
+                forward(shape_s, bg, xs, Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
 
-        ss = timed_steps(step_small, 50, 5)
-        sg = timed_steps(step_grouped, 50, 5)
-        out["small_batch_fwd"][f"T{Ts}"] = {
-            "small_us": round(1000 * ss["median"], 1), "grouped_us": round(1000 * sg["median"], 1),
-            "small_kernels_us_avg": kernel_averages(step_small, B, 5)}
-        del bs, bg
-    # -- one rank of eight at the DeepSeek-V3 shape, balanced gate
-    wd = MI.WORKLOADS["dsv3_ep8_rank_fwdbwd_T32768_d7168_E256_loc32_k8_I2048"]
-    g = torch.Generator(device="cuda").manual_seed(wd.seed)
-    El = wd.E_loc
+            ss = timed_steps(step_small, 50, 5)
+            sg = timed_steps(step_grouped, 50, 5)
+            out["small_batch_fwd"][f"T{Ts}"] = {
+                "small_us": round(1000 * ss["median"], 1),
+                "grouped_us": round(1000 * sg["median"], 1),
+                "small_kernels_us_avg": kernel_averages(step_small, B, 5)}
+            del bs, bg
+    if "dsv3" in want:  # one rank of eight at the DeepSeek-V3 shape, balanced gate
+        wd = MI.WORKLOADS["dsv3_ep8_rank_fwdbwd_T32768_d7168_E256_loc32_k8_I2048"]
+        g = torch.Generator(device="cuda").manual_seed(wd.seed)
+        El = wd.E_loc
 
-    def rnd(*sh, sigma):
-        return (torch.randn(*sh, device="cuda", generator=g) * sigma).to(torch.bfloat16)
+        def rnd(*sh, sigma):
+            return (torch.randn(*sh, device="cuda", generator=g) * sigma).to(torch.bfloat16)
 
-    d5 = {"x": rnd(wd.T, wd.d, sigma=wd.x_sigma), "Wg": rnd(El, wd.d, wd.I, sigma=wd.w_sigma),
-          "Wu": rnd(El, wd.d, wd.I, sigma=wd.w_sigma), "Wd": rnd(El, wd.I, wd.d, sigma=wd.w_sigma),
-          "dY": rnd(wd.T, wd.d, sigma=wd.dy_sigma)}
-    shape = B.MoEShape.make(wd.T, wd.d, wd.E, wd.k, wd.I, dtype="bf16", gate="balanced",
-                            e_lo=wd.e_lo, e_hi=wd.e_end)
-    buf = LayerBuffers(shape, training=True, gather=gather)
+        d5 = {"x": rnd(wd.T, wd.d, sigma=wd.x_sigma), "Wg": rnd(El, wd.d, wd.I, sigma=wd.w_sigma),
+              "Wu": rnd(El, wd.d, wd.I, sigma=wd.w_sigma),
+              "Wd": rnd(El, wd.I, wd.d, sigma=wd.w_sigma),
+              "dY": rnd(wd.T, wd.d, sigma=wd.dy_sigma)}
+        shape_d = B.MoEShape.make(wd.T, wd.d, wd.E, wd.k, wd.I, dtype="bf16", gate="balanced",
+                                  e_lo=wd.e_lo, e_hi=wd.e_end)
+        buf = LayerBuffers(shape_d, training=True, gather=gather != "plain",
+                           fused=gather == "fused")
 
-    def step_ds():
-        forward(shape, buf, d5["x"], None, None, d5["Wg"], d5["Wu"], d5["Wd"])
-        backward(shape, buf, d5["dY"], d5["x"], None, d5["Wg"], d5["Wu"], d5["Wd"])
+        def step_ds():
+            forward(shape_d, buf, d5["x"], None, None, d5["Wg"], d5["Wu"], d5["Wd"])
+            backward(shape_d, buf, d5["dY"], d5["x"], None, d5["Wg"], d5["Wu"], d5["Wd"])
 
-    st = timed_steps(step_ds, 5, 2)
-    ker = kernel_averages(step_ds, B, 2)
-    R = int(buf["offsets"][-1].item())
-    gem_us = sum(ker[n] for n in GEMMS if n in ker)
-    gem_fl = sum(GEMMS[n][0](R, wd.d, wd.I, El, wd.T) for n in GEMMS if n in ker)
-    out["dsv3_rank_share_fwdbwd"] = {
-        "workload": wd.name, "routed_rows": R,
-        "tokens_per_s": round(wd.T / (st["median"] / 1e3), 1), "step_ms": st,
-        "grouped_gemm_tflops": round(gem_fl / gem_us / 1e6, 1),
-        "grouped_gemm_mfma_frac": round(gem_fl / gem_us / 1e6 / PEAK_BF16_TFLOPS, 4),
-        "kernels_us_avg": ker}
-    del buf, d5
+        st = timed_steps(step_ds, 5, 2)
+        ker = kernel_averages(step_ds, B, 2)
+        R = int(buf["offsets"][-1].item())
+        gem_us = sum(ker[n] for n in GEMMS if n in ker)
+        gem_fl = sum(GEMMS[n][0](R, wd.d, wd.I, El, wd.T) for n in GEMMS if n in ker)
+        out["dsv3_rank_share_fwdbwd"] = {
+            "workload": wd.name, "routed_rows": R,
+            "tokens_per_s": round(wd.T / (st["median"] / 1e3), 1), "step_ms": st,
+            "grouped_gemm_tflops": round(gem_fl / gem_us / 1e6, 1),
+            "grouped_gemm_mfma_frac": round(gem_fl / gem_us / 1e6 / PEAK_BF16_TFLOPS, 4),
+            "kernels_us_avg": ker}
+        del buf, d5
     torch.cuda.empty_cache()
     return out
 
@@ -310,12 +417,19 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
-    ap.add_argument("--ffn", choices=("gather", "plain"), default="gather",
+    ap.add_argument("--pass", dest="pass_", choices=("default", "fwd", "fwdbwd"), default="default",
+                    help="run the workload forward only or forward+backward (default: as the "
+                         "workload is defined)")
+    ap.add_argument("--ffn", choices=("gather", "plain", "fused"), default="gather",
                     help="gather: the FFN reads the rows of Xp from x through the token table "
-                         "(no Xp buffer); plain: the permute writes Xp")
+                         "(no Xp buffer); plain: the permute writes Xp; fused: gather, and the "
+                         "combine runs in the down projection's epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the natural-router and DeepSeek-V3 rank-share timings")
+    ap.add_argument("--secondary", default="all",
+                    help="comma-separated secondary timings to run (other_ffn, natural, "
+                         "natural_aux, small, dsv3) or 'all'")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="also run a fill and a sum of this size (HBM counter calibration)")
@@ -346,7 +460,9 @@ def main():
     B.load_library()
     torch.cuda.set_device(0)
     w = MI.WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name}: generating inputs")
+    if args.pass_ != "default" and (args.pass_ == "fwdbwd") != w.backward:
+        w = MI.Workload(**{**w.__dict__, "backward": args.pass_ == "fwdbwd"})
+    log(f"[bench] workload {w.name} ({'fwd+bwd' if w.backward else 'fwd'}): generating inputs")
     a = MI.generate(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = {k: (torch.from_numpy(v) if k == "b" else torch.from_numpy(v).to(dt)).cuda()
@@ -354,8 +470,12 @@ def main():
     del a
     shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate, e_lo=w.e_lo,
                             e_hi=w.e_end)
-    gather = args.ffn == "gather"
-    buf = LayerBuffers(shape, training=w.backward, gather=gather)
+    gather = args.ffn  # the FFN form: plain, gather or fused
+    torch.cuda.synchronize()
+    inputs_bytes = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    buf = LayerBuffers(shape, training=w.backward, gather=gather != "plain",
+                       fused=gather == "fused")
     stream = torch.cuda.current_stream()
 
     def step():
@@ -415,6 +535,28 @@ def main():
     kernels[dom] = {"us_avg": 1000.0 * dom_ms / max(dom_n, 1), "launches": dom_n}
     B.prof_enable(False)
 
+    peak_bytes = torch.cuda.max_memory_allocated()
+    # the token kernels (route, sort, combine and their backwards) with the
+    # memory-side cache flushed before every step: a 512 MiB buffer is
+    # rewritten between steps, so the step's first kernels find none of the
+    # previous step's data in the 256 MB MALL
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    B.prof_enable(True)
+    B.prof_select(None)
+    B.prof_reset()
+    for i in range(5):
+        flush.fill_(i)
+        step()
+    torch.cuda.synchronize()
+    flushed = {}
+    for name in B.prof_names():
+        if name in GEMMS:
+            continue
+        tot, n = B.prof_read(name)
+        flushed[name] = round(1000.0 * tot / max(n, 1), 2)
+    B.prof_enable(False)
+    del flush
+
     R = int(buf["offsets"][-1].item())
     El = w.E_loc
     gem = {}
@@ -471,12 +613,17 @@ def main():
                          "mfma_frac_all_six": round(gemm_flops / gemm_total_us / 1e6 / PEAK_BF16_TFLOPS, 4),
                          "kernels": gem},
         "wall_s_timed": round(wall, 3),
+        "peak_device_memory": {"bytes": int(peak_bytes), "inputs_bytes": int(inputs_bytes),
+                               "layer_buffers_bytes": int(peak_bytes - inputs_bytes),
+                               "what": "torch.cuda.max_memory_allocated over the warm-up and "
+                                       "timed steps (inputs: x, weights, upstream gradient)"},
+        "token_kernels_us_mall_flushed": flushed,
         "kernels_us_avg": {k: round(v["us_avg"], 2) for k, v in kernels.items()},
     }
     out["step_ms_stats"] = timed_steps(step, max(5, args.steps), 2)
     if not args.no_secondary and w.name == WORKLOAD:
         log("[bench] natural-router and DeepSeek-V3 rank-share timings")
-        out["secondary"] = secondary_workloads(B, dev, w, gather)
+        out["secondary"] = secondary_workloads(B, dev, w, gather, args.secondary)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)

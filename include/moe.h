@@ -79,7 +79,7 @@ typedef enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_BALANCED = 1 } moe_gate_t;
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7,
-  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9
+  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9, MOE_OP_FFN_FWD_FUSED = 10
 } moe_op_t;
 
 typedef void* moe_stream_t; /* hipStream_t */
@@ -193,6 +193,32 @@ moe_status_t moe_grouped_ffn_fwd_gather_noalloc(const moe_shape_t* shape, const 
                                                 const void* w_gate, const void* w_up,
                                                 const void* w_down, void* h_save, void* a_save,
                                                 void* yp, moe_stream_t stream);
+
+/* a2 + a3 + a4 + a5 fused -- the gathered FFN forward with the combine run in
+ * the down projection's epilogue, the one-GPU counterpart of dispatch and
+ * combine fused with the expert computation ([P3] section 加速来源, DeepEP
+ * item; the pages' DeepEP kernels move tokens between GPUs, here the rows stay
+ * on one).  Row p of Xp is read as x[perm[p] / k] (as in
+ * moe_grouped_ffn_fwd_gather), and
+ *   y[t] = sum_j topk_w[t,j] * yp[inv[t*k+j]]   (slots with inv >= 0, ascending j)
+ * is computed by the workgroup that writes the last of token t's row blocks of
+ * yp (integer arrival counters per token and 64-column block; no
+ * floating-point atomics): y is bit-identical to moe_combine after
+ * moe_grouped_ffn_fwd_gather, and every other output is bit-identical to that
+ * call's.  Tokens with no kept slot get y[t] = 0.  yp is still written (the
+ * combine reads it back, and the backward needs it).  x [T,d]; perm [R_cap],
+ * inv [T*k] as written by moe_permute; topk_w [T,k] fp32; y [T,d]; the other
+ * arguments as for moe_grouped_ffn_fwd.  ws: moe_workspace_size(
+ * MOE_OP_FFN_FWD_FUSED) (the tile tables, kept slots per token [T], arrival
+ * counters [T, d/64]).  Needs T*d and R_cap*d element bytes < 2^31 (else
+ * MOE_ERR_UNSUPPORTED).  fp32 layers run the same steps with the combine
+ * kernel after the GEMM. */
+moe_status_t moe_grouped_ffn_fwd_fused(const moe_shape_t* shape, const void* x,
+                                       const int32_t* perm, const int32_t* inv,
+                                       const float* topk_w, const int32_t* group_offsets,
+                                       const void* w_gate, const void* w_up, const void* w_down,
+                                       void* h_save, void* a_save, void* yp, void* y, void* ws,
+                                       size_t ws_bytes, moe_stream_t stream);
 
 /* a5 -- combine (the second of the two token-movement kernels, [P3] section 加速来源, DeepEP item):
  * y[t] = sum_j topk_w[t,j] * yp[inv[t*k+j]] over the slots with inv >= 0, in

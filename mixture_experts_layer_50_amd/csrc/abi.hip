@@ -268,6 +268,7 @@ struct TileTables {
   const int32_t* off;
   hipStream_t s;
   const int32_t* perm = nullptr;
+  const CombinePrep* cmb = nullptr;  // the fused combine's preparation, in the same launch
   bool built = false;
   int32_t* t256() const { return base; }
   int32_t* t128() const { return base + one_table_bytes(D, 256) / 4; }
@@ -276,7 +277,7 @@ struct TileTables {
   moe_status_t ensure() {  // all tables in one launch, on first use
     if (!built) {
       MOE_TRY(launch_tile_tables(off, D.E_loc, t256(), t128(), kcost(), s, perm, D.k, tok(),
-                                 D.R_cap));
+                                 D.R_cap, cmb));
       built = true;
     }
     return MOE_OK;
@@ -323,8 +324,15 @@ struct RouteBwdWs {
   }
 };
 
+// The fused combine's workspace after the tile tables: kept slots per token
+// [T] and the arrival counters [T][d/64].
+int64_t fused_kept_bytes(const Dims& D) { return round_up((int64_t)D.T * 4, 256); }
+int64_t fused_cnt_bytes(const Dims& D) { return round_up((int64_t)D.T * (D.d / 64) * 4, 256); }
+
 int64_t ws_bytes(const Dims& D, int op) {
   switch (op) {
+    case MOE_OP_FFN_FWD_FUSED:
+      return D.bf16 ? tile_table_bytes(D) + fused_kept_bytes(D) + fused_cnt_bytes(D) : 0;
     case MOE_OP_PERMUTE: return round_up(permute_ws_bytes(D.T, D.E_loc), 256);
     case MOE_OP_FFN_FWD: return D.bf16 ? tile_table_bytes(D) : 0;
     case MOE_OP_FFN_BWD:
@@ -358,7 +366,7 @@ extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, siz
   Dims D;
   if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
   MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
-  if (op < MOE_OP_ROUTE || op > MOE_OP_AUX_LOSS)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FWD_FUSED)
     return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
   *bytes = (size_t)ws_bytes(D, op);
   return MOE_OK;
@@ -411,13 +419,29 @@ moe_status_t check_gather(const char* fn, const Dims& D) {
   return MOE_OK;
 }
 
-// Forward FFN over Xp rows: xp itself, or (gather) x read through perm.
+// The fused combine's arguments (moe_grouped_ffn_fwd_fused).
+struct FusedCombine {
+  const int32_t* inv;
+  const float* topk_w;
+  void* y;
+};
+
+// Forward FFN over Xp rows: xp itself, or (gather) x read through perm; with
+// fc, the combine runs in the down projection's epilogue (bf16) or right after
+// it (fp32).
 moe_status_t ffn_fwd(const char* fn, bool gather, const moe_shape_t* shape, const void* a_src,
                      const int32_t* perm, const int32_t* group_offsets, const void* w_gate,
                      const void* w_up, const void* w_down, void* h_save, void* a_save, void* yp,
-                     void* ws, size_t ws_bytes_, moe_stream_t stream) {
+                     void* ws, size_t ws_bytes_, moe_stream_t stream,
+                     const FusedCombine* fc = nullptr) {
   Dims D;
   MOE_TRY(check_shape(shape, fn, &D));
+  if (fc) {
+    MOE_TRY(need(fn, {{"inv", fc->inv}, {"topk_w", fc->topk_w}, {"y", fc->y}}));
+    if ((int64_t)D.R_cap * D.d * D.eb >= ((int64_t)1 << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: yp of %lld bytes; the fused combine needs < 2^31", fn,
+                  (long long)D.R_cap * D.d * D.eb);
+  }
   MOE_TRY(need(fn, {{gather ? "x" : "xp", a_src}, {"group_offsets", group_offsets},
                     {"w_gate", w_gate}, {"w_up", w_up}, {"w_down", w_down}, {"a_save", a_save}, {"yp", yp}}));
   if (!gather) perm = nullptr;
@@ -426,8 +450,22 @@ moe_status_t ffn_fwd(const char* fn, bool gather, const moe_shape_t* shape, cons
     MOE_TRY(check_gather(fn, D));
   }
   MOE_TRY(opt(fn, {{"h_save", h_save}}));
-  MOE_TRY(check_ws(fn, D, MOE_OP_FFN_FWD, ws, ws_bytes_));
+  MOE_TRY(check_ws(fn, D, fc ? MOE_OP_FFN_FWD_FUSED : MOE_OP_FFN_FWD, ws, ws_bytes_));
   TileTables tt{D, static_cast<int32_t*>(ws), group_offsets, S(stream), perm};
+  CombinePrep prep{};
+  const bool fuse = fc && D.bf16;
+  if (fuse) {
+    char* base = static_cast<char*>(ws) + tile_table_bytes(D);
+    prep.inv = fc->inv;
+    prep.T = D.T;
+    prep.k = D.k;
+    prep.kept = reinterpret_cast<int32_t*>(base);
+    prep.cnt = reinterpret_cast<int32_t*>(base + fused_kept_bytes(D));
+    prep.ncb = D.d / 64;
+    prep.y = fc->y;
+    prep.y_row_bytes = D.d * D.eb;
+    tt.cmb = &prep;
+  }
   // fp32: the row count; bf16: the most M tiles the tile table can hold
   auto rows_or_tiles = [&](GemmRole r) { return D.bf16 ? max_m_tiles(D, tile_bm(role_tile(r))) : D.R_cap; };
 
@@ -443,15 +481,30 @@ moe_status_t ffn_fwd(const char* fn, bool gather, const moe_shape_t* shape, cons
   if (D.bf16) MOE_TRY(tt.get(gu, &g.tiles));
   MOE_TRY(launch_gemm(D.bf16, gu, g, rows_or_tiles(gu), S(stream)));
 
+  const GemmRole dr = fuse ? R_DOWN_FWD_COMBINE : R_DOWN_FWD;
   GemmParams p{};
   p.A = a_save; p.lda = D.I;
   p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
   p.N = D.d; p.K = D.I;
   p.off = group_offsets; p.groups = D.E_loc;
-  p.n_tiles = (int)ceil_div(D.d, tile_bn(role_tile(R_DOWN_FWD)));
+  p.n_tiles = (int)ceil_div(D.d, tile_bn(role_tile(dr)));
   p.C0 = yp; p.ldc = D.d;
-  if (D.bf16) MOE_TRY(tt.get(R_DOWN_FWD, &p.tiles));
-  return launch_gemm(D.bf16, R_DOWN_FWD, p, rows_or_tiles(R_DOWN_FWD), S(stream));
+  if (D.bf16) MOE_TRY(tt.get(dr, &p.tiles));
+  if (fuse) {
+    MOE_TRY(tt.ensure());  // built above with the gate/up GEMM's table; here for clarity
+    p.cmb_tok = tt.tok();
+    p.cmb_inv = fc->inv;
+    p.cmb_w = fc->topk_w;
+    p.cmb_kept = prep.kept;
+    p.cmb_cnt = prep.cnt;
+    p.cmb_y = fc->y;
+    p.cmb_k = D.k;
+  }
+  MOE_TRY(launch_gemm(D.bf16, dr, p, rows_or_tiles(dr), S(stream)));
+  if (fc && !fuse)  // fp32 layers: the combine kernel after the GEMM
+    return launch_gather_sum(yp, fc->inv, fc->topk_w, D.T, D.d, D.k, D.eb, fc->y, S(stream),
+                             "combine");
+  return MOE_OK;
 }
 
 }  // namespace
@@ -531,6 +584,19 @@ extern "C" moe_status_t moe_grouped_ffn_fwd_gather_noalloc(
   MOE_TRY(noalloc_scratch(fn, &ws));
   return ffn_fwd(fn, true, shape, x, perm, group_offsets, w_gate, w_up, w_down, h_save, a_save, yp,
                  ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+extern "C" moe_status_t moe_grouped_ffn_fwd_fused(const moe_shape_t* shape, const void* x,
+                                                  const int32_t* perm, const int32_t* inv,
+                                                  const float* topk_w,
+                                                  const int32_t* group_offsets,
+                                                  const void* w_gate, const void* w_up,
+                                                  const void* w_down, void* h_save, void* a_save,
+                                                  void* yp, void* y, void* ws, size_t ws_bytes_,
+                                                  moe_stream_t stream) {
+  const FusedCombine fc{inv, topk_w, y};
+  return ffn_fwd("moe_grouped_ffn_fwd_fused", true, shape, x, perm, group_offsets, w_gate, w_up,
+                 w_down, h_save, a_save, yp, ws, ws_bytes_, stream, &fc);
 }
 
 extern "C" moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x,

@@ -66,6 +66,29 @@ struct GemmParams {
   const int32_t* a_rows;  // gather roles: A row p (the M index for G_MROWS, the K index for
   int a_rows_div;         // G_KROWS) is row a_rows[p] / a_rows_div of the matrix at A (the
                           // bf16 kernels take a table of rows: a_rows_div must be 1)
+  // R_DOWN_FWD_COMBINE: the combine y[t] = sum_j w[t,j] C0[inv[t*k+j]] run by the
+  // workgroup that writes a token's last row block (see CombinePrep)
+  const int32_t* cmb_tok;   // token of every routed row [R_cap]
+  const int32_t* cmb_inv;   // [T*k]
+  const float* cmb_w;       // gate weights [T*k]
+  const int32_t* cmb_kept;  // kept slots per token [T]
+  int32_t* cmb_cnt;         // arrival counters [T][N/64], zero on entry
+  void* cmb_y;              // [T][N]
+  int cmb_k;
+};
+
+// Preparation of the fused combine, done by the tile-table launch before the
+// FFN's GEMMs: kept[t] = slots of token t with inv >= 0, the token's arrival
+// counters zeroed, and y[t] = 0 for a token with no kept slot (no row block of
+// it is ever written, so no workgroup would write it).
+struct CombinePrep {
+  const int32_t* inv;
+  int T, k;
+  int32_t* kept;
+  int32_t* cnt;
+  int ncb;          // counters per token (N / 64)
+  void* y;
+  int y_row_bytes;  // N * element bytes (a multiple of 16)
 };
 
 // Tile shapes of the bf16 MFMA kernels.
@@ -86,7 +109,10 @@ enum GemmRole {
   // R_GATEUP_FWD and R_GATEUP_WGRAD with the rows of Xp read from x through
   // perm (Xp is never written): a_rows = perm, a_rows_div = k
   R_GATEUP_FWD_GATHER = 9,
-  R_GATEUP_WGRAD_GATHER = 10
+  R_GATEUP_WGRAD_GATHER = 10,
+  // R_DOWN_FWD with the combine in its epilogue (dispatch's counterpart, the
+  // combine, fused into the expert GEMM)
+  R_DOWN_FWD_COMBINE = 11
 };
 
 // Tile shape each role runs with (bf16), for a GEMM with n output columns
@@ -110,7 +136,7 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
 moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
                                 int32_t* tiles128, int32_t* kcost, hipStream_t s,
                                 const int32_t* perm = nullptr, int k = 1, int32_t* tok = nullptr,
-                                int rows_cap = 0);
+                                int rows_cap = 0, const CombinePrep* cmb = nullptr);
 // Per-tile cost of a weight-gradient tile beyond its K slices (its epilogue).
 constexpr int KCOST_FIXED = 2;
 

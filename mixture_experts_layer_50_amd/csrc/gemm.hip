@@ -47,8 +47,11 @@ __device__ __forceinline__ int remap_xcd(int pid, int count) {
 }
 
 // Linear tile id -> (m tile, n tile), GM m tiles at a time over all n tiles.
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 4
+#endif
 __device__ __forceinline__ void group_order(int L, int mt_count, int nt_count, int& mt, int& nt) {
-  constexpr int GM = 4;
+  constexpr int GM = MOE_GROUP_M;
   int per_group = GM * nt_count;
   int g = L / per_group;
   int first = g * GM;
@@ -1245,6 +1248,94 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_persistent_kernel(Ge
 }
 
 // ---------------------------------------------------------------------------
+// Combine fused into the down projection's epilogue (R_DOWN_FWD_COMBINE).
+// A compute wave has just stored its block of Yp: rows [mb, m_hi) (one per
+// lane), the 64 columns from nb.  Those stores used the device-coherent cache
+// policy (sc1: written through to the point every XCD reads from).  Per row,
+// the wave waits for its stores, then bumps the integer arrival counter of
+// (the row's token, the column block); the wave whose increment completes a
+// token's count (its kept slots) is the last writer of that token's row
+// blocks, and computes y[t] for those 64 columns: sum over the token's slots
+// in ascending j of w[t,j] * Yp[inv[t,j]] (device-coherent loads), in fp32,
+// the same operations in the same order as the combine kernel, so y is
+// bit-identical to moe_combine's.  Deterministic: counters are integers and
+// the sum order does not depend on who arrives last.
+// ---------------------------------------------------------------------------
+constexpr int CMB_STORE_CPOL = 16;  // sc1: device-coherent store
+constexpr int CMB_LOAD_CPOL = 16;   // sc1: device-coherent load
+
+__device__ __forceinline__ void combine_rows(const GemmParams& p, int mb, int m_hi, int nb,
+                                             int lane) {
+  if (nb >= p.N) return;  // a block of padding columns (uniform)
+  const int ncb = p.N >> 6;
+  const int cb = nb >> 6;
+  // this wave's stores of its block are complete before its counters move
+  // (vmcnt(0); the exp and lgkm counters left as they are)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  const int row = mb + lane;
+  int tok = 0;
+  bool last = false;
+  if (row < m_hi) {
+    tok = p.cmb_tok[row];
+    const int old = __hip_atomic_fetch_add(p.cmb_cnt + (int64_t)tok * ncb + cb, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == p.cmb_kept[tok] - 1;
+  }
+  // the reads below stay after the counter updates
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  uint64_t mask = __ballot(last);
+  const __amdgpu_buffer_rsrc_t ryp = make_rsrc(static_cast<const bf16_t*>(p.C0) + nb);
+  bf16_t* Y = static_cast<bf16_t*>(p.cmb_y);
+  const int grp = lane >> 3, c = lane & 7;  // 8 tokens at a time, 8 chunks of 8 columns each
+  const int k = p.cmb_k;
+  while (mask) {  // uniform
+    int r[8], n = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      r[g] = mask ? (int)__builtin_ctzll(mask) : 0;
+      if (mask) { mask &= mask - 1; ++n; }
+    }
+    int my = r[0];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) my = grp == g ? r[g] : my;
+    const int t = __shfl(tok, my, 64);
+    if (grp < n) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        int pj[8];
+        float gj[8];
+        uint4 v[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = j0 + jj;
+          pj[jj] = j < k ? p.cmb_inv[(int64_t)t * k + j] : -1;
+          gj[jj] = j < k ? p.cmb_w[(int64_t)t * k + j] : 0.f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          v[jj] = buf_load16<CMB_LOAD_CPOL>(
+              ryp, pj[jj] >= 0 ? (int)(((int64_t)pj[jj] * p.ldc + c * 8) * 2) : OOB, 0);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          if (pj[jj] < 0) continue;
+          const uint32_t w4[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(gj[jj], __uint_as_float(w4[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(gj[jj], __uint_as_float(w4[i] & 0xffff0000u), acc[2 * i + 1]);
+          }
+        }
+      }
+      *reinterpret_cast<uint4*>(Y + (int64_t)t * p.N + nb + c * 8) =
+          make_uint4(pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
+                     pack_bf2(acc[6], acc[7]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Warp-specialised persistent bf16 MFMA GEMM.  Compute waves (WGM x WGN)
 // only read LDS, run the MFMAs and write results; producer waves (NPW) only
 // load K slices from memory into LDS, with PD slices in flight in their own
@@ -1384,9 +1475,15 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
         const int r = q / SCPR, c = q % SCPR;
         const int n = nb + c * 8;
         // weight gradients are not read again soon: stream them past the
-        // caches; other results (read by the next kernel) stay cacheable
-        bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, v[i], r, n, mb + r < t.m_hi && n < p.N);
+        // caches; other results (read by the next kernel) stay cacheable;
+        // with the fused combine, device-coherent (other XCDs read them)
+        bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : ROLE == R_DOWN_FWD_COMBINE ? CMB_STORE_CPOL : 0>(
+            p, v[i], r, n, mb + r < t.m_hi && n < p.N);
       }
+    }
+    if constexpr (ROLE == R_DOWN_FWD_COMBINE) {
+      static_assert(WTM == 64 && WTN == 64, "one row per lane, 64-column counter blocks");
+      combine_rows(p, mb, t.m_hi, nb, lane);
     }
   };
 
@@ -1554,15 +1651,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Workgroup 0 builds the table for 256-row tiles, workgroup 1 the one for
 // 128-row tiles.
-// Workgroups 3 and up (launched with a token table only) write the token
-// rows of the routed rows.
+// Workgroups 3 .. 3 + ntok - 1 (launched with a token table only) write the
+// token rows of the routed rows; the workgroups after them (launched with a
+// CombinePrep only) prepare the fused combine, one thread per token.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups,
                                                           int32_t* tiles256, int32_t* tiles128,
                                                           int32_t* kcost, const int32_t* perm,
-                                                          int k, int32_t* tok) {
+                                                          int k, int32_t* tok, int ntok,
+                                                          CombinePrep cmb) {
+  if (blockIdx.x >= 3 + ntok) {
+    const int t = (blockIdx.x - 3 - ntok) * 1024 + threadIdx.x;
+    if (t >= cmb.T) return;
+    int kept = 0;
+    for (int j = 0; j < cmb.k; ++j) kept += cmb.inv[(int64_t)t * cmb.k + j] >= 0;
+    cmb.kept[t] = kept;
+    for (int c = 0; c < cmb.ncb; ++c) cmb.cnt[(int64_t)t * cmb.ncb + c] = 0;
+    if (kept == 0) {
+      uint4* y = reinterpret_cast<uint4*>(static_cast<char*>(cmb.y) + (int64_t)t * cmb.y_row_bytes);
+      for (int c = 0; c < cmb.y_row_bytes / 16; ++c) y[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
   if (blockIdx.x >= 3) {
     const int R = off[groups];
-    for (int p = (blockIdx.x - 3) * 1024 + threadIdx.x; p < R; p += (gridDim.x - 3) * 1024)
+    for (int p = (blockIdx.x - 3) * 1024 + threadIdx.x; p < R; p += ntok * 1024)
       tok[p] = (int)((uint32_t)perm[p] / (uint32_t)k);
     return;
   }
@@ -1610,11 +1722,15 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
 
 moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles256,
                                 int32_t* tiles128, int32_t* kcost, hipStream_t s,
-                                const int32_t* perm, int k, int32_t* tok, int rows_cap) {
+                                const int32_t* perm, int k, int32_t* tok, int rows_cap,
+                                const CombinePrep* cmb) {
   ProfScope prof("tile_table", s);
-  const int extra =
+  const int ntok =
       perm ? (int)std::min<int64_t>(64, std::max<int64_t>(1, ceil_div(rows_cap, 1024))) : 0;
-  tile_table_kernel<<<3 + extra, 1024, 0, s>>>(off, groups, tiles256, tiles128, kcost, perm, k, tok);
+  const int ncmb = cmb ? (int)ceil_div(cmb->T, 1024) : 0;
+  const CombinePrep none{};
+  tile_table_kernel<<<3 + ntok + ncmb, 1024, 0, s>>>(off, groups, tiles256, tiles128, kcost, perm,
+                                                     k, tok, ntok, cmb ? *cmb : none);
   return check_launch("tile_table_kernel");
 }
 
@@ -1668,6 +1784,8 @@ int tile_bn(TileCfg cfg) {
   X(R_GATEUP_FWD_GATHER, "ffn_gateup_fwd_gather", MOE_TILE_GATEUP_FWD, A_KC, B_NC, G_MROWS, B2_NHALF, \
     EPI_SWIGLU)                                                                                    \
   X(R_GATEUP_WGRAD_GATHER, "ffn_gateup_wgrad_gather", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, \
+    EPI_STORE)                                                                                     \
+  X(R_DOWN_FWD_COMBINE, "ffn_down_fwd_combine", MOE_TILE_DOWN_FWD, A_KC, B_NC, G_MROWS, B2_NONE,    \
     EPI_STORE)
 
 // A role may take a second tile shape when its N (output columns) is large:
@@ -1722,7 +1840,8 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 // persistent kernel (bit r = role r; build-time tunable).
 #ifndef MOE_WS_ROLES
 #define MOE_WS_ROLES \
-  ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD) | (1 << R_GATEUP_WGRAD_GATHER))
+  ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD) | (1 << R_GATEUP_WGRAD_GATHER) | \
+   (1 << R_DOWN_FWD_COMBINE))
 #endif
 #ifndef MOE_PERSIST_ROLES
 #define MOE_PERSIST_ROLES 0

@@ -23,10 +23,13 @@ class LayerBuffers:
     device: str = "cuda"
     training: bool = True
     gather: bool = False  # FFN reads x through perm (the _gather calls); no Xp buffer
+    fused: bool = False   # gathered FFN forward with the combine in its epilogue (implies gather)
     aux_alpha: Optional[float] = None  # router balancing loss weight (softmax top-k gate)
     t: Dict[str, torch.Tensor] = field(default_factory=dict)
 
     def __post_init__(self):
+        if self.fused:
+            self.gather = True
         s, dev = self.shape, self.device
         dt = torch_dtype(s)
         R, T, d, E, k, I, El = s.rows_cap, s.T, s.d, s.E, s.k, s.I, s.E_loc
@@ -47,7 +50,7 @@ class LayerBuffers:
         t["a"] = e(R, I)
         t["yp"] = e(R, d)
         t["y"] = e(T, d)
-        for op in ("permute", "ffn_fwd"):
+        for op in ("permute", "ffn_fwd_fused" if self.fused else "ffn_fwd"):
             t["ws_" + op] = self._ws(op)
         if self.aux_alpha is not None:
             t["aux_loss"] = e(1, dtype=f32)
@@ -78,7 +81,8 @@ class LayerBuffers:
 def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
             stream=None):
     """route -> permute -> grouped SwiGLU FFN -> combine; y lands in buf['y'].
-    With buf.gather the permute only sorts and the FFN reads x through perm.
+    With buf.gather the permute only sorts and the FFN reads x through perm;
+    with buf.fused the combine also runs inside the FFN's down projection.
     With buf.aux_alpha the router's balancing loss lands in buf['aux_loss']."""
     t = buf.t
     B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
@@ -87,6 +91,11 @@ def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_u
                        t["ws_aux_loss"], stream)
     B.moe_permute(shape, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"],
                   t["ws_permute"], stream)
+    if buf.fused:  # combine included
+        B.moe_grouped_ffn_fwd_fused(shape, x, t["perm"], t["inv"], t["topk_w"], t["offsets"],
+                                    w_gate, w_up, w_down, t["h"], t["a"], t["yp"], t["y"],
+                                    t["ws_ffn_fwd_fused"], stream)
+        return
     if buf.gather:
         B.moe_grouped_ffn_fwd_gather(shape, x, t["perm"], t["offsets"], w_gate, w_up, w_down,
                                      t["h"], t["a"], t["yp"], t["ws_ffn_fwd"], stream)

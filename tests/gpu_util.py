@@ -28,9 +28,9 @@ def upload(w: MI.Workload, arrays):
 
 
 def run_layer(w: MI.Workload, dev, R_cap=0, training=True, poison=False, gather=False,
-              aux_alpha=None):
+              aux_alpha=None, fused=False):
     s = shape_of(w, R_cap)
-    buf = LayerBuffers(s, training=training, gather=gather, aux_alpha=aux_alpha)
+    buf = LayerBuffers(s, training=training, gather=gather, aux_alpha=aux_alpha, fused=fused)
     if poison:
         for v in buf.t.values():
             if v is not None and v.is_floating_point():

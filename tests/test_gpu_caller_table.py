@@ -39,30 +39,36 @@ def _table(T, E, k, seed):
     return idx, g
 
 
-@pytest.mark.parametrize("gather", [False, True], ids=["plain", "gather"])
+@pytest.mark.parametrize("form", ["plain", "gather", "fused"])
 @pytest.mark.parametrize("dtype,e_lo,e_hi", [("bf16", 4, 12), ("f32", 4, 12), ("bf16", 0, 16)])
-def test_caller_table_grouped_path(dtype, e_lo, e_hi, gather):
+def test_caller_table_grouped_path(dtype, e_lo, e_hi, form):
+    gather = form != "plain"
     T, d, E, k, I = 45, 128, 16, 4, 192
     w = MI.small_workload(f"table_{dtype}_{e_lo}_{e_hi}", T, d, E, k, I, dtype=dtype, e_lo=e_lo,
                           e_hi=e_hi, seed=41, backward=True)
-    _announce(f"caller table {w.name} gather={gather}")
+    _announce(f"caller table {w.name} {form}")
     a = MI.generate(w, parts=("x", "Wg", "Wu", "Wd", "dY"))
     idx, g = _table(T, E, k, 43)
     dev = U.upload(w, a)
     s = U.shape_of(w)
-    buf = LayerBuffers(s, training=True, gather=gather)
+    buf = LayerBuffers(s, training=True, gather=gather, fused=form == "fused")
     t = buf.t
     t["topk_idx"].copy_(torch.from_numpy(idx))
     t["topk_w"].copy_(torch.from_numpy(g))
     x = dev["x"]
     B.moe_permute(s, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"], t["ws_permute"])
-    if gather:
-        B.moe_grouped_ffn_fwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"],
-                                     t["h"], t["a"], t["yp"], t["ws_ffn_fwd"])
+    if form == "fused":
+        B.moe_grouped_ffn_fwd_fused(s, x, t["perm"], t["inv"], t["topk_w"], t["offsets"],
+                                    dev["Wg"], dev["Wu"], dev["Wd"], t["h"], t["a"], t["yp"],
+                                    t["y"], t["ws_ffn_fwd_fused"])
     else:
-        B.moe_grouped_ffn_fwd(s, t["xp"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"], t["h"],
-                              t["a"], t["yp"], t["ws_ffn_fwd"])
-    B.moe_combine(s, t["yp"], t["inv"], t["topk_w"], t["y"])
+        if gather:
+            B.moe_grouped_ffn_fwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"],
+                                         dev["Wd"], t["h"], t["a"], t["yp"], t["ws_ffn_fwd"])
+        else:
+            B.moe_grouped_ffn_fwd(s, t["xp"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"],
+                                  t["h"], t["a"], t["yp"], t["ws_ffn_fwd"])
+        B.moe_combine(s, t["yp"], t["inv"], t["topk_w"], t["y"])
     B.moe_combine_bwd(s, dev["dY"], t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"])
     if gather:
         B.moe_grouped_ffn_bwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"],
