@@ -1426,8 +1426,11 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
   // Write the wave's WTM x WTN block: accumulators -> private LDS area
   // (16-byte chunk c of row r at c ^ (r mod SCPR)) -> whole chunks to memory
   // with buffer stores (masked lanes get an out-of-range offset).
+#ifndef MOE_WS_STAGED
+#define MOE_WS_STAGED 1
+#endif
   auto store_block = [&](const TileDesc& t) __attribute__((always_inline)) {
-    if constexpr (EPI != EPI_STORE) {
+    if constexpr (EPI != EPI_STORE || !MOE_WS_STAGED) {
       epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, t.m_lo, t.m_hi, t.n0, t.e, wm, wn, lane);
       return;
     }
@@ -1653,22 +1656,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // 128-row tiles.
 // Workgroups 3 .. 3 + ntok - 1 (launched with a token table only) write the
 // token rows of the routed rows; the workgroups after them (launched with a
-// CombinePrep only) prepare the fused combine, one thread per token.
+// CombinePrep only) prepare the fused combine, one wavefront per token.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, int groups,
                                                           int32_t* tiles256, int32_t* tiles128,
                                                           int32_t* kcost, const int32_t* perm,
                                                           int k, int32_t* tok, int ntok,
                                                           CombinePrep cmb) {
-  if (blockIdx.x >= 3 + ntok) {
-    const int t = (blockIdx.x - 3 - ntok) * 1024 + threadIdx.x;
+  if (blockIdx.x >= 3 + ntok) {  // one wavefront per token
+    const int lane = threadIdx.x & 63;
+    const int t = (blockIdx.x - 3 - ntok) * 16 + (threadIdx.x >> 6);
     if (t >= cmb.T) return;
-    int kept = 0;
-    for (int j = 0; j < cmb.k; ++j) kept += cmb.inv[(int64_t)t * cmb.k + j] >= 0;
-    cmb.kept[t] = kept;
-    for (int c = 0; c < cmb.ncb; ++c) cmb.cnt[(int64_t)t * cmb.ncb + c] = 0;
+    const bool kept_j = lane < cmb.k && cmb.inv[(int64_t)t * cmb.k + lane] >= 0;
+    const int kept = __popcll(__ballot(kept_j));
+    if (lane == 0) cmb.kept[t] = kept;
+    for (int c = lane; c < cmb.ncb; c += 64) cmb.cnt[(int64_t)t * cmb.ncb + c] = 0;
     if (kept == 0) {
       uint4* y = reinterpret_cast<uint4*>(static_cast<char*>(cmb.y) + (int64_t)t * cmb.y_row_bytes);
-      for (int c = 0; c < cmb.y_row_bytes / 16; ++c) y[c] = make_uint4(0u, 0u, 0u, 0u);
+      for (int c = lane; c < cmb.y_row_bytes / 16; c += 64) y[c] = make_uint4(0u, 0u, 0u, 0u);
     }
     return;
   }
@@ -1727,7 +1731,7 @@ moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles25
   ProfScope prof("tile_table", s);
   const int ntok =
       perm ? (int)std::min<int64_t>(64, std::max<int64_t>(1, ceil_div(rows_cap, 1024))) : 0;
-  const int ncmb = cmb ? (int)ceil_div(cmb->T, 1024) : 0;
+  const int ncmb = cmb ? (int)ceil_div(cmb->T, 16) : 0;  // 16 tokens per workgroup
   const CombinePrep none{};
   tile_table_kernel<<<3 + ntok + ncmb, 1024, 0, s>>>(off, groups, tiles256, tiles128, kcost, perm,
                                                      k, tok, ntok, cmb ? *cmb : none);
@@ -1882,8 +1886,10 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
   constexpr int NT = 64 * 2 * WGN;
   if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && (EPI != EPI_STORE || B2 != B2_NHALF)) {
-    // compute waves with MOE_WS_WAVE_ROWS x 64 blocks, and the producer waves
-    constexpr int CWM = BMt / MOE_WS_WAVE_ROWS, CWN = BNt / 64;
+    // compute waves with MOE_WS_WAVE_ROWS x 64 blocks (64 x 64 for the fused
+    // combine, whose counters go one row per lane), and the producer waves
+    constexpr int WROWS = ROLE == R_DOWN_FWD_COMBINE ? 64 : MOE_WS_WAVE_ROWS;
+    constexpr int CWM = BMt / WROWS, CWN = BNt / 64;
     constexpr int WS_NT = 64 * (CWM * CWN + MOE_WS_PRODUCER_WAVES);
     const auto kern = gemm_bf16_ws_kernel<BMt, BNt, CWM, CWN, MOE_WS_PRODUCER_WAVES, MOE_WS_STAGES,
                                           AM, BMD, GMD, B2, EPI, ROLE>;

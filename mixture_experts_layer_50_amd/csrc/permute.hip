@@ -3,12 +3,13 @@
 // The permutation sorts the (token, slot) rows by expert, so that one grouped
 // GEMM can run over the expert groups (page "Accelerating Transformers
 // fine-tuning with NVIDIA NeMo AutoModel", section 专家后端, grouped_mm row).
-// It is a deterministic counting sort in three passes:
+// It is a deterministic counting sort in three passes and two launches:
 //   1. per block of 256 tokens, one 256-bit token mask per local expert is
 //      built in LDS (atomic OR: order-free), and its popcounts are the
 //      block's expert histogram;
-//   2. one workgroup scans the histograms in (expert, block) order, giving
-//      each block its first position per expert and the group offsets;
+//   2. (second launch) every block scans the histograms in (expert, block)
+//      order for itself, giving its first position per expert (block 0 also
+//      writes the group offsets);
 //   3. each block rebuilds its masks and places row (t, j) of expert e at
 //      base[block][e] + popcount(mask_e below t): stable by token, and since
 //      a token's kept experts are distinct, stable by row t*k + j (a slot
@@ -68,78 +69,73 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_count_kernel(const int32_t* 
   }
 }
 
-// One workgroup; E_loc <= 1024.  counts[b][e] becomes the first sorted
-// position of block b's rows of expert e.  TPE = 1024 / E_loc (rounded down
-// to a power of two) threads share an expert, each summing a contiguous run
-// of blocks; the runs and then the experts are scanned in order.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* counts, int nb, int E_loc, int R_cap,
-                                                         int32_t* offsets) {
-  __shared__ int32_t part[1024];
-  __shared__ int32_t scan[1024];
-  int tpe = 1;
-  while (tpe * 2 * E_loc <= 1024) tpe *= 2;
-  const int e = threadIdx.x / tpe, c = threadIdx.x % tpe;
-  const int run = (nb + tpe - 1) / tpe;
-  const int b_lo = min(nb, c * run), b_hi = min(nb, b_lo + run);
-  constexpr int U = 8;  // block counts in flight per thread
-  int sum = 0;
-  if (e < E_loc) {
-    for (int b0 = b_lo; b0 < b_hi; b0 += U) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = b0 + u < b_hi ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) sum += v[u];
-    }
-  }
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  int before = 0, total = 0;  // this run's start within its expert; the expert's total
-  if (e < E_loc) {
-    for (int cc = 0; cc < tpe; ++cc) {
-      const int v = part[e * tpe + cc];
-      if (cc < c) before += v;
-      total += v;
-    }
-  }
-  scan[threadIdx.x] = (e < E_loc && c == 0) ? total : 0;  // one entry per expert, at its first thread
-  __syncthreads();
-  for (int s = 1; s < 1024; s <<= 1) {  // inclusive Hillis-Steele scan
-    const int v = threadIdx.x >= s ? scan[threadIdx.x - s] : 0;
-    __syncthreads();
-    scan[threadIdx.x] += v;
-    __syncthreads();
-  }
-  if (e < E_loc) {
-    const int o = scan[e * tpe] - total;  // exclusive prefix over experts
-    int pos = o + before;
-    for (int b0 = b_lo; b0 < b_hi; b0 += U) {
-      int v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = b0 + u < b_hi ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (b0 + u < b_hi) {
-          counts[(int64_t)(b0 + u) * E_loc + e] = pos;
-          pos += v[u];
-        }
-    }
-    if (c == 0) {
-      offsets[e] = min(o, R_cap);
-      if (e == E_loc - 1) offsets[E_loc] = min(o + total, R_cap);
-    }
-  }
-}
+// Scatter with the scan folded in: workgroup b reads the block counts of all
+// blocks (nb x E_loc, written by perm_count_kernel) and works out its own
+// first position per expert: the expert's offset (exclusive scan of the
+// experts' totals) plus its counts in the blocks before b.  Every workgroup
+// repeats this small scan instead of waiting for a separate scan launch;
+// workgroup 0 writes the group offsets.  Positions are those of the
+// three-kernel path.
+constexpr int SCAT_MAX_E = 512;  // local experts: the entry points allow E <= 512
 
-__global__ __launch_bounds__(PERM_TOKENS) void perm_scatter_kernel(const int32_t* idx, int T, int k,
-                                                                   int e_lo, int e_hi, int R_cap,
-                                                                   const int32_t* base,
-                                                                   int32_t* perm, int32_t* inv) {
+__global__ __launch_bounds__(PERM_TOKENS) void perm_scan_scatter_kernel(
+    const int32_t* idx, int T, int k, int e_lo, int e_hi, int R_cap, const int32_t* counts, int nb,
+    int32_t* offsets, int32_t* perm, int32_t* inv) {
   extern __shared__ uint32_t mask[];
+  __shared__ int32_t sbase[SCAT_MAX_E];
+  __shared__ int32_t stot[SCAT_MAX_E];
+  __shared__ int32_t wsum[PERM_TOKENS / 64];
   const int E_loc = e_hi - e_lo;
+  const int b = blockIdx.x;
+  // 1. per expert: counts of the blocks before b, and the total (U loads in flight)
+  for (int e = threadIdx.x; e < E_loc; e += PERM_TOKENS) {
+    constexpr int U = 8;
+    int before = 0, total = 0;
+    for (int b0 = 0; b0 < nb; b0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = b0 + u < nb ? counts[(int64_t)(b0 + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u < b) before += v[u];
+        total += v[u];
+      }
+    }
+    sbase[e] = before;
+    stot[e] = total;
+  }
+  __syncthreads();
+  // 2. exclusive scan of the totals over experts: each thread a contiguous run
+  //    of experts, then the runs' sums across the workgroup
+  constexpr int NTH = PERM_TOKENS;
+  const int per = (E_loc + NTH - 1) / NTH;
+  const int lo = min(E_loc, (int)threadIdx.x * per), hi = min(E_loc, lo + per);
+  int run = 0;
+  for (int e = lo; e < hi; ++e) run += stot[e];
+  // inclusive scan of run over the threads: within a wavefront, then waves
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += v;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int prev = 0;
+  for (int w = 0; w < wv; ++w) prev += wsum[w];
+  int o = prev + inc - run;  // exclusive prefix of this thread's first expert
+  for (int e = lo; e < hi; ++e) {
+    const int t_e = stot[e];
+    sbase[e] += o;
+    if (b == 0) offsets[e] = min(o, R_cap);
+    o += t_e;
+  }
+  if (b == 0 && hi == E_loc && lo < hi) offsets[E_loc] = min(o, R_cap);
+  // 3. the block's masks, ranks and positions
   int ids[MAXK];
   load_ids(ids, idx, T, k);
-  build_masks(mask, ids, e_lo, e_hi, E_loc);
+  build_masks(mask, ids, e_lo, e_hi, E_loc);  // starts and ends with a barrier
   const int t = blockIdx.x * PERM_TOKENS + threadIdx.x;
   if (t >= T) return;
   const int w = threadIdx.x >> 5;
@@ -158,7 +154,7 @@ __global__ __launch_bounds__(PERM_TOKENS) void perm_scatter_kernel(const int32_t
       const uint32_t* m = mask + (e - e_lo) * MASK_WORDS;
       int rank = __popc(m[w] & below);
       for (int ww = 0; ww < w; ++ww) rank += __popc(m[ww]);
-      pos = base[(int64_t)blockIdx.x * E_loc + (e - e_lo)] + rank;
+      pos = sbase[e - e_lo] + rank;
       if (pos >= R_cap) pos = -1;
       else perm[pos] = (int32_t)r;
     }
@@ -201,15 +197,11 @@ moe_status_t launch_permute(const int32_t* idx, const void* x, int T, int d, int
     perm_count_kernel<<<nb, PERM_TOKENS, lds, s>>>(idx, T, k, e_lo, e_hi, counts);
     if ((st = check_launch("perm_count_kernel")) != MOE_OK) return st;
   }
-  {
-    ProfScope prof("permute_scan", s);
-    perm_scan_kernel<<<1, 1024, 0, s>>>(counts, nb, E_loc, R_cap, offsets);
-    if ((st = check_launch("perm_scan_kernel")) != MOE_OK) return st;
-  }
-  {
+  {  // the scan runs inside the scatter kernel (every workgroup its own part)
     ProfScope prof("permute_scatter", s);
-    perm_scatter_kernel<<<nb, PERM_TOKENS, lds, s>>>(idx, T, k, e_lo, e_hi, R_cap, counts, perm, inv);
-    if ((st = check_launch("perm_scatter_kernel")) != MOE_OK) return st;
+    perm_scan_scatter_kernel<<<nb, PERM_TOKENS, lds, s>>>(idx, T, k, e_lo, e_hi, R_cap, counts, nb,
+                                                          offsets, perm, inv);
+    if ((st = check_launch("perm_scan_scatter_kernel")) != MOE_OK) return st;
   }
   if (xp) {  // without xp only the sort runs (the gathered GEMMs read x through perm)
     ProfScope prof("permute_gather", s);
