@@ -79,7 +79,7 @@ typedef enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_BALANCED = 1 } moe_gate_t;
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7,
-  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9, MOE_OP_FFN_FWD_FUSED = 10
+  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9, MOE_OP_FFN_FWD_FUSED = 10, MOE_OP_ROUTE_PERMUTE = 11
 } moe_op_t;
 
 typedef void* moe_stream_t; /* hipStream_t */
@@ -139,6 +139,20 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
 moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, const void* x,
                          int32_t* group_offsets, int32_t* perm, int32_t* inv, void* xp,
                          void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* a1 + a2 in one call: moe_route followed by moe_permute, with the same
+ * arguments, outputs and results (bit-identical).  Under the balanced gate
+ * the sort has a closed form (expert e = (t mod P) + j*P receives the tokens
+ * t = e mod P, e mod P + P, ... in token order), so idx, topk_w,
+ * group_offsets, perm and inv come from one kernel and x, w_router, bias and
+ * logits are not touched (xp, when given, is still filled from x).  Under the
+ * softmax top-k gate the router kernels run, then the sort.  ws:
+ * moe_workspace_size(MOE_OP_ROUTE_PERMUTE) (0 for the balanced gate, else
+ * the permute's workspace). */
+moe_status_t moe_route_permute(const moe_shape_t* shape, const void* x, const void* w_router,
+                               const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                               int32_t* group_offsets, int32_t* perm, int32_t* inv, void* xp,
+                               void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* a3 + a4 -- expert FFN over the expert groups as grouped GEMMs (one grouped
  * GEMM over all groups, [P3] section 专家后端; experts are fused 3-D weight tensors,

@@ -331,6 +331,8 @@ int64_t fused_cnt_bytes(const Dims& D) { return round_up((int64_t)D.T * (D.d / 6
 
 int64_t ws_bytes(const Dims& D, int op) {
   switch (op) {
+    case MOE_OP_ROUTE_PERMUTE:
+      return D.balanced ? 0 : round_up(permute_ws_bytes(D.T, D.E_loc), 256);
     case MOE_OP_FFN_FWD_FUSED:
       return D.bf16 ? tile_table_bytes(D) + fused_kept_bytes(D) + fused_cnt_bytes(D) : 0;
     case MOE_OP_PERMUTE: return round_up(permute_ws_bytes(D.T, D.E_loc), 256);
@@ -366,7 +368,7 @@ extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, siz
   Dims D;
   if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
   MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FFN_FWD_FUSED)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_ROUTE_PERMUTE)
     return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
   *bytes = (size_t)ws_bytes(D, op);
   return MOE_OK;
@@ -406,6 +408,32 @@ extern "C" moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* top
   MOE_TRY(check_ws(fn, D, MOE_OP_PERMUTE, ws, ws_bytes_));
   return launch_permute(topk_idx, x, D.T, D.d, D.k, D.e_lo, D.e_hi, D.R_cap, D.eb, group_offsets,
                         perm, inv, xp, ws, S(stream));
+}
+
+extern "C" moe_status_t moe_route_permute(const moe_shape_t* shape, const void* x,
+                                          const void* w_router, const float* bias, float* logits,
+                                          int32_t* topk_idx, float* topk_w,
+                                          int32_t* group_offsets, int32_t* perm, int32_t* inv,
+                                          void* xp, void* ws, size_t ws_bytes_,
+                                          moe_stream_t stream) {
+  const char* fn = "moe_route_permute";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"topk_idx", topk_idx}, {"topk_w", topk_w}, {"group_offsets", group_offsets},
+                    {"perm", perm}, {"inv", inv}}));
+  if (xp) MOE_TRY(need(fn, {{"x", x}, {"xp", xp}}));
+  if (!D.balanced) {  // the router, then the sort
+    MOE_TRY(need(fn, {{"x", x}, {"w_router", w_router}, {"logits", logits}}));
+    MOE_TRY(opt(fn, {{"bias", bias}}));
+    MOE_TRY(check_ws(fn, D, MOE_OP_ROUTE_PERMUTE, ws, ws_bytes_));
+    MOE_TRY(moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, stream));
+    return launch_permute(topk_idx, x, D.T, D.d, D.k, D.e_lo, D.e_hi, D.R_cap, D.eb,
+                          group_offsets, perm, inv, xp, ws, S(stream));
+  }
+  MOE_TRY(launch_balanced_route_permute(D.T, D.E, D.k, D.e_lo, D.e_hi, D.R_cap, topk_idx, topk_w,
+                                        group_offsets, perm, inv, S(stream)));
+  if (xp) return launch_permute_gather(x, inv, D.T, D.d, D.k, D.eb, xp, S(stream));
+  return MOE_OK;
 }
 
 namespace {

@@ -11,6 +11,13 @@ namespace moe {
 
 // route.hip
 moe_status_t launch_balanced_gate(int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
+// The balanced gate with the expert sort in closed form (idx, w, offsets, perm, inv).
+moe_status_t launch_balanced_route_permute(int T, int E, int k, int e_lo, int e_hi, int R_cap,
+                                           int32_t* idx, float* w, int32_t* offsets,
+                                           int32_t* perm, int32_t* inv, hipStream_t s);
+// The row copy Xp[p] = x[perm[p] / k] of the permute (perm_gather_kernel).
+moe_status_t launch_permute_gather(const void* x, const int32_t* inv, int T, int d, int k,
+                                   int elt_bytes, void* xp, hipStream_t s);
 moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                  hipStream_t s);
 // Tokens per workgroup of the router backward (one bias-gradient partial each).

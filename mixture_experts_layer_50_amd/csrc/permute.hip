@@ -203,14 +203,18 @@ moe_status_t launch_permute(const int32_t* idx, const void* x, int T, int d, int
                                                           offsets, perm, inv);
     if ((st = check_launch("perm_scan_scatter_kernel")) != MOE_OK) return st;
   }
-  if (xp) {  // without xp only the sort runs (the gathered GEMMs read x through perm)
-    ProfScope prof("permute_gather", s);
-    const int chunks = d * elt_bytes / 16;
-    perm_gather_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(
-        static_cast<const uint4*>(x), inv, T, k, chunks, static_cast<uint4*>(xp));
-    if ((st = check_launch("perm_gather_kernel")) != MOE_OK) return st;
-  }
+  if (xp)  // without xp only the sort runs (the gathered GEMMs read x through perm)
+    return launch_permute_gather(x, inv, T, d, k, elt_bytes, xp, s);
   return MOE_OK;
+}
+
+moe_status_t launch_permute_gather(const void* x, const int32_t* inv, int T, int d, int k,
+                                   int elt_bytes, void* xp, hipStream_t s) {
+  ProfScope prof("permute_gather", s);
+  const int chunks = d * elt_bytes / 16;
+  perm_gather_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(
+      static_cast<const uint4*>(x), inv, T, k, chunks, static_cast<uint4*>(xp));
+  return check_launch("perm_gather_kernel");
 }
 
 // ---------------------------------------------------------------- combine

@@ -28,6 +28,53 @@ moe_status_t launch_balanced_gate(int T, int E, int k, int32_t* idx, float* w, h
   return check_launch("balanced_gate_kernel");
 }
 
+// Balanced gate and the expert sort in one kernel.  Expert e = (t mod P) +
+// j*P (P = E/k) receives the tokens t = e mod P + m*P, m = 0, 1, ..., in
+// token order, so a row's sorted position has a closed form: the rows of the
+// local experts before e, plus m = t div P.  With c(r) = the number of tokens
+// t < T with t mod P = r, the rows of experts [0, n) number
+//   F(n) = (n div P) T + (T div P) (n mod P) + min(T mod P, n mod P),
+// and local expert e starts at F(e) - F(e_lo).  Positions >= R_cap are
+// dropped (inv = -1), as in the sort.
+__device__ __forceinline__ int64_t balanced_rows_before(int64_t n, int T, int P) {
+  const int64_t q = n / P, r = n % P;
+  return q * T + (int64_t)(T / P) * r + min((int64_t)(T % P), r);
+}
+
+__global__ void balanced_route_permute_kernel(int T, int E, int k, int e_lo, int e_hi, int R_cap,
+                                              int32_t* idx, float* w, int32_t* offsets,
+                                              int32_t* perm, int32_t* inv) {
+  const int P = E / k;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t base = balanced_rows_before(e_lo, T, P);
+  if (i <= e_hi - e_lo)  // group offsets of the local experts
+    offsets[i] = (int32_t)min(balanced_rows_before(e_lo + i, T, P) - base, (int64_t)R_cap);
+  if (i >= (int64_t)T * k) return;
+  const int t = (int)(i / k), j = (int)(i - (int64_t)t * k);
+  const int e = (t % P) + j * P;
+  idx[i] = e;
+  w[i] = 1.0f / (float)k;
+  int pos = -1;
+  if (e >= e_lo && e < e_hi) {
+    const int64_t p = balanced_rows_before(e, T, P) - base + t / P;
+    if (p < R_cap) {
+      pos = (int)p;
+      perm[pos] = (int32_t)i;
+    }
+  }
+  inv[i] = pos;
+}
+
+moe_status_t launch_balanced_route_permute(int T, int E, int k, int e_lo, int e_hi, int R_cap,
+                                           int32_t* idx, float* w, int32_t* offsets,
+                                           int32_t* perm, int32_t* inv, hipStream_t s) {
+  ProfScope prof("route_permute_balanced", s);
+  const int64_t n = std::max<int64_t>((int64_t)T * k, e_hi - e_lo + 1);
+  balanced_route_permute_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(
+      T, E, k, e_lo, e_hi, R_cap, idx, w, offsets, perm, inv);
+  return check_launch("balanced_route_permute_kernel");
+}
+
 // ---------------------------------------------------------------- top-k
 // One wavefront per token.  Lane l holds the logits of experts l + 64 v.
 // k rounds: every lane proposes its best untaken expert, a butterfly over the

@@ -50,7 +50,7 @@ class LayerBuffers:
         t["a"] = e(R, I)
         t["yp"] = e(R, d)
         t["y"] = e(T, d)
-        for op in ("permute", "ffn_fwd_fused" if self.fused else "ffn_fwd"):
+        for op in ("permute", "route_permute", "ffn_fwd_fused" if self.fused else "ffn_fwd"):
             t["ws_" + op] = self._ws(op)
         if self.aux_alpha is not None:
             t["aux_loss"] = e(1, dtype=f32)
@@ -80,17 +80,16 @@ class LayerBuffers:
 
 def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
             stream=None):
-    """route -> permute -> grouped SwiGLU FFN -> combine; y lands in buf['y'].
+    """route + permute (one call) -> grouped SwiGLU FFN -> combine; y lands in buf['y'].
     With buf.gather the permute only sorts and the FFN reads x through perm;
     with buf.fused the combine also runs inside the FFN's down projection.
     With buf.aux_alpha the router's balancing loss lands in buf['aux_loss']."""
     t = buf.t
-    B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
+    B.moe_route_permute(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"],
+                        t["offsets"], t["perm"], t["inv"], t["xp"], t["ws_route_permute"], stream)
     if buf.aux_alpha is not None:
         B.moe_aux_loss(shape, t["logits"], t["topk_idx"], buf.aux_alpha, t["aux_loss"], t["aux_w"],
                        t["ws_aux_loss"], stream)
-    B.moe_permute(shape, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"],
-                  t["ws_permute"], stream)
     if buf.fused:  # combine included
         B.moe_grouped_ffn_fwd_fused(shape, x, t["perm"], t["inv"], t["topk_w"], t["offsets"],
                                     w_gate, w_up, w_down, t["h"], t["a"], t["yp"], t["y"],
