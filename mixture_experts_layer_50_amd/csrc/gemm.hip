@@ -514,8 +514,12 @@ struct NoHook {
 
 // `hook(integral_constant<ks>)` runs before MFMA step ks (the other form);
 // with `active` false only the hooks run.
-template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, bool PIPE = false, int FM,
-          int FN, typename Hook = NoHook>
+// RSKIP (PIPE only): test the row blocks against `rows` at all; GEMMs whose
+// tiles are always full (the weight gradients: M is d or I) leave it off, so
+// that the slice is straight-line code (the tests split it into small blocks
+// the scheduler cannot interleave across).
+template <int BM, int BN, int WGM, int WGN, int AM, int BMD, int B2, bool PIPE = false,
+          bool RSKIP = true, int FM, int FN, typename Hook = NoHook>
 __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* as, int wm, int wn,
                                           int lane, int rows, Hook hook = Hook(),
                                           bool active = true) {
@@ -524,18 +528,18 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[FM][FN], const bf16_t* a
   constexpr int KS = BK / 16;
   if constexpr (PIPE) {
     bf16x8 af[2][FM], bfg[2][FN];
-    load_frags<BM, BN, WGM, WGN, AM, BMD, B2, true>(af[0], bfg[0], as, 0, wm, wn, lane, rows);
+    load_frags<BM, BN, WGM, WGN, AM, BMD, B2, RSKIP>(af[0], bfg[0], as, 0, wm, wn, lane, rows);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS)
-        load_frags<BM, BN, WGM, WGN, AM, BMD, B2, true>(af[(ks + 1) & 1], bfg[(ks + 1) & 1], as,
-                                                        ks + 1, wm, wn, lane, rows);
+        load_frags<BM, BN, WGM, WGN, AM, BMD, B2, RSKIP>(af[(ks + 1) & 1], bfg[(ks + 1) & 1], as,
+                                                         ks + 1, wm, wn, lane, rows);
       // keep the next step's reads above this step's MFMAs (the scheduler
       // would otherwise move each read down to its first use)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if (wm * WTM + i * 32 >= rows) continue;
+        if (RSKIP && wm * WTM + i * 32 >= rows) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[ks & 1][j], af[ks & 1][i],
@@ -1558,8 +1562,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
     int g = 0;
     auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
       constexpr int U = decltype(Uc)::value;
-      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2, true>(acc, smem + U * BUF, wm, wn, lane,
-                                                     ct.m_hi - ct.m_lo);
+      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2, true, GMD == G_MROWS>(acc, smem + U * BUF, wm, wn,
+                                                                     lane, ct.m_hi - ct.m_lo);
       __syncthreads();
       ++g;
       return advance(std::true_type{});
