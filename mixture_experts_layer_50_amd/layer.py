@@ -67,6 +67,12 @@ class LayerBuffers:
             t["dlogits"] = e(T, E, dtype=f32)
             t["dw_router"] = e(d, E)
             t["dbias"] = e(E, dtype=f32)
+            if s.gate == B.GATES["balanced"]:
+                # the balanced gate's weights are constants: the router
+                # gradients are identically zero, set once here (the backward
+                # passes NULL for them, so nothing rewrites them)
+                for name in ("dlogits", "dw_router", "dbias"):
+                    t[name].zero_()
             for op in ("ffn_bwd", "route_bwd"):
                 t["ws_" + op] = self._ws(op)
 
@@ -135,6 +141,11 @@ def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up
         B.moe_route_bwd_aux(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"],
                             t["logits"], t["aux_w"], t["dlogits"], t["dw_router"], t["dbias"],
                             t["dx"], t["ws_route_bwd"], stream)
+        return
+    if shape.gate == B.GATES["balanced"]:
+        # zero router gradients, already in the buffers (LayerBuffers)
+        B.moe_route_bwd(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"], None, None,
+                        None, t["dx"], t["ws_route_bwd"], stream)
         return
     B.moe_route_bwd(shape, x, w_router, t["topk_idx"], t["topk_w"], t["dtopk_w"], t["dlogits"],
                     t["dw_router"], t["dbias"], t["dx"], t["ws_route_bwd"], stream)

@@ -32,10 +32,15 @@ def run_layer(w: MI.Workload, dev, R_cap=0, training=True, poison=False, gather=
     s = shape_of(w, R_cap)
     buf = LayerBuffers(s, training=training, gather=gather, aux_alpha=aux_alpha, fused=fused)
     if poison:
-        for v in buf.t.values():
-            if v is not None and v.is_floating_point():
+        # (under the balanced gate the router gradients are constants the
+        # layer zeroes once at allocation; the backward does not rewrite them)
+        keep = ("dlogits", "dw_router", "dbias") if w.gate == "balanced" else ()
+        for name, v in buf.t.items():
+            if v is None or name in keep:
+                continue
+            if v.is_floating_point():
                 v.fill_(float("nan"))
-            elif v is not None and v.dtype == torch.int32:
+            elif v.dtype == torch.int32:
                 v.fill_(-7)
     forward(s, buf, dev["x"], dev.get("Wr"), dev.get("b"), dev["Wg"], dev["Wu"], dev["Wd"])
     if training:

@@ -70,3 +70,21 @@ def test_route_permute_matches_separate_calls_and_oracle(case):
     assert np.array_equal(U.np64(t1["xp"][:R]), p["Xp"]), "xp is not an exact copy"
     if R < s.rows_cap:
         assert (t1["perm"][R:] == -7).all(), "perm written past the routed rows"
+
+
+def test_balanced_route_bwd_zeroes_given_gradients():
+    """Under the balanced gate the router's gradients are zero: moe_route_bwd
+    writes zeros into the buffers it is given (the layer passes none and keeps
+    buffers zeroed at allocation)."""
+    print("\n[gpu case] balanced route_bwd zero fill", flush=True)
+    T, d, E, k = 300, 128, 16, 4
+    s = B.MoEShape.make(T, d, E, k, 64, dtype="bf16", gate="balanced")
+    dl = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    dw = torch.full((d, E), float("nan"), dtype=torch.bfloat16, device="cuda")
+    db = torch.full((E,), float("nan"), dtype=torch.float32, device="cuda")
+    dx = torch.ones((T, d), dtype=torch.bfloat16, device="cuda")
+    B.moe_route_bwd(s, None, None, None, None, None, dl, dw, db, dx, None)
+    torch.cuda.synchronize()
+    assert not dl.abs().max().item() and not dw.float().abs().max().item()
+    assert not db.abs().max().item()
+    assert (dx == 1).all(), "the balanced gate adds nothing to dx"
