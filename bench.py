@@ -219,6 +219,31 @@ def timed_steps(step, steps: int, warmup: int):
             "mean": round(sum(t) / len(t), 4)}
 
 
+def graph_step_ms(step, replays: int):
+    """GPU time per call of step, captured once in a HIP graph and replayed
+    `replays` times between two events (no host enqueue in the span)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / replays
+    del g
+    return ms
+
+
 def kernel_averages(step, B, n: int):
     """Per-kernel averages (us) over n instrumented steps."""
     import torch
@@ -353,8 +378,12 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
             "kernels_us_avg": {k: v for k, v in ka.items() if k.startswith(("aux", "route"))}}
         del buf
     if "small" in want:  # decode-sized batches, natural router, forward only
-        out["small_batch_fwd"] = {}
-        for Ts in (1, 8, 64):
+        out["small_batch_fwd"] = {
+            "note": "us per forward; *_us: HIP events around eager calls (host enqueue "
+                    "included when it is the longer), *_graph_us: the same calls replayed "
+                    "from a HIP graph (GPU time); the size rule takes the small call for "
+                    "2*T*k <= E_loc (T <= 8 here)"}
+        for Ts in (1, 8, 16, 64):
             shape_s = B.MoEShape.make(Ts, wn.d, wn.E, wn.k, wn.I, dtype="bf16",
                                       gate="softmax_topk")
             xs = dev["x"][:Ts].contiguous()
@@ -372,6 +401,8 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
             out["small_batch_fwd"][f"T{Ts}"] = {
                 "small_us": round(1000 * ss["median"], 1),
                 "grouped_us": round(1000 * sg["median"], 1),
+                "small_graph_us": round(1000 * graph_step_ms(step_small, 50), 1),
+                "grouped_graph_us": round(1000 * graph_step_ms(step_grouped, 50), 1),
                 "small_kernels_us_avg": kernel_averages(step_small, B, 5)}
             del bs, bg
     if "dsv3" in want:  # one rank of eight at the DeepSeek-V3 shape, balanced gate

@@ -79,7 +79,8 @@ typedef enum { MOE_GATE_SOFTMAX_TOPK = 0, MOE_GATE_BALANCED = 1 } moe_gate_t;
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7,
-  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9, MOE_OP_FFN_FWD_FUSED = 10, MOE_OP_ROUTE_PERMUTE = 11
+  MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9, MOE_OP_FFN_FWD_FUSED = 10, MOE_OP_ROUTE_PERMUTE = 11,
+  MOE_OP_SMALL_ROUTED_FWD = 12
 } moe_op_t;
 
 typedef void* moe_stream_t; /* hipStream_t */
@@ -242,10 +243,11 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t
                          const float* topk_w, void* y, moe_stream_t stream);
 
 /* a3 + a4 + a5 for a few tokens -- the batched_mm expert backend ([P3] section
- * 专家后端, backend table: each routed pair multiplies by its own expert's
- * weights in one batched product, for small inputs).  No sort and no grouped
- * GEMM: every (token, slot) pair with a local, first-occurrence expert
- * e = topk_idx[t,j] reads that expert's weights directly, and
+ * 专家后端, backend table: the routed pairs multiply by their experts' weights
+ * in batched products, for small inputs).  No sort and no grouped GEMM: the
+ * workgroups of each active local expert find that expert's (token, slot)
+ * pairs (local, first-occurrence slots e = topk_idx[t,j]) in the table
+ * themselves and read its weights once per column block, and
  *   y[t] = sum_j topk_w[t,j] * (silu(x[t] Wg[e]) * (x[t] Wu[e])) Wd[e]
  * in ascending j with fp32 accumulation (A rounded to the dtype, as in
  * moe_grouped_ffn_fwd); tokens with no local slot get y[t] = 0.  The same
@@ -253,16 +255,32 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t
  * (the sums run in another order).  x [T,d]; topk_idx, topk_w [T,k];
  * weights as for moe_grouped_ffn_fwd; y [T,d].  ws:
  * moe_workspace_size(MOE_OP_SMALL_FWD) (fp32 partial sums of [Hg | Hu] over
- * up to 8 ranges of d, the per-slot outputs and the slot map).  Every pair
- * re-reads its expert's weights (3*d*I elements), so the form is faster than
- * the grouped path only while T*k is at most about E_loc: measured at the
- * Qwen3-30B-A3B shape (E_loc = 128, k = 8), 50 vs 102 us at T = 1, about equal
- * at T = 8, 3.6x slower at T = 64.  Needs T*k <= 65535, d and I <= 12288 and no row capacity
- * (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
+ * up to 8 ranges of d, the per-slot outputs, the combine's counters).  The
+ * combine runs inside the second kernel (the workgroup that writes a token's
+ * last pair row of a column block, by an integer arrival counter, sums the
+ * token's pairs in ascending slot order: deterministic).  With no tile
+ * padding and no sort it is the faster form while T*k is at most about
+ * E_loc / 2 (the layer's size rule).  Needs T*k <= 4096, d and I <= 8192 and no row
+ * capacity (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
 moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const int32_t* topk_idx,
                                const float* topk_w, const void* w_gate, const void* w_up,
                                const void* w_down, void* y, void* ws, size_t ws_bytes,
                                moe_stream_t stream);
+
+/* a1 + a3 + a4 + a5 for a few tokens, in one call: the gate, then
+ * moe_ffn_small_fwd's FFN and combine.  Under the softmax top-k gate with
+ * T <= 16 the router runs split over d (partial logits of 64-row chunks of d
+ * in parallel workgroups, then one wavefront per token adds them in chunk
+ * order, adds the bias and takes the top k with softmax, as moe_route does;
+ * the sums run in another order than moe_route's, so logits may differ from
+ * it in the last bits); for more tokens moe_route's kernels run.  Outputs
+ * logits (softmax gate), topk_idx, topk_w and y as moe_route and
+ * moe_ffn_small_fwd would; the same arguments and limits.  ws:
+ * moe_workspace_size(MOE_OP_SMALL_ROUTED_FWD). */
+moe_status_t moe_small_fwd(const moe_shape_t* shape, const void* x, const void* w_router,
+                           const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                           const void* w_gate, const void* w_up, const void* w_down, void* y,
+                           void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------ backward */
 /* Full-parameter fine-tuning needs every gradient ([P3] Qwen3 and Nemotron

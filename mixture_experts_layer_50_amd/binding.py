@@ -18,7 +18,9 @@ DTYPES = {"f32": 0, "bf16": 1}
 GATES = {"softmax_topk": 0, "balanced": 1}
 OPS = {"route": 0, "permute": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4, "ffn_bwd": 5,
        "permute_bwd": 6, "route_bwd": 7, "small_fwd": 8, "aux_loss": 9, "ffn_fwd_fused": 10,
-       "route_permute": 11}
+       "route_permute": 11, "small_routed_fwd": 12}
+SMALL_MAX_WIDTH = 8192  # moe_ffn_small_fwd / moe_small_fwd: d and I at most this
+SMALL_MAX_PAIRS = 4096  # and T*k at most this
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP", 6: "MOE_ERR_UNSUPPORTED"}
 
@@ -29,7 +31,7 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_
            "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names",
            "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd",
            "moe_aux_loss", "moe_route_bwd_aux", "moe_grouped_ffn_fwd_gather_noalloc",
-           "moe_grouped_ffn_fwd_fused", "moe_route_permute"]
+           "moe_grouped_ffn_fwd_fused", "moe_route_permute", "moe_small_fwd"]
 
 
 class MoEError(RuntimeError):
@@ -95,6 +97,7 @@ def load_library() -> ctypes.CDLL:
         "moe_grouped_ffn_fwd_gather_noalloc": [S, P, P, P, P, P, P, P, P, P, P],
         "moe_grouped_ffn_fwd_fused": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_route_permute": [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_small_fwd": [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_ffn_small_fwd": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
@@ -201,6 +204,14 @@ def moe_ffn_small_fwd(shape, x, topk_idx, topk_w, w_gate, w_up, w_down, y, ws, s
     _check("moe_ffn_small_fwd", load_library().moe_ffn_small_fwd(
         ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_small_fwd(shape, x, w_router, bias, logits, topk_idx, topk_w, w_gate, w_up, w_down, y, ws,
+                  stream=None):
+    _check("moe_small_fwd", load_library().moe_small_fwd(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
 
 
 def moe_combine(shape, yp, inv, topk_w, y, stream=None):

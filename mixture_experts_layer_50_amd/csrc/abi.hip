@@ -324,6 +324,14 @@ struct RouteBwdWs {
   }
 };
 
+// The few-token router's partial logits (softmax top-k gate, T small enough),
+// then the small-batch FFN's workspace.
+bool small_router_used(const Dims& D) { return !D.balanced && D.T <= SMALL_ROUTE_MAX_T; }
+int64_t small_routed_ws_bytes(const Dims& D) {
+  return (small_router_used(D) ? small_router_ws_bytes(D.T, D.d, D.E) : 0) +
+         round_up(small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.e_lo, D.e_hi, D.eb), 256);
+}
+
 // The fused combine's workspace after the tile tables: kept slots per token
 // [T] and the arrival counters [T][d/64].
 int64_t fused_kept_bytes(const Dims& D) { return round_up((int64_t)D.T * 4, 256); }
@@ -331,6 +339,8 @@ int64_t fused_cnt_bytes(const Dims& D) { return round_up((int64_t)D.T * (D.d / 6
 
 int64_t ws_bytes(const Dims& D, int op) {
   switch (op) {
+    case MOE_OP_SMALL_ROUTED_FWD:
+      return small_routed_ws_bytes(D);
     case MOE_OP_ROUTE_PERMUTE:
       return D.balanced ? 0 : round_up(permute_ws_bytes(D.T, D.E_loc), 256);
     case MOE_OP_FFN_FWD_FUSED:
@@ -340,7 +350,7 @@ int64_t ws_bytes(const Dims& D, int op) {
     case MOE_OP_FFN_BWD:
       return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
              (D.bf16 ? tile_table_bytes(D) : 0);
-    case MOE_OP_SMALL_FWD: return small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.eb);
+    case MOE_OP_SMALL_FWD: return small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.e_lo, D.e_hi, D.eb);
     case MOE_OP_AUX_LOSS: return D.balanced ? 0 : aux_loss_ws_bytes(D.T, D.E);
     case MOE_OP_ROUTE_BWD: {
       if (D.balanced) return 0;
@@ -368,7 +378,7 @@ extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, siz
   Dims D;
   if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
   MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
-  if (op < MOE_OP_ROUTE || op > MOE_OP_ROUTE_PERMUTE)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_SMALL_ROUTED_FWD)
     return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
   *bytes = (size_t)ws_bytes(D, op);
   return MOE_OK;
@@ -627,6 +637,20 @@ extern "C" moe_status_t moe_grouped_ffn_fwd_fused(const moe_shape_t* shape, cons
                  w_down, h_save, a_save, yp, ws, ws_bytes_, stream, &fc);
 }
 
+namespace {
+// Shapes the small-batch FFN takes.
+moe_status_t check_small(const char* fn, const Dims& D) {
+  if ((int64_t)D.T * D.k > SMALL_MAX_PAIRS)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld > %lld (use the grouped FFN)", fn,
+                (long long)D.T * D.k, (long long)SMALL_MAX_PAIRS);
+  if (D.d > SMALL_MAX_WIDTH || D.I > SMALL_MAX_WIDTH)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d and I must be <= %d", fn, SMALL_MAX_WIDTH);
+  if (D.R_cap != D.T * D.k)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: no row capacity (R_cap must be 0 or T*k)", fn);
+  return MOE_OK;
+}
+}  // namespace
+
 extern "C" moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x,
                                           const int32_t* topk_idx, const float* topk_w,
                                           const void* w_gate, const void* w_up,
@@ -637,16 +661,42 @@ extern "C" moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* 
   MOE_TRY(check_shape(shape, fn, &D));
   MOE_TRY(need(fn, {{"x", x}, {"topk_idx", topk_idx}, {"topk_w", topk_w}, {"w_gate", w_gate},
                     {"w_up", w_up}, {"w_down", w_down}, {"y", y}}));
-  if ((int64_t)D.T * D.k > SMALL_MAX_PAIRS)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld > %lld (use the grouped FFN)", fn,
-                (long long)D.T * D.k, (long long)SMALL_MAX_PAIRS);
-  if (D.d > SMALL_MAX_WIDTH || D.I > SMALL_MAX_WIDTH)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: d and I must be <= %d", fn, SMALL_MAX_WIDTH);
-  if (D.R_cap != D.T * D.k)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: no row capacity (R_cap must be 0 or T*k)", fn);
+  MOE_TRY(check_small(fn, D));
   MOE_TRY(check_ws(fn, D, MOE_OP_SMALL_FWD, ws, ws_bytes_));
   return launch_small_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, D.T, D.d, D.k, D.I, D.e_lo,
                           D.e_hi, D.eb, y, ws, S(stream));
+}
+
+extern "C" moe_status_t moe_small_fwd(const moe_shape_t* shape, const void* x,
+                                      const void* w_router, const float* bias, float* logits,
+                                      int32_t* topk_idx, float* topk_w, const void* w_gate,
+                                      const void* w_up, const void* w_down, void* y, void* ws,
+                                      size_t ws_bytes_, moe_stream_t stream) {
+  const char* fn = "moe_small_fwd";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"x", x}, {"topk_idx", topk_idx}, {"topk_w", topk_w}, {"w_gate", w_gate},
+                    {"w_up", w_up}, {"w_down", w_down}, {"y", y}}));
+  if (!D.balanced) {
+    MOE_TRY(need(fn, {{"w_router", w_router}, {"logits", logits}}));
+    MOE_TRY(opt(fn, {{"bias", bias}}));
+  }
+  MOE_TRY(check_small(fn, D));
+  MOE_TRY(check_ws(fn, D, MOE_OP_SMALL_ROUTED_FWD, ws, ws_bytes_));
+  char* wsb = static_cast<char*>(ws);
+  hipStream_t s = S(stream);
+  int64_t ffn_at = 0;
+  if (D.balanced) {
+    MOE_TRY(launch_balanced_gate(D.T, D.E, D.k, topk_idx, topk_w, s));
+  } else if (small_router_used(D)) {
+    MOE_TRY(launch_small_router(x, w_router, bias, D.T, D.d, D.E, D.k, D.eb, logits, topk_idx,
+                                topk_w, reinterpret_cast<float*>(wsb), s));
+    ffn_at = small_router_ws_bytes(D.T, D.d, D.E);
+  } else {
+    MOE_TRY(moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, stream));
+  }
+  return launch_small_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, D.T, D.d, D.k, D.I, D.e_lo,
+                          D.e_hi, D.eb, y, wsb + ffn_at, s);
 }
 
 extern "C" moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t* inv,

@@ -20,6 +20,15 @@ moe_status_t launch_permute_gather(const void* x, const int32_t* inv, int T, int
                                    int elt_bytes, void* xp, hipStream_t s);
 moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                  hipStream_t s);
+// The router for a few tokens (T <= SMALL_ROUTE_MAX_T): split over K in
+// chunks of SMALL_ROUTE_KC rows of d (d % 64 == 0), then a fixed-order sum,
+// the bias, top-k and softmax.  Workspace: the partial logits.
+constexpr int SMALL_ROUTE_MAX_T = 16;
+constexpr int SMALL_ROUTE_KC = 64;
+int64_t small_router_ws_bytes(int T, int d, int E);
+moe_status_t launch_small_router(const void* x, const void* wr, const float* bias, int T, int d,
+                                 int E, int k, int elt_bytes, float* logits, int32_t* idx,
+                                 float* w, float* part, hipStream_t s);
 // Tokens per workgroup of the router backward (one bias-gradient partial each).
 constexpr int ROUTE_BWD_TOKENS = 32;
 // logits / aux_w (both or neither): add the auxiliary loss's logit gradient.
@@ -52,10 +61,12 @@ moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* i
 
 // small.hip: the small-batch FFN (no sort): y[t] = sum_j w[t,j] FFN_e(x[t]) over
 // the local, first-occurrence slots.  Workspace: fp32 gate/up partial sums
-// [T*k, KS, 2I] (KS splits of d), Yp [T*k, d], the slot map [T*k].  Needs T*k <= SMALL_MAX_PAIRS, d and I <= SMALL_MAX_WIDTH.
-constexpr int64_t SMALL_MAX_PAIRS = 65535;
-constexpr int SMALL_MAX_WIDTH = 12288;
-int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int elt_bytes);
+// [T*k, KS, 2I] (KS splits of d), Yp [T*k, d], the combine's arrival
+// counters [T, d / (8 N)].  Needs T*k <= SMALL_MAX_PAIRS, d and I <=
+// SMALL_MAX_WIDTH (the LDS the kernels' routing table and token rows take).
+constexpr int64_t SMALL_MAX_PAIRS = 4096;
+constexpr int SMALL_MAX_WIDTH = 8192;
+int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int e_lo, int e_hi, int elt_bytes);
 moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_topk,
                               const void* wg, const void* wu, const void* wd, int T, int d, int k,
                               int I, int e_lo, int e_hi, int elt_bytes, void* y, void* ws,

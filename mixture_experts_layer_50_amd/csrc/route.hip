@@ -84,21 +84,14 @@ __device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
   return v > bv || (v == bv && id < bid);
 }
 
+// Top-k and softmax of one token's logits, held by one wavefront (lane l:
+// experts l + 64 q in v[q], -inf past E); writes the token's k slots.
 template <int VPL>
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* logits, int T, int E, int k,
-                                                           int32_t* idx, float* w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
-  float v[VPL];
+__device__ __forceinline__ void topk_softmax_wave(const float (&v)[VPL], int E, int k, int lane,
+                                                  int32_t* idx_t, float* w_t) {
   bool taken[VPL];
 #pragma unroll
-  for (int q = 0; q < VPL; ++q) {
-    int e = lane + 64 * q;
-    v[q] = e < E ? row[e] : -INFINITY;
-    taken[q] = e >= E;
-  }
+  for (int q = 0; q < VPL; ++q) taken[q] = lane + 64 * q >= E;
   float my_v = -INFINITY;
   int my_id = 0x7fffffff;
   for (int j = 0; j < k; ++j) {
@@ -126,9 +119,189 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* logits, 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
   if (lane < k) {
-    idx[(int64_t)t * k + lane] = my_id;
-    w[(int64_t)t * k + lane] = z / sum;
+    idx_t[lane] = my_id;
+    w_t[lane] = z / sum;
   }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* logits, int T, int E, int k,
+                                                           int32_t* idx, float* w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  float v[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) {
+    int e = lane + 64 * q;
+    v[q] = e < E ? row[e] : -INFINITY;
+  }
+  topk_softmax_wave<VPL>(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
+}
+
+// ---------------------------------------------------------------- few tokens
+// The router for a few tokens, split over K: workgroup s computes the partial
+// logits of every token over rows [s*64, s*64 + 64) of d into part[s][t][e];
+// then one workgroup per token adds the d/64 partials in split order, adds
+// the bias, writes the logits and runs the top-k and softmax.  With a few
+// tokens the MFMA router's two column tiles each walk all of d on one CU;
+// here d/64 workgroups share the router weights.  (The sums run in another
+// order than the MFMA router's, so the logits may differ from it in the last
+// bits.)
+//
+// In a workgroup, G = 256 / (columns per pass) row groups split the 64 rows:
+// thread (g, e) loads its 64/G weights of column e before using any, then
+// the G group sums are added in group order through LDS.
+template <typename ELT, int G>
+__global__ __launch_bounds__(256) void small_router_part_kernel(const ELT* x, const ELT* wr, int T,
+                                                                int d, int E, float* part) {
+  constexpr int KC = SMALL_ROUTE_KC, RPG = KC / G, EW = 256 / G, MT = SMALL_ROUTE_MAX_T;
+  __shared__ float sx[MT * KC];
+  __shared__ float red[G > 1 ? G * MT * EW : 1];
+  const int s = blockIdx.x, k0 = s * KC;
+  const int g = threadIdx.x / EW, el = threadIdx.x % EW, r0 = g * RPG;
+  // weight loads unconditional (a clamped column past E, its sums never
+  // stored), all RPG in flight together; the first pass's go out before x
+  // is staged
+  float wv[RPG];
+  {
+    const ELT* wc = wr + (int64_t)(k0 + r0) * E + min(el, E - 1);
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) wv[r] = Elt<ELT>::load(wc + (int64_t)r * E);
+  }
+  for (int i = threadIdx.x; i < T * KC; i += 256)
+    sx[i] = Elt<ELT>::load(x + (int64_t)(i / KC) * d + k0 + i % KC);
+  __syncthreads();
+  for (int e0 = 0; e0 < E; e0 += EW) {
+    const int e = e0 + el;
+    if (e0 > 0) {
+      const ELT* wc = wr + (int64_t)(k0 + r0) * E + min(e, E - 1);
+#pragma unroll
+      for (int r = 0; r < RPG; ++r) wv[r] = Elt<ELT>::load(wc + (int64_t)r * E);
+    }
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      acc[t] = 0.f;
+      if (t < T)
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) acc[t] = fmaf(sx[t * KC + r0 + r], wv[r], acc[t]);
+    }
+    if constexpr (G == 1) {
+      if (e < E)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          if (t < T) part[((int64_t)s * T + t) * E + e] = acc[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if (t < T) red[(g * MT + t) * EW + el] = acc[t];
+      __syncthreads();
+      for (int i = threadIdx.x; i < T * EW; i += 256) {
+        const int t = i / EW, ec = i % EW;
+        if (e0 + ec >= E) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) v += red[(gg * MT + t) * EW + ec];
+        part[((int64_t)s * T + t) * E + e0 + ec] = v;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// One workgroup per token: the logits (partials added in split order, then
+// the bias), then the top k by rank -- value e's slot is the number of
+// values that come before it (a larger logit, or an equal one with a lower
+// id), so slots run in the order of the wavefront top-k above with no chain
+// of cross-lane steps -- and the softmax over the k slots in slot order.
+__global__ __launch_bounds__(256) void small_router_final_kernel(const float* part, int nsplit,
+                                                                 const float* bias, int T, int E,
+                                                                 int k, float* logits, int32_t* idx,
+                                                                 float* w) {
+  constexpr int SB = 32;  // split partials in flight per thread
+  __shared__ __align__(16) float sl[512];
+  __shared__ float sv[512];
+  __shared__ int sid[512];
+  const int t = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float a = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += SB) {
+      // unconditional loads (a clamped split past the last, never added)
+      float pv[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) pv[j] = part[((int64_t)min(s0 + j, nsplit - 1) * T + t) * E + e];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (s0 + j < nsplit) a += pv[j];
+    }
+    if (bias) a += bias[e];
+    logits[(int64_t)t * E + e] = a;
+    sl[e] = a;
+  }
+  const int E4 = (E + 3) & ~3;  // the row padded to whole float4s with -inf
+  if (threadIdx.x < E4 - E) sl[E + threadIdx.x] = -INFINITY;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const float v = sl[e];
+    int rank = 0;
+#pragma unroll 8
+    for (int o = 0; o < E4; o += 4) {
+      const float4 u = *reinterpret_cast<const float4*>(sl + o);
+      rank += (u.x > v || (u.x == v && o < e)) + (u.y > v || (u.y == v && o + 1 < e)) +
+              (u.z > v || (u.z == v && o + 2 < e)) + (u.w > v || (u.w == v && o + 3 < e));
+    }
+    if (rank < k) {
+      sv[rank] = v;
+      sid[rank] = e;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float vmax = sv[0];
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(sv[j] - vmax);
+    for (int j = 0; j < k; ++j) {
+      idx[(int64_t)t * k + j] = sid[j];
+      w[(int64_t)t * k + j] = expf(sv[j] - vmax) / sum;
+    }
+  }
+}
+
+int64_t small_router_ws_bytes(int T, int d, int E) {
+  return round_up((int64_t)(d / SMALL_ROUTE_KC) * T * E * 4, 256);
+}
+
+moe_status_t launch_small_router(const void* x, const void* wr, const float* bias, int T, int d,
+                                 int E, int k, int elt_bytes, float* logits, int32_t* idx,
+                                 float* w, float* part, hipStream_t s) {
+  const int nsplit = d / SMALL_ROUTE_KC;
+  {
+    ProfScope prof("small_route_part", s);
+    // row groups: as many as leave one pass of at least E columns
+    const int G = E <= 8 ? 32 : E <= 16 ? 16 : E <= 32 ? 8 : E <= 64 ? 4 : E <= 128 ? 2 : 1;
+#define L_(E_, G_)                                                                 \
+  small_router_part_kernel<E_, G_><<<nsplit, 256, 0, s>>>(static_cast<const E_*>(x), \
+                                                          static_cast<const E_*>(wr), T, d, E, part)
+#define LG_(E_)                  \
+  switch (G) {                   \
+    case 32: L_(E_, 32); break;  \
+    case 16: L_(E_, 16); break;  \
+    case 8: L_(E_, 8); break;    \
+    case 4: L_(E_, 4); break;    \
+    case 2: L_(E_, 2); break;    \
+    default: L_(E_, 1); break;   \
+  }
+    if (elt_bytes == 2) { LG_(bf16_t) } else { LG_(float) }
+#undef LG_
+#undef L_
+    const moe_status_t st = check_launch("small_router_part_kernel");
+    if (st != MOE_OK) return st;
+  }
+  ProfScope prof("small_route_topk", s);
+  small_router_final_kernel<<<T, 256, 0, s>>>(part, nsplit, bias, T, E, k, logits, idx, w);
+  return check_launch("small_router_final_kernel");
 }
 
 moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,

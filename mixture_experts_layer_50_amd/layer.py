@@ -110,16 +110,39 @@ def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_u
     B.moe_combine(shape, t["yp"], t["inv"], t["topk_w"], t["y"], stream)
 
 
+def small_path_fits(shape: B.MoEShape, training: bool) -> bool:
+    """The size rule for the small-batch forward: inference only (it keeps no
+    activations for a backward), no row capacity, and at most half as many
+    routed (token, slot) pairs as local experts -- below that the sort, the
+    tile tables and the grouped GEMMs' padded tiles cost more than the
+    matrix-vector kernels (measured at the Qwen3-30B-A3B shape, E_loc = 128
+    and k = 8: about 2.3x faster at T = 1, even at T = 8, slower from T = 16)."""
+    return (not training and shape.rows_cap == shape.T * shape.k
+            and 2 * shape.T * shape.k <= shape.E_loc
+            and shape.T * shape.k <= B.SMALL_MAX_PAIRS
+            and shape.d <= B.SMALL_MAX_WIDTH and shape.I <= B.SMALL_MAX_WIDTH)
+
+
 def forward_small(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up, w_down,
                   stream=None):
-    """route -> small-batch FFN with the combine (no sort; for a few tokens);
-    y lands in buf['y']."""
+    """route -> small-batch FFN with the combine, in one call (no sort; for a
+    few tokens); y lands in buf['y']."""
     t = buf.t
-    if t.get("ws_small_fwd") is None:
-        t["ws_small_fwd"] = buf._ws("small_fwd")
-    B.moe_route(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], stream)
-    B.moe_ffn_small_fwd(shape, x, t["topk_idx"], t["topk_w"], w_gate, w_up, w_down, t["y"],
-                        t["ws_small_fwd"], stream)
+    if t.get("ws_small_routed_fwd") is None:
+        t["ws_small_routed_fwd"] = buf._ws("small_routed_fwd")
+    B.moe_small_fwd(shape, x, w_router, bias, t["logits"], t["topk_idx"], t["topk_w"], w_gate,
+                    w_up, w_down, t["y"], t["ws_small_routed_fwd"], stream)
+
+
+def forward_inference(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_up,
+                      w_down, stream=None):
+    """Inference forward by the size rule: the small-batch call for a few
+    tokens, else the grouped path (the balancing loss is a training term and
+    is not computed on the small path)."""
+    if small_path_fits(shape, buf.training) and buf.aux_alpha is None:
+        forward_small(shape, buf, x, w_router, bias, w_gate, w_up, w_down, stream)
+    else:
+        forward(shape, buf, x, w_router, bias, w_gate, w_up, w_down, stream)
 
 
 def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up, w_down,

@@ -190,20 +190,22 @@ def test_small_batch_ffn_validation(lib):
     s = shape(T=64, d=128, E=8, k=2, I=256)
     n = B.workspace_size(s, "small_fwd")
     # fp32 [Hg | Hu] partials (one K range at d = 128), the slot outputs
-    # [T*k, d] in bf16, the slot map [T*k] int32
-    assert n == 128 * 2 * 256 * 4 + 128 * 128 * 2 + 512
-    # at T = 1 of the Qwen3 shape (96 column blocks) d splits in 4 ranges
+    # [T*k, d] in bf16, the combine's arrival counters [T][d / 64] int32
+    assert n == 128 * 2 * 256 * 4 + 128 * 128 * 2 + 64 * 2 * 4
+    # at T = 1 of the Qwen3 shape (8 active experts x 12 column blocks) d
+    # splits in 8 ranges
     n1 = B.workspace_size(shape(T=1, d=2048, E=128, k=8, I=768), "small_fwd")
-    assert n1 == 8 * 4 * 2 * 768 * 4 + 8 * 2048 * 2 + 256
+    assert n1 == 8 * 8 * 2 * 768 * 4 + 8 * 2048 * 2 + 256  # counters: 32 int32, padded
 
     def call(sh, ws_bytes=1 << 30, y=P):
         return B.STATUS[lib.moe_ffn_small_fwd(ctypes.byref(sh), P, P, P, P, P, P, y, P, ws_bytes,
                                                None)], lib.moe_last_error().decode()
 
     assert call(s, y=None) == ("MOE_ERR_ARG", "moe_ffn_small_fwd: y is NULL")
-    st, msg = call(shape(T=40000, d=128, E=8, k=2, I=256))
+    st, msg = call(shape(T=2049, d=128, E=8, k=2, I=256))
     assert st == "MOE_ERR_UNSUPPORTED" and "T*k" in msg
-    st, msg = call(shape(T=4, d=16384, E=8, k=2, I=256))
+    assert call(shape(T=2048, d=128, E=8, k=2, I=256), ws_bytes=0)[0] == "MOE_ERR_WORKSPACE"
+    st, msg = call(shape(T=4, d=8256, E=8, k=2, I=256))
     assert st == "MOE_ERR_UNSUPPORTED" and "<=" in msg
     st, msg = call(shape(T=64, d=128, E=8, k=2, I=256, R_cap=100))
     assert st == "MOE_ERR_UNSUPPORTED" and "capacity" in msg
@@ -254,3 +256,53 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
                                                 FAKE, None, FAKE, FAKE, None)
     assert B.STATUS[st] == "MOE_ERR_UNSUPPORTED"
     assert "static scratch" in lib.moe_last_error().decode()
+
+
+def test_small_routed_fwd_validation(lib):
+    """moe_small_fwd: workspace = the few-token router's partial logits (softmax
+    gate, T <= 16) + the small-batch FFN's; the router's pointers are required
+    under the softmax gate only; the FFN's limits hold."""
+    P = FAKE
+    q1 = shape(T=1, d=2048, E=128, k=8, I=768)
+    n_ffn = B.workspace_size(q1, "small_fwd")
+    # d / 64 partial logit rows of [T][E] fp32
+    assert B.workspace_size(q1, "small_routed_fwd") == 32 * 1 * 128 * 4 + n_ffn
+    q17 = shape(T=17, d=2048, E=128, k=2, I=768)  # more tokens: the MFMA router, no partials
+    assert B.workspace_size(q17, "small_routed_fwd") == B.workspace_size(q17, "small_fwd")
+    qb = shape(T=4, d=2048, E=128, k=8, I=768, gate="balanced")
+    assert B.workspace_size(qb, "small_routed_fwd") == B.workspace_size(qb, "small_fwd")
+
+    def call(sh, wr=P, logits=P, y=P, ws_bytes=1 << 30):
+        st = lib.moe_small_fwd(ctypes.byref(sh), P, wr, None, logits, P, P, P, P, P, y, P,
+                               ws_bytes, None)
+        return B.STATUS[st], lib.moe_last_error().decode()
+
+    assert call(q1, wr=None) == ("MOE_ERR_ARG", "moe_small_fwd: w_router is NULL")
+    assert call(q1, logits=None) == ("MOE_ERR_ARG", "moe_small_fwd: logits is NULL")
+    assert call(q1, y=None) == ("MOE_ERR_ARG", "moe_small_fwd: y is NULL")
+    st, msg = call(shape(T=2049, d=128, E=8, k=2, I=256))
+    assert st == "MOE_ERR_UNSUPPORTED" and "T*k" in msg
+    st, msg = call(shape(T=64, d=128, E=8, k=2, I=256, R_cap=100))
+    assert st == "MOE_ERR_UNSUPPORTED" and "capacity" in msg
+    st, _ = call(q1, ws_bytes=B.workspace_size(q1, "small_routed_fwd") - 1)
+    assert st == "MOE_ERR_WORKSPACE"
+    # the balanced gate reads no router weights and writes no logits: its
+    # argument checks pass with them NULL and only the workspace is short
+    st, _ = call(qb, wr=None, logits=None, ws_bytes=0)
+    assert st == "MOE_ERR_WORKSPACE"
+
+
+def test_small_path_size_rule():
+    """The layer takes the small-batch forward for inference with at most
+    E_loc / 2 routed pairs and no row capacity, the grouped path otherwise."""
+    from mixture_experts_layer_50_amd.layer import small_path_fits
+    q = lambda T, **kw: B.MoEShape.make(T, 2048, 128, 8, 768, **kw)
+    assert small_path_fits(q(1), training=False)
+    assert small_path_fits(q(8), training=False)
+    assert not small_path_fits(q(9), training=False)
+    assert not small_path_fits(q(1), training=True)
+    assert not small_path_fits(q(8, R_cap=40), training=False)
+    assert small_path_fits(B.MoEShape.make(4, 2048, 128, 8, 768, e_lo=64, e_hi=128), False)
+    assert not small_path_fits(B.MoEShape.make(5, 2048, 128, 8, 768, e_lo=64, e_hi=128), False)
+    # wider than the small kernels take
+    assert not small_path_fits(B.MoEShape.make(1, 8256, 128, 8, 768), False)

@@ -41,8 +41,8 @@ SMALL = [
     # partial second wave
     MI.small_workload("tail_split_T3200_d64_E8_k8_I768", 3200, 64, 8, 8, 768, bias_sigma=1.0,
                       seed=43),
-    # 512 experts: the token masks of all blocks do not fit in LDS together,
-    # so the sort runs as three kernels (count, scan, scatter)
+    # 512 experts: the sort's per-block histograms at their largest (every
+    # scatter workgroup scans 512 experts' counts over all blocks)
     MI.small_workload("many_experts_T1500_d64_E512_k4_I64", 1500, 64, 512, 4, 64, bias_sigma=2.0,
                       seed=44),
 ]

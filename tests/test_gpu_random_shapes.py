@@ -11,6 +11,7 @@ import pytest
 
 import moe_inputs as MI
 import gpu_util as U
+from mixture_experts_layer_50_amd import binding as B
 from oracle import moe_oracle as O
 from test_gpu_small import run_small
 
@@ -71,6 +72,6 @@ def test_random_shape(case):
     if w.gate == "softmax_topk":  # with the router's balancing loss
         _, buf = U.run_layer(w, dev, R_cap=R_cap, aux_alpha=0.05)
         U.compare_aux(w, a, buf, f, bw, 0.05)
-    if not R_cap and w.T * w.k <= 65535:
+    if not R_cap and w.T * w.k <= B.SMALL_MAX_PAIRS and max(w.d, w.I) <= B.SMALL_MAX_WIDTH:
         _, sb = run_small(w, dev)
         U.check("y(small)", U.np64(sb["y"]), f["y"], U.TOL[w.dtype])
