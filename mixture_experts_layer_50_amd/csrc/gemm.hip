@@ -322,6 +322,126 @@ struct PickLoader<false, ROWS, TWO, NT, CPOL, GATHER, FULLK, SEL> {
   typedef LoaderKN<ROWS, TWO, NT, CPOL, GATHER, SEL> type;
 };
 
+// ---------------------------------------------------------------------------
+// Loaders that copy a K slice from memory straight into LDS (gfx950 16-byte
+// buffer loads with the LDS as destination: lane l of a load writes bytes
+// [16 l, 16 l + 16) from the load's LDS address on, and a lane past the
+// buffer's range writes zeros).  Load i of producer wave w fills the 64
+// consecutive physical chunks from 64 w + NT i on, so each lane loads the
+// logical chunk that the slice's layout puts at its physical slot (the
+// swizzles are XORs of the chunk index, their own inverses): the LDS layout
+// is the register-staged loaders' exactly.  K must be a multiple of 64 for
+// the k-contiguous form; the k-major form reads rows past the K range as
+// zeros through the buffer's range (or masked offsets when gathered).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int CPOL>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, CPOL);
+}
+
+template <int ROWS, int NT, int CPOL>
+struct DmaKC {
+  static constexpr int CH = ROWS * 8;
+  static constexpr int NR = CH / NT;
+  static constexpr int NLOAD = NR;  // loads per producer thread and slice
+  static_assert(CH % NT == 0, "whole loads per producer thread");
+  int voff[NR];
+  const bf16_t* p0;
+  int k_lo, k_hi;
+  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t*, int64_t ld, int row0,
+                                       int row_hi, int k_lo_, int k_hi_, int, int tid,
+                                       const int32_t*) {
+    p0 = s0 + (int64_t)row0 * ld;
+    k_lo = k_lo_;
+    k_hi = k_hi_;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + NT * i, row = q >> 3;
+      const int c = (q & 7) ^ (row & 7) ^ ((row >> 3) & 1);  // swz(row, .) inverted
+      voff[i] = row0 + row < row_hi ? (int)(((int64_t)row * ld + c * 8) * 2) : OOB;
+    }
+  }
+  // the slice starting at k_lo + kofs into `lds` (this operand's tile)
+  __device__ __forceinline__ void issue(bf16_t* lds, int kofs, int tid) const {
+    const int k0 = k_lo + kofs;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(p0, k_hi - k0 > 0 ? 0x7fffffff : 0);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) dma16<CPOL>(rs, lds + (64 * w + NT * i) * 8, voff[i], k0 * 2);
+  }
+};
+
+template <int COLS, int NT, int CPOL, bool GATHER>
+struct DmaKN {
+  static constexpr int CPR = COLS / 8;  // chunks per row
+  static constexpr int CH = BK * CPR;
+  static constexpr int NS = CH / NT;
+  static constexpr int RW = GATHER ? 64 / CPR : 1;  // rows per wave and load (GATHER)
+  static constexpr int NLOAD = NS;                   // loads per producer thread and slice
+  static_assert(CH % NT == 0 && (!GATHER || (64 % CPR == 0 && NT % 64 == 0)), "load shape");
+  int voff[NS];  // byte offset of the lane's chunk (OOB: masked column)
+  __amdgpu_buffer_rsrc_t rs0;  // GATHER
+  const bf16_t* p0;            // the source at (k_lo, col0)
+  int64_t ld;
+  int k_lo, k_hi;
+  const int32_t* rows;
+  int wrow;
+  int nxt[NS][RW];
+  __device__ __forceinline__ void prefetch(int kofs) {
+    const uint64_t a = (uint64_t)rows;
+    const int32_t* tab = (const int32_t*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                                          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int j = 0; j < RW; ++j)
+        nxt[i][j] = ld_table(tab, min(k_lo + kofs + wrow + i * (NT / CPR) + j, k_hi - 1));
+  }
+  __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t*, int64_t ld_, int col0,
+                                       int col_hi, int k_lo_, int k_hi_, int, int tid,
+                                       const int32_t* rows_) {
+    ld = ld_;
+    k_lo = k_lo_;
+    k_hi = k_hi_;
+    p0 = s0 + (int64_t)k_lo * ld + col0;
+    rs0 = make_rsrc(s0 + col0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int q = tid + NT * i, k = q / CPR;
+      const int col = ((q % CPR) ^ (((k & 3) << 2) & (CPR - 1))) * 8;  // kn_swz(k, .) inverted
+      voff[i] = col0 + col < col_hi ? (int)(((GATHER ? 0 : (int64_t)k * ld) + col) * 2) : OOB;
+    }
+    if constexpr (GATHER) {
+      rows = rows_;
+      wrow = __builtin_amdgcn_readfirstlane((tid >> 6) * (64 / CPR));
+      if (k_hi > k_lo) prefetch(0);
+    }
+  }
+  __device__ __forceinline__ void issue(bf16_t* lds, int kofs, int tid) {
+    const int lim = k_hi - k_lo - kofs;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if constexpr (GATHER) {
+      const int sub = (tid & 63) / CPR;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        int r = nxt[i][0];
+#pragma unroll
+        for (int j = 1; j < RW; ++j) r = sub == j ? nxt[i][j] : r;
+        const bool ok = (tid + NT * i) / CPR < lim && voff[i] != OOB;
+        dma16<CPOL>(rs0, lds + (64 * w + NT * i) * 8, ok ? (int)(r * ld * 2) + voff[i] : OOB, 0);
+      }
+      if (kofs + BK < k_hi - k_lo) prefetch(kofs + BK);
+    } else {
+      const int nrec = lim <= 0 ? 0 : lim >= BK ? 0x7fffffff : (int)((int64_t)lim * ld * 2);
+      const __amdgpu_buffer_rsrc_t r0 = make_rsrc_n(p0 + (int64_t)kofs * ld, nrec);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) dma16<CPOL>(r0, lds + (64 * w + NT * i) * 8, voff[i], 0);
+    }
+  }
+};
+
 // MFMA operand fragment (32 rows x 16 k): lane l holds row base + (l & 31),
 // k = 16 ks + 8 (l >> 5) + 0..7.
 __device__ __forceinline__ bf16x8 frag_kc(const bf16_t* lds, int base, int ks, int lane) {
@@ -457,6 +577,17 @@ struct Loaders {
   // next to a gathered A operand, B keeps per-load selects (measured faster)
   typedef typename PickLoader<AM == A_KC, BM, false, NT, 0, AG, FK, AG>::type LA;
   typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL, false, FK, AG>::type LB;
+};
+
+// The copy-to-LDS loaders of a GEMM (one B source; cache policies as above).
+template <int BM, int BN, int NT, int AM, int BMD, int GMD, bool AG>
+struct DmaLoaders {
+  static constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
+  template <bool KC, int N_, int CP, bool G_> struct Pick { typedef DmaKN<N_, NT, CP, G_> type; };
+  template <int N_, int CP, bool G_> struct Pick<true, N_, CP, G_> { typedef DmaKC<N_, NT, CP> type; };
+  typedef typename Pick<AM == A_KC, BM, 0, AG>::type LA;
+  typedef typename Pick<BMD == B_KC, BN, BPOL, false>::type LB;
+  static constexpr int LOADS = LA::NLOAD + LB::NLOAD;  // per producer thread and slice
 };
 
 template <int GMD, int B2, typename LA, typename LB>
@@ -1574,6 +1705,206 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
 }
 
 // ---------------------------------------------------------------------------
+// Warp-specialised persistent bf16 GEMM whose producer waves copy the K
+// slices straight into LDS (DmaKC / DmaKN) instead of through registers.
+// Three slice buffers: at step g the compute waves multiply slice g (buffer
+// g mod 3) while the producers send slice g + 2 into the buffer slice g - 1
+// has left and then wait for slice g + 1 alone (a vmcnt of one slice's loads:
+// loads retire in order), so every slice has two steps to arrive where the
+// register-staged form gives it one.  The three buffers take 144 KB of the
+// LDS, so the compute waves stage their results 16 rows at a time.  Tile
+// order, cursors and the plain-store epilogue's output are those of
+// gemm_bf16_ws_kernel; the LDS tiles and the MFMAs are the same, so the
+// results are bit-identical.
+// ---------------------------------------------------------------------------
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int BM, int BN, int WGM, int WGN, int NPW, int AM, int BMD, int GMD, int ROLE>
+__global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(GemmParams p) {
+  constexpr int NB = 3;
+  constexpr int NC = WGM * WGN;       // compute waves
+  constexpr int NTP = 64 * NPW;       // producer threads
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int BUF = (BM + BN) * BK;
+  constexpr int SCPR = WTN / 8;       // 16-byte chunks per staged row
+  static_assert(SCPR == 8 && WTM % 32 == 0, "wave blocks of 64 columns");
+  constexpr int SR = 16;              // staged rows per pass
+  constexpr int WST = SR * WTN;       // staging elements per compute wave
+  __shared__ __attribute__((aligned(16))) bf16_t smem[NB * BUF + NC * WST];
+  typedef DmaLoaders<BM, BN, NTP, AM, BMD, GMD, gathers_a(ROLE)> DL;
+  typedef typename DL::LA LA;
+  typedef typename DL::LB LB;
+  constexpr int L = DL::LOADS;
+  static_assert(L * (NB - 2) <= 63, "a slice's loads within the vmcnt range");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= NC;
+  const int wm = wave / WGN, wn = wave % WGN;  // compute waves only
+  const int ptid = tid - NC * 64;              // producer waves only
+
+  const int count = tile_count<GMD>(p);
+  const int xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD, S = gridDim.x / NXCD;
+  int x_lo, x_n;
+  xcd_tile_range<GMD>(p, count, xcd, x_lo, x_n);
+  if (slot >= x_n) return;
+  auto slices = [](const TileDesc& t) { return (t.k_hi - t.k_lo + BK - 1) / BK; };
+
+  // ---- producer state: loaders and load cursor
+  LA la;
+  LB lb;
+  int l_pos = slot, l_ks = 0, l_nk = 0;
+  auto load_seek = [&]() __attribute__((always_inline)) {
+    for (; l_pos < x_n; l_pos += S) {
+      const TileDesc t = tile_desc<BM, BN, GMD, B2_NONE>(p, x_lo + l_pos);
+      const int nk = slices(t);
+      if (nk > 0) {
+        l_nk = nk;
+        l_ks = 0;
+        init_loaders<GMD, B2_NONE>(p, t, la, lb, ptid);
+        break;
+      }
+    }
+  };
+  // The next slice into buffer `buf`.  Past the last slice the loaders'
+  // last state is sent again (a K offset past its range: zeros into a
+  // buffer nobody reads), so every step sends the same number of loads.
+  auto issue = [&](int buf) __attribute__((always_inline)) {
+    la.issue(smem + buf * BUF, l_ks * BK, ptid);
+    lb.issue(smem + buf * BUF + BM * BK, l_ks * BK, ptid);
+    if (l_pos < x_n && ++l_ks == l_nk) {
+      l_pos += S;
+      load_seek();
+    }
+  };
+
+  // ---- compute state
+  f32x16 acc[FM][FN];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  bf16_t* stage = smem + NB * BUF + (producer ? 0 : wave) * WST;
+  // The wave's WTM x 64 block, SR rows at a time: accumulators -> private
+  // LDS area (chunk c of row r at c ^ (r mod 8)) -> whole 16-byte chunks to
+  // memory with buffer stores (masked lanes get an out-of-range offset).
+  auto store_block = [&](const TileDesc& t) __attribute__((always_inline)) {
+    const int half = lane >> 5;
+    bf16_t* C0 = static_cast<bf16_t*>(p.C0);
+    bf16_t* C1 = static_cast<bf16_t*>(p.C1);
+    if (GMD == G_KROWS) {
+      C0 += (int64_t)t.e * p.c_estride;
+      if (C1) C1 += (int64_t)t.e * p.c_estride;
+    }
+    const int mb = t.m_lo + wm * WTM;
+    const int nb = t.n0 + wn * WTN;
+    const BlockOut bo(p, C0, C1, (int64_t)mb * p.ldc, nb, nb + WTN);
+#pragma unroll
+    for (int ps = 0; ps < WTM / SR; ++ps) {
+      constexpr int PPB = 32 / SR;  // passes per 32-row accumulator block
+      const int i = ps / PPB;
+      const int rs = (lane & 31) - (ps % PPB) * SR;  // the lane's row in this pass
+      if (rs >= 0 && rs < SR) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = j * 32 + 8 * q + 4 * half;
+            const int c = (n >> 3) ^ (rs & 7);
+            *reinterpret_cast<uint2*>(stage + rs * WTN + c * 8 + (n & 7)) =
+                make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                           pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          }
+      }
+      // the wave's own LDS writes and reads execute in order; keep the
+      // compiler from moving reads above writes (or the next pass's writes
+      // above this pass's reads)
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      constexpr int NQ = SR * SCPR / 64;  // chunks per lane and pass
+      uint4 v[NQ];
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) {
+        const int q = h * 64 + lane, r = q / SCPR, c = q % SCPR;
+        v[h] = *reinterpret_cast<const uint4*>(stage + r * WTN + (c ^ (r & 7)) * 8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) {
+        const int q = h * 64 + lane, r = ps * SR + q / SCPR, c = q % SCPR;
+        const int n = nb + c * 8;
+        bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, v[h], r, n, mb + r < t.m_hi && n < p.N);
+      }
+    }
+  };
+
+  // ---- compute cursor (every wave keeps it; it decides when the loop ends)
+  int c_pos = slot, c_ks = 0, c_nk = 0;
+  TileDesc ct;
+  auto compute_seek = [&](auto Cc) __attribute__((always_inline)) {
+    for (; c_pos < x_n; c_pos += S) {
+      ct = tile_desc<BM, BN, GMD, B2_NONE>(p, x_lo + c_pos);
+      c_nk = slices(ct);
+      c_ks = 0;
+      if (c_nk > 0) break;
+      if constexpr (decltype(Cc)::value) store_block(ct);  // a tile without K slices is zero
+    }
+  };
+  auto advance = [&](auto Cc) __attribute__((always_inline)) -> bool {
+    if (++c_ks < c_nk) return true;
+    if constexpr (decltype(Cc)::value) {
+      store_block(ct);
+      zero_acc();
+    }
+    c_pos += S;
+    compute_seek(Cc);
+    return c_pos < x_n;
+  };
+
+  if (producer) {
+    load_seek();
+    compute_seek(std::false_type{});
+    if (c_pos >= x_n) return;  // every tile of this workgroup was empty
+    // slices 0 .. NB-2 go out; slice 0 lands before the first step
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) issue(b);
+    // The producers meet the compute waves' barriers with a bare s_barrier:
+    // their only writes are the copies into LDS, and the explicit vmcnt wait
+    // before it is what makes a slice visible (a workgroup fence would wait
+    // for every copy in flight, the next slice's too).
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(L * (NB - 2)));
+    __builtin_amdgcn_s_barrier();
+    // step g: slice g + NB - 1 into buffer (g - 1) mod NB, then wait for
+    // slice g + 1 (the buffer index is a runtime value: one set of address
+    // registers for all buffers)
+    int fill = NB - 1;
+    do {
+      issue(fill);
+      fill = fill == NB - 1 ? 0 : fill + 1;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(L * (NB - 2)));  // slice g + 1 has landed
+      __builtin_amdgcn_s_barrier();
+    } while (advance(std::false_type{}));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy into LDS outlives the workgroup
+  } else {
+    zero_acc();
+    compute_seek(std::true_type{});
+    if (c_pos >= x_n) return;
+    __syncthreads();
+    int use = 0;  // buffer of slice g
+    do {
+      mma_slice<BM, BN, WGM, WGN, AM, BMD, B2_NONE, true, GMD == G_MROWS>(acc, smem + use * BUF, wm,
+                                                                         wn, lane, ct.m_hi - ct.m_lo);
+      use = use == NB - 1 ? 0 : use + 1;
+      __syncthreads();
+    } while (advance(std::true_type{}));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: one output (or one gate/up pair) per thread, fp32 FMA.
 // ---------------------------------------------------------------------------
 template <int AM, int BMD, int GMD, int B2, int EPI, int ROLE>
@@ -1854,6 +2185,12 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 #ifndef MOE_PERSIST_ROLES
 #define MOE_PERSIST_ROLES 0
 #endif
+// Warp-specialised roles whose producers copy K slices straight into LDS
+// (build-time tunable; the fused combine keeps the register-staged form).
+#ifndef MOE_DMA_ROLES
+#define MOE_DMA_ROLES \
+  ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD) | (1 << R_GATEUP_WGRAD_GATHER))
+#endif
 // Register stages of the warp-specialised kernel's producer waves; its
 // compute waves each own a 64 x 64 block of the tile.
 #ifndef MOE_WS_STAGES
@@ -1889,7 +2226,18 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   // 256x256 tiles: MOE_WIDE_WAVES = 8 runs two waves per SIMD (2 x 4 grid)
   constexpr int WGN = (BMt == 256 && BNt == 256 && MOE_WIDE_WAVES == 8) ? 4 : 2;
   constexpr int NT = 64 * 2 * WGN;
-  if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && (EPI != EPI_STORE || B2 != B2_NHALF)) {
+  if constexpr (((MOE_DMA_ROLES >> ROLE) & 1) && EPI == EPI_STORE && B2 == B2_NONE &&
+                ROLE != R_DOWN_FWD_COMBINE) {
+    constexpr int CWM = BMt / 64, CWN = BNt / 64;
+    constexpr int WS_NT = 64 * (CWM * CWN + MOE_WS_PRODUCER_WAVES);
+    const auto kern =
+        gemm_bf16_dma_kernel<BMt, BNt, CWM, CWN, MOE_WS_PRODUCER_WAVES, AM, BMD, GMD, ROLE>;
+    static int occupancy = 0;
+    if (occupancy <= 0 &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, kern, WS_NT, 0) != hipSuccess)
+      occupancy = 1;
+    kern<<<persistent_grid(occupancy, grid), WS_NT, 0, s>>>(p);
+  } else if constexpr (((MOE_WS_ROLES >> ROLE) & 1) && (EPI != EPI_STORE || B2 != B2_NHALF)) {
     // compute waves with MOE_WS_WAVE_ROWS x 64 blocks (64 x 64 for the fused
     // combine, whose counters go one row per lane), and the producer waves
     constexpr int WROWS = ROLE == R_DOWN_FWD_COMBINE ? 64 : MOE_WS_WAVE_ROWS;
