@@ -1719,9 +1719,9 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
 // ---------------------------------------------------------------------------
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int BM, int BN, int WGM, int WGN, int NPW, int AM, int BMD, int GMD, int ROLE>
+template <int BM, int BN, int WGM, int WGN, int NPW, int NB, int AM, int BMD, int GMD, int ROLE>
 __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(GemmParams p) {
-  constexpr int NB = 3;
+  static_assert(NB == 2 || NB == 3, "two or three slice buffers");
   constexpr int NC = WGM * WGN;       // compute waves
   constexpr int NTP = 64 * NPW;       // producer threads
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -1729,6 +1729,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
   constexpr int BUF = (BM + BN) * BK;
   constexpr int SCPR = WTN / 8;       // 16-byte chunks per staged row
   static_assert(SCPR == 8 && WTM % 32 == 0, "wave blocks of 64 columns");
+  static_assert(NB * BUF * 2 + NC * 16 * WTN * 2 <= 160 * 1024, "LDS");
   constexpr int SR = 16;              // staged rows per pass
   constexpr int WST = SR * WTN;       // staging elements per compute wave
   __shared__ __attribute__((aligned(16))) bf16_t smem[NB * BUF + NC * WST];
@@ -2187,6 +2188,9 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 #endif
 // Warp-specialised roles whose producers copy K slices straight into LDS
 // (build-time tunable; the fused combine keeps the register-staged form).
+#ifndef MOE_DMA_WAVE_ROWS
+#define MOE_DMA_WAVE_ROWS 64
+#endif
 #ifndef MOE_DMA_ROLES
 #define MOE_DMA_ROLES \
   ((1 << R_DOWN_FWD) | (1 << R_DOWN_WGRAD) | (1 << R_GATEUP_WGRAD) | (1 << R_GATEUP_WGRAD_GATHER))
@@ -2228,10 +2232,13 @@ static void launch_bf16(const GemmParams& p, int grid, hipStream_t s) {
   constexpr int NT = 64 * 2 * WGN;
   if constexpr (((MOE_DMA_ROLES >> ROLE) & 1) && EPI == EPI_STORE && B2 == B2_NONE &&
                 ROLE != R_DOWN_FWD_COMBINE) {
-    constexpr int CWM = BMt / 64, CWN = BNt / 64;
+    // compute waves with MOE_DMA_WAVE_ROWS x 64 blocks; three slice buffers
+    // while they fit in the LDS, else two
+    constexpr int CWM = BMt / MOE_DMA_WAVE_ROWS, CWN = BNt / 64;
+    constexpr int NBUF = 3 * (BMt + BNt) * BK * 2 + CWM * CWN * 16 * 64 * 2 <= 160 * 1024 ? 3 : 2;
     constexpr int WS_NT = 64 * (CWM * CWN + MOE_WS_PRODUCER_WAVES);
     const auto kern =
-        gemm_bf16_dma_kernel<BMt, BNt, CWM, CWN, MOE_WS_PRODUCER_WAVES, AM, BMD, GMD, ROLE>;
+        gemm_bf16_dma_kernel<BMt, BNt, CWM, CWN, MOE_WS_PRODUCER_WAVES, NBUF, AM, BMD, GMD, ROLE>;
     static int occupancy = 0;
     if (occupancy <= 0 &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, kern, WS_NT, 0) != hipSuccess)
