@@ -273,7 +273,10 @@ moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const in
  * in parallel workgroups, then one wavefront per token adds them in chunk
  * order, adds the bias and takes the top k with softmax, as moe_route does;
  * the sums run in another order than moe_route's, so logits may differ from
- * it in the last bits); for more tokens moe_route's kernels run.  Outputs
+ * it in the last bits); when T*E <= 1024 and T*E*d/64 <= 8192 (one or two
+ * tokens at E = 128, d = 2048) that last step runs inside the FFN's first
+ * kernel, each of its workgroups taking the same top k (one launch less);
+ * for more tokens moe_route's kernels run.  Outputs
  * logits (softmax gate), topk_idx, topk_w and y as moe_route and
  * moe_ffn_small_fwd would; the same arguments and limits.  ws:
  * moe_workspace_size(MOE_OP_SMALL_ROUTED_FWD). */

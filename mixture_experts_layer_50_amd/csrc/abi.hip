@@ -689,9 +689,19 @@ extern "C" moe_status_t moe_small_fwd(const moe_shape_t* shape, const void* x,
   if (D.balanced) {
     MOE_TRY(launch_balanced_gate(D.T, D.E, D.k, topk_idx, topk_w, s));
   } else if (small_router_used(D)) {
-    MOE_TRY(launch_small_router(x, w_router, bias, D.T, D.d, D.E, D.k, D.eb, logits, topk_idx,
-                                topk_w, reinterpret_cast<float*>(wsb), s));
+    float* rpart = reinterpret_cast<float*>(wsb);
+    const int nsplit = D.d / SMALL_ROUTE_KC;
     ffn_at = small_router_ws_bytes(D.T, D.d, D.E);
+    if ((int64_t)D.T * D.E <= SMALL_FUSED_ROUTE_MAX_TE &&
+        (int64_t)D.T * D.E * nsplit <= SMALL_FUSED_ROUTE_MAX) {
+      // the top-k runs inside the FFN's first kernel: one launch less
+      MOE_TRY(launch_small_router_part(x, w_router, D.T, D.d, D.E, D.eb, rpart, s));
+      const SmallRoute r{rpart, bias, nsplit, D.E, logits, topk_idx, topk_w};
+      return launch_small_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, D.T, D.d, D.k, D.I,
+                              D.e_lo, D.e_hi, D.eb, y, wsb + ffn_at, s, &r);
+    }
+    MOE_TRY(launch_small_router(x, w_router, bias, D.T, D.d, D.E, D.k, D.eb, logits, topk_idx,
+                                topk_w, rpart, s));
   } else {
     MOE_TRY(moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, stream));
   }

@@ -26,6 +26,10 @@ moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32
 constexpr int SMALL_ROUTE_MAX_T = 16;
 constexpr int SMALL_ROUTE_KC = 64;
 int64_t small_router_ws_bytes(int T, int d, int E);
+// The partial-logit kernel alone (the top-k then runs inside the small FFN's
+// first kernel, see SmallRoute).
+moe_status_t launch_small_router_part(const void* x, const void* wr, int T, int d, int E,
+                                      int elt_bytes, float* part, hipStream_t s);
 moe_status_t launch_small_router(const void* x, const void* wr, const float* bias, int T, int d,
                                  int E, int k, int elt_bytes, float* logits, int32_t* idx,
                                  float* w, float* part, hipStream_t s);
@@ -66,10 +70,26 @@ moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* i
 // SMALL_MAX_WIDTH (the LDS the kernels' routing table and token rows take).
 constexpr int64_t SMALL_MAX_PAIRS = 4096;
 constexpr int SMALL_MAX_WIDTH = 8192;
+// The gate folded into the small FFN's first kernel: every workgroup adds
+// the router's partial logits [nsplit][T][E] itself (in split order, then the
+// bias) and takes the top k by rank, as small_router_final_kernel does;
+// workgroup 0 writes logits, idx and w.  For T*E <= SMALL_FUSED_ROUTE_MAX_TE
+// and T*E*nsplit <= SMALL_FUSED_ROUTE_MAX (the partials one workgroup adds).
+struct SmallRoute {
+  const float* part;
+  const float* bias;
+  int nsplit, E;
+  float* logits;
+  int32_t* idx;
+  float* w;
+};
+constexpr int SMALL_FUSED_ROUTE_MAX_TE = 1024;
+constexpr int64_t SMALL_FUSED_ROUTE_MAX = 8192;
 int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int e_lo, int e_hi, int elt_bytes);
+// route: the gate folded in (idx and w_topk are then its outputs), or null.
 moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_topk,
                               const void* wg, const void* wu, const void* wd, int T, int d, int k,
                               int I, int e_lo, int e_hi, int elt_bytes, void* y, void* ws,
-                              hipStream_t s);
+                              hipStream_t s, const SmallRoute* route = nullptr);
 
 }  // namespace moe

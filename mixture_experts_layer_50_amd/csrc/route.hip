@@ -273,9 +273,8 @@ int64_t small_router_ws_bytes(int T, int d, int E) {
   return round_up((int64_t)(d / SMALL_ROUTE_KC) * T * E * 4, 256);
 }
 
-moe_status_t launch_small_router(const void* x, const void* wr, const float* bias, int T, int d,
-                                 int E, int k, int elt_bytes, float* logits, int32_t* idx,
-                                 float* w, float* part, hipStream_t s) {
+moe_status_t launch_small_router_part(const void* x, const void* wr, int T, int d, int E,
+                                      int elt_bytes, float* part, hipStream_t s) {
   const int nsplit = d / SMALL_ROUTE_KC;
   {
     ProfScope prof("small_route_part", s);
@@ -296,9 +295,16 @@ moe_status_t launch_small_router(const void* x, const void* wr, const float* bia
     if (elt_bytes == 2) { LG_(bf16_t) } else { LG_(float) }
 #undef LG_
 #undef L_
-    const moe_status_t st = check_launch("small_router_part_kernel");
-    if (st != MOE_OK) return st;
+    return check_launch("small_router_part_kernel");
   }
+}
+
+moe_status_t launch_small_router(const void* x, const void* wr, const float* bias, int T, int d,
+                                 int E, int k, int elt_bytes, float* logits, int32_t* idx,
+                                 float* w, float* part, hipStream_t s) {
+  const int nsplit = d / SMALL_ROUTE_KC;
+  const moe_status_t st = launch_small_router_part(x, wr, T, d, E, elt_bytes, part, s);
+  if (st != MOE_OK) return st;
   ProfScope prof("small_route_topk", s);
   small_router_final_kernel<<<T, 256, 0, s>>>(part, nsplit, bias, T, E, k, logits, idx, w);
   return check_launch("small_router_final_kernel");

@@ -215,16 +215,77 @@ __device__ int find_expert_pairs(PairTable& pt, const int32_t* idx, int npairs, 
   return total;
 }
 
-template <typename ELT, int TG>
+// The gate inside the workgroup (SmallRoute): logits of all T tokens from
+// the router's partials (split order, then the bias), the top k by rank
+// (a larger logit, or an equal one with a lower id, comes first) and the
+// softmax in slot order, the operations of small_router_final_kernel.  The
+// table lands in sidx [T*k]; `write`: also to the outputs.
+__device__ void route_in_block(const SmallRoute& r, int T, int k, float* sl, int32_t* sidx,
+                               float* sv, bool write) {
+  const int E = r.E, ns = r.nsplit, tid = threadIdx.x;
+  constexpr int SB = 32;  // partials in flight per item
+  for (int i = tid; i < T * E; i += 256) {
+    const int t = i / E, e = i % E;
+    float a = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+      float pv[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) pv[j] = r.part[((int64_t)min(s0 + j, ns - 1) * T + t) * E + e];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (s0 + j < ns) a += pv[j];
+    }
+    if (r.bias) a += r.bias[e];
+    sl[i] = a;
+    if (write) r.logits[i] = a;
+  }
+  __syncthreads();
+  for (int i = tid; i < T * E; i += 256) {
+    const int t = i / E, e = i % E;
+    const float v = sl[i];
+    const float* row = sl + t * E;
+    int rank = 0;
+#pragma unroll 8
+    for (int o = 0; o < E; ++o) rank += row[o] > v || (row[o] == v && o < e);
+    if (rank < k) {
+      sidx[t * k + rank] = e;
+      sv[t * k + rank] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    const int t = tid;
+    const float vmax = sv[t * k];
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += expf(sv[t * k + j] - vmax);
+    if (write)
+      for (int j = 0; j < k; ++j) {
+        r.idx[t * k + j] = sidx[t * k + j];
+        r.w[t * k + j] = expf(sv[t * k + j] - vmax) / sum;
+      }
+  }
+  __syncthreads();
+}
+
+template <typename ELT, int TG, bool ROUTE>
 __global__ __launch_bounds__(256) void small_gateup_kernel(const ELT* x, const int32_t* idx,
-                                                           const ELT* wg, const ELT* wu, int T,
-                                                           int d, int I, int k, int e_lo,
-                                                           int e_hi, float* part, int32_t* cnt,
-                                                           ELT* y) {
+                                                           SmallRoute route, const ELT* wg,
+                                                           const ELT* wu, int T, int d, int I,
+                                                           int k, int e_lo, int e_hi, float* part,
+                                                           int32_t* cnt, ELT* y) {
   constexpr int N = Vec16<ELT>::N, CB = 8 * N;
+  constexpr int RT = ROUTE ? SMALL_FUSED_ROUTE_MAX_TE : 1;
   __shared__ PairTable pt;
+  __shared__ float r_logit[RT], r_val[RT];
+  __shared__ int32_t r_idx[RT];
   const int npairs = T * k, ks = blockIdx.z, KS = gridDim.z;
-  const int n = find_expert_pairs(pt, idx, npairs, k, e_lo, e_hi, blockIdx.y);
+  const int32_t* table = idx;
+  if constexpr (ROUTE) {
+    route_in_block(route, T, k, r_logit, r_idx, r_val,
+                   blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0);
+    table = r_idx;
+  }
+  const int n = find_expert_pairs(pt, table, npairs, k, e_lo, e_hi, blockIdx.y);
   // the combine's counters, and y = 0 for tokens with no kept slot, strided
   // over the grid
   {
@@ -478,7 +539,7 @@ int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int e_lo, int e_hi, int e
 moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_topk,
                               const void* wg, const void* wu, const void* wd, int T, int d, int k,
                               int I, int e_lo, int e_hi, int elt_bytes, void* y, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, const SmallRoute* route) {
   const int64_t pairs = (int64_t)T * k, nexp = small_nexp(T, k, e_lo, e_hi);
   const int KS = small_ks(nexp, d, I, elt_bytes);
   char* base = static_cast<char*>(ws);
@@ -493,12 +554,17 @@ moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_
     const dim3 grid((unsigned)(I / CB), (unsigned)nexp, (unsigned)KS);
     const int TG = small_tg(pairs, nexp, 0);
     const size_t lds = (size_t)(4 * TG * 2 * CB) * 4;
-#define L_(E_, TG_)                                                                           \
-  small_gateup_kernel<E_, TG_><<<grid, 256, lds, s>>>(                                        \
-      static_cast<const E_*>(x), idx, static_cast<const E_*>(wg), static_cast<const E_*>(wu), \
-      T, d, I, k, e_lo, e_hi, part, cnt, static_cast<E_*>(y))
-    if (elt_bytes == 2) { if (TG == 4) L_(bf16_t, 4); else L_(bf16_t, 2); }
-    else { if (TG == 4) L_(float, 4); else L_(float, 2); }
+    const SmallRoute r = route ? *route : SmallRoute{nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr};
+#define L_(E_, TG_, R_)                                                                       \
+  small_gateup_kernel<E_, TG_, R_><<<grid, 256, lds, s>>>(                                    \
+      static_cast<const E_*>(x), idx, r, static_cast<const E_*>(wg),                          \
+      static_cast<const E_*>(wu), T, d, I, k, e_lo, e_hi, part, cnt, static_cast<E_*>(y))
+#define LR_(E_, TG_)        \
+  if (route) L_(E_, TG_, true); \
+  else L_(E_, TG_, false);
+    if (elt_bytes == 2) { if (TG == 4) { LR_(bf16_t, 4) } else { LR_(bf16_t, 2) } }
+    else { if (TG == 4) { LR_(float, 4) } else { LR_(float, 2) } }
+#undef LR_
 #undef L_
     if ((st = check_launch("small_gateup_kernel")) != MOE_OK) return st;
   }
