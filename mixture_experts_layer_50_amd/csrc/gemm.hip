@@ -579,17 +579,13 @@ struct Loaders {
   typedef typename PickLoader<BMD == B_KC, BN, B2 != B2_NONE, NT, BPOL, false, FK, AG>::type LB;
 };
 
-// The copy-to-LDS loaders of a GEMM (one B source; cache policies as above,
-// plus build-time bits for the activation operands).
-#ifndef MOE_DMA_ACT_CPOL
-#define MOE_DMA_ACT_CPOL 0
-#endif
+// The copy-to-LDS loaders of a GEMM (one B source; cache policies as above).
 template <int BM, int BN, int NT, int AM, int BMD, int GMD, bool AG>
 struct DmaLoaders {
-  static constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : MOE_DMA_ACT_CPOL;
+  static constexpr int BPOL = GMD == G_MROWS ? MOE_WEIGHT_CPOL : 0;
   template <bool KC, int N_, int CP, bool G_> struct Pick { typedef DmaKN<N_, NT, CP, G_> type; };
   template <int N_, int CP, bool G_> struct Pick<true, N_, CP, G_> { typedef DmaKC<N_, NT, CP> type; };
-  typedef typename Pick<AM == A_KC, BM, MOE_DMA_ACT_CPOL, AG>::type LA;
+  typedef typename Pick<AM == A_KC, BM, 0, AG>::type LA;
   typedef typename Pick<BMD == B_KC, BN, BPOL, false>::type LB;
   static constexpr int LOADS = LA::NLOAD + LB::NLOAD;  // per producer thread and slice
 };
