@@ -382,8 +382,8 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
             "note": "us per forward; *_us: HIP events around eager calls (host enqueue "
                     "included when it is the longer), *_graph_us: the same calls replayed "
                     "from a HIP graph (GPU time); the size rule takes the small call for "
-                    "2*T*k <= E_loc (T <= 8 here)"}
-        for Ts in (1, 8, 16, 64):
+                    "2*T*k < E_loc (T <= 7 here)"}
+        for Ts in (1, 2, 4, 8, 16, 64):
             shape_s = B.MoEShape.make(Ts, wn.d, wn.E, wn.k, wn.I, dtype="bf16",
                                       gate="softmax_topk")
             xs = dev["x"][:Ts].contiguous()

@@ -259,7 +259,7 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t
  * combine runs inside the second kernel (the workgroup that writes a token's
  * last pair row of a column block, by an integer arrival counter, sums the
  * token's pairs in ascending slot order: deterministic).  With no tile
- * padding and no sort it is the faster form while T*k is at most about
+ * padding and no sort it is the faster form while T*k is below about
  * E_loc / 2 (the layer's size rule).  Needs T*k <= 4096, d and I <= 8192 and no row
  * capacity (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
 moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const int32_t* topk_idx,

@@ -112,13 +112,14 @@ def forward(shape: B.MoEShape, buf: LayerBuffers, x, w_router, bias, w_gate, w_u
 
 def small_path_fits(shape: B.MoEShape, training: bool) -> bool:
     """The size rule for the small-batch forward: inference only (it keeps no
-    activations for a backward), no row capacity, and at most half as many
-    routed (token, slot) pairs as local experts -- below that the sort, the
-    tile tables and the grouped GEMMs' padded tiles cost more than the
+    activations for a backward), no row capacity, and fewer than half as
+    many routed (token, slot) pairs as local experts -- below that the sort,
+    the tile tables and the grouped GEMMs' padded tiles cost more than the
     matrix-vector kernels (measured at the Qwen3-30B-A3B shape, E_loc = 128
-    and k = 8: about 2.3x faster at T = 1, even at T = 8, slower from T = 16)."""
+    and k = 8: 41 vs 99 us at T = 1, 71 vs 103 at T = 4, 111 vs 107 at T = 8,
+    so T <= 7 there)."""
     return (not training and shape.rows_cap == shape.T * shape.k
-            and 2 * shape.T * shape.k <= shape.E_loc
+            and 2 * shape.T * shape.k < shape.E_loc
             and shape.T * shape.k <= B.SMALL_MAX_PAIRS
             and shape.d <= B.SMALL_MAX_WIDTH and shape.I <= B.SMALL_MAX_WIDTH)
 
