@@ -136,6 +136,13 @@ FEW = [
     # ... and A rows of width 2112 > 2048 in the down kernel (one token per pass)
     MI.small_workload("wide_I_T20_d256_E8_k2_I2112", 20, 256, 8, 2, 2112, bias_sigma=1.0,
                       seed=78),
+    # fp32 with E not a multiple of 4: the final top-k kernel pads its row
+    # (T*E = 1136 > 1024 keeps it out of the gate/up kernel), and the folded
+    # form with an odd E
+    MI.small_workload("few_f32_T16_d128_E71_k5_I64", 16, 128, 71, 5, 64, dtype="f32",
+                      bias_sigma=1.0, seed=79, x_sigma=0.5),
+    MI.small_workload("few_f32_T3_d192_E7_k3_I64", 3, 192, 7, 3, 64, dtype="f32",
+                      bias_sigma=1.0, seed=80, x_sigma=0.5),
 ]
 
 
