@@ -260,8 +260,9 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* yp, const int32_t
  * last pair row of a column block, by an integer arrival counter, sums the
  * token's pairs in ascending slot order: deterministic).  With no tile
  * padding and no sort it is the faster form while T*k is below about
- * E_loc / 2 (the layer's size rule).  Needs T*k <= 4096, d and I <= 8192 and no row
- * capacity (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward only. */
+ * E_loc / 2 (the layer's size rule).  Needs T*k <= 4096, d and I <= 8192
+ * and no row capacity (R_cap 0 or T*k); else MOE_ERR_UNSUPPORTED.  Forward
+ * only. */
 moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const int32_t* topk_idx,
                                const float* topk_w, const void* w_gate, const void* w_up,
                                const void* w_down, void* y, void* ws, size_t ws_bytes,
@@ -270,10 +271,11 @@ moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const in
 /* a1 + a3 + a4 + a5 for a few tokens, in one call: the gate, then
  * moe_ffn_small_fwd's FFN and combine.  Under the softmax top-k gate with
  * T <= 16 the router runs split over d (partial logits of 64-row chunks of d
- * in parallel workgroups, then one wavefront per token adds them in chunk
- * order, adds the bias and takes the top k with softmax, as moe_route does;
- * the sums run in another order than moe_route's, so logits may differ from
- * it in the last bits); when T*E <= 1024 and T*E*d/64 <= 8192 (one or two
+ * in parallel workgroups, then one workgroup per token adds them in chunk
+ * order, adds the bias, takes the top k by rank -- the same selection and
+ * tie rule as moe_route -- and the softmax over the k slots; the sums run in
+ * another order than moe_route's, so logits may differ from it in the last
+ * bits); when T*E <= 1024 and T*E*d/64 <= 8192 (one or two
  * tokens at E = 128, d = 2048) that last step runs inside the FFN's first
  * kernel, each of its workgroups taking the same top k (one launch less);
  * for more tokens moe_route's kernels run.  Outputs

@@ -21,8 +21,9 @@ moe_status_t launch_permute_gather(const void* x, const int32_t* inv, int T, int
 moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                  hipStream_t s);
 // The router for a few tokens (T <= SMALL_ROUTE_MAX_T): split over K in
-// chunks of SMALL_ROUTE_KC rows of d (d % 64 == 0), then a fixed-order sum,
-// the bias, top-k and softmax.  Workspace: the partial logits.
+// chunks of SMALL_ROUTE_KC rows of d (d % 64 == 0), then per token a
+// fixed-order sum, the bias, the top k by rank and the softmax.  Workspace:
+// the partial logits.
 constexpr int SMALL_ROUTE_MAX_T = 16;
 constexpr int SMALL_ROUTE_KC = 64;
 int64_t small_router_ws_bytes(int T, int d, int E);
