@@ -7,13 +7,16 @@
 // activations read transposed) are copied as is and read back with the gfx950
 // LDS transpose read.  Tiles are ordered so that consecutive tiles land on the
 // same XCD (its own L2) and tiles that share an A row block or a weight column
-// block run together (GROUP_M order).  Three kernel forms:
+// block run together (GROUP_M order).  Four kernel forms:
 //  * gemm_bf16_kernel: one workgroup per tile;
 //  * gemm_bf16_persistent_kernel: one workgroup per CU running a list of
 //    tiles with the K-slice pipeline running on across tile boundaries;
-//  * gemm_bf16_ws_kernel: persistent and warp-specialised (producer waves
-//    load, compute waves multiply and store), for plain-store epilogues with
-//    much output per unit of work (the weight gradients, the down projection).
+//  * gemm_bf16_dma_kernel: persistent and warp-specialised (producer waves
+//    copy K slices straight into LDS, compute waves multiply and store), for
+//    plain-store epilogues with much output per unit of work (the weight
+//    gradients, the down projection);
+//  * gemm_bf16_ws_kernel: the same with register-staged producers (the down
+//    projection with the combine fused into its epilogue).
 // The gather roles read the rows of their A operand through a table of row
 // numbers (the permuted rows Xp read from x: the dispatch copy folded into
 // the GEMM's operand loads, page "Accelerating Transformers fine-tuning with

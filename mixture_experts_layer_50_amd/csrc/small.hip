@@ -18,7 +18,9 @@
 // the block's columns and one of KS ranges of d (KS > 1 only when there are
 // too few active experts to fill the GPU), into part[pair][ks].  It also
 // zeroes the combine's counters and the output rows of tokens with no kept
-// slot (strided over the whole grid).
+// slot (strided over the whole grid).  For one or two tokens it can also take
+// the gate's last step (SmallRoute): every workgroup adds the router's
+// partial logits and takes the top k itself before it builds its table.
 // Kernel 2, one workgroup per (column block of d, active expert): adds the KS
 // partials in order, A = silu(Hg) Hu (rounded to the dtype), then
 // Yp[pair] = A Wd[e] over the block's columns.  The combine runs inside
@@ -27,10 +29,13 @@
 // increment after the block's stores are complete) sums the token's pairs in
 // ascending slot order from the stored rows, the operations and order of the
 // combine kernel.
-// Inside a workgroup, lane (rs, c) of wave w accumulates the rows
-// r = 8w + rs (mod 32) for its 16-byte column chunk c; a column's 32 partial
-// sums are added by a butterfly over rs within the wave, then over the four
-// waves in order: results are deterministic.
+// Inside a workgroup, in each batch of 32 U rows lane (rs, c) of wave w
+// accumulates the U consecutive rows from (8w + rs) U on for its 16-byte
+// column chunk c (its factors then come in one vector load); a column's 32
+// partial sums are added by a butterfly over rs within the wave, then over
+// the four waves in order: results are deterministic.  Every load of a batch
+// is unconditional (clamped addresses, zero factors past the end), so that
+// all of them are in flight together.
 #include "kernels.h"
 
 namespace moe {
