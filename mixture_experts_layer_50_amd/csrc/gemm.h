@@ -49,6 +49,8 @@ struct GemmParams {
   const int32_t* off;  // group offsets [groups+1] (G_MROWS, G_KROWS); NULL in G_KROWS: see k_chunk
   int k_chunk;         // G_KROWS without offsets: group g sums K rows [g*k_chunk, (g+1)*k_chunk)
                        // (a split of K into partial results); 0 = one group [0, K)
+  int k_strip;         // G_KROWS with offsets: experts with at most k_strip rows are left to
+                       // the strip kernel (the tile kernels neither read nor write them); 0 = none
   const int32_t* tiles;// G_MROWS tile table: tiles[0] = count, then (expert, first row) pairs
   const int32_t* kcost;// G_KROWS (optional): prefix sums [groups+1] of the per-expert tile cost
                        // (K slices + a fixed part), for balancing the persistent kernels
@@ -139,5 +141,13 @@ moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles25
                                 int rows_cap = 0, const CombinePrep* cmb = nullptr);
 // Per-tile cost of a weight-gradient tile beyond its K slices (its epilogue).
 constexpr int KCOST_FIXED = 2;
+// Experts with at most STRIP_K rows run their weight gradients in the strip
+// kernel (gemm.hip), whose workgroups hold all of an expert's K rows; their
+// K-cost entries are zero, so the tile kernels' balancing leaves them out.
+// Build-time tunable: 0 turns the strip kernel off.
+#ifndef MOE_STRIP_K
+#define MOE_STRIP_K 256
+#endif
+constexpr int STRIP_K = MOE_STRIP_K;
 
 }  // namespace moe

@@ -511,7 +511,14 @@ __device__ __forceinline__ TileDesc tile_desc(const GemmParams& p, int L) {
   } else {
     t.m_lo = mt * BM;
     t.m_hi = min(t.m_lo + BM, p.M);
-    if (GMD == G_KROWS && p.off) { t.k_lo = ld_table(p.off, t.e); t.k_hi = ld_table(p.off, t.e + 1); }
+    if (GMD == G_KROWS && p.off) {
+      t.k_lo = ld_table(p.off, t.e);
+      t.k_hi = ld_table(p.off, t.e + 1);
+      if (p.k_strip > 0 && t.k_hi - t.k_lo <= p.k_strip) {  // the strip kernel's expert
+        t.k_hi = t.k_lo;
+        t.m_hi = t.m_lo;
+      }
+    }
     else if (GMD == G_KROWS && p.k_chunk > 0) {
       t.k_lo = min(p.K, t.e * p.k_chunk);
       t.k_hi = min(p.K, t.k_lo + p.k_chunk);
@@ -1707,6 +1714,60 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_ws_kernel(Ge
   }
 }
 
+// Plain-store epilogue of one wave's (32 FM) x 64 block: rows [mb, mb + 32 FM)
+// (rows from m_hi on are dropped), columns [nb, nb + 64) (columns from N on
+// are dropped), through the wave's own 16 x 64 LDS area `stage`, 16 rows at a
+// time: accumulators -> stage (chunk c of row r at c ^ (r mod 8)) -> whole
+// 16-byte chunks to memory with buffer stores (a masked lane gets an
+// out-of-range offset).  The area is the wave's alone: no workgroup barrier.
+template <int FM, int FN, int CPOL>
+__device__ __forceinline__ void store_wave_block(const GemmParams& p, f32x16 (&acc)[FM][FN],
+                                                 bf16_t* stage, bf16_t* C0, bf16_t* C1, int mb,
+                                                 int m_hi, int nb, int lane) {
+  constexpr int WTM = 32 * FM, WTN = 32 * FN;
+  constexpr int SR = 16;         // staged rows per pass
+  constexpr int SCPR = WTN / 8;  // 16-byte chunks per staged row
+  static_assert(SCPR == 8, "64-column blocks");
+  const int half = lane >> 5;
+  const BlockOut bo(p, C0, C1, (int64_t)mb * p.ldc, nb, nb + WTN);
+#pragma unroll
+  for (int ps = 0; ps < WTM / SR; ++ps) {
+    constexpr int PPB = 32 / SR;  // passes per 32-row accumulator block
+    const int i = ps / PPB;
+    const int rs = (lane & 31) - (ps % PPB) * SR;  // the lane's row in this pass
+    if (rs >= 0 && rs < SR) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = j * 32 + 8 * q + 4 * half;
+          const int c = (n >> 3) ^ (rs & 7);
+          *reinterpret_cast<uint2*>(stage + rs * WTN + c * 8 + (n & 7)) =
+              make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+        }
+    }
+    // the wave's own LDS writes and reads execute in order; keep the
+    // compiler from moving reads above writes (or the next pass's writes
+    // above this pass's reads)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int NQ = SR * SCPR / 64;  // chunks per lane and pass
+    uint4 v[NQ];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      const int q = h * 64 + lane, r = q / SCPR, c = q % SCPR;
+      v[h] = *reinterpret_cast<const uint4*>(stage + r * WTN + (c ^ (r & 7)) * 8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      const int q = h * 64 + lane, r = ps * SR + q / SCPR, c = q % SCPR;
+      const int n = nb + c * 8;
+      bo.store<CPOL>(p, v[h], r, n, mb + r < m_hi && n < p.N);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Warp-specialised persistent bf16 GEMM whose producer waves copy the K
 // slices straight into LDS (DmaKC / DmaKN) instead of through registers.
@@ -1794,56 +1855,16 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   };
   bf16_t* stage = smem + NB * BUF + (producer ? 0 : wave) * WST;
-  // The wave's WTM x 64 block, SR rows at a time: accumulators -> private
-  // LDS area (chunk c of row r at c ^ (r mod 8)) -> whole 16-byte chunks to
-  // memory with buffer stores (masked lanes get an out-of-range offset).
   auto store_block = [&](const TileDesc& t) __attribute__((always_inline)) {
-    const int half = lane >> 5;
     bf16_t* C0 = static_cast<bf16_t*>(p.C0);
     bf16_t* C1 = static_cast<bf16_t*>(p.C1);
     if (GMD == G_KROWS) {
       C0 += (int64_t)t.e * p.c_estride;
       if (C1) C1 += (int64_t)t.e * p.c_estride;
     }
-    const int mb = t.m_lo + wm * WTM;
-    const int nb = t.n0 + wn * WTN;
-    const BlockOut bo(p, C0, C1, (int64_t)mb * p.ldc, nb, nb + WTN);
-#pragma unroll
-    for (int ps = 0; ps < WTM / SR; ++ps) {
-      constexpr int PPB = 32 / SR;  // passes per 32-row accumulator block
-      const int i = ps / PPB;
-      const int rs = (lane & 31) - (ps % PPB) * SR;  // the lane's row in this pass
-      if (rs >= 0 && rs < SR) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = j * 32 + 8 * q + 4 * half;
-            const int c = (n >> 3) ^ (rs & 7);
-            *reinterpret_cast<uint2*>(stage + rs * WTN + c * 8 + (n & 7)) =
-                make_uint2(pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                           pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-          }
-      }
-      // the wave's own LDS writes and reads execute in order; keep the
-      // compiler from moving reads above writes (or the next pass's writes
-      // above this pass's reads)
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      constexpr int NQ = SR * SCPR / 64;  // chunks per lane and pass
-      uint4 v[NQ];
-#pragma unroll
-      for (int h = 0; h < NQ; ++h) {
-        const int q = h * 64 + lane, r = q / SCPR, c = q % SCPR;
-        v[h] = *reinterpret_cast<const uint4*>(stage + r * WTN + (c ^ (r & 7)) * 8);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-      for (int h = 0; h < NQ; ++h) {
-        const int q = h * 64 + lane, r = ps * SR + q / SCPR, c = q % SCPR;
-        const int n = nb + c * 8;
-        bo.store<GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, v[h], r, n, mb + r < t.m_hi && n < p.N);
-      }
-    }
+    store_wave_block<FM, FN, GMD == G_KROWS ? MOE_OUT_CPOL : 0>(p, acc, stage, C0, C1,
+                                                               t.m_lo + wm * WTM, t.m_hi,
+                                                               t.n0 + wn * WTN, lane);
   };
 
   // ---- compute cursor (every wave keeps it; it decides when the loop ends)
@@ -1906,6 +1927,212 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
       __syncthreads();
     } while (advance(std::true_type{}));
   }
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradients of experts with at most STRIP_K rows ("strip" kernel).
+// C_e = A_e^T B_e sums over expert e's rows only, and with K <= 256 one
+// workgroup holds all of them: a workgroup per (expert, 256-row block of C_e)
+// reads its A block (256 rows of C by the expert's K rows) once, into its
+// waves' registers (through the LDS, read back transposed), then streams the
+// expert's B rows through the LDS one 64-deep slice of a 128-column tile at a
+// time and writes the block's 256 x 128 output tiles along the whole row of
+// C_e.  A crosses from L2 into a CU once per block of C rows instead of once
+// per output tile: at K = 256 a 64 KB output tile costs its 64 KB of B plus a
+// share of 128 KB of A spread over the whole row, where the tile kernels read
+// 192 KB for it.  Each 64-deep slice of B, and each half of A's 256 columns
+// in the first steps, fills one of eight 16 KB LDS buffers; slice g + 7 is
+// sent while slice g is multiplied.  Eight waves, two per SIMD, each own 32
+// rows of the block (their A: 64 registers) and all 128 columns of a tile,
+// and send the copies themselves.  Every 32 x 32 output block takes its MFMAs
+// in the tile kernels' order (K steps of 16 in order), so the results are the
+// same bits.
+//
+// The copies into the LDS are issued as inline assembly, which the compiler
+// does not track, and each step waits for its slice with an explicit vmcnt:
+// the compiler, tracking them, waited for every copy in flight before some
+// LDS reads.  A lane's vector memory operations complete in the order they
+// were issued (copies and stores alike), so at step g slice g has landed once
+// at most the operations issued after it are outstanding: the copies of
+// slices g + 1 .. g + 6 and the stores of the tiles finished since.  The
+// wait counts take the fewest stores a tile can issue (a count too small
+// only waits longer).
+// ---------------------------------------------------------------------------
+constexpr int STRIP_M = 256;  // output rows per workgroup
+constexpr int STRIP_N = 128;  // columns of a B tile
+
+// s_waitcnt immediate: vector memory count vm, LDS/scalar count lgkm.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// Buffer descriptor words over 2^31 - 1 bytes from `base` (as make_rsrc).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base) {
+  const uint64_t a = (uint64_t)base;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const bf16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) bf16_t*)p;
+}
+// 16 bytes per lane from the buffer (byte offset voff; out of range: zeros)
+// into the LDS at lds_byte + 16 lane, untracked by the compiler.  No output
+// registers; the caller waits for the copy with vmcnt.
+__device__ __forceinline__ void dma16_untracked(u32x4 r, uint32_t lds_byte, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_byte), "v"(voff), "s"(r)
+      : "memory", "m0");
+}
+
+template <int ROLE>
+__global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
+  constexpr bool AG = gathers_a(ROLE);
+  constexpr int SL = BK * STRIP_N;  // one buffer: [64][128] bf16 (the KN layout)
+  __shared__ __attribute__((aligned(16))) bf16_t sbuf[8 * SL];
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[8 * 16 * 64];
+  using std::integral_constant;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // rows 32 wave .. + 31 of the block
+  const int mstrips = (p.M + STRIP_M - 1) / STRIP_M;
+  const int id = remap_xcd(blockIdx.x, gridDim.x);  // an expert's blocks on one XCD
+  const int e = __builtin_amdgcn_readfirstlane(id / mstrips);
+  const int m0 = __builtin_amdgcn_readfirstlane((id - e * mstrips) * STRIP_M);
+  const int k_lo = ld_table(p.off, e), k_hi = ld_table(p.off, e + 1);
+  const int kn = k_hi - k_lo;
+  if (kn > STRIP_K) return;  // the tile kernels' expert
+  const bf16_t* A = static_cast<const bf16_t*>(p.A);
+  const bf16_t* B = static_cast<const bf16_t*>(p.B0);
+  // lane chunk q = tid + 512 i of a buffer: row q / 16 of the slice, logical
+  // 16-byte chunk (q mod 16) ^ ((row mod 4) * 4) (kn_swz inverted)
+  int crow[2], ccol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 512 * i;
+    crow[i] = q >> 4;
+    ccol[i] = ((q & 15) ^ ((crow[i] & 3) << 2)) * 8;
+  }
+  const uint32_t lds0 = lds_addr(sbuf) + 64 * wave * 16;  // the wave's first chunk in buffer 0
+
+  // ---- A: K slice s, C rows m0 + 128 h .. + 127 into buffer 2 s + h (the
+  // gather roles find row k's source row in the row table)
+  {
+    const u32x4 ra = rsrc_words(AG ? A : A + (int64_t)k_lo * p.lda);
+    int vo[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k = s * BK + crow[i];
+        int64_t row = k;
+        if constexpr (AG) row = kn > 0 ? p.a_rows[min(k_lo + k, k_hi - 1)] : 0;
+        vo[s][i] = k < kn ? (int)((row * p.lda + m0 + ccol[i]) * 2) : OOB;
+      }
+#pragma unroll
+    for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int h = bi & 1;
+        const bool ok = vo[bi >> 1][i] != OOB && m0 + h * STRIP_N + ccol[i] < p.M;
+        dma16_untracked(ra, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? vo[bi >> 1][i] + h * STRIP_N * 2 : OOB);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  __syncthreads();
+  bf16x8 af[16];  // the wave's 32 rows of A over K, one fragment per K step of 16
+  {
+    const int h = wave >> 2, mb = (wave & 3) * 32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) af[4 * s + ks] = frag_kn<STRIP_N>(sbuf + (2 * s + h) * SL, mb, ks, lane);
+  }
+  __syncthreads();  // every wave has its A before B overwrites the buffers
+
+  // ---- B: tile t's K slice s goes out as slice 4 t + s, into buffer
+  // (4 t + s) mod 8; tiles from `ntile` on (the pad to an even count, and the
+  // sends past the last slice) read nothing
+  const int ntile = (p.N + STRIP_N - 1) / STRIP_N;
+  int bo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) bo[i] = (int)(((int64_t)crow[i] * p.ldb + ccol[i]) * 2);
+  auto send_b = [&](int bi, int t, int s) __attribute__((always_inline)) {
+    const u32x4 rb = rsrc_words(B + (int64_t)(k_lo + s * BK) * p.ldb);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = s * BK + crow[i] < kn && t * STRIP_N + ccol[i] < p.N;
+      dma16_untracked(rb, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? bo[i] + t * STRIP_N * 2 : OOB);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 7; ++j) send_b(j, j >> 2, j & 3);
+
+  bf16_t* C0 = static_cast<bf16_t*>(p.C0) + (int64_t)e * p.c_estride;
+  bf16_t* C1 = p.C1 ? static_cast<bf16_t*>(p.C1) + (int64_t)e * p.c_estride : nullptr;
+  bf16_t* stage = stage_all + wave * 16 * 64;
+  f32x16 acc[2][1][2];  // [64-column half of the tile][32-row block][32-column block]
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[h][0][j][r] = 0.f;
+  };
+  zero_acc();
+
+  // step u of the pair of tiles (t0, t0 + 1): slice 4 t0 + u, in buffer u.
+  // Stores of finished tiles issued after this slice's copies: at least one
+  // tile's (8 per lane) for every tile finished in the 7 steps before, which
+  // is none or one in the first pair and one or two after it.
+  auto step = [&](auto Uc, auto Fc, int t0) __attribute__((always_inline)) {
+    constexpr int u = decltype(Uc)::value;
+    constexpr bool first = decltype(Fc)::value;
+    constexpr int tiles_since = first ? (u >= 4 ? 1 : 0) : ((u & 3) == 3 ? 1 : 2);
+    constexpr int after = 2 * 6 + 8 * tiles_since;
+    static_assert(after <= 63, "vmcnt range");
+    // this lane's copies of the slice have landed and its reads of the last
+    // slice are done; then every wave's
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(after, 0));
+    __builtin_amdgcn_s_barrier();
+    // slice 4 t0 + u + 7 into the buffer slice 4 t0 + u - 1 has left
+    send_b((u + 7) & 7, t0 + (u + 7) / 4, (u + 3) & 3);
+    const bf16_t* bs = sbuf + u * SL;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 bfr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = frag_kn<STRIP_N>(bs, 32 * j, ks, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j >> 1][0][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            bfr[j], af[4 * (u & 3) + ks], acc[j >> 1][0][j & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr ((u & 3) == 3) {  // tile t0 + u / 4 is complete
+      const int n0 = (t0 + (u >> 2)) * STRIP_N;
+      store_wave_block<1, 2, MOE_OUT_CPOL>(p, acc[0], stage, C0, C1, m0 + wave * 32, p.M, n0, lane);
+      store_wave_block<1, 2, MOE_OUT_CPOL>(p, acc[1], stage, C0, C1, m0 + wave * 32, p.M, n0 + 64, lane);
+      zero_acc();
+    }
+  };
+  auto pair = [&](auto Fc, int t0) __attribute__((always_inline)) {
+    step(integral_constant<int, 0>{}, Fc, t0);
+    step(integral_constant<int, 1>{}, Fc, t0);
+    step(integral_constant<int, 2>{}, Fc, t0);
+    step(integral_constant<int, 3>{}, Fc, t0);
+    step(integral_constant<int, 4>{}, Fc, t0);
+    step(integral_constant<int, 5>{}, Fc, t0);
+    step(integral_constant<int, 6>{}, Fc, t0);
+    step(integral_constant<int, 7>{}, Fc, t0);
+  };
+  pair(std::true_type{}, 0);
+  for (int t0 = 2; t0 < ntile; t0 += 2) pair(std::false_type{}, t0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no copy into LDS outlives the workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -2034,7 +2261,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
     int cnt = 0, o = 0;
     if (e < groups) {
       o = off[e];
-      cnt = cost ? (off[e + 1] - o + BK - 1) / BK + KCOST_FIXED : (off[e + 1] - o + bm - 1) / bm;
+      const int rows = off[e + 1] - o;
+      cnt = !cost                        ? (rows + bm - 1) / bm
+            : STRIP_K > 0 && rows <= STRIP_K ? 0
+                                             : (rows + BK - 1) / BK + KCOST_FIXED;
     }
     scan[threadIdx.x] = cnt;
     __syncthreads();
@@ -2311,6 +2541,23 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
     }
     return check_launch(name);
   }
+  // weight gradients: the experts with at most STRIP_K rows in the strip
+  // kernel first, then the others in the role's tile kernel
+  GemmParams q = p;
+  if (STRIP_K > 0 && p.off != nullptr && p.groups > 0 && p.M > 0 &&
+      (role == R_DOWN_WGRAD || role == R_GATEUP_WGRAD || role == R_GATEUP_WGRAD_GATHER)) {
+    const int64_t grid = (int64_t)p.groups * ceil_div(p.M, STRIP_M);
+    if (grid > 0x7fffffff) {
+      set_error("GEMM %s: grid too large", name);
+      return MOE_ERR_UNSUPPORTED;
+    }
+    if (role == R_DOWN_WGRAD) gemm_bf16_strip_kernel<R_DOWN_WGRAD><<<(int)grid, 512, 0, s>>>(p);
+    else if (role == R_GATEUP_WGRAD) gemm_bf16_strip_kernel<R_GATEUP_WGRAD><<<(int)grid, 512, 0, s>>>(p);
+    else gemm_bf16_strip_kernel<R_GATEUP_WGRAD_GATHER><<<(int)grid, 512, 0, s>>>(p);
+    const moe_status_t st = check_launch(name);
+    if (st != MOE_OK) return st;
+    q.k_strip = STRIP_K;
+  }
   switch (role) {
 #define X(r, n, t, a, b, g, t2, e)                                                        \
   case r: {                                                                               \
@@ -2322,7 +2569,7 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
       return MOE_ERR_UNSUPPORTED;                                                         \
     }                                                                                     \
     launch_bf16_role<role_alt_tile(r), t, a, b, g, t2, e, r>(                               \
-        p, (int)grid, s, role_tile(r, p.N) != t);                                          \
+        q, (int)grid, s, role_tile(r, p.N) != t);                                          \
     break;                                                                                \
   }
     MOE_GEMM_ROLES(X)
