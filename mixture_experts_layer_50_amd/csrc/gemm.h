@@ -49,11 +49,14 @@ struct GemmParams {
   const int32_t* off;  // group offsets [groups+1] (G_MROWS, G_KROWS); NULL in G_KROWS: see k_chunk
   int k_chunk;         // G_KROWS without offsets: group g sums K rows [g*k_chunk, (g+1)*k_chunk)
                        // (a split of K into partial results); 0 = one group [0, K)
-  int k_strip;         // G_KROWS with offsets: experts with at most k_strip rows are left to
-                       // the strip kernel (the tile kernels neither read nor write them); 0 = none
+  int k_strip;         // G_KROWS with offsets and kcost: nonzero when the strip kernel ran
+                       // first; the tile kernels then neither read nor write the experts of
+                       // zero K cost (the strip kernel's)
+  int col_parts;       // strip kernel: parts (of whole column tiles) a row block is split in
   const int32_t* tiles;// G_MROWS tile table: tiles[0] = count, then (expert, first row) pairs
   const int32_t* kcost;// G_KROWS (optional): prefix sums [groups+1] of the per-expert tile cost
-                       // (K slices + a fixed part), for balancing the persistent kernels
+                       // (K slices + a fixed part), for balancing the persistent kernels; all
+                       // zero when every expert fits the strip kernel
   int groups;          // number of local experts
   int m_tiles, n_tiles;
   void* C0;
@@ -141,10 +144,12 @@ moe_status_t launch_tile_tables(const int32_t* off, int groups, int32_t* tiles25
                                 int rows_cap = 0, const CombinePrep* cmb = nullptr);
 // Per-tile cost of a weight-gradient tile beyond its K slices (its epilogue).
 constexpr int KCOST_FIXED = 2;
-// Experts with at most STRIP_K rows run their weight gradients in the strip
-// kernel (gemm.hip), whose workgroups hold all of an expert's K rows; their
-// K-cost entries are zero, so the tile kernels' balancing leaves them out.
-// Build-time tunable: 0 turns the strip kernel off.
+// When every expert has at most STRIP_K rows, the weight gradients run in the
+// strip kernel (gemm.hip), whose workgroups hold all of an expert's K rows:
+// the tile-table launch then gives every expert zero K cost, and the tile
+// kernels leave them all out.  With a larger expert the tile kernels run
+// every expert (two kernels splitting the experts ran slower, one after the
+// other).  Build-time tunable: 0 turns the strip kernel off.
 #ifndef MOE_STRIP_K
 #define MOE_STRIP_K 256
 #endif

@@ -514,7 +514,7 @@ __device__ __forceinline__ TileDesc tile_desc(const GemmParams& p, int L) {
     if (GMD == G_KROWS && p.off) {
       t.k_lo = ld_table(p.off, t.e);
       t.k_hi = ld_table(p.off, t.e + 1);
-      if (p.k_strip > 0 && t.k_hi - t.k_lo <= p.k_strip) {  // the strip kernel's expert
+      if (p.k_strip && ld_table(p.kcost, t.e + 1) == ld_table(p.kcost, t.e)) {  // the strip kernel's
         t.k_hi = t.k_lo;
         t.m_hi = t.m_lo;
       }
@@ -1768,6 +1768,49 @@ __device__ __forceinline__ void store_wave_block(const GemmParams& p, f32x16 (&a
   }
 }
 
+// The same for one wave's 32 x 64 block in a single pass through a 32 x 64
+// LDS area (4 KB).  Every lane writes its accumulators: row r = lane mod 32,
+// 8-byte half h = lane / 32 of 16-byte chunk c.  The chunk sits at physical
+// chunk c ^ f(r) of LDS row r, f(r) = (r / 2 mod 4) + 4 (r / 16 mod 2), with
+// its two halves swapped in rows with r / 8 odd: the 32 rows' 8-byte pieces
+// of one chunk then fall on 64 different banks (row r's LDS row starts at
+// bank 32 (r mod 2)).  The readers take whole chunks, 8 lanes per row.
+__device__ __forceinline__ int stage32_f(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+template <int CPOL>
+__device__ __forceinline__ void store_wave_block32(const GemmParams& p, f32x16 (&acc)[1][2],
+                                                   bf16_t* stage, bf16_t* C0, bf16_t* C1, int mb,
+                                                   int m_hi, int nb, int lane) {
+  const int half = lane >> 5, r = lane & 31;
+  const int sw = (r >> 3) & 1;
+  const BlockOut bo(p, C0, C1, (int64_t)mb * p.ldc, nb, nb + 64);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 4 * j + q;  // logical chunk: columns 8 c .. 8 c + 7
+      *reinterpret_cast<uint2*>(stage + r * 64 + (c ^ stage32_f(r)) * 8 + 4 * (half ^ sw)) =
+          make_uint2(pack_bf2(acc[0][j][4 * q], acc[0][j][4 * q + 1]),
+                     pack_bf2(acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]));
+    }
+  // the wave's own LDS writes and reads execute in order; keep the compiler
+  // from moving the reads above the writes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = i * 64 + lane, rr = q >> 3, c = q & 7;
+    v[i] = swap_halves(*reinterpret_cast<const uint4*>(stage + rr * 64 + (c ^ stage32_f(rr)) * 8),
+                       (rr >> 3) & 1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = i * 64 + lane, rr = q >> 3, c = q & 7;
+    const int n = nb + c * 8;
+    bo.store<CPOL>(p, v[i], rr, n, mb + rr < m_hi && n < p.N);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Warp-specialised persistent bf16 GEMM whose producer waves copy the K
 // slices straight into LDS (DmaKC / DmaKN) instead of through registers.
@@ -1933,7 +1976,8 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
 // Weight gradients of experts with at most STRIP_K rows ("strip" kernel).
 // C_e = A_e^T B_e sums over expert e's rows only, and with K <= 256 one
 // workgroup holds all of them: a workgroup per (expert, 256-row block of C_e)
-// reads its A block (256 rows of C by the expert's K rows) once, into its
+// (or a part of its columns) reads its A block (256 rows of C by the
+// expert's K rows) once, into its
 // waves' registers (through the LDS, read back transposed), then streams the
 // expert's B rows through the LDS one 64-deep slice of a 128-column tile at a
 // time and writes the block's 256 x 128 output tiles along the whole row of
@@ -1941,22 +1985,22 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
 // per output tile: at K = 256 a 64 KB output tile costs its 64 KB of B plus a
 // share of 128 KB of A spread over the whole row, where the tile kernels read
 // 192 KB for it.  Each 64-deep slice of B, and each half of A's 256 columns
-// in the first steps, fills one of eight 16 KB LDS buffers; slice g + 7 is
-// sent while slice g is multiplied.  Eight waves, two per SIMD, each own 32
+// in the first steps, fills one of eight 16 KB LDS buffers: two tiles of B,
+// the next one sent slice by slice while the current one is multiplied, with
+// one workgroup barrier per tile.  Eight waves, two per SIMD, each own 32
 // rows of the block (their A: 64 registers) and all 128 columns of a tile,
 // and send the copies themselves.  Every 32 x 32 output block takes its MFMAs
 // in the tile kernels' order (K steps of 16 in order), so the results are the
 // same bits.
 //
 // The copies into the LDS are issued as inline assembly, which the compiler
-// does not track, and each step waits for its slice with an explicit vmcnt:
+// does not track, and each tile waits for its copies with an explicit vmcnt:
 // the compiler, tracking them, waited for every copy in flight before some
 // LDS reads.  A lane's vector memory operations complete in the order they
-// were issued (copies and stores alike), so at step g slice g has landed once
-// at most the operations issued after it are outstanding: the copies of
-// slices g + 1 .. g + 6 and the stores of the tiles finished since.  The
-// wait counts take the fewest stores a tile can issue (a count too small
-// only waits longer).
+// were issued (copies and stores alike), so tile t has landed once at most
+// the operations issued after its copies are outstanding: the stores of tile
+// t - 1.  The wait counts take the fewest stores a tile can issue (a count
+// too small only waits longer).
 // ---------------------------------------------------------------------------
 constexpr int STRIP_M = 256;  // output rows per workgroup
 constexpr int STRIP_N = 128;  // columns of a B tile
@@ -1993,18 +2037,30 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
   constexpr bool AG = gathers_a(ROLE);
   constexpr int SL = BK * STRIP_N;  // one buffer: [64][128] bf16 (the KN layout)
   __shared__ __attribute__((aligned(16))) bf16_t sbuf[8 * SL];
-  __shared__ __attribute__((aligned(16))) bf16_t stage_all[8 * 16 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t stage_all[8 * 32 * 64];
   using std::integral_constant;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // rows 32 wave .. + 31 of the block
-  const int mstrips = (p.M + STRIP_M - 1) / STRIP_M;
-  const int id = remap_xcd(blockIdx.x, gridDim.x);  // an expert's blocks on one XCD
-  const int e = __builtin_amdgcn_readfirstlane(id / mstrips);
-  const int m0 = __builtin_amdgcn_readfirstlane((id - e * mstrips) * STRIP_M);
+  // work item (expert e, row block, column part): the columns of C_e are
+  // split in `ncs` parts of whole tiles, so that the items fill the CUs
+  // evenly
+  const int mstrips = (p.M + STRIP_M - 1) / STRIP_M, ncs = p.col_parts;
+  const int ntile_all = (p.N + STRIP_N - 1) / STRIP_N;
+  const int id = remap_xcd(blockIdx.x, gridDim.x);  // an expert's items on one XCD
+  const int e = __builtin_amdgcn_readfirstlane(id / (mstrips * ncs));
+  const int rem = id - e * mstrips * ncs;
+  const int mblk = __builtin_amdgcn_readfirstlane(rem / ncs);
+  const int cpart = __builtin_amdgcn_readfirstlane(rem - mblk * ncs);
+  const int m0 = mblk * STRIP_M;
+  const int t_first = cpart * ntile_all / ncs;  // the part's tiles [t_first, t_first + ntile)
+  const int ntile = (cpart + 1) * ntile_all / ncs - t_first;
+  // the strip path is on when the tile-table launch gave every expert zero
+  // cost (every expert has at most STRIP_K rows); else the tile kernels run
+  // them all
+  if (ld_table(p.kcost, e + 1) != ld_table(p.kcost, e)) return;
   const int k_lo = ld_table(p.off, e), k_hi = ld_table(p.off, e + 1);
   const int kn = k_hi - k_lo;
-  if (kn > STRIP_K) return;  // the tile kernels' expert
   const bf16_t* A = static_cast<const bf16_t*>(p.A);
   const bf16_t* B = static_cast<const bf16_t*>(p.B0);
   // lane chunk q = tid + 512 i of a buffer: row q / 16 of the slice, logical
@@ -2053,27 +2109,28 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
   }
   __syncthreads();  // every wave has its A before B overwrites the buffers
 
-  // ---- B: tile t's K slice s goes out as slice 4 t + s, into buffer
-  // (4 t + s) mod 8; tiles from `ntile` on (the pad to an even count, and the
-  // sends past the last slice) read nothing
-  const int ntile = (p.N + STRIP_N - 1) / STRIP_N;
+  // ---- B: tile t's K slice s into buffer 4 (t mod 2) + s; tiles from
+  // `ntile` on (the pad to an even count, and the sends past the last tile)
+  // read nothing
+  auto col_tile = [&](int t) { return t < ntile ? t_first + t : ntile_all; };
   int bo[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) bo[i] = (int)(((int64_t)crow[i] * p.ldb + ccol[i]) * 2);
   auto send_b = [&](int bi, int t, int s) __attribute__((always_inline)) {
     const u32x4 rb = rsrc_words(B + (int64_t)(k_lo + s * BK) * p.ldb);
+    const int c = col_tile(t);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool ok = s * BK + crow[i] < kn && t * STRIP_N + ccol[i] < p.N;
-      dma16_untracked(rb, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? bo[i] + t * STRIP_N * 2 : OOB);
+      const bool ok = s * BK + crow[i] < kn && c * STRIP_N + ccol[i] < p.N;
+      dma16_untracked(rb, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? bo[i] + c * STRIP_N * 2 : OOB);
     }
   };
 #pragma unroll
-  for (int j = 0; j < 7; ++j) send_b(j, j >> 2, j & 3);
+  for (int j = 0; j < 4; ++j) send_b(j, 0, j);
 
   bf16_t* C0 = static_cast<bf16_t*>(p.C0) + (int64_t)e * p.c_estride;
   bf16_t* C1 = p.C1 ? static_cast<bf16_t*>(p.C1) + (int64_t)e * p.c_estride : nullptr;
-  bf16_t* stage = stage_all + wave * 16 * 64;
+  bf16_t* stage = stage_all + wave * 32 * 64;
   f32x16 acc[2][1][2];  // [64-column half of the tile][32-row block][32-column block]
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -2085,53 +2142,46 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
   };
   zero_acc();
 
-  // step u of the pair of tiles (t0, t0 + 1): slice 4 t0 + u, in buffer u.
-  // Stores of finished tiles issued after this slice's copies: at least one
-  // tile's (8 per lane) for every tile finished in the 7 steps before, which
-  // is none or one in the first pair and one or two after it.
-  auto step = [&](auto Uc, auto Fc, int t0) __attribute__((always_inline)) {
-    constexpr int u = decltype(Uc)::value;
+  // Tile t (its slices in buffers 4 h .. 4 h + 3, h = t mod 2).  Its copies
+  // went out during tile t - 1 (tile 0's before the loop); issued after them:
+  // the stores of tile t - 1 (8 per lane at least).
+  auto tile = [&](auto Hc, auto Fc, int t) __attribute__((always_inline)) {
+    constexpr int h = decltype(Hc)::value;
     constexpr bool first = decltype(Fc)::value;
-    constexpr int tiles_since = first ? (u >= 4 ? 1 : 0) : ((u & 3) == 3 ? 1 : 2);
-    constexpr int after = 2 * 6 + 8 * tiles_since;
-    static_assert(after <= 63, "vmcnt range");
-    // this lane's copies of the slice have landed and its reads of the last
-    // slice are done; then every wave's
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(after, 0));
+    // this lane's copies of the tile have landed and its reads of the last
+    // tile are done; then every wave's
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(first && h == 0 ? 0 : 8, 0));
     __builtin_amdgcn_s_barrier();
-    // slice 4 t0 + u + 7 into the buffer slice 4 t0 + u - 1 has left
-    send_b((u + 7) & 7, t0 + (u + 7) / 4, (u + 3) & 3);
-    const bf16_t* bs = sbuf + u * SL;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bfr[4];
+    for (int s = 0; s < 4; ++s) {
+      // slice s of tile t + 1 into the buffer tile t - 1's slice s has left,
+      // one slice per slice of MFMAs (a wave whose copies wait for room in
+      // the memory pipeline stalls at the copy, not at all four)
+      send_b(4 * (1 - h) + s, t + 1, s);
+      const bf16_t* bs = sbuf + (4 * h + s) * SL;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = frag_kn<STRIP_N>(bs, 32 * j, ks, lane);
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 bfr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[j >> 1][0][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            bfr[j], af[4 * (u & 3) + ks], acc[j >> 1][0][j & 1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) bfr[j] = frag_kn<STRIP_N>(bs, 32 * j, ks, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j >> 1][0][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              bfr[j], af[4 * s + ks], acc[j >> 1][0][j & 1], 0, 0, 0);
+      }
     }
-    if constexpr ((u & 3) == 3) {  // tile t0 + u / 4 is complete
-      const int n0 = (t0 + (u >> 2)) * STRIP_N;
-      store_wave_block<1, 2, MOE_OUT_CPOL>(p, acc[0], stage, C0, C1, m0 + wave * 32, p.M, n0, lane);
-      store_wave_block<1, 2, MOE_OUT_CPOL>(p, acc[1], stage, C0, C1, m0 + wave * 32, p.M, n0 + 64, lane);
-      zero_acc();
-    }
+    const int n0 = col_tile(t) * STRIP_N;
+    store_wave_block32<MOE_OUT_CPOL>(p, acc[0], stage, C0, C1, m0 + wave * 32, p.M, n0, lane);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the first half's reads are done
+    store_wave_block32<MOE_OUT_CPOL>(p, acc[1], stage, C0, C1, m0 + wave * 32, p.M, n0 + 64, lane);
+    zero_acc();
   };
-  auto pair = [&](auto Fc, int t0) __attribute__((always_inline)) {
-    step(integral_constant<int, 0>{}, Fc, t0);
-    step(integral_constant<int, 1>{}, Fc, t0);
-    step(integral_constant<int, 2>{}, Fc, t0);
-    step(integral_constant<int, 3>{}, Fc, t0);
-    step(integral_constant<int, 4>{}, Fc, t0);
-    step(integral_constant<int, 5>{}, Fc, t0);
-    step(integral_constant<int, 6>{}, Fc, t0);
-    step(integral_constant<int, 7>{}, Fc, t0);
-  };
-  pair(std::true_type{}, 0);
-  for (int t0 = 2; t0 < ntile; t0 += 2) pair(std::false_type{}, t0);
+  tile(integral_constant<int, 0>{}, std::true_type{}, 0);
+  tile(integral_constant<int, 1>{}, std::true_type{}, 1);
+  for (int t0 = 2; t0 < ntile; t0 += 2) {
+    tile(integral_constant<int, 0>{}, std::false_type{}, t0);
+    tile(integral_constant<int, 1>{}, std::false_type{}, t0 + 1);
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no copy into LDS outlives the workgroup
 }
 
@@ -2254,17 +2304,25 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* off, in
   int32_t* tiles = blockIdx.x == 0 ? tiles256 : tiles128;
   __shared__ int32_t scan[1024];
   __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
+  __shared__ int32_t strip_all;  // every expert fits the strip kernel (cost workgroup)
+  if (threadIdx.x == 0) {
+    carry = 0;
+    strip_all = STRIP_K > 0;
+  }
   __syncthreads();
+  if (cost && STRIP_K > 0) {
+    bool big = false;
+    for (int e = threadIdx.x; e < groups; e += 1024) big |= off[e + 1] - off[e] > STRIP_K;
+    if (big) strip_all = 0;  // benign race: every writer stores 0
+    __syncthreads();
+  }
   for (int base = 0; base < groups; base += 1024) {
     int e = base + threadIdx.x;
     int cnt = 0, o = 0;
     if (e < groups) {
       o = off[e];
       const int rows = off[e + 1] - o;
-      cnt = !cost                        ? (rows + bm - 1) / bm
-            : STRIP_K > 0 && rows <= STRIP_K ? 0
-                                             : (rows + BK - 1) / BK + KCOST_FIXED;
+      cnt = !cost ? (rows + bm - 1) / bm : strip_all ? 0 : (rows + BK - 1) / BK + KCOST_FIXED;
     }
     scan[threadIdx.x] = cnt;
     __syncthreads();
@@ -2522,6 +2580,27 @@ static void launch_f32(const GemmParams& p, int max_rows, hipStream_t s) {
   gemm_f32_kernel<AM, BMD, GMD, B2, EPI, ROLE><<<grid, 256, 0, s>>>(p);
 }
 
+// Column parts of the strip kernel's work items: the split (1 to 4 parts of
+// whole tiles) that moves the fewest bytes through the busiest CU, with every
+// expert taken to be the strip kernel's (rounds of one item per CU, each
+// reading its A block once and its part of the B tiles).
+static int strip_column_parts(const GemmParams& p) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  const int64_t ntile = ceil_div(p.N, STRIP_N);
+  const int64_t items1 = (int64_t)p.groups * ceil_div(p.M, STRIP_M);
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int c = 1; c <= 4 && c <= ntile; ++c) {
+    const int64_t rounds = ceil_div(items1 * c, cus);
+    const int64_t cost = rounds * (STRIP_M + ceil_div(ntile, c) * STRIP_N);  // A rows + B columns
+    if (best_cost < 0 || cost < best_cost) { best = c; best_cost = cost; }
+  }
+  return best;
+}
+
 moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
                          hipStream_t s) {
   const char* name = role_name(role);
@@ -2544,19 +2623,21 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
   // weight gradients: the experts with at most STRIP_K rows in the strip
   // kernel first, then the others in the role's tile kernel
   GemmParams q = p;
-  if (STRIP_K > 0 && p.off != nullptr && p.groups > 0 && p.M > 0 &&
+  if (STRIP_K > 0 && p.off != nullptr && p.kcost != nullptr && p.groups > 0 && p.M > 0 &&
       (role == R_DOWN_WGRAD || role == R_GATEUP_WGRAD || role == R_GATEUP_WGRAD_GATHER)) {
-    const int64_t grid = (int64_t)p.groups * ceil_div(p.M, STRIP_M);
+    GemmParams sp = p;
+    sp.col_parts = strip_column_parts(p);
+    const int64_t grid = (int64_t)p.groups * ceil_div(p.M, STRIP_M) * sp.col_parts;
     if (grid > 0x7fffffff) {
       set_error("GEMM %s: grid too large", name);
       return MOE_ERR_UNSUPPORTED;
     }
-    if (role == R_DOWN_WGRAD) gemm_bf16_strip_kernel<R_DOWN_WGRAD><<<(int)grid, 512, 0, s>>>(p);
-    else if (role == R_GATEUP_WGRAD) gemm_bf16_strip_kernel<R_GATEUP_WGRAD><<<(int)grid, 512, 0, s>>>(p);
-    else gemm_bf16_strip_kernel<R_GATEUP_WGRAD_GATHER><<<(int)grid, 512, 0, s>>>(p);
+    if (role == R_DOWN_WGRAD) gemm_bf16_strip_kernel<R_DOWN_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
+    else if (role == R_GATEUP_WGRAD) gemm_bf16_strip_kernel<R_GATEUP_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
+    else gemm_bf16_strip_kernel<R_GATEUP_WGRAD_GATHER><<<(int)grid, 512, 0, s>>>(sp);
     const moe_status_t st = check_launch(name);
     if (st != MOE_OK) return st;
-    q.k_strip = STRIP_K;
+    q.k_strip = 1;
   }
   switch (role) {
 #define X(r, n, t, a, b, g, t2, e)                                                        \
