@@ -194,9 +194,13 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int) -> dict:
         out["raw_kib_per_dispatch"][k] = {"FETCH_SIZE": round(f, 1), "WRITE_SIZE": round(w_, 1)}
         role = gemm_role_of(k)
         if role:
-            out["kernels"][role] = {"bytes_per_launch": int(f * 1024 * f_read + w_ * 1024 * f_write),
-                                    "read_bytes": int(f * 1024 * f_read),
-                                    "write_bytes": int(w_ * 1024 * f_write)}
+            # a role may launch two kernels (the weight gradients' strip
+            # kernel and tile kernel): its bytes per call are their sum
+            ent = out["kernels"].setdefault(role, {"bytes_per_launch": 0, "read_bytes": 0,
+                                                   "write_bytes": 0})
+            ent["read_bytes"] += int(f * 1024 * f_read)
+            ent["write_bytes"] += int(w_ * 1024 * f_write)
+            ent["bytes_per_launch"] = ent["read_bytes"] + ent["write_bytes"]
     return out
 
 

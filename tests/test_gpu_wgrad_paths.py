@@ -1,0 +1,105 @@
+"""GPU parity of the expert weight gradients on both of their paths: the
+strip kernel, taken when every local expert has at most 256 rows, and the
+tile kernel, taken when one expert has more (the choice is made on the
+device from the group offsets).  Group sizes are set exactly by a routing
+table handed in by the caller: 256-row groups (one whole K block), empty
+groups, ragged ones, and a single 257-row group that moves every expert to
+the tile kernel.  The output rows (d = 320) end in a partial 256-row block,
+the gate/up gradient has an odd number of 128-column tiles (2I = 384) and
+the down gradient a partial last tile (d = 320).  Checked against the
+oracle's backward, expert by expert."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as MI
+import gpu_util as U
+from mixture_experts_layer_50_amd import binding as B
+from mixture_experts_layer_50_amd.layer import LayerBuffers
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+SIZES = {
+    "strip": [256, 0, 256, 100, 7, 256, 0, 137],
+    "tile": [257, 0, 255, 100, 7, 256, 0, 137],
+}
+
+
+def _announce(name):
+    print(f"\n[gpu case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+def _table(sizes, k, seed):
+    """A (T, k) routing table whose experts receive exactly `sizes` rows and
+    no token names an expert twice."""
+    ids = np.repeat(np.arange(len(sizes), dtype=np.int32), sizes)
+    T = len(ids) // k
+    assert T * k == len(ids) and max(sizes) < T
+    idx = ids.reshape(k, T).T.copy()  # token t takes ids t, T + t, ...: no repeats
+    rng = np.random.default_rng(seed)
+    idx = idx[rng.permutation(T)]
+    g = rng.random(idx.shape).astype(np.float32)
+    return idx, g
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["plain", "gather"])
+@pytest.mark.parametrize("path", ["strip", "tile"])
+def test_weight_gradient_paths(path, gather):
+    sizes = SIZES[path]
+    E, k, d, I = len(sizes), 2, 320, 192
+    idx, g = _table(sizes, k, 71)
+    T = idx.shape[0]
+    w = MI.small_workload(f"wgrad_{path}_T{T}_d{d}_E{E}_k{k}_I{I}", T, d, E, k, I, seed=73,
+                          backward=True)
+    _announce(f"{w.name} gather={gather}")
+    a = MI.generate(w, parts=("x", "Wg", "Wu", "Wd", "dY"))
+    dev = U.upload(w, a)
+    s = U.shape_of(w)
+    buf = LayerBuffers(s, training=True, gather=gather)
+    t = buf.t
+    t["topk_idx"].copy_(torch.from_numpy(idx))
+    t["topk_w"].copy_(torch.from_numpy(g))
+    x = dev["x"]
+    B.moe_permute(s, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"], t["ws_permute"])
+    if gather:
+        B.moe_grouped_ffn_fwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"],
+                                     t["h"], t["a"], t["yp"], t["ws_ffn_fwd"])
+    else:
+        B.moe_grouped_ffn_fwd(s, t["xp"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"], t["h"],
+                              t["a"], t["yp"], t["ws_ffn_fwd"])
+    B.moe_combine_bwd(s, dev["dY"], t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"])
+    # the gradients' buffers start poisoned: every element must be written
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        t[name].fill_(float("nan"))
+    if gather:
+        B.moe_grouped_ffn_bwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"],
+                                     dev["Wd"], t["h"], t["a"], t["dyp"], t["dxp"], t["dw_gate"],
+                                     t["dw_up"], t["dw_down"], t["ws_ffn_bwd"])
+    else:
+        B.moe_grouped_ffn_bwd(s, t["xp"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"], t["h"],
+                              t["a"], t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"],
+                              t["ws_ffn_bwd"])
+    torch.cuda.synchronize()
+
+    g64 = g.astype(np.float64)
+    p = O.permute(idx, a["x"], E, 0, E)
+    assert list(p["counts"]) == sizes
+    assert np.array_equal(t["offsets"].cpu().numpy(), p["offsets"]), "group offsets differ"
+    f = O.expert_ffn_fwd(p["Xp"], p["offsets"], a["Wg"], a["Wu"], a["Wd"])
+    dYp, _ = O.combine_bwd(a["dY"], f["Yp"], p["inv"], g64, T, k)
+    fb = O.expert_ffn_bwd(p["Xp"], p["offsets"], a["Wg"], a["Wu"], a["Wd"], f["Hg"], f["Hu"],
+                          f["A"], dYp)
+    R = int(p["offsets"][-1])
+    tol = U.TOL["bf16"]
+    U.check("dxp", U.np64(t["dxp"][:R]), fb["dXp"], tol)
+    for gname, oname in (("dw_gate", "dWg"), ("dw_up", "dWu"), ("dw_down", "dWd")):
+        got = U.np64(t[gname])
+        assert np.isfinite(got).all(), f"{gname}: elements left unwritten"
+        for e in range(E):
+            U.check(f"{gname}[{e}]", got[e], fb[oname][e], tol)
+            if sizes[e] == 0:
+                assert not got[e].any(), f"{gname}[{e}]: an expert with no rows is not zero"
