@@ -2498,9 +2498,8 @@ template <> struct TileDims<TILE_128x256> { static constexpr int BM = 128, BN = 
 #define MOE_WS_PRODUCER_WAVES 4
 #endif
 
-// Workgroups of a persistent launch: as many as fit on the device at once,
-// at most one per tile, a multiple of the XCD count.
-static int persistent_grid(int occupancy, int max_tiles) {
+// Compute units of the current device (queried once per device).
+static int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -2510,7 +2509,13 @@ static int persistent_grid(int occupancy, int max_tiles) {
       n = 256;
     cus[dev] = n;
   }
-  int64_t g = std::min<int64_t>((int64_t)std::max(occupancy, 1) * cus[dev], max_tiles);
+  return cus[dev];
+}
+
+// Workgroups of a persistent launch: as many as fit on the device at once,
+// at most one per tile, a multiple of the XCD count.
+static int persistent_grid(int occupancy, int max_tiles) {
+  int64_t g = std::min<int64_t>((int64_t)std::max(occupancy, 1) * device_cus(), max_tiles);
   return (int)std::max<int64_t>(NXCD, g / NXCD * NXCD);
 }
 
@@ -2585,10 +2590,7 @@ static void launch_f32(const GemmParams& p, int max_rows, hipStream_t s) {
 // expert taken to be the strip kernel's (rounds of one item per CU, each
 // reading its A block once and its part of the B tiles).
 static int strip_column_parts(const GemmParams& p) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
+  const int cus = device_cus();
   const int64_t ntile = ceil_div(p.N, STRIP_N);
   const int64_t items1 = (int64_t)p.groups * ceil_div(p.M, STRIP_M);
   int best = 1;
