@@ -2004,6 +2004,14 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
 // ---------------------------------------------------------------------------
 constexpr int STRIP_M = 256;  // output rows per workgroup
 constexpr int STRIP_N = 128;  // columns of a B tile
+// Cache policy of the strip kernel's result stores: non-temporal for the
+// gate/up gradient, sc1 for the down projection's (measured: the down
+// gradient 146-149 vs 165-167 us and the gate/up gradient, which runs two
+// kernels later, 247-252 vs 267-270 us, the down input gradient in between
+// 8 us slower; sc1 for the gate/up gradient made it slower).
+#ifndef MOE_STRIP_DOWN_CPOL
+#define MOE_STRIP_DOWN_CPOL 16
+#endif
 
 // s_waitcnt immediate: vector memory count vm, LDS/scalar count lgkm.
 constexpr int waitcnt_imm(int vm, int lgkm) {
@@ -2035,6 +2043,7 @@ __device__ __forceinline__ void dma16_untracked(u32x4 r, uint32_t lds_byte, int 
 template <int ROLE>
 __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
   constexpr bool AG = gathers_a(ROLE);
+  constexpr int OCP = ROLE == R_DOWN_WGRAD ? MOE_STRIP_DOWN_CPOL : MOE_OUT_CPOL;
   constexpr int SL = BK * STRIP_N;  // one buffer: [64][128] bf16 (the KN layout)
   __shared__ __attribute__((aligned(16))) bf16_t sbuf[8 * SL];
   __shared__ __attribute__((aligned(16))) bf16_t stage_all[8 * 32 * 64];
@@ -2171,9 +2180,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
       }
     }
     const int n0 = col_tile(t) * STRIP_N;
-    store_wave_block32<MOE_OUT_CPOL>(p, acc[0], stage, C0, C1, m0 + wave * 32, p.M, n0, lane);
+    store_wave_block32<OCP>(p, acc[0], stage, C0, C1, m0 + wave * 32, p.M, n0, lane);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the first half's reads are done
-    store_wave_block32<MOE_OUT_CPOL>(p, acc[1], stage, C0, C1, m0 + wave * 32, p.M, n0 + 64, lane);
+    store_wave_block32<OCP>(p, acc[1], stage, C0, C1, m0 + wave * 32, p.M, n0 + 64, lane);
     zero_acc();
   };
   tile(integral_constant<int, 0>{}, std::true_type{}, 0);
