@@ -7,7 +7,10 @@ groups, ragged ones, and a single 257-row group that moves every expert to
 the tile kernel.  The output rows (d = 320) end in a partial 256-row block,
 the gate/up gradient has an odd number of 128-column tiles (2I = 384) and
 the down gradient a partial last tile (d = 320).  Checked against the
-oracle's backward, expert by expert."""
+oracle's backward, expert by expert; and the MFMA GEMMs (the gate/up
+forward and the down weight gradient on both paths) element by element
+against the rounding bound of a bf16 result of an fp32 sum, recomputed from
+the bf16 operands the kernels read."""
 import sys
 
 import numpy as np
@@ -103,3 +106,56 @@ def test_weight_gradient_paths(path, gather):
             U.check(f"{gname}[{e}]", got[e], fb[oname][e], tol)
             if sizes[e] == 0:
                 assert not got[e].any(), f"{gname}[{e}]: an expert with no rows is not zero"
+
+
+def _rounding_check(name, got, a, b):
+    """Every element of got (bf16) against C = a @ b recomputed in fp64 from
+    the same bf16 operands: a bf16 result within half an ulp of the exact
+    value (2^-9 relative) after an fp32 sum over K terms (error below
+    K 2^-24 sum |a||b|); both terms doubled as margin."""
+    ref = a @ b
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * a.shape[1] * 2.0 ** -24 * (np.abs(a) @ np.abs(b))
+    err = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert (err <= bound).all(), (f"{name}: element {worst} off by {err[worst]:.3e} "
+                                  f"(bound {bound[worst]:.3e}, value {ref[worst]:.3e})")
+
+
+@pytest.mark.parametrize("path", ["strip", "tile"])
+def test_gemm_engine_rounding_bound(path):
+    """The bf16 MFMA GEMMs element by element at the precision their storage
+    allows, on their own inputs (no chain of earlier roundings in between):
+    the gate/up forward's H = Xp [Wg | Wu] and the down projection's weight
+    gradient dWd = A^T dYp (strip or tile kernel), each recomputed in fp64
+    from the bf16 tensors the kernel read."""
+    sizes = SIZES[path]
+    E, k, d, I = len(sizes), 2, 320, 192
+    idx, g = _table(sizes, k, 79)
+    T = idx.shape[0]
+    w = MI.small_workload(f"engine_{path}_T{T}_d{d}_E{E}_k{k}_I{I}", T, d, E, k, I, seed=83,
+                          backward=True)
+    _announce(w.name)
+    a = MI.generate(w, parts=("x", "Wg", "Wu", "Wd", "dY"))
+    dev = U.upload(w, a)
+    s = U.shape_of(w)
+    buf = LayerBuffers(s, training=True)
+    t = buf.t
+    t["topk_idx"].copy_(torch.from_numpy(idx))
+    t["topk_w"].copy_(torch.from_numpy(g))
+    B.moe_permute(s, t["topk_idx"], dev["x"], t["offsets"], t["perm"], t["inv"], t["xp"],
+                  t["ws_permute"])
+    B.moe_grouped_ffn_fwd(s, t["xp"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"], t["h"], t["a"],
+                          t["yp"], t["ws_ffn_fwd"])
+    B.moe_combine_bwd(s, dev["dY"], t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"])
+    B.moe_grouped_ffn_bwd(s, t["xp"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"], t["h"], t["a"],
+                          t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"], t["ws_ffn_bwd"])
+    torch.cuda.synchronize()
+    off = t["offsets"].cpu().numpy()
+    xp, h, act, dyp = (U.np64(t[n][:off[-1]]) for n in ("xp", "h", "a", "dyp"))
+    wg, wu = U.np64(dev["Wg"]), U.np64(dev["Wu"])
+    dwd = U.np64(t["dw_down"])
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            _rounding_check(f"h[{e}]", h[r0:r1], xp[r0:r1], np.concatenate([wg[e], wu[e]], 1))
+        _rounding_check(f"dw_down[{e}]", dwd[e], act[r0:r1].T, dyp[r0:r1])
