@@ -113,6 +113,7 @@ def _rounding_check(name, got, a, b):
     the same bf16 operands: a bf16 result within half an ulp of the exact
     value (2^-9 relative) after an fp32 sum over K terms (error below
     K 2^-24 sum |a||b|); both terms doubled as margin."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
     ref = a @ b
     bound = 2.0 ** -8 * np.abs(ref) + 2 * a.shape[1] * 2.0 ** -24 * (np.abs(a) @ np.abs(b))
     err = np.abs(got - ref)
@@ -125,9 +126,9 @@ def _rounding_check(name, got, a, b):
 def test_gemm_engine_rounding_bound(path):
     """The bf16 MFMA GEMMs element by element at the precision their storage
     allows, on their own inputs (no chain of earlier roundings in between):
-    the gate/up forward's H = Xp [Wg | Wu] and the down projection's weight
-    gradient dWd = A^T dYp (strip or tile kernel), each recomputed in fp64
-    from the bf16 tensors the kernel read."""
+    the gate/up forward's H = Xp [Wg | Wu], the down projection's Yp = A Wd
+    and its weight gradient dWd = A^T dYp (strip or tile kernel), each
+    recomputed in fp64 from the bf16 tensors the kernel read."""
     sizes = SIZES[path]
     E, k, d, I = len(sizes), 2, 320, 192
     idx, g = _table(sizes, k, 79)
@@ -151,11 +152,35 @@ def test_gemm_engine_rounding_bound(path):
                           t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"], t["ws_ffn_bwd"])
     torch.cuda.synchronize()
     off = t["offsets"].cpu().numpy()
-    xp, h, act, dyp = (U.np64(t[n][:off[-1]]) for n in ("xp", "h", "a", "dyp"))
-    wg, wu = U.np64(dev["Wg"]), U.np64(dev["Wu"])
+    xp, h, act, yp, dyp = (U.np64(t[n][:off[-1]]) for n in ("xp", "h", "a", "yp", "dyp"))
+    wg, wu, wd = U.np64(dev["Wg"]), U.np64(dev["Wu"]), U.np64(dev["Wd"])
     dwd = U.np64(t["dw_down"])
     for e in range(E):
         r0, r1 = off[e], off[e + 1]
         if r1 > r0:
             _rounding_check(f"h[{e}]", h[r0:r1], xp[r0:r1], np.concatenate([wg[e], wu[e]], 1))
+            _rounding_check(f"yp[{e}]", yp[r0:r1], act[r0:r1], wd[e])
         _rounding_check(f"dw_down[{e}]", dwd[e], act[r0:r1].T, dyp[r0:r1])
+
+
+def test_gemm_engine_rounding_bound_full_size():
+    """The same element-by-element bound at the Qwen3 balanced shape in the
+    bench's gathered form (the strip kernel with its real row blocks and
+    column parts): H and Yp of the forward and the down weight gradient, for
+    four sampled experts (each expert's GEMMs are computed by its own
+    workgroups, so a sample covers the kernels' tile and column-part logic)."""
+    w = MI.WORKLOADS["qwen3_balanced_fwdbwd_T4096_d2048_E128_k8_I768"]
+    _announce(w.name + " engine bound")
+    a = MI.generate(w)
+    s, buf = U.run_layer(w, U.upload(w, a), gather=True)
+    t = buf.t
+    off = t["offsets"].cpu().numpy()
+    perm = t["perm"].cpu().numpy()
+    x = a["x"]
+    for e in (0, 41, 86, 127):
+        r0, r1 = off[e], off[e + 1]
+        xp = x[perm[r0:r1] // w.k]  # the rows the gathered kernels read
+        h, act, yp, dyp = (U.np64(t[n][r0:r1]) for n in ("h", "a", "yp", "dyp"))
+        _rounding_check(f"h[{e}]", h, xp, np.concatenate([a["Wg"][e], a["Wu"][e]], 1))
+        _rounding_check(f"yp[{e}]", yp, act, a["Wd"][e])
+        _rounding_check(f"dw_down[{e}]", U.np64(t["dw_down"][e]), act.T, dyp)
