@@ -258,3 +258,17 @@ def compare_aux(w: MI.Workload, a, buf, f, bw, alpha):
     check("dw_router(aux)", np64(t["dw_router"]), bw["dWr"] + rb["dWr"], tol)
     check("dbias(aux)", np64(t["dbias"]), bw["db"] + rb["db"], tol)
     check("dx(aux)", np64(t["dx"]), bw["dX"] + rb["dX"], tol)
+
+
+def check_rounding_bound(name, got, a, b):
+    """Every element of got (bf16) against C = a @ b recomputed in fp64 from
+    the same bf16 operands: a bf16 result within half an ulp of the exact
+    value (2^-9 relative) after an fp32 sum over K terms (error below
+    K 2^-24 sum |a||b|); both terms doubled as margin."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    ref = a @ b
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * a.shape[1] * 2.0 ** -24 * (np.abs(a) @ np.abs(b))
+    err = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert (err <= bound).all(), (f"{name}: element {worst} off by {err[worst]:.3e} "
+                                  f"(bound {bound[worst]:.3e}, value {ref[worst]:.3e})")

@@ -172,3 +172,9 @@ def test_full_size_dsv3_rank_share():
     offs = buf["offsets"].cpu().numpy()
     assert (np.diff(offs) == 1024).all() and offs[-1] == 32768
     U.compare_sampled(w, a, buf, np.r_[0:4, 32764:32768], experts=[0, 31])
+    # expert 0's GEMMs element by element against their rounding bound on the
+    # bf16 operands they read (K = 7168, 2048 and 1024: the long K loops)
+    xp, h, act, yp, dyp = (U.np64(buf[n][:1024]) for n in ("xp", "h", "a", "yp", "dyp"))
+    U.check_rounding_bound("h[0]", h, xp, np.concatenate([a["Wg"][0], a["Wu"][0]], 1))
+    U.check_rounding_bound("yp[0]", yp, act, a["Wd"][0])
+    U.check_rounding_bound("dw_down[0]", U.np64(buf["dw_down"][0]), act.T, dyp)

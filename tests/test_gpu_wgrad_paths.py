@@ -108,20 +108,6 @@ def test_weight_gradient_paths(path, gather):
                 assert not got[e].any(), f"{gname}[{e}]: an expert with no rows is not zero"
 
 
-def _rounding_check(name, got, a, b):
-    """Every element of got (bf16) against C = a @ b recomputed in fp64 from
-    the same bf16 operands: a bf16 result within half an ulp of the exact
-    value (2^-9 relative) after an fp32 sum over K terms (error below
-    K 2^-24 sum |a||b|); both terms doubled as margin."""
-    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
-    ref = a @ b
-    bound = 2.0 ** -8 * np.abs(ref) + 2 * a.shape[1] * 2.0 ** -24 * (np.abs(a) @ np.abs(b))
-    err = np.abs(got - ref)
-    worst = np.unravel_index(np.argmax(err - bound), err.shape)
-    assert (err <= bound).all(), (f"{name}: element {worst} off by {err[worst]:.3e} "
-                                  f"(bound {bound[worst]:.3e}, value {ref[worst]:.3e})")
-
-
 @pytest.mark.parametrize("path", ["strip", "tile"])
 def test_gemm_engine_rounding_bound(path):
     """The bf16 MFMA GEMMs element by element at the precision their storage
@@ -158,9 +144,10 @@ def test_gemm_engine_rounding_bound(path):
     for e in range(E):
         r0, r1 = off[e], off[e + 1]
         if r1 > r0:
-            _rounding_check(f"h[{e}]", h[r0:r1], xp[r0:r1], np.concatenate([wg[e], wu[e]], 1))
-            _rounding_check(f"yp[{e}]", yp[r0:r1], act[r0:r1], wd[e])
-        _rounding_check(f"dw_down[{e}]", dwd[e], act[r0:r1].T, dyp[r0:r1])
+            U.check_rounding_bound(f"h[{e}]", h[r0:r1], xp[r0:r1],
+                                   np.concatenate([wg[e], wu[e]], 1))
+            U.check_rounding_bound(f"yp[{e}]", yp[r0:r1], act[r0:r1], wd[e])
+        U.check_rounding_bound(f"dw_down[{e}]", dwd[e], act[r0:r1].T, dyp[r0:r1])
 
 
 def test_gemm_engine_rounding_bound_full_size():
@@ -181,6 +168,6 @@ def test_gemm_engine_rounding_bound_full_size():
         r0, r1 = off[e], off[e + 1]
         xp = x[perm[r0:r1] // w.k]  # the rows the gathered kernels read
         h, act, yp, dyp = (U.np64(t[n][r0:r1]) for n in ("h", "a", "yp", "dyp"))
-        _rounding_check(f"h[{e}]", h, xp, np.concatenate([a["Wg"][e], a["Wu"][e]], 1))
-        _rounding_check(f"yp[{e}]", yp, act, a["Wd"][e])
-        _rounding_check(f"dw_down[{e}]", U.np64(t["dw_down"][e]), act.T, dyp)
+        U.check_rounding_bound(f"h[{e}]", h, xp, np.concatenate([a["Wg"][e], a["Wu"][e]], 1))
+        U.check_rounding_bound(f"yp[{e}]", yp, act, a["Wd"][e])
+        U.check_rounding_bound(f"dw_down[{e}]", U.np64(t["dw_down"][e]), act.T, dyp)
