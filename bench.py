@@ -532,12 +532,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # calibration (untimed): one step with every kernel on the HIP-event timer
-    # to find the dominant grouped GEMM
+    # calibration (untimed): three steps with every kernel on the HIP-event
+    # timer to find the dominant grouped GEMM (the slowest on their sum: two
+    # GEMMs within a few per cent of each other would swap on one step)
     B.prof_select(None)
     B.prof_enable(True)
     B.prof_reset()
-    step()
+    for _ in range(3):
+        step()
     torch.cuda.synchronize()
     calib = {n: B.prof_read(n)[0] for n in B.prof_names()}
     dom = max((n for n in calib if n in GEMMS), key=lambda n: calib[n])
