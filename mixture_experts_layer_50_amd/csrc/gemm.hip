@@ -1824,7 +1824,12 @@ __device__ __forceinline__ void store_wave_block32(const GemmParams& p, f32x16 (
 // gemm_bf16_ws_kernel; the LDS tiles and the MFMAs are the same, so the
 // results are bit-identical.
 // ---------------------------------------------------------------------------
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate: vector memory count vm, LDS/scalar count lgkm (15:
+// no wait on it).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+constexpr int vmcnt_imm(int n) { return waitcnt_imm(n, 15); }
 
 template <int BM, int BN, int WGM, int WGN, int NPW, int NB, int AM, int BMD, int GMD, int ROLE>
 __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(GemmParams p) {
@@ -1975,23 +1980,24 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
 // ---------------------------------------------------------------------------
 // Weight gradients of experts with at most STRIP_K rows ("strip" kernel).
 // C_e = A_e^T B_e sums over expert e's rows only, and with K <= 256 one
-// workgroup holds all of them: a workgroup per (expert, 256-row block of C_e)
-// (or a part of its columns) reads its A block (256 rows of C by the
-// expert's K rows) once, into its
-// waves' registers (through the LDS, read back transposed), then streams the
-// expert's B rows through the LDS one 64-deep slice of a 128-column tile at a
-// time and writes the block's 256 x 128 output tiles along the whole row of
-// C_e.  A crosses from L2 into a CU once per block of C rows instead of once
-// per output tile: at K = 256 a 64 KB output tile costs its 64 KB of B plus a
-// share of 128 KB of A spread over the whole row, where the tile kernels read
-// 192 KB for it.  Each 64-deep slice of B, and each half of A's 256 columns
-// in the first steps, fills one of eight 16 KB LDS buffers: two tiles of B,
-// the next one sent slice by slice while the current one is multiplied, with
-// one workgroup barrier per tile.  Eight waves, two per SIMD, each own 32
-// rows of the block (their A: 64 registers) and all 128 columns of a tile,
-// and send the copies themselves.  Every 32 x 32 output block takes its MFMAs
-// in the tile kernels' order (K steps of 16 in order), so the results are the
-// same bits.
+// workgroup holds all of them.  A workgroup per (expert, 256-row block of
+// C_e, part of its columns) reads its A block (those 256 rows of C by the
+// expert's K rows) once, into its waves' registers (through the LDS, read
+// back transposed), then streams the expert's B rows through the LDS one
+// 64-deep slice of a 128-column tile at a time and writes the block's
+// 256 x 128 output tiles along the row of C_e.  A crosses from L2 into a CU
+// once per block of C rows instead of once per output tile: at K = 256 a
+// 64 KB output tile costs its 64 KB of B plus a share of 128 KB of A spread
+// over the whole row, where the tile kernels read 192 KB for it.  Eight
+// 16 KB LDS buffers: in the first steps each holds one 64-deep K slice of
+// one half (128 rows of C) of the A block; then two tiles of B, the next one
+// sent slice by slice while the current one is multiplied, with one
+// workgroup barrier per tile.  Eight waves, two per SIMD, each own 32 rows of
+// the block (their A: 64 registers) and all 128 columns of a tile, send the
+// copies themselves and stage their results 32 rows at a time.  Every
+// 32 x 32 output block takes its MFMAs in the tile kernels' order (K steps of
+// 16 in order), so the results are the same bits.  The tile-table launch
+// decides on the device which experts are the strip kernel's (zero K cost).
 //
 // The copies into the LDS are issued as inline assembly, which the compiler
 // does not track, and each tile waits for its copies with an explicit vmcnt:
@@ -2004,6 +2010,7 @@ __global__ __launch_bounds__(64 * (WGM * WGN + NPW)) void gemm_bf16_dma_kernel(G
 // ---------------------------------------------------------------------------
 constexpr int STRIP_M = 256;  // output rows per workgroup
 constexpr int STRIP_N = 128;  // columns of a B tile
+static_assert(STRIP_K >= 0 && STRIP_K <= 4 * BK, "the strip kernel holds at most four K slices");
 // Cache policy of the strip kernel's result stores: non-temporal for the
 // gate/up gradient, sc1 for the down projection's (measured: the down
 // gradient 146-149 vs 165-167 us and the gate/up gradient, which runs two
@@ -2012,11 +2019,6 @@ constexpr int STRIP_N = 128;  // columns of a B tile
 #ifndef MOE_STRIP_DOWN_CPOL
 #define MOE_STRIP_DOWN_CPOL 16
 #endif
-
-// s_waitcnt immediate: vector memory count vm, LDS/scalar count lgkm.
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
 
 // Buffer descriptor words over 2^31 - 1 bytes from `base` (as make_rsrc).
 __device__ __forceinline__ u32x4 rsrc_words(const void* base) {
