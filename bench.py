@@ -54,6 +54,14 @@ GEMMS = {
     "ffn_gateup_wgrad_gather":
                         (lambda R, d, I, El, T: 4 * R * d * I,
                          lambda R, d, I, El, T: 2 * (T * d + 2 * R * I + 2 * El * d * I)),
+    # the dY form of the backward: the rows of dYp read as g * dY[t] (A or B
+    # operand: dY itself, T rows)
+    "ffn_down_dgrad_dy":
+                        (lambda R, d, I, El, T: 2 * R * d * I,
+                         lambda R, d, I, El, T: 2 * (T * d + El * I * d + 2 * R * I + 2 * R * I)),
+    "ffn_down_wgrad_dy":
+                        (lambda R, d, I, El, T: 2 * R * I * d,
+                         lambda R, d, I, El, T: 2 * (R * I + T * d + El * I * d)),
     # the down projection with the combine in its epilogue: also reads the
     # token's rows of Yp back and writes y
     "ffn_down_fwd_combine":
@@ -154,13 +162,15 @@ def cpu_baseline(budget_s: float, dsv3_sample: bool = True):
 ROLE_NAMES = {0: "route_logits", 1: "ffn_gateup_fwd", 2: "ffn_down_fwd", 3: "ffn_down_dgrad",
               4: "ffn_gateup_dgrad", 5: "ffn_down_wgrad", 6: "ffn_gateup_wgrad", 7: "route_bwd_dw",
               8: "route_bwd_dx", 9: "ffn_gateup_fwd_gather", 10: "ffn_gateup_wgrad_gather",
-              11: "ffn_down_fwd_combine"}
+              11: "ffn_down_fwd_combine", 12: "ffn_down_dgrad_dy"}
 
 
 def gemm_role_of(kernel_name: str):
     if "gemm_bf16" not in kernel_name:
         return None
     args = kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")
+    if args[0].strip() == "true":  # the strip kernel's dY form
+        return "ffn_down_wgrad_dy"
     return ROLE_NAMES.get(int(args[-1]))
 
 
@@ -248,6 +258,16 @@ def graph_step_ms(step, replays: int):
     return ms
 
 
+def form_buffers(shape, training: bool, form: str, **kw):
+    """The layer's buffers for one FFN form: plain (the permute writes Xp),
+    gather (the FFN reads x through the token table), fused (gather, with the
+    combine in the down projection's epilogue), dy (gather, with the
+    backward's dYp rows formed from dY inside the kernels)."""
+    from mixture_experts_layer_50_amd.layer import LayerBuffers
+    return LayerBuffers(shape, training=training, gather=form != "plain", fused=form == "fused",
+                        dy_form=form == "dy", **kw)
+
+
 def kernel_averages(step, B, n: int):
     """Per-kernel averages (us) over n instrumented steps."""
     import torch
@@ -291,8 +311,7 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
         # 40 empty experts, largest group 3,275 rows)
         shape_b = B.MoEShape.make(w_main.T, w_main.d, w_main.E, w_main.k, w_main.I,
                                   dtype=w_main.dtype, gate="balanced")
-        buf = LayerBuffers(shape_b, training=False, gather=gather != "plain",
-                           fused=gather == "fused")
+        buf = form_buffers(shape_b, False, gather)
 
         def step_fwd_b():
             forward(shape_b, buf, dev["x"], None, None, dev["Wg"], dev["Wu"], dev["Wd"])
@@ -310,8 +329,7 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
         Wr3 = torch.from_numpy(a3["Wr"]).to(torch.bfloat16).cuda()
         b3 = torch.from_numpy(a3["b"]).cuda()
         shape_n = B.MoEShape.make(w3.T, w3.d, w3.E, w3.k, w3.I, dtype="bf16", gate="softmax_topk")
-        buf = LayerBuffers(shape_n, training=False, gather=gather != "plain",
-                           fused=gather == "fused")
+        buf = form_buffers(shape_n, False, gather)
 
         def step_fwd_n():
             forward(shape_n, buf, x3, Wr3, b3, dev["Wg"], dev["Wu"], dev["Wd"])
@@ -328,18 +346,17 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
     if "other_ffn" in want:  # the main workload, the FFN forms the main run did not use
         shape = B.MoEShape.make(w_main.T, w_main.d, w_main.E, w_main.k, w_main.I,
                                 dtype=w_main.dtype, gate=w_main.gate)
-        for form in ("plain", "gather", "fused"):
+        for form in ("plain", "gather", "fused", "dy"):
             if form == gather:
                 continue
-            buf = LayerBuffers(shape, training=True, gather=form != "plain",
-                               fused=form == "fused")
+            buf = form_buffers(shape, True, form)
 
             def step_other():
                 forward(shape, buf, dev["x"], None, None, dev["Wg"], dev["Wu"], dev["Wd"])
                 backward(shape, buf, dev["dY"], dev["x"], None, dev["Wg"], dev["Wu"], dev["Wd"])
 
             st = timed_steps(step_other, 10, 3)
-            key = {"plain": "plain", "gather": "gathered", "fused": "fused"}[form]
+            key = {"plain": "plain", "gather": "gathered", "fused": "fused", "dy": "dy_form"}[form]
             out[key + "_ffn_fwdbwd"] = {
                 "workload": w_main.name, "ffn": form,
                 "tokens_per_s": round(w_main.T / (st["median"] / 1e3), 1), "step_ms": st,
@@ -351,7 +368,7 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
     bias = torch.from_numpy(r["b"]).cuda()
     shape = B.MoEShape.make(wn.T, wn.d, wn.E, wn.k, wn.I, dtype="bf16", gate="softmax_topk")
     if "natural" in want:  # natural router, Qwen3 shape
-        buf = LayerBuffers(shape, training=True, gather=gather != "plain", fused=gather == "fused")
+        buf = form_buffers(shape, True, gather)
 
         def step_nat():
             forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
@@ -366,8 +383,7 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
             "kernels_us_avg": kernel_averages(step_nat, B, 3)}
         del buf
     if "natural_aux" in want:  # the same with the balancing loss (alpha 0.01)
-        buf = LayerBuffers(shape, training=True, gather=gather != "plain", fused=gather == "fused",
-                           aux_alpha=0.01)
+        buf = form_buffers(shape, True, gather, aux_alpha=0.01)
 
         def step_nat_aux():
             forward(shape, buf, dev["x"], Wr, bias, dev["Wg"], dev["Wu"], dev["Wd"])
@@ -423,8 +439,7 @@ def secondary_workloads(B, dev, w_main, gather, which="all"):
               "dY": rnd(wd.T, wd.d, sigma=wd.dy_sigma)}
         shape_d = B.MoEShape.make(wd.T, wd.d, wd.E, wd.k, wd.I, dtype="bf16", gate="balanced",
                                   e_lo=wd.e_lo, e_hi=wd.e_end)
-        buf = LayerBuffers(shape_d, training=True, gather=gather != "plain",
-                           fused=gather == "fused")
+        buf = form_buffers(shape_d, True, gather)
 
         def step_ds():
             forward(shape_d, buf, d5["x"], None, None, d5["Wg"], d5["Wu"], d5["Wd"])
@@ -455,10 +470,11 @@ def main():
     ap.add_argument("--pass", dest="pass_", choices=("default", "fwd", "fwdbwd"), default="default",
                     help="run the workload forward only or forward+backward (default: as the "
                          "workload is defined)")
-    ap.add_argument("--ffn", choices=("gather", "plain", "fused"), default="gather",
+    ap.add_argument("--ffn", choices=("gather", "plain", "fused", "dy"), default="gather",
                     help="gather: the FFN reads the rows of Xp from x through the token table "
                          "(no Xp buffer); plain: the permute writes Xp; fused: gather, and the "
-                         "combine runs in the down projection's epilogue")
+                         "combine runs in the down projection's epilogue; dy: gather, and the "
+                         "backward forms the rows of dYp from dY inside its kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the natural-router and DeepSeek-V3 rank-share timings")
@@ -509,8 +525,7 @@ def main():
     torch.cuda.synchronize()
     inputs_bytes = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    buf = LayerBuffers(shape, training=w.backward, gather=gather != "plain",
-                       fused=gather == "fused")
+    buf = form_buffers(shape, w.backward, gather)
     stream = torch.cuda.current_stream()
 
     def step():

@@ -328,6 +328,31 @@ moe_status_t moe_grouped_ffn_bwd_gather(const moe_shape_t* shape, const void* x,
                                         void* dw_gate, void* dw_up, void* dw_down, void* ws,
                                         size_t ws_bytes, moe_stream_t stream);
 
+/* a6..a10 in one call: moe_combine_bwd followed by moe_grouped_ffn_bwd_gather,
+ * with dyp written only where a kernel reads it.  Same outputs: dtopk_w as
+ * moe_combine_bwd; dxp, dw_gate, dw_up, dw_down as moe_grouped_ffn_bwd_gather
+ * on that dyp, to rounding (not bit for bit): in bf16, while every local
+ * expert has at most 256 rows, the rows g * dy[t] of dyp (g = topk_w[t,j],
+ * t*k + j = perm[p]) are formed inside the kernels -- dA's rows scaled by g
+ * in fp32 after the product dy[t] w_down^T, the rows of A scaled by g and
+ * rounded to bf16 in dw_down = sum_p (g A[p])^T dy[t] -- and dyp is never
+ * written; with a larger expert, and in fp32, dyp is written with the values
+ * moe_combine_bwd gives and read as in moe_grouped_ffn_bwd_gather.  The
+ * choice is made on the device from group_offsets.  dyp [R_cap,d] is
+ * caller-owned scratch whose contents afterwards are unspecified.  Arguments
+ * as for moe_combine_bwd and moe_grouped_ffn_bwd_gather; the workspace is
+ * moe_workspace_size(MOE_OP_FFN_BWD).  Needs T*d*element bytes < 2^31 (else
+ * MOE_ERR_UNSUPPORTED). */
+moe_status_t moe_combine_ffn_bwd_gather(const moe_shape_t* shape, const void* x,
+                                        const int32_t* perm, const int32_t* inv,
+                                        const int32_t* group_offsets, const float* topk_w,
+                                        const void* w_gate, const void* w_up,
+                                        const void* w_down, const void* h_save,
+                                        const void* a_save, const void* yp, const void* dy,
+                                        void* dyp, float* dtopk_w, void* dxp, void* dw_gate,
+                                        void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                        moe_stream_t stream);
+
 /* a11 -- permute backward: dx[t] = sum_j dxp[inv[t*k+j]] over slots with
  * inv >= 0, ascending j, fp32 accumulation (tokens with no slot get 0).
  * dxp [R_cap,d]; dx [T,d] (overwritten). */

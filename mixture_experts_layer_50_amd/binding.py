@@ -31,7 +31,8 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_
            "moe_prof_select", "moe_prof_reset", "moe_prof_read", "moe_prof_names",
            "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd",
            "moe_aux_loss", "moe_route_bwd_aux", "moe_grouped_ffn_fwd_gather_noalloc",
-           "moe_grouped_ffn_fwd_fused", "moe_route_permute", "moe_small_fwd"]
+           "moe_grouped_ffn_fwd_fused", "moe_route_permute", "moe_small_fwd",
+           "moe_combine_ffn_bwd_gather"]
 
 
 class MoEError(RuntimeError):
@@ -100,6 +101,7 @@ def load_library() -> ctypes.CDLL:
         "moe_small_fwd": [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_ffn_small_fwd": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_combine_ffn_bwd_gather": [S] + [P] * 19 + [SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
         "moe_route_bwd": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_aux_loss": [S, P, P, ctypes.c_float, P, P, P, SZ, P],
@@ -239,6 +241,16 @@ def moe_grouped_ffn_bwd_gather(shape, x, perm, group_offsets, w_gate, w_up, w_do
         ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(group_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(dyp), _ptr(dxp), _ptr(dw_gate),
         _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_combine_ffn_bwd_gather(shape, x, perm, inv, group_offsets, topk_w, w_gate, w_up, w_down,
+                               h_save, a_save, yp, dy, dyp, dtopk_w, dxp, dw_gate, dw_up, dw_down,
+                               ws, stream=None):
+    _check("moe_combine_ffn_bwd_gather", load_library().moe_combine_ffn_bwd_gather(
+        ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(inv), _ptr(group_offsets), _ptr(topk_w),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h_save), _ptr(a_save), _ptr(yp), _ptr(dy),
+        _ptr(dyp), _ptr(dtopk_w), _ptr(dxp), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
 
 
 def moe_permute_bwd(shape, dxp, inv, dx, stream=None):

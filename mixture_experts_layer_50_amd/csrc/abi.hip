@@ -732,12 +732,25 @@ extern "C" moe_status_t moe_combine_bwd(const moe_shape_t* shape, const void* dy
 
 namespace {
 
+// The combine backward run inside the gathered FFN backward
+// (moe_combine_ffn_bwd_gather): after the tile-table launch, so that dyp is
+// written only when a kernel reads it; where it is not, the kernels form the
+// rows g * dY[t] of dYp from dY through the token table.
+struct DyForm {
+  const void* dy;
+  const void* yp;
+  const int32_t* inv;
+  const float* topk_w;
+  float* dtopk_w;
+};
+
 // Backward FFN over Xp rows: xp itself, or (gather) x read through perm.
 moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, const void* xp,
                      const int32_t* perm, const int32_t* group_offsets, const void* w_gate,
                      const void* w_up, const void* w_down, const void* h_save,
                      const void* a_save, const void* dyp, void* dxp, void* dw_gate, void* dw_up,
-                     void* dw_down, void* ws, size_t ws_bytes_, moe_stream_t stream) {
+                     void* dw_down, void* ws, size_t ws_bytes_, moe_stream_t stream,
+                     const DyForm* dyf = nullptr) {
   Dims D;
   MOE_TRY(check_shape(shape, fn, &D));
   if (!gather) perm = nullptr;
@@ -745,6 +758,9 @@ moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, cons
     MOE_TRY(need(fn, {{"perm", perm}}));
     MOE_TRY(check_gather(fn, D));
   }
+  if (dyf)
+    MOE_TRY(need(fn, {{"dy", dyf->dy}, {"yp", dyf->yp}, {"inv", dyf->inv},
+                      {"topk_w", dyf->topk_w}, {"dtopk_w", dyf->dtopk_w}}));
   MOE_TRY(need(fn, {{gather ? "x" : "xp", xp}, {"group_offsets", group_offsets},
                     {"w_gate", w_gate}, {"w_up", w_up}, {"w_down", w_down}, {"h_save", h_save}, {"a_save", a_save},
                     {"dyp", dyp}, {"dxp", dxp}, {"dw_gate", dw_gate}, {"dw_up", dw_up},
@@ -762,6 +778,16 @@ moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, cons
   // gradient reads dH right after it is written, and dXp is written last, so
   // that the permute backward that follows reads it back from that cache.
   if (D.bf16) MOE_TRY(tt.ensure());
+  // the bf16 kernels on g * dY[t] (dy_k); the fp32 path reads dYp throughout
+  const bool dy_k = dyf && D.bf16;
+  if (dyf) {
+    // a6: the gate gradient; dYp only when the weight gradients' tile kernels
+    // have work (kcost[groups] > 0: some expert has more than STRIP_K rows),
+    // and always in fp32
+    MOE_TRY(launch_combine_bwd(dyf->dy, dyf->yp, dyf->inv, dyf->topk_w, D.T, D.d, D.k, D.eb,
+                               const_cast<void*>(dyp), dyf->dtopk_w, s,
+                               dy_k ? tt.kcost() + D.E_loc : nullptr));
+  }
   {  // a8: dWd[e] = A_e^T dYp_e
     GemmParams p{};
     p.A = a_save; p.lda = D.I;
@@ -772,18 +798,35 @@ moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, cons
     p.m_tiles = (int)ceil_div(D.I, tile_bm(t)); p.n_tiles = (int)ceil_div(D.d, tile_bn(t));
     p.C0 = dw_down; p.ldc = D.d; p.c_estride = (int64_t)D.I * D.d;
     if (D.bf16) p.kcost = tt.kcost();
-    MOE_TRY(launch_gemm(D.bf16, R_DOWN_WGRAD, p, p.m_tiles, s));
+    if (dy_k) {  // the strip kernel reads g * dY[t]; the tile kernel dYp
+      p.B0 = dyf->dy;
+      MOE_TRY(tt.rows(&p));
+      p.row_gate = dyf->topk_w;
+      p.row_slot = perm;
+      MOE_TRY(launch_down_wgrad_dy(p, dyp, p.m_tiles, s));
+    } else {
+      MOE_TRY(launch_gemm(D.bf16, R_DOWN_WGRAD, p, p.m_tiles, s));
+    }
   }
   {  // a7: dA = dYp Wd^T with the dSwiGLU epilogue -> dH = [dHg | dHu]
+    const GemmRole r = dy_k ? R_DOWN_DGRAD_GATHER : R_DOWN_DGRAD;
     GemmParams p{};
     p.A = dyp; p.lda = D.d;
+    if (dy_k) {  // dA = g * (dY[t] Wd^T), or dYp Wd^T where dYp was written
+      p.A = dyf->dy;
+      MOE_TRY(tt.rows(&p));
+      p.row_gate = dyf->topk_w;
+      p.row_slot = perm;
+      p.a_alt = dyp;
+      p.kcost = tt.kcost();
+    }
     p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
     p.N = D.I; p.K = D.d;
     p.off = group_offsets; p.groups = D.E_loc;
-    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(R_DOWN_DGRAD, D.I)));
+    p.n_tiles = (int)ceil_div(D.I, tile_bn(role_tile(r, D.I)));
     p.C0 = dH; p.aux = h_save; p.I = D.I;
-    if (D.bf16) MOE_TRY(tt.get(R_DOWN_DGRAD, &p.tiles));
-    MOE_TRY(launch_gemm(D.bf16, R_DOWN_DGRAD, p, rows_or_tiles(R_DOWN_DGRAD), s));
+    if (D.bf16) MOE_TRY(tt.get(r, &p.tiles));
+    MOE_TRY(launch_gemm(D.bf16, r, p, rows_or_tiles(r), s));
   }
   {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
     const GemmRole gw = perm ? R_GATEUP_WGRAD_GATHER : R_GATEUP_WGRAD;
@@ -839,6 +882,18 @@ extern "C" moe_status_t moe_grouped_ffn_bwd_gather(const moe_shape_t* shape, con
                                                    moe_stream_t stream) {
   return ffn_bwd("moe_grouped_ffn_bwd_gather", true, shape, x, perm, group_offsets, w_gate, w_up,
                  w_down, h_save, a_save, dyp, dxp, dw_gate, dw_up, dw_down, ws, ws_bytes_, stream);
+}
+
+extern "C" moe_status_t moe_combine_ffn_bwd_gather(
+    const moe_shape_t* shape, const void* x, const int32_t* perm, const int32_t* inv,
+    const int32_t* group_offsets, const float* topk_w, const void* w_gate, const void* w_up,
+    const void* w_down, const void* h_save, const void* a_save, const void* yp, const void* dy,
+    void* dyp, float* dtopk_w, void* dxp, void* dw_gate, void* dw_up, void* dw_down, void* ws,
+    size_t ws_bytes_, moe_stream_t stream) {
+  const DyForm dyf{dy, yp, inv, topk_w, dtopk_w};
+  return ffn_bwd("moe_combine_ffn_bwd_gather", true, shape, x, perm, group_offsets, w_gate, w_up,
+                 w_down, h_save, a_save, dyp, dxp, dw_gate, dw_up, dw_down, ws, ws_bytes_, stream,
+                 &dyf);
 }
 
 extern "C" moe_status_t moe_permute_bwd(const moe_shape_t* shape, const void* dxp, const int32_t* inv,

@@ -53,10 +53,20 @@ struct GemmParams {
                        // first; the tile kernels then neither read nor write the experts of
                        // zero K cost (the strip kernel's)
   int col_parts;       // strip kernel: parts (of whole column tiles) a row block is split in
+  // R_DOWN_DGRAD_GATHER and the strip kernel's dY form: the gate weight of
+  // routed row p is row_gate[row_slot[p]] (row_slot = perm: t*k + j)
+  const float* row_gate;
+  const int32_t* row_slot;
+  // R_DOWN_DGRAD_GATHER: the materialised dYp.  When the tile-table launch
+  // gave the weight gradients' tile kernels any expert (kcost[groups] > 0),
+  // the combine backward has written it and the kernel reads its rows in
+  // order, with no gate weight; else A = dY through a_rows, scaled by row_gate.
+  const void* a_alt;
   const int32_t* tiles;// G_MROWS tile table: tiles[0] = count, then (expert, first row) pairs
   const int32_t* kcost;// G_KROWS (optional): prefix sums [groups+1] of the per-expert tile cost
                        // (K slices + a fixed part), for balancing the persistent kernels; all
-                       // zero when every expert fits the strip kernel
+                       // zero when every expert fits the strip kernel (R_DOWN_DGRAD_GATHER
+                       // reads kcost[groups] to pick its A source)
   int groups;          // number of local experts
   int m_tiles, n_tiles;
   void* C0;
@@ -117,7 +127,11 @@ enum GemmRole {
   R_GATEUP_WGRAD_GATHER = 10,
   // R_DOWN_FWD with the combine in its epilogue (dispatch's counterpart, the
   // combine, fused into the expert GEMM)
-  R_DOWN_FWD_COMBINE = 11
+  R_DOWN_FWD_COMBINE = 11,
+  // R_DOWN_DGRAD on the rows g * dY[t] of dYp formed in the kernel: dY read
+  // through the token table (a_rows), the accumulator rows scaled by g in the
+  // epilogue; or on dYp itself (a_alt), as the device decides (bf16 only)
+  R_DOWN_DGRAD_GATHER = 12
 };
 
 // Tile shape each role runs with (bf16), for a GEMM with n output columns
@@ -132,6 +146,16 @@ const char* role_name(GemmRole role);
 // tile_bm(role_tile(role)); max_m_tiles bounds its entries (fp32: the row count).
 moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
                          hipStream_t s);
+
+// The down projection's weight gradient with dYp never written (bf16):
+// dWd = sum_p (g_p A[p])^T dY[tok[p]].  The strip kernel reads dY through the
+// token table (p.a_rows) and scales its A fragments by the gate weights
+// (p.row_gate / p.row_slot); when the device gave the tile kernels any expert
+// (one has more than STRIP_K rows), they run R_DOWN_WGRAD on `dyp`, which
+// the combine backward has then written.  p: R_DOWN_WGRAD's parameters with
+// B0 = dY.
+moe_status_t launch_down_wgrad_dy(const GemmParams& p, const void* dyp, int max_m_tiles,
+                                  hipStream_t s);
 
 // Tile tables for G_MROWS, for 256-row and for 128-row tiles (one launch):
 // tiles[0] = number of M tiles, then for each tile (expert, first row) in

@@ -118,7 +118,8 @@ __device__ __forceinline__ int ld_table(const int32_t* tab, int i) { return ((ci
 //
 // GATHER: tile row r is row rows[row0 + r] of the source (the rows of Xp
 // read from x through the token table); the row numbers are loaded once per
-// tile.
+// tile.  rows == NULL: row row0 + r, addressed from the tile's first row as
+// without GATHER (the byte offsets stay within one tile).
 template <int ROWS, bool TWO, int NT, int CPOL, bool GATHER, bool FULLK>
 struct LoaderKC {
   static_assert(!(GATHER && TWO), "a gathered operand has one source");
@@ -132,7 +133,7 @@ struct LoaderKC {
   __device__ __forceinline__ void init(const bf16_t* s0, const bf16_t* s1, int64_t ld, int row0,
                                        int row_hi, int k_lo_, int k_hi_, int ksplit_, int tid,
                                        const int32_t* rows) {
-    p0 = GATHER ? s0 : s0 + (int64_t)row0 * ld;
+    p0 = GATHER && rows ? s0 : s0 + (int64_t)row0 * ld;
     p1 = TWO ? s1 + (int64_t)row0 * ld : p0;
     rs0 = make_rsrc(p0);
     rs1 = make_rsrc(p1);
@@ -144,7 +145,7 @@ struct LoaderKC {
       int q = tid + NT * i;
       int row = q >> 3;
       bool ok = (CH % NT == 0 || q < CH) && row0 + row < row_hi;
-      if (GATHER) row = ok ? rows[row0 + row] : 0;
+      if (GATHER && rows) row = ok ? rows[row0 + row] : 0;
       voff[i] = ok ? (int)(((int64_t)row * ld + (q & 7) * 8) * 2) : OOB;
     }
   }
@@ -575,7 +576,9 @@ __device__ __forceinline__ void xcd_tile_range(const GemmParams& p, int count, i
 // stream through once and are loaded non-temporal; the activation rows (A)
 // are re-read by every column tile of the expert and stay cached.
 // The gather roles read the rows of A through a_rows.
-constexpr bool gathers_a(int role) { return role == R_GATEUP_FWD_GATHER || role == R_GATEUP_WGRAD_GATHER; }
+constexpr bool gathers_a(int role) {
+  return role == R_GATEUP_FWD_GATHER || role == R_GATEUP_WGRAD_GATHER || role == R_DOWN_DGRAD_GATHER;
+}
 // Roles whose k-contiguous operands have K a multiple of 64 (d or I, which
 // the entry points require to be); the router's input gradient runs over the
 // E expert logits instead.
@@ -600,17 +603,28 @@ struct DmaLoaders {
   static constexpr int LOADS = LA::NLOAD + LB::NLOAD;  // per producer thread and slice
 };
 
+// R_DOWN_DGRAD_GATHER reads the materialised dYp (a_alt) when the weight
+// gradients' tile kernels have work (see GemmParams::a_alt).
+__device__ __forceinline__ bool reads_alt(const GemmParams& p) {
+  return p.a_alt != nullptr && ld_table(p.kcost, p.groups) != 0;
+}
+
 template <int GMD, int B2, typename LA, typename LB>
 __device__ __forceinline__ void init_loaders(const GemmParams& p, const TileDesc& t, LA& la, LB& lb,
                                              int tid) {
-  const bf16_t* A = static_cast<const bf16_t*>(p.A);
+  // (a select of the two pointer values: a select of the two kernel
+  // arguments as lvalues put them in scratch memory)
+  const bool alt = reads_alt(p);
+  const void* a_main = p.A;
+  const void* a_dyp = p.a_alt;
+  const bf16_t* A = static_cast<const bf16_t*>(alt ? a_dyp : a_main);
   const bf16_t* B0 = static_cast<const bf16_t*>(p.B0);
   const bf16_t* B1 = static_cast<const bf16_t*>(p.B1);
   if (GMD == G_MROWS) {
     B0 += (int64_t)t.e * p.b_estride;
     if (B2 != B2_NONE) B1 += (int64_t)t.e * p.b_estride;
   }
-  la.init(A, A, p.lda, t.m_lo, t.m_hi, t.k_lo, t.k_hi, 0, tid, p.a_rows);
+  la.init(A, A, p.lda, t.m_lo, t.m_hi, t.k_lo, t.k_hi, 0, tid, alt ? nullptr : p.a_rows);
   // columns are bounded in the B source's column space
   lb.init(B0, B1, p.ldb, t.n0, p.N, t.k_lo, t.k_hi, p.k_split, tid, nullptr);
 }
@@ -774,6 +788,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[FM][
             const bf16_t* H = static_cast<const bf16_t*>(p.aux);
             bf16_t* dH = static_cast<bf16_t*>(p.C0);
             const int64_t I = p.I;
+            if (p.row_gate && !reads_alt(p)) {  // dA rows of g * dY[t]: the gate weight here
+              const float gw = p.row_gate[p.row_slot[m]];
+#pragma unroll
+              for (int s = 0; s < 4; ++s) v[s] *= gw;
+            }
             uint2 hg = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + n);
             uint2 hu = *reinterpret_cast<const uint2*>(H + (int64_t)m * 2 * I + I + n);
             float g[4] = {bf2f((bf16_t)(hg.x & 0xffff)), bf2f((bf16_t)(hg.x >> 16)),
@@ -1032,11 +1051,15 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
       }
     }
     __syncthreads();
-    // 2. the band's waves turn (dA, Hg, Hu) into (dHg, dHu) in place
+    // 2. the band's waves turn (dA, Hg, Hu) into (dHg, dHu) in place (dA rows
+    // of g * dY[t] take their gate weight g here; rows past m_hi read the
+    // last valid row's and are not stored)
     if (wm == rd) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = i * 32 + (lane & 31);
+        const float gw = p.row_gate && !reads_alt(p) ? p.row_gate[p.row_slot[min(mb + r, m_hi - 1)]]
+                                                     : 1.0f;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -1052,7 +1075,7 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
             float dg[4], du[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const float v = acc[i][j][4 * q + t];
+              const float v = acc[i][j][4 * q + t] * gw;
               const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[t]));
               dg[t] = v * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
               du[t] = v * g[t] * sg;
@@ -2042,8 +2065,12 @@ __device__ __forceinline__ void dma16_untracked(u32x4 r, uint32_t lds_byte, int 
       : "memory", "m0");
 }
 
-template <int ROLE>
+// GDY (the down projection's gradient with dYp never written): B row k is
+// row a_rows[k] of dY and A row k is scaled by the row's gate weight once, in
+// the registers (bf16, round to nearest even).
+template <bool GDY, int ROLE>
 __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
+  static_assert(!GDY || ROLE == R_DOWN_WGRAD, "the dY form is the down projection's");
   constexpr bool AG = gathers_a(ROLE);
   constexpr int OCP = ROLE == R_DOWN_WGRAD ? MOE_STRIP_DOWN_CPOL : MOE_OUT_CPOL;
   constexpr int SL = BK * STRIP_N;  // one buffer: [64][128] bf16 (the KN layout)
@@ -2108,6 +2135,21 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
         dma16_untracked(ra, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? vo[bi >> 1][i] + h * STRIP_N * 2 : OOB);
       }
   }
+  // GDY: the K rows' gate weights and dY rows (byte offsets of the lane's
+  // chunks' rows, OOB past the expert's rows)
+  float* gs = reinterpret_cast<float*>(stage_all);
+  int bro[4][2];
+  if constexpr (GDY) {
+    if (tid < 4 * BK) gs[tid] = tid < kn ? p.row_gate[p.row_slot[k_lo + tid]] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k = s * BK + crow[i];
+        const int64_t row = kn > 0 ? p.a_rows[min(k_lo + k, k_hi - 1)] : 0;
+        bro[s][i] = k < kn ? (int)(row * p.ldb * 2) : OOB;
+      }
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   __syncthreads();
   bf16x8 af[16];  // the wave's 32 rows of A over K, one fragment per K step of 16
@@ -2117,6 +2159,17 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) af[4 * s + ks] = frag_kn<STRIP_N>(sbuf + (2 * s + h) * SL, mb, ks, lane);
+    if constexpr (GDY) {
+      // the fragment of K step ks holds rows 16 ks + 8 (lane / 32) + 0..7
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const float4 g0 = *reinterpret_cast<const float4*>(gs + 16 * ks + 8 * (lane >> 5));
+        const float4 g1 = *reinterpret_cast<const float4*>(gs + 16 * ks + 8 * (lane >> 5) + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) af[ks][j] = (__bf16)((float)af[ks][j] * gv[j]);
+      }
+    }
   }
   __syncthreads();  // every wave has its A before B overwrites the buffers
 
@@ -2128,12 +2181,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_strip_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) bo[i] = (int)(((int64_t)crow[i] * p.ldb + ccol[i]) * 2);
   auto send_b = [&](int bi, int t, int s) __attribute__((always_inline)) {
-    const u32x4 rb = rsrc_words(B + (int64_t)(k_lo + s * BK) * p.ldb);
+    const u32x4 rb = rsrc_words(GDY ? B : B + (int64_t)(k_lo + s * BK) * p.ldb);
     const int c = col_tile(t);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const bool ok = s * BK + crow[i] < kn && c * STRIP_N + ccol[i] < p.N;
-      dma16_untracked(rb, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? bo[i] + c * STRIP_N * 2 : OOB);
+      const int o = GDY ? bro[s][i] + (c * STRIP_N + ccol[i]) * 2 : bo[i] + c * STRIP_N * 2;
+      dma16_untracked(rb, lds0 + (bi * SL + 512 * i * 8) * 2, ok ? o : OOB);
     }
   };
 #pragma unroll
@@ -2428,7 +2482,9 @@ int tile_bn(TileCfg cfg) {
   X(R_GATEUP_WGRAD_GATHER, "ffn_gateup_wgrad_gather", MOE_WGRAD_TILE, A_MC, B_NC, G_KROWS, B2_NONE, \
     EPI_STORE)                                                                                     \
   X(R_DOWN_FWD_COMBINE, "ffn_down_fwd_combine", MOE_TILE_DOWN_FWD, A_KC, B_NC, G_MROWS, B2_NONE,    \
-    EPI_STORE)
+    EPI_STORE)                                                                                     \
+  X(R_DOWN_DGRAD_GATHER, "ffn_down_dgrad_dy", MOE_TILE_DOWN_DGRAD, A_KC, B_KC, G_MROWS, B2_NONE,    \
+    EPI_DSWIGLU)
 
 // A role may take a second tile shape when its N (output columns) is large:
 // role, tile, smallest N (build-time tunable).
@@ -2437,7 +2493,9 @@ int tile_bn(TileCfg cfg) {
 #ifndef MOE_DOWN_DGRAD_WIDE_N
 #define MOE_DOWN_DGRAD_WIDE_N 768
 #endif
-#define MOE_GEMM_ALT_TILES(X) X(R_DOWN_DGRAD, TILE_256x256, MOE_DOWN_DGRAD_WIDE_N)
+#define MOE_GEMM_ALT_TILES(X)                              \
+  X(R_DOWN_DGRAD, TILE_256x256, MOE_DOWN_DGRAD_WIDE_N) \
+  X(R_DOWN_DGRAD_GATHER, TILE_256x256, MOE_DOWN_DGRAD_WIDE_N)
 
 constexpr int role_alt_tile(GemmRole role) {
 #define X(r, t, nmin) \
@@ -2614,11 +2672,14 @@ static int strip_column_parts(const GemmParams& p) {
   return best;
 }
 
-moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
-                         hipStream_t s) {
+static moe_status_t launch_gemm_kernels(bool is_bf16, GemmRole role, const GemmParams& p,
+                                        int max_m_tiles, hipStream_t s) {
   const char* name = role_name(role);
-  ProfScope prof(name, s);
   if (!is_bf16) {
+    if (role == R_DOWN_DGRAD_GATHER) {
+      set_error("GEMM %s: bf16 only", name);
+      return MOE_ERR_UNSUPPORTED;
+    }
     // rows to cover: G_MROWS row capacity (passed as max_m_tiles), else M
     switch (role) {
 #define X(r, n, t, a, b, g, t2, e)                        \
@@ -2636,7 +2697,7 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
   // weight gradients: the experts with at most STRIP_K rows in the strip
   // kernel first, then the others in the role's tile kernel
   GemmParams q = p;
-  if (STRIP_K > 0 && p.off != nullptr && p.kcost != nullptr && p.groups > 0 && p.M > 0 &&
+  if (STRIP_K > 0 && !p.k_strip && p.off != nullptr && p.kcost != nullptr && p.groups > 0 && p.M > 0 &&
       (role == R_DOWN_WGRAD || role == R_GATEUP_WGRAD || role == R_GATEUP_WGRAD_GATHER)) {
     GemmParams sp = p;
     sp.col_parts = strip_column_parts(p);
@@ -2645,9 +2706,10 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
       set_error("GEMM %s: grid too large", name);
       return MOE_ERR_UNSUPPORTED;
     }
-    if (role == R_DOWN_WGRAD) gemm_bf16_strip_kernel<R_DOWN_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
-    else if (role == R_GATEUP_WGRAD) gemm_bf16_strip_kernel<R_GATEUP_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
-    else gemm_bf16_strip_kernel<R_GATEUP_WGRAD_GATHER><<<(int)grid, 512, 0, s>>>(sp);
+    if (role == R_DOWN_WGRAD) gemm_bf16_strip_kernel<false, R_DOWN_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
+    else if (role == R_GATEUP_WGRAD)
+      gemm_bf16_strip_kernel<false, R_GATEUP_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
+    else gemm_bf16_strip_kernel<false, R_GATEUP_WGRAD_GATHER><<<(int)grid, 512, 0, s>>>(sp);
     const moe_status_t st = check_launch(name);
     if (st != MOE_OK) return st;
     q.k_strip = 1;
@@ -2670,6 +2732,43 @@ moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int m
 #undef X
   }
   return check_launch(name);
+}
+
+moe_status_t launch_gemm(bool is_bf16, GemmRole role, const GemmParams& p, int max_m_tiles,
+                         hipStream_t s) {
+  ProfScope prof(role_name(role), s);
+  return launch_gemm_kernels(is_bf16, role, p, max_m_tiles, s);
+}
+
+moe_status_t launch_down_wgrad_dy(const GemmParams& p, const void* dyp, int max_m_tiles,
+                                  hipStream_t s) {
+  const char* name = "ffn_down_wgrad_dy";
+  if (STRIP_K <= 0 || !p.off || !p.kcost || !p.a_rows || !p.row_gate || !p.row_slot || !dyp) {
+    set_error("GEMM %s (dY form): needs offsets, K costs, the token table, the gate weights "
+              "and dYp, and the strip kernel", name);
+    return MOE_ERR_ARG;
+  }
+  ProfScope prof(name, s);
+  if (p.groups <= 0 || p.M <= 0) return MOE_OK;
+  GemmParams sp = p;
+  sp.col_parts = strip_column_parts(p);
+  const int64_t grid = (int64_t)p.groups * ceil_div(p.M, STRIP_M) * sp.col_parts;
+  if (grid > 0x7fffffff) {
+    set_error("GEMM %s: grid too large", name);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  gemm_bf16_strip_kernel<true, R_DOWN_WGRAD><<<(int)grid, 512, 0, s>>>(sp);
+  const moe_status_t st = check_launch(name);
+  if (st != MOE_OK) return st;
+  // the experts of nonzero K cost (all of them, when one has more than
+  // STRIP_K rows) in the tile kernel, on dYp
+  GemmParams q = p;
+  q.B0 = dyp;
+  q.a_rows = nullptr;
+  q.row_gate = nullptr;
+  q.row_slot = nullptr;
+  q.k_strip = 1;
+  return launch_gemm_kernels(true, R_DOWN_WGRAD, q, max_m_tiles, s);
 }
 
 }  // namespace moe

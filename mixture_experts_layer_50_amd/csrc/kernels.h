@@ -60,9 +60,11 @@ moe_status_t launch_permute(const int32_t* idx, const void* x, int T, int d, int
 // y[t] = sum_j w[t,j] * src[inv[t*k+j]] (w == NULL: weight 1), fp32 accumulation.
 moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float* w, int T, int d,
                                int k, int elt_bytes, void* y, hipStream_t s, const char* name);
+// dyp[inv[t*k+j]] = w[t,j] dy[t] and dw[t,j] = <dy[t], yp[inv[t*k+j]]>; with
+// dyp_flag (device memory), dyp is written only when *dyp_flag is nonzero.
 moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv, const float* w,
                                 int T, int d, int k, int elt_bytes, void* dyp, float* dw,
-                                hipStream_t s);
+                                hipStream_t s, const int32_t* dyp_flag = nullptr);
 
 // small.hip: the small-batch FFN (no sort): y[t] = sum_j w[t,j] FFN_e(x[t]) over
 // the local, first-occurrence slots.  Workspace: fp32 gate/up partial sums

@@ -307,18 +307,20 @@ moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float*
   return check_launch(name);
 }
 
-// dyp[inv[t,j]] = w[t,j] * dy[t];  dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when dropped).
+// dyp[inv[t,j]] = w[t,j] * dy[t] (unless dyp_flag points to a zero);
+// dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when dropped).
 // One wavefront per token, slot data broadcast from lane j as above (the
 // chunk loop over whole wavefronts of chunks, all lanes active).
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const uint4* yp,
                                                           const int32_t* inv, const float* w,
                                                           int Tn, int k, int chunks, uint4* dyp,
-                                                          float* dw) {
+                                                          const int32_t* dyp_flag, float* dw) {
   constexpr int N = Chunk<T>::N;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
+  if (dyp_flag && *dyp_flag == 0) dyp = nullptr;  // no kernel after this one reads dyp
   const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
   const float myw = lane < k ? w[(int64_t)t * k + lane] : 0.0f;
   float part[MAXK];
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
           o[i] = g * fy[i];
         }
         part[j] += a;  // lanes past the last chunk add zeros
-        if (ok) dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
+        if (ok && dyp) dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
       }
     }
   }
@@ -372,18 +374,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
 
 moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv, const float* w,
                                 int T, int d, int k, int elt_bytes, void* dyp, float* dw,
-                                hipStream_t s) {
+                                hipStream_t s, const int32_t* dyp_flag) {
   ProfScope prof("combine_bwd", s);
   const int chunks = d * elt_bytes / 16;
   const unsigned grid = (unsigned)ceil_div(T, 4);
   if (elt_bytes == 2)
     combine_bwd_kernel<bf16_t><<<grid, 256, 0, s>>>(
         static_cast<const uint4*>(dy), static_cast<const uint4*>(yp), inv, w, T, k, chunks,
-        static_cast<uint4*>(dyp), dw);
+        static_cast<uint4*>(dyp), dyp_flag, dw);
   else
     combine_bwd_kernel<float><<<grid, 256, 0, s>>>(
         static_cast<const uint4*>(dy), static_cast<const uint4*>(yp), inv, w, T, k, chunks,
-        static_cast<uint4*>(dyp), dw);
+        static_cast<uint4*>(dyp), dyp_flag, dw);
   return check_launch("combine_bwd_kernel");
 }
 

@@ -25,10 +25,15 @@ class LayerBuffers:
     gather: bool = False  # FFN reads x through perm (the _gather calls); no Xp buffer
     fused: bool = False   # gathered FFN forward with the combine in its epilogue (implies gather)
     aux_alpha: Optional[float] = None  # router balancing loss weight (softmax top-k gate)
+    # gathered backward with the combine backward inside it
+    # (moe_combine_ffn_bwd_gather): dYp written only where a kernel reads it,
+    # else its rows formed from dY and the gate weights inside the kernels
+    # (implies gather)
+    dy_form: bool = False
     t: Dict[str, torch.Tensor] = field(default_factory=dict)
 
     def __post_init__(self):
-        if self.fused:
+        if self.fused or self.dy_form:
             self.gather = True
         s, dev = self.shape, self.device
         dt = torch_dtype(s)
@@ -151,12 +156,20 @@ def backward(shape: B.MoEShape, buf: LayerBuffers, dy, x, w_router, w_gate, w_up
     """combine_bwd -> grouped FFN bwd -> permute_bwd -> route_bwd (with the
     balancing loss's gradient when buf.aux_alpha is set)."""
     t = buf.t
-    B.moe_combine_bwd(shape, dy, t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"], stream)
-    if buf.gather:
+    if buf.dy_form:  # dYp is the call's scratch, written only where a kernel reads it
+        B.moe_combine_ffn_bwd_gather(shape, x, t["perm"], t["inv"], t["offsets"], t["topk_w"],
+                                     w_gate, w_up, w_down, t["h"], t["a"], t["yp"], dy, t["dyp"],
+                                     t["dtopk_w"], t["dxp"], t["dw_gate"], t["dw_up"],
+                                     t["dw_down"], t["ws_ffn_bwd"], stream)
+    elif buf.gather:
+        B.moe_combine_bwd(shape, dy, t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"],
+                          stream)
         B.moe_grouped_ffn_bwd_gather(shape, x, t["perm"], t["offsets"], w_gate, w_up, w_down,
                                      t["h"], t["a"], t["dyp"], t["dxp"], t["dw_gate"],
                                      t["dw_up"], t["dw_down"], t["ws_ffn_bwd"], stream)
     else:
+        B.moe_combine_bwd(shape, dy, t["yp"], t["inv"], t["topk_w"], t["dyp"], t["dtopk_w"],
+                          stream)
         B.moe_grouped_ffn_bwd(shape, t["xp"], t["offsets"], w_gate, w_up, w_down, t["h"], t["a"],
                               t["dyp"], t["dxp"], t["dw_gate"], t["dw_up"], t["dw_down"],
                               t["ws_ffn_bwd"], stream)

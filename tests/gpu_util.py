@@ -28,9 +28,10 @@ def upload(w: MI.Workload, arrays):
 
 
 def run_layer(w: MI.Workload, dev, R_cap=0, training=True, poison=False, gather=False,
-              aux_alpha=None, fused=False):
+              aux_alpha=None, fused=False, dy_form=False):
     s = shape_of(w, R_cap)
-    buf = LayerBuffers(s, training=training, gather=gather, aux_alpha=aux_alpha, fused=fused)
+    buf = LayerBuffers(s, training=training, gather=gather, aux_alpha=aux_alpha, fused=fused,
+                       dy_form=dy_form)
     if poison:
         # (under the balanced gate the router gradients are constants the
         # layer zeroes once at allocation; the backward does not rewrite them)
@@ -104,8 +105,9 @@ def oracle_full(w: MI.Workload, a, R_cap=None):
     return f, bw
 
 
-def compare_full(w: MI.Workload, a, buf, f, bw):
-    """Element-by-element comparison of every output with the oracle."""
+def compare_full(w: MI.Workload, a, buf, f, bw, check_dyp=True):
+    """Element-by-element comparison of every output with the oracle (dyp
+    left out with check_dyp=False: the dY form's scratch)."""
     tol = TOL[w.dtype]
     t = buf.t
     R = int(f["offsets"][-1])
@@ -127,7 +129,8 @@ def compare_full(w: MI.Workload, a, buf, f, bw):
     out["y"] = check("y", np64(t["y"]), f["y"], tol)
     if bw is None:
         return out
-    out["dyp"] = check("dyp", np64(t["dyp"][:R]), bw["dYp"], tol)
+    if check_dyp:
+        out["dyp"] = check("dyp", np64(t["dyp"][:R]), bw["dYp"], tol)
     out["dtopk_w"] = check("dtopk_w", np64(t["dtopk_w"]), bw["dG"], tol)
     out["dxp"] = check("dxp", np64(t["dxp"][:R]), bw["dXp"], tol)
     for gname, oname in (("dw_gate", "dWg"), ("dw_up", "dWu"), ("dw_down", "dWd")):
@@ -161,9 +164,10 @@ def subset_rows(f, tokens, k):
     return rows, inv_sub, sub_off
 
 
-def compare_sampled(w: MI.Workload, a, buf, tokens, experts, route_full=True):
+def compare_sampled(w: MI.Workload, a, buf, tokens, experts, route_full=True, check_dyp=True):
     """Full-size check on sampled tokens (every row they touch) and on the
-    weight gradients of sampled experts (every row of those experts)."""
+    weight gradients of sampled experts (every row of those experts); dyp
+    left out with check_dyp=False."""
     tol = TOL[w.dtype]
     t = buf.t
     x = a["x"]
@@ -198,7 +202,8 @@ def compare_sampled(w: MI.Workload, a, buf, tokens, experts, route_full=True):
     if "dY" not in a:
         return
     dYp, dG = O.combine_bwd(a["dY"][tokens], ff["Yp"], inv_sub, gs, len(tokens), w.k)
-    check("dyp(rows)", np64(t["dyp"][rsel]), dYp, tol)
+    if check_dyp:
+        check("dyp(rows)", np64(t["dyp"][rsel]), dYp, tol)
     check("dtopk_w(tokens)", np64(t["dtopk_w"][tsel]), dG, tol)
     fb = O.expert_ffn_bwd(Xp, sub_off, a["Wg"], a["Wu"], a["Wd"], ff["Hg"], ff["Hu"], ff["A"], dYp)
     check("dxp(rows)", np64(t["dxp"][rsel]), fb["dXp"], tol)

@@ -31,6 +31,52 @@ def test_header_and_binding_agree():
     assert declared_functions() == sorted(B.EXPORTS)
 
 
+def declared_parameters():
+    """{function: [kind of each parameter]} from the header's prototypes;
+    kinds: ptr (pointers and the stream handle), size, int, float."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(moe_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", src):
+        kinds = []
+        for prm in [q.strip() for q in params.split(",")]:
+            if prm in ("", "void"):
+                continue
+            if "*" in prm or prm.startswith("moe_stream_t"):
+                kinds.append("ptr")
+            elif prm.startswith("size_t"):
+                kinds.append("size")
+            elif prm.startswith("float"):
+                kinds.append("float")
+            else:
+                kinds.append("int")
+        out[name] = kinds
+    return out
+
+
+def _kind(ct):
+    if ct is ctypes.c_size_t:
+        return "size"
+    if ct is ctypes.c_float:
+        return "float"
+    if ct is ctypes.c_int:
+        return "int"
+    return "ptr"
+
+
+def test_binding_argtypes_match_the_prototypes(lib):
+    """Every binding's ctypes argument list has the header prototype's
+    length and kinds, position by position (a missing pointer shifts the
+    size and the stream handle, which the library cannot detect)."""
+    decl = declared_parameters()
+    assert sorted(decl) == declared_functions()
+    for name, kinds in decl.items():
+        f = getattr(lib, name)
+        if f.argtypes is None:  # no arguments set: the prototype must take none
+            assert kinds == [], name
+            continue
+        assert [_kind(t) for t in f.argtypes] == kinds, name
+
+
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True,
                          text=True, check=True).stdout
@@ -307,3 +353,24 @@ def test_small_path_size_rule():
     assert not small_path_fits(B.MoEShape.make(4, 2048, 128, 8, 768, e_lo=64, e_hi=128), False)
     # wider than the small kernels take
     assert not small_path_fits(B.MoEShape.make(1, 8256, 128, 8, 768), False)
+
+
+def test_combine_ffn_bwd_gather_validation(lib):
+    """moe_combine_ffn_bwd_gather checks its arguments before any launch: an
+    invalid shape, each NULL input of the combine backward, and x of 2^31
+    bytes or more."""
+    P = FAKE
+    bad = shape(k=9)
+    args = [P] * 19  # x .. ws
+    st = lib.moe_combine_ffn_bwd_gather(ctypes.byref(bad), *args, 1 << 30, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG"
+    good = shape()
+    for i, name in ((2, "inv"), (4, "topk_w"), (10, "yp"), (11, "dy"), (12, "dyp"),
+                    (13, "dtopk_w")):
+        a = list(args)
+        a[i] = None
+        st = lib.moe_combine_ffn_bwd_gather(ctypes.byref(good), *a, 1 << 30, None)
+        assert B.STATUS[st] == "MOE_ERR_ARG" and f"{name} is NULL" in lib.moe_last_error().decode()
+    big = shape(T=65536, d=16384, E=8, k=2, I=64)
+    st = lib.moe_combine_ffn_bwd_gather(ctypes.byref(big), *args, 1 << 40, None)
+    assert B.STATUS[st] == "MOE_ERR_UNSUPPORTED" and "2^31" in lib.moe_last_error().decode()

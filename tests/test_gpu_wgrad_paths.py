@@ -49,16 +49,22 @@ def _table(sizes, k, seed):
     return idx, g
 
 
-@pytest.mark.parametrize("gather", [False, True], ids=["plain", "gather"])
+@pytest.mark.parametrize("form", ["plain", "gather", "dy"])
 @pytest.mark.parametrize("path", ["strip", "tile"])
-def test_weight_gradient_paths(path, gather):
+def test_weight_gradient_paths(path, form):
+    """dy: moe_combine_ffn_bwd_gather (the combine backward inside the FFN
+    backward, dYp formed from dY and the gate weights in the kernels where no
+    kernel reads it); its scratch dYp, poisoned first, stays unwritten on the
+    strip path and holds moe_combine_bwd's bits on the tile path, and its
+    gate gradient is moe_combine_bwd's."""
+    gather = form != "plain"
     sizes = SIZES[path]
     E, k, d, I = len(sizes), 2, 320, 192
     idx, g = _table(sizes, k, 71)
     T = idx.shape[0]
     w = MI.small_workload(f"wgrad_{path}_T{T}_d{d}_E{E}_k{k}_I{I}", T, d, E, k, I, seed=73,
                           backward=True)
-    _announce(f"{w.name} gather={gather}")
+    _announce(f"{w.name} form={form}")
     a = MI.generate(w, parts=("x", "Wg", "Wu", "Wd", "dY"))
     dev = U.upload(w, a)
     s = U.shape_of(w)
@@ -78,7 +84,23 @@ def test_weight_gradient_paths(path, gather):
     # the gradients' buffers start poisoned: every element must be written
     for name in ("dw_gate", "dw_up", "dw_down"):
         t[name].fill_(float("nan"))
-    if gather:
+    if form == "dy":
+        dyp_ref, dg_ref = t["dyp"].clone(), t["dtopk_w"].clone()
+        t["dyp"].fill_(float("nan"))
+        t["dtopk_w"].fill_(float("nan"))
+        B.moe_combine_ffn_bwd_gather(s, x, t["perm"], t["inv"], t["offsets"], t["topk_w"],
+                                     dev["Wg"], dev["Wu"], dev["Wd"], t["h"], t["a"], t["yp"],
+                                     dev["dY"], t["dyp"], t["dtopk_w"], t["dxp"], t["dw_gate"],
+                                     t["dw_up"], t["dw_down"], t["ws_ffn_bwd"])
+        torch.cuda.synchronize()
+        R = sum(sizes)
+        assert torch.equal(t["dtopk_w"], dg_ref), "dtopk_w differs from moe_combine_bwd's"
+        if path == "strip":
+            assert torch.isnan(t["dyp"][:R].float()).all(), "dYp written on the strip path"
+        else:
+            assert torch.equal(t["dyp"][:R].view(torch.int16), dyp_ref[:R].view(torch.int16)), \
+                "the scratch dYp differs from the combine backward's"
+    elif gather:
         B.moe_grouped_ffn_bwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"],
                                      dev["Wd"], t["h"], t["a"], t["dyp"], t["dxp"], t["dw_gate"],
                                      t["dw_up"], t["dw_down"], t["ws_ffn_bwd"])
@@ -171,3 +193,43 @@ def test_gemm_engine_rounding_bound_full_size():
         U.check_rounding_bound(f"h[{e}]", h, xp, np.concatenate([a["Wg"][e], a["Wu"][e]], 1))
         U.check_rounding_bound(f"yp[{e}]", yp, act, a["Wd"][e])
         U.check_rounding_bound(f"dw_down[{e}]", U.np64(t["dw_down"][e]), act.T, dyp)
+
+
+def test_dy_form_down_wgrad_rounding_bound():
+    """The strip kernel's dY form of dWd = sum_p (g_p A[p])^T dY[t_p] element
+    by element against the rounding bound of its own operands (A rows scaled
+    by their gate weights and rounded to bf16, nearest even, as the kernel
+    does; the rows of dY through the token table), on 256-row, empty and
+    ragged groups and a partial last column tile."""
+    sizes = SIZES["strip"]
+    E, k, d, I = len(sizes), 2, 320, 192
+    idx, g = _table(sizes, k, 89)
+    T = idx.shape[0]
+    w = MI.small_workload(f"dyform_T{T}_d{d}_E{E}_k{k}_I{I}", T, d, E, k, I, seed=97,
+                          backward=True)
+    _announce(w.name)
+    a = MI.generate(w, parts=("x", "Wg", "Wu", "Wd", "dY"))
+    dev = U.upload(w, a)
+    s = U.shape_of(w)
+    buf = LayerBuffers(s, training=True, dy_form=True)
+    t = buf.t
+    t["topk_idx"].copy_(torch.from_numpy(idx))
+    t["topk_w"].copy_(torch.from_numpy(g))
+    x = dev["x"]
+    B.moe_permute(s, t["topk_idx"], x, t["offsets"], t["perm"], t["inv"], t["xp"], t["ws_permute"])
+    B.moe_grouped_ffn_fwd_gather(s, x, t["perm"], t["offsets"], dev["Wg"], dev["Wu"], dev["Wd"],
+                                 t["h"], t["a"], t["yp"], t["ws_ffn_fwd"])
+    t["dw_down"].fill_(float("nan"))
+    B.moe_combine_ffn_bwd_gather(s, x, t["perm"], t["inv"], t["offsets"], t["topk_w"], dev["Wg"],
+                                 dev["Wu"], dev["Wd"], t["h"], t["a"], t["yp"], dev["dY"],
+                                 t["dyp"], t["dtopk_w"], t["dxp"], t["dw_gate"], t["dw_up"],
+                                 t["dw_down"], t["ws_ffn_bwd"])
+    torch.cuda.synchronize()
+    off = t["offsets"].cpu().numpy()
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        perm = t["perm"][r0:r1].long()
+        gw = t["topk_w"].reshape(-1)[perm]
+        a_s = (t["a"][r0:r1].float() * gw[:, None]).to(torch.bfloat16)
+        U.check_rounding_bound(f"dw_down[{e}]", U.np64(t["dw_down"][e]), U.np64(a_s).T,
+                               U.np64(dev["dY"][perm // k]))
