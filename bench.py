@@ -165,13 +165,17 @@ ROLE_NAMES = {0: "route_logits", 1: "ffn_gateup_fwd", 2: "ffn_down_fwd", 3: "ffn
               11: "ffn_down_fwd_combine", 12: "ffn_down_dgrad_dy"}
 
 
-def gemm_role_of(kernel_name: str):
+def gemm_role_of(kernel_name: str, dy_form: bool = False):
+    """The GEMM role of a kernel from its name; dy_form: the run used
+    moe_combine_ffn_bwd_gather, whose down weight gradient launches the strip
+    kernel's dY form and then the role's tile kernel."""
     if "gemm_bf16" not in kernel_name:
         return None
     args = kernel_name.split("<", 1)[1].split(">", 1)[0].split(",")
     if args[0].strip() == "true":  # the strip kernel's dY form
         return "ffn_down_wgrad_dy"
-    return ROLE_NAMES.get(int(args[-1]))
+    role = ROLE_NAMES.get(int(args[-1]))
+    return "ffn_down_wgrad_dy" if dy_form and role == "ffn_down_wgrad" else role
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int) -> dict:
@@ -198,11 +202,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int) -> dict:
     out = {"source_hash": kernel_source_hash(), "calibration": {
         "read_factor": round(f_read, 4), "write_factor": round(f_write, 4),
         "calib_bytes": calib}, "kernels": {}, "raw_kib_per_dispatch": {}}
+    dy_form = any(gemm_role_of(k) == "ffn_down_wgrad_dy" for k in fetch)
     for k in fetch:
         f = sum(fetch[k]) / len(fetch[k])
         w_ = sum(write.get(k, [0.0])) / max(len(write.get(k, [])), 1)
         out["raw_kib_per_dispatch"][k] = {"FETCH_SIZE": round(f, 1), "WRITE_SIZE": round(w_, 1)}
-        role = gemm_role_of(k)
+        role = gemm_role_of(k, dy_form)
         if role:
             # a role may launch two kernels (the weight gradients' strip
             # kernel and tile kernel): its bytes per call are their sum
@@ -470,11 +475,12 @@ def main():
     ap.add_argument("--pass", dest="pass_", choices=("default", "fwd", "fwdbwd"), default="default",
                     help="run the workload forward only or forward+backward (default: as the "
                          "workload is defined)")
-    ap.add_argument("--ffn", choices=("gather", "plain", "fused", "dy"), default="gather",
+    ap.add_argument("--ffn", choices=("dy", "gather", "plain", "fused"), default="dy",
                     help="gather: the FFN reads the rows of Xp from x through the token table "
                          "(no Xp buffer); plain: the permute writes Xp; fused: gather, and the "
-                         "combine runs in the down projection's epilogue; dy: gather, and the "
-                         "backward forms the rows of dYp from dY inside its kernels")
+                         "combine runs in the down projection's epilogue; dy: gather, with the "
+                         "combine backward inside the FFN backward (dYp written only where a "
+                         "kernel reads it, else its rows formed from dY inside the kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the natural-router and DeepSeek-V3 rank-share timings")
@@ -521,7 +527,7 @@ def main():
     del a
     shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate, e_lo=w.e_lo,
                             e_hi=w.e_end)
-    gather = args.ffn  # the FFN form: plain, gather or fused
+    gather = args.ffn  # the FFN form: dy, gather, plain or fused
     torch.cuda.synchronize()
     inputs_bytes = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
