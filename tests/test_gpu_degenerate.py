@@ -9,6 +9,9 @@ oracle (every output, element by element, as in test_gpu_parity.py):
 * a local expert range that no token is routed to: no routed rows at all,
   every output of the expert path is zero;
 * a single token.
+
+Each runs the plain, the gathered and the dY form of the FFN (the combine
+backward inside the FFN backward).
 """
 import sys
 
@@ -57,7 +60,11 @@ def test_degenerate(name):
         assert (f["idx"] == np.arange(w.k)).all() and counts[:w.k].tolist() == [w.T] * w.k
     if name == "no_local_rows":
         assert int(f["offsets"][-1]) == 0 and not f["y"].any()
+    dev = U.upload(w, a)
     for gather in (False, True):
-        _, buf = U.run_layer(w, U.upload(w, a), gather=gather)
+        _, buf = U.run_layer(w, dev, gather=gather)
         errs = U.compare_full(w, a, buf, f, bw)
     print({k: f"{v:.2e}" for k, v in errs.items()})
+    # the combine backward inside the FFN backward, from poisoned buffers
+    _, buf = U.run_layer(w, dev, dy_form=True, poison=True)
+    U.compare_full(w, a, buf, f, bw, check_dyp=False)

@@ -2,8 +2,10 @@
 gate, the dtype, a local expert range and a row capacity drawn at random
 (within the supported shapes), so that ragged tails land differently in every
 tile shape the GEMMs pick.  Each case runs the plain and the gathered FFN
-(and, for the forward, the small-batch path; for the natural gate, the
-router's balancing loss too) against the CPU oracle."""
+and the gathered FFN with the combine backward inside its backward (from
+poisoned buffers: dYp is written only where a kernel reads it) (and, for the
+forward, the small-batch path; for the natural gate, the router's balancing
+loss too) against the CPU oracle."""
 import sys
 
 import numpy as np
@@ -69,6 +71,8 @@ def test_random_shape(case):
     for gather in (False, True):
         _, buf = U.run_layer(w, dev, R_cap=R_cap, gather=gather)
         U.compare_full(w, a, buf, f, bw)
+    _, buf = U.run_layer(w, dev, R_cap=R_cap, dy_form=True, poison=True)
+    U.compare_full(w, a, buf, f, bw, check_dyp=False)
     if w.gate == "softmax_topk":  # with the router's balancing loss
         _, buf = U.run_layer(w, dev, R_cap=R_cap, aux_alpha=0.05)
         U.compare_aux(w, a, buf, f, bw, 0.05)
