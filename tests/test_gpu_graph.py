@@ -21,12 +21,14 @@ OUTS = ["logits", "topk_idx", "topk_w", "y", "dx", "dw_gate", "dw_up", "dw_down"
 @pytest.mark.parametrize("gate,path", [("softmax_topk", "plain"), ("balanced", "plain"),
                                        ("softmax_topk", "gather"), ("balanced", "gather"),
                                        ("softmax_topk", "small"), ("softmax_topk", "small_few"),
-                                       ("softmax_topk", "aux")])
+                                       ("softmax_topk", "aux"), ("softmax_topk", "dy"),
+                                       ("balanced", "dy")])
 def test_graph_replay_matches_eager(gate, path):
     """path: plain (permute writes Xp), gather (the FFN reads x through the
     token table), small (the small-batch forward, no backward; small_few: 8
     tokens, the few-token router and the combine's arrival counters), aux
-    (plain with the router's balancing loss and its gradient)."""
+    (plain with the router's balancing loss and its gradient), dy (gather
+    with the combine backward inside the FFN backward)."""
     T = 8 if path == "small_few" else 384
     w = MI.small_workload(f"graph_{gate}_{path}_T{T}_d256_E16_k4_I256", T, 256, 16, 4, 256,
                           gate=gate, bias_sigma=1.0 if gate == "softmax_topk" else None, seed=31)
@@ -35,7 +37,7 @@ def test_graph_replay_matches_eager(gate, path):
     dev = U.upload(w, MI.generate(w))
     shape = B.MoEShape.make(w.T, w.d, w.E, w.k, w.I, dtype=w.dtype, gate=w.gate)
     small = path.startswith("small")
-    buf = LayerBuffers(shape, training=not small, gather=path == "gather",
+    buf = LayerBuffers(shape, training=not small, gather=path == "gather", dy_form=path == "dy",
                        aux_alpha=0.05 if path == "aux" else None)
 
     def step():
