@@ -329,19 +329,22 @@ moe_status_t moe_grouped_ffn_bwd_gather(const moe_shape_t* shape, const void* x,
                                         size_t ws_bytes, moe_stream_t stream);
 
 /* a6..a10 in one call: moe_combine_bwd followed by moe_grouped_ffn_bwd_gather,
- * with dyp written only where a kernel reads it.  Same outputs: dtopk_w as
- * moe_combine_bwd; dxp, dw_gate, dw_up, dw_down as moe_grouped_ffn_bwd_gather
- * on that dyp, to rounding (not bit for bit): in bf16, while every local
- * expert has at most 256 rows, the rows g * dy[t] of dyp (g = topk_w[t,j],
- * t*k + j = perm[p]) are formed inside the kernels -- dA's rows scaled by g
- * in fp32 after the product dy[t] w_down^T, the rows of A scaled by g and
- * rounded to bf16 in dw_down = sum_p (g A[p])^T dy[t] -- and dyp is never
- * written; with a larger expert, and in fp32, dyp is written with the values
- * moe_combine_bwd gives and read as in moe_grouped_ffn_bwd_gather.  The
- * choice is made on the device from group_offsets.  dyp [R_cap,d] is
- * caller-owned scratch whose contents afterwards are unspecified.  Arguments
- * as for moe_combine_bwd and moe_grouped_ffn_bwd_gather; the workspace is
- * moe_workspace_size(MOE_OP_FFN_BWD).  Needs T*d*element bytes < 2^31 (else
+ * with dyp written only where a kernel reads it.  Same outputs, to rounding:
+ * in bf16, while every local expert has at most 256 rows, dyp is never
+ * written and the a6 kernel does not run: the rows g * dy[t] of dyp
+ * (g = topk_w[t,j], t*k + j = perm[p]) are formed inside the kernels -- dA's
+ * rows scaled by g in fp32 after the product dA0 = dy[t] w_down^T, the rows
+ * of A scaled by g and rounded to bf16 in dw_down = sum_p (g A[p])^T dy[t]
+ * -- and dtopk_w[t,j] = <dA0[p], silu(Hg[p]) * Hu[p]> (fp32, from the saved
+ * H), which is <dy[t], yp[p]> = <dy[t], A[p] w_down> up to rounding; with a
+ * larger expert, and in fp32, a6 runs as moe_combine_bwd (dyp written, the
+ * same dtopk_w) and a7..a10 as moe_grouped_ffn_bwd_gather on that dyp (the
+ * same bits).  The choice is made on the device from group_offsets.  dyp
+ * [R_cap,d] is caller-owned scratch whose contents afterwards are
+ * unspecified.  Arguments as for moe_combine_bwd and
+ * moe_grouped_ffn_bwd_gather; the workspace is moe_workspace_size(
+ * MOE_OP_FFN_BWD) (in bf16 it also holds fp32 [R_cap][I/32] shares of the
+ * gate gradient).  Needs T*d*element bytes < 2^31 (else
  * MOE_ERR_UNSUPPORTED). */
 moe_status_t moe_combine_ffn_bwd_gather(const moe_shape_t* shape, const void* x,
                                         const int32_t* perm, const int32_t* inv,

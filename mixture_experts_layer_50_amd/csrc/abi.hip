@@ -255,6 +255,9 @@ int64_t one_table_bytes(const Dims& D, int bm) {
 }
 int64_t kcost_bytes(const Dims& D) { return round_up((int64_t)(D.E_loc + 1) * 4, 256); }
 int64_t tok_bytes(const Dims& D) { return round_up((int64_t)D.R_cap * 4, 256); }
+// moe_combine_ffn_bwd_gather (bf16): the gate gradient's shares from the
+// dSwiGLU GEMM, fp32 [R_cap][I / 32].
+int64_t gate_part_bytes(const Dims& D) { return round_up((int64_t)D.R_cap * (D.I / 32) * 4, 256); }
 int64_t tile_table_bytes(const Dims& D) {
   return one_table_bytes(D, 256) + one_table_bytes(D, 128) + kcost_bytes(D) + tok_bytes(D);
 }
@@ -349,7 +352,7 @@ int64_t ws_bytes(const Dims& D, int op) {
     case MOE_OP_FFN_FWD: return D.bf16 ? tile_table_bytes(D) : 0;
     case MOE_OP_FFN_BWD:
       return round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) +
-             (D.bf16 ? tile_table_bytes(D) : 0);
+             (D.bf16 ? tile_table_bytes(D) + gate_part_bytes(D) : 0);
     case MOE_OP_SMALL_FWD: return small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.e_lo, D.e_hi, D.eb);
     case MOE_OP_AUX_LOSS: return D.balanced ? 0 : aux_loss_ws_bytes(D.T, D.E);
     case MOE_OP_ROUTE_BWD: {
@@ -780,10 +783,14 @@ moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, cons
   if (D.bf16) MOE_TRY(tt.ensure());
   // the bf16 kernels on g * dY[t] (dy_k); the fp32 path reads dYp throughout
   const bool dy_k = dyf && D.bf16;
+  // the gate gradient's shares (dy_k, while no expert has more than STRIP_K rows)
+  float* dg_part = reinterpret_cast<float*>(
+      wsb + round_up((int64_t)D.R_cap * 2 * D.I * D.eb, 256) + (D.bf16 ? tile_table_bytes(D) : 0));
   if (dyf) {
-    // a6: the gate gradient; dYp only when the weight gradients' tile kernels
-    // have work (kcost[groups] > 0: some expert has more than STRIP_K rows),
-    // and always in fp32
+    // a6 (dYp and the gate gradient) only when the weight gradients' tile
+    // kernels have work (kcost[groups] > 0: some expert has more than STRIP_K
+    // rows), and always in fp32; else the dSwiGLU GEMM yields the gate
+    // gradient and no kernel reads dYp
     MOE_TRY(launch_combine_bwd(dyf->dy, dyf->yp, dyf->inv, dyf->topk_w, D.T, D.d, D.k, D.eb,
                                const_cast<void*>(dyp), dyf->dtopk_w, s,
                                dy_k ? tt.kcost() + D.E_loc : nullptr));
@@ -819,6 +826,8 @@ moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, cons
       p.row_slot = perm;
       p.a_alt = dyp;
       p.kcost = tt.kcost();
+      p.dg_part = dg_part;
+      p.dg_stride = D.I / 32;
     }
     p.B0 = w_down; p.ldb = D.d; p.b_estride = (int64_t)D.I * D.d;
     p.N = D.I; p.K = D.d;
@@ -827,6 +836,9 @@ moe_status_t ffn_bwd(const char* fn, bool gather, const moe_shape_t* shape, cons
     p.C0 = dH; p.aux = h_save; p.I = D.I;
     if (D.bf16) MOE_TRY(tt.get(r, &p.tiles));
     MOE_TRY(launch_gemm(D.bf16, r, p, rows_or_tiles(r), s));
+    if (dy_k)  // dG[t,j] = <dY[t], Yp[p]> = sum of the row's shares (when a6 did not run)
+      MOE_TRY(launch_gate_grad_sum(dyf->inv, dg_part, D.I / 32, D.T * D.k, tt.kcost() + D.E_loc,
+                                   dyf->dtopk_w, s));
   }
   {  // a10: [dWg | dWu][e] = Xp_e^T [dHg | dHu]_e
     const GemmRole gw = perm ? R_GATEUP_WGRAD_GATHER : R_GATEUP_WGRAD;

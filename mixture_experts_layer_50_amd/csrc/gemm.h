@@ -62,6 +62,12 @@ struct GemmParams {
   // the combine backward has written it and the kernel reads its rows in
   // order, with no gate weight; else A = dY through a_rows, scaled by row_gate.
   const void* a_alt;
+  // R_DOWN_DGRAD_GATHER reading dY (not a_alt): the gate gradient's shares,
+  // dg_part[p * dg_stride + b] = sum over the 32 columns i of block b of
+  // dA0[p,i] * silu(Hg[p,i]) Hu[p,i], with dA0 = dY[t] Wd^T before the gate
+  // weight (so that dG = <dY[t], A Wd> = sum_b dg_part[p, b]); NULL: none
+  float* dg_part;
+  int dg_stride;       // I / 32
   const int32_t* tiles;// G_MROWS tile table: tiles[0] = count, then (expert, first row) pairs
   const int32_t* kcost;// G_KROWS (optional): prefix sums [groups+1] of the per-expert tile cost
                        // (K slices + a fixed part), for balancing the persistent kernels; all

@@ -1053,7 +1053,11 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
     __syncthreads();
     // 2. the band's waves turn (dA, Hg, Hu) into (dHg, dHu) in place (dA rows
     // of g * dY[t] take their gate weight g here; rows past m_hi read the
-    // last valid row's and are not stored)
+    // last valid row's and are not stored).  With dg_part, each 32-column
+    // block's share of the gate gradient, sum of dA0 * silu(Hg) Hu over the
+    // block (dA0: before the gate weight), goes out too: a lane sums its 16
+    // columns, the lane 32 apart (same row, the other 16) adds its sum.
+    const bool dgw = p.dg_part != nullptr && !reads_alt(p);
     if (wm == rd) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -1061,7 +1065,8 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
         const float gw = p.row_gate && !reads_alt(p) ? p.row_gate[p.row_slot[min(mb + r, m_hi - 1)]]
                                                      : 1.0f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          float dgs = 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int n = wn * WTN + j * 32 + 8 * q + 4 * half;
@@ -1075,14 +1080,23 @@ __device__ __forceinline__ void epilogue_dswiglu_staged(const GemmParams& p, f32
             float dg[4], du[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const float v = acc[i][j][4 * q + t] * gw;
+              const float a0 = acc[i][j][4 * q + t];
+              const float v = a0 * gw;
               const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[t]));
               dg[t] = v * u[t] * sg * (1.0f + g[t] * (1.0f - sg));
               du[t] = v * g[t] * sg;
+              dgs = fmaf(a0, g[t] * sg * u[t], dgs);
             }
             *reinterpret_cast<uint2*>(Gs + o) = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
             *reinterpret_cast<uint2*>(Us + o) = make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
           }
+          if (dgw) {
+            dgs += __shfl_xor(dgs, 32, 64);
+            const int blk = (n0 + wn * WTN + j * 32) / 32;
+            if (half == 0 && mb + r < m_hi && blk < p.dg_stride)
+              p.dg_part[(int64_t)(mb + r) * p.dg_stride + blk] = dgs;
+          }
+        }
       }
     }
     __syncthreads();
@@ -1249,8 +1263,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmParams p)
                      2 * WTM * BN <= LDS_ELEMS)
     epilogue_dswiglu_staged<BM, BN, WGM, FM, FN, WTM, WTN, NT>(p, acc, smem, m_lo, m_hi, n0, wm, wn,
                                                              lane, tid);
-  else
+  else {
+    // (the gate gradient's shares are written by the staged dSwiGLU epilogue only)
+    static_assert(ROLE != R_DOWN_DGRAD_GATHER, "R_DOWN_DGRAD_GATHER needs the staged epilogue");
     epilogue<FM, FN, WTM, WTN, GMD, EPI>(p, acc, m_lo, m_hi, n0, e, wm, wn, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------

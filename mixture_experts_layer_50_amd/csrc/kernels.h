@@ -60,8 +60,13 @@ moe_status_t launch_permute(const int32_t* idx, const void* x, int T, int d, int
 // y[t] = sum_j w[t,j] * src[inv[t*k+j]] (w == NULL: weight 1), fp32 accumulation.
 moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float* w, int T, int d,
                                int k, int elt_bytes, void* y, hipStream_t s, const char* name);
+// The gate gradient from the dSwiGLU GEMM's shares: dw[s] = sum of the
+// stride values part[inv[s]][0 .. stride) in order (0 when inv[s] < 0), only
+// when *flag (device memory) is zero.
+moe_status_t launch_gate_grad_sum(const int32_t* inv, const float* part, int stride, int slots,
+                                  const int32_t* flag, float* dw, hipStream_t s);
 // dyp[inv[t*k+j]] = w[t,j] dy[t] and dw[t,j] = <dy[t], yp[inv[t*k+j]]>; with
-// dyp_flag (device memory), dyp is written only when *dyp_flag is nonzero.
+// dyp_flag (device memory), the kernel runs only when *dyp_flag is nonzero.
 moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv, const float* w,
                                 int T, int d, int k, int elt_bytes, void* dyp, float* dw,
                                 hipStream_t s, const int32_t* dyp_flag = nullptr);

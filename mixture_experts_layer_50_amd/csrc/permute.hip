@@ -307,8 +307,8 @@ moe_status_t launch_gather_sum(const void* src, const int32_t* inv, const float*
   return check_launch(name);
 }
 
-// dyp[inv[t,j]] = w[t,j] * dy[t] (unless dyp_flag points to a zero);
-// dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when dropped).
+// dyp[inv[t,j]] = w[t,j] * dy[t];  dw[t,j] = <dy[t], yp[inv[t,j]]> (0 when
+// dropped); nothing when dyp_flag points to a zero.
 // One wavefront per token, slot data broadcast from lane j as above (the
 // chunk loop over whole wavefronts of chunks, all lanes active).
 template <typename T>
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
-  if (dyp_flag && *dyp_flag == 0) dyp = nullptr;  // no kernel after this one reads dyp
+  if (dyp_flag && *dyp_flag == 0) return;  // neither output is wanted from this kernel
   const int myp = lane < k ? inv[(int64_t)t * k + lane] : -1;
   const float myw = lane < k ? w[(int64_t)t * k + lane] : 0.0f;
   float part[MAXK];
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
           o[i] = g * fy[i];
         }
         part[j] += a;  // lanes past the last chunk add zeros
-        if (ok && dyp) dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
+        if (ok) dyp[(int64_t)p * chunks + c] = Chunk<T>::pack(o);
       }
     }
   }
@@ -370,6 +370,37 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* dy, const
       if (lane == 0) dw[(int64_t)t * k + j] = kept ? v : 0.f;
     }
   }
+}
+
+// dw[s] = sum_b part[inv[s] * stride + b] in ascending b for every slot s
+// with inv[s] >= 0, else 0; nothing when flag points to a nonzero value.
+__global__ __launch_bounds__(256) void gate_grad_sum_kernel(const int32_t* inv, const float* part,
+                                                            int stride, int slots,
+                                                            const int32_t* flag, float* dw) {
+  if (*flag != 0) return;
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= slots) return;
+  const int p = inv[s];
+  float v = 0.f;
+  if (p >= 0) {  // stride is even (I / 32, I a multiple of 64): the row in 8-byte pairs
+    const float2* row = reinterpret_cast<const float2*>(part + (int64_t)p * stride);
+#pragma unroll 4
+    for (int b = 0; b < stride / 2; ++b) {
+      const float2 x = row[b];
+      v += x.x;
+      v += x.y;
+    }
+  }
+  dw[s] = v;
+}
+
+moe_status_t launch_gate_grad_sum(const int32_t* inv, const float* part, int stride, int slots,
+                                  const int32_t* flag, float* dw, hipStream_t s) {
+  ProfScope prof("gate_grad_sum", s);
+  if (slots <= 0) return MOE_OK;
+  gate_grad_sum_kernel<<<(unsigned)ceil_div(slots, 256), 256, 0, s>>>(inv, part, stride, slots,
+                                                                     flag, dw);
+  return check_launch("gate_grad_sum_kernel");
 }
 
 moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv, const float* w,

@@ -153,7 +153,8 @@ def test_workspace_sizes_and_short_workspace(lib):
     # + weight-gradient cost prefix [E_loc + 1] + token row of each routed row (gathered calls)
     tiles = table(256) + table(128) + 768 + R * 4
     assert B.workspace_size(s, "ffn_fwd") == tiles
-    assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + tiles
+    # [dHg | dHu] + the tables + the gate gradient's fp32 shares [R][I / 32]
+    assert B.workspace_size(s, "ffn_bwd") == R * 2 * 768 * 2 + tiles + R * (768 // 32) * 4
     assert B.workspace_size(s, "route_bwd") == 0                    # balanced gate: no dL copy
     n = B.workspace_size(shape(T=4096, d=2048, E=128, k=8, I=768), "route_bwd")
     # bf16 copy of dL, column sums per 32 tokens, 8 split-K partials of x^T dL (fp32)
