@@ -427,6 +427,40 @@ def test_combine_backward_by_finite_differences():
     assert (dYp[np.setdiff1d(np.arange(R), inv[inv >= 0])] == 0).all()
 
 
+def test_regrouped_gate_products_equal_the_definition():
+    """The backward's dY form regroups where the gate weight g of row p
+    (token t, slot j) is applied: dA = g (dY[t] Wd^T) instead of (g dY[t]) Wd^T,
+    dWd = sum_p (g A[p])^T dY[t] instead of A^T dYp, and dG = <dY[t] Wd^T, A[p]>
+    instead of <dY[t], Yp[p]>.  In exact arithmetic both sides are the same;
+    here in fp64 against the oracle's backward, per expert, with empty and
+    dropped rows (R_cap < T*k)."""
+    r = _rng(53)
+    T, d, E, k, I = 40, 16, 6, 3, 12
+    x = r.standard_normal((T, d))
+    Wr = r.standard_normal((d, E))
+    Wg, Wu = r.standard_normal((E, d, I)) / 4, r.standard_normal((E, d, I)) / 4
+    Wd = r.standard_normal((E, I, d)) / 4
+    dY = r.standard_normal((T, d))
+    f = O.layer_fwd(x, Wr, None, Wg, Wu, Wd, k, "softmax_topk", E, R_cap=100)
+    off, perm = f["offsets"], f["perm"]
+    R = int(off[-1])
+    assert R == 100  # 20 of the 120 slots dropped
+    dYp, dG = O.combine_bwd(dY, f["Yp"], f["inv"], f["g"], T, k)
+    fb = O.expert_ffn_bwd(f["Xp"], off, Wg, Wu, Wd, f["Hg"], f["Hu"], f["A"], dYp)
+    tok, gw = perm // k, f["g"].reshape(-1)[perm]
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        dA0 = dY[tok[rows]] @ Wd[e].T                     # before the gate weight
+        assert np.allclose(gw[rows, None] * dA0, dYp[rows] @ Wd[e].T, rtol=0, atol=1e-12)
+        dWd = (gw[rows, None] * f["A"][rows]).T @ dY[tok[rows]]
+        assert np.allclose(dWd, fb["dWd"][e], rtol=0, atol=1e-12)
+        dg = np.einsum("pi,pi->p", dA0, f["A"][rows])
+        assert np.allclose(dg, dG.reshape(-1)[perm[rows]], rtol=0, atol=1e-12)
+    # every kept slot's dG comes from its row; dropped slots stay 0
+    kept = f["inv"] >= 0
+    assert not dG.reshape(-1)[~kept].any() and kept.sum() == R
+
+
 def test_permute_backward_is_adjoint_of_gather():
     r = _rng(52)
     T, k, d, E = 10, 3, 5, 6
