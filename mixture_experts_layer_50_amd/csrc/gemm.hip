@@ -2675,12 +2675,7 @@ static void launch_f32(const GemmParams& p, int max_rows, hipStream_t s) {
 // whole tiles) that moves the fewest bytes through the busiest CU, with every
 // expert taken to be the strip kernel's (rounds of one item per CU, each
 // reading its A block once and its part of the B tiles).
-// (MOE_STRIP_PARTS > 0 fixes the count instead: build-time tunable.)
-#ifndef MOE_STRIP_PARTS
-#define MOE_STRIP_PARTS 0
-#endif
 static int strip_column_parts(const GemmParams& p) {
-  if (MOE_STRIP_PARTS > 0) return (int)std::min<int64_t>(MOE_STRIP_PARTS, ceil_div(p.N, STRIP_N));
   const int cus = device_cus();
   const int64_t ntile = ceil_div(p.N, STRIP_N);
   const int64_t items1 = (int64_t)p.groups * ceil_div(p.M, STRIP_M);
