@@ -80,7 +80,7 @@ typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_FFN_FWD = 2, MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4, MOE_OP_FFN_BWD = 5, MOE_OP_PERMUTE_BWD = 6, MOE_OP_ROUTE_BWD = 7,
   MOE_OP_SMALL_FWD = 8, MOE_OP_AUX_LOSS = 9, MOE_OP_FFN_FWD_FUSED = 10, MOE_OP_ROUTE_PERMUTE = 11,
-  MOE_OP_SMALL_ROUTED_FWD = 12
+  MOE_OP_SMALL_ROUTED_FWD = 12, MOE_OP_CHECK_ROUTING = 13
 } moe_op_t;
 
 typedef void* moe_stream_t; /* hipStream_t */
@@ -286,6 +286,35 @@ moe_status_t moe_small_fwd(const moe_shape_t* shape, const void* x, const void* 
                            const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
                            const void* w_gate, const void* w_up, const void* w_down, void* y,
                            void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------- checks */
+
+/* Device-side check of a routing table and its group offsets: the layer's
+ * debug check.  The kernels take any expert id outside [e_lo, e_hi) for
+ * another GPU's expert and drop its row, so an id outside [0, E) in a caller's
+ * table would otherwise pass unnoticed.  ORs into *flags (one device int32;
+ * bits are only ever set, so the caller zeroes it once and may run several
+ * checks into it; read it once the stream has finished):
+ *   MOE_CHECK_IDX_RANGE   some topk_idx[t,j] < 0 or >= E;
+ *   MOE_CHECK_IDX_REPEAT  some token names one expert in two slots (allowed:
+ *                         only the first of those slots is routed, as in
+ *                         moe_permute);
+ *   MOE_CHECK_OFFSETS     group_offsets (when not NULL) is not what
+ *                         moe_permute writes for this table: the exclusive
+ *                         prefix of the local experts' group sizes (rows under
+ *                         the first-slot rule), each entry clamped to R_cap.
+ * The order of the expert-sorted rows ([P3] section 专家后端, grouped_mm row)
+ * is not checked here: perm and inv follow from the table by moe_permute.
+ * topk_idx [T,k] int32; group_offsets [E_loc+1] int32 or NULL; flags [1]
+ * int32.  ws: moe_workspace_size(MOE_OP_CHECK_ROUTING) (the group sizes,
+ * E_loc int32), needed only with group_offsets.  Errors: MOE_ERR_ARG for a
+ * NULL topk_idx or flags, MOE_ERR_WORKSPACE for a short workspace. */
+#define MOE_CHECK_IDX_RANGE 1
+#define MOE_CHECK_IDX_REPEAT 2
+#define MOE_CHECK_OFFSETS 4
+moe_status_t moe_check_routing(const moe_shape_t* shape, const int32_t* topk_idx,
+                               const int32_t* group_offsets, int32_t* flags, void* ws,
+                               size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------ backward */
 /* Full-parameter fine-tuning needs every gradient ([P3] Qwen3 and Nemotron

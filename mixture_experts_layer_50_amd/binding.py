@@ -18,7 +18,7 @@ DTYPES = {"f32": 0, "bf16": 1}
 GATES = {"softmax_topk": 0, "balanced": 1}
 OPS = {"route": 0, "permute": 1, "ffn_fwd": 2, "combine": 3, "combine_bwd": 4, "ffn_bwd": 5,
        "permute_bwd": 6, "route_bwd": 7, "small_fwd": 8, "aux_loss": 9, "ffn_fwd_fused": 10,
-       "route_permute": 11, "small_routed_fwd": 12}
+       "route_permute": 11, "small_routed_fwd": 12, "check_routing": 13}
 SMALL_MAX_WIDTH = 8192  # moe_ffn_small_fwd / moe_small_fwd: d and I at most this
 SMALL_MAX_PAIRS = 4096  # and T*k at most this
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE",
@@ -32,7 +32,7 @@ EXPORTS = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_
            "moe_grouped_ffn_fwd_gather", "moe_grouped_ffn_bwd_gather", "moe_ffn_small_fwd",
            "moe_aux_loss", "moe_route_bwd_aux", "moe_grouped_ffn_fwd_gather_noalloc",
            "moe_grouped_ffn_fwd_fused", "moe_route_permute", "moe_small_fwd",
-           "moe_combine_ffn_bwd_gather"]
+           "moe_combine_ffn_bwd_gather", "moe_check_routing"]
 
 
 class MoEError(RuntimeError):
@@ -103,6 +103,7 @@ def load_library() -> ctypes.CDLL:
         "moe_grouped_ffn_bwd_gather": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_combine_ffn_bwd_gather": [S] + [P] * 19 + [SZ, P],
         "moe_permute_bwd": [S, P, P, P, P],
+        "moe_check_routing": [S, P, P, P, P, SZ, P],
         "moe_route_bwd": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_aux_loss": [S, P, P, ctypes.c_float, P, P, P, SZ, P],
         "moe_route_bwd_aux": [S, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -256,6 +257,12 @@ def moe_combine_ffn_bwd_gather(shape, x, perm, inv, group_offsets, topk_w, w_gat
 def moe_permute_bwd(shape, dxp, inv, dx, stream=None):
     _check("moe_permute_bwd", load_library().moe_permute_bwd(
         ctypes.byref(shape), _ptr(dxp), _ptr(inv), _ptr(dx), _stream(stream)))
+
+
+def moe_check_routing(shape, topk_idx, group_offsets, flags, ws, stream=None):
+    _check("moe_check_routing", load_library().moe_check_routing(
+        ctypes.byref(shape), _ptr(topk_idx), _ptr(group_offsets), _ptr(flags), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
 
 
 def moe_route_bwd(shape, x, w_router, topk_idx, topk_w, dtopk_w, dlogits, dw_router, dbias, dx,

@@ -355,6 +355,7 @@ int64_t ws_bytes(const Dims& D, int op) {
              (D.bf16 ? tile_table_bytes(D) + gate_part_bytes(D) : 0);
     case MOE_OP_SMALL_FWD: return small_ffn_ws_bytes(D.T, D.d, D.k, D.I, D.e_lo, D.e_hi, D.eb);
     case MOE_OP_AUX_LOSS: return D.balanced ? 0 : aux_loss_ws_bytes(D.T, D.E);
+    case MOE_OP_CHECK_ROUTING: return round_up((int64_t)D.E_loc * 4, 256);
     case MOE_OP_ROUTE_BWD: {
       if (D.balanced) return 0;
       const RouteBwdWs r(D);
@@ -381,7 +382,7 @@ extern "C" moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, siz
   Dims D;
   if (!bytes) return fail(MOE_ERR_ARG, "moe_workspace_size: bytes is NULL");
   MOE_TRY(check_shape(shape, "moe_workspace_size", &D));
-  if (op < MOE_OP_ROUTE || op > MOE_OP_SMALL_ROUTED_FWD)
+  if (op < MOE_OP_ROUTE || op > MOE_OP_CHECK_ROUTING)
     return fail(MOE_ERR_ARG, "moe_workspace_size: unknown op %d", op);
   *bytes = (size_t)ws_bytes(D, op);
   return MOE_OK;
@@ -447,6 +448,18 @@ extern "C" moe_status_t moe_route_permute(const moe_shape_t* shape, const void* 
                                         group_offsets, perm, inv, S(stream)));
   if (xp) return launch_permute_gather(x, inv, D.T, D.d, D.k, D.eb, xp, S(stream));
   return MOE_OK;
+}
+
+extern "C" moe_status_t moe_check_routing(const moe_shape_t* shape, const int32_t* topk_idx,
+                                          const int32_t* group_offsets, int32_t* flags, void* ws,
+                                          size_t ws_bytes_, moe_stream_t stream) {
+  const char* fn = "moe_check_routing";
+  Dims D;
+  MOE_TRY(check_shape(shape, fn, &D));
+  MOE_TRY(need(fn, {{"topk_idx", topk_idx}, {"flags", flags}}));
+  if (group_offsets) MOE_TRY(check_ws(fn, D, MOE_OP_CHECK_ROUTING, ws, ws_bytes_));
+  return launch_check_routing(topk_idx, D.T, D.k, D.E, D.e_lo, D.e_hi, D.R_cap, group_offsets,
+                              static_cast<int32_t*>(ws), flags, S(stream));
 }
 
 namespace {

@@ -71,6 +71,14 @@ moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* i
                                 int T, int d, int k, int elt_bytes, void* dyp, float* dw,
                                 hipStream_t s, const int32_t* dyp_flag = nullptr);
 
+// The routing-table check (moe_check_routing): range and repeat bits of the
+// table into *flags; with offsets, also the group sizes (counts [E_loc],
+// zeroed by the launcher) and the offsets compared with their prefix.
+constexpr int CHECK_IDX_RANGE = 1, CHECK_IDX_REPEAT = 2, CHECK_OFFSETS = 4;
+moe_status_t launch_check_routing(const int32_t* idx, int T, int k, int E, int e_lo, int e_hi,
+                                  int R_cap, const int32_t* offsets, int32_t* counts,
+                                  int32_t* flags, hipStream_t s);
+
 // small.hip: the small-batch FFN (no sort): y[t] = sum_j w[t,j] FFN_e(x[t]) over
 // the local, first-occurrence slots.  Workspace: fp32 gate/up partial sums
 // [T*k, KS, 2I] (KS splits of d), Yp [T*k, d], the combine's arrival

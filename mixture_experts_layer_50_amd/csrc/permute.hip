@@ -420,4 +420,85 @@ moe_status_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* i
   return check_launch("combine_bwd_kernel");
 }
 
+// ---------------------------------------------------------------------------
+// Routing-table check (moe_check_routing).  check_table_kernel: one thread
+// per token tests its k ids against [0, E) and against the token's earlier
+// slots; with counts, the local ids under the first-slot rule go into the
+// block's LDS histogram, whose nonzero bins are added into counts (integer
+// adds: the totals do not depend on their order).  The block's bits are ORed
+// in LDS, then once into *flags.  check_offsets_kernel (one wavefront) forms
+// the exclusive prefix of counts, clamps each entry to R_cap as the permute
+// does, and compares it with the caller's offsets.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void check_table_kernel(const int32_t* idx, int T, int k, int E,
+                                                          int e_lo, int e_hi, int32_t* counts,
+                                                          int32_t* flags) {
+  __shared__ int hist[512];
+  __shared__ int bits;
+  const int E_loc = e_hi - e_lo;
+  if (threadIdx.x == 0) bits = 0;
+  if (counts)
+    for (int i = threadIdx.x; i < E_loc; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int b = 0;
+  if (t < T) {
+    const int32_t* row = idx + (int64_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      const int e = row[j];
+      if (e < 0 || e >= E) b |= CHECK_IDX_RANGE;
+      bool first = true;
+      for (int jj = 0; jj < j; ++jj) first = first && row[jj] != e;
+      if (!first) b |= CHECK_IDX_REPEAT;
+      if (counts && first && e >= e_lo && e < e_hi) atomicAdd(&hist[e - e_lo], 1);
+    }
+  }
+  if (b) atomicOr(&bits, b);
+  __syncthreads();
+  if (counts)
+    for (int i = threadIdx.x; i < E_loc; i += 256)
+      if (hist[i]) atomicAdd(&counts[i], hist[i]);
+  if (threadIdx.x == 0 && bits) atomicOr(flags, bits);
+}
+
+__global__ __launch_bounds__(64) void check_offsets_kernel(const int32_t* counts, int E_loc,
+                                                           int R_cap, const int32_t* offsets,
+                                                           int32_t* flags) {
+  const int lane = threadIdx.x;
+  // (the counts add up to at most T*k < 2^31: int sums do not overflow)
+  int run = 0;  // rows of the experts before this chunk of 64
+  bool bad = false;
+  for (int c0 = 0; c0 <= E_loc; c0 += 64) {
+    const int i = c0 + lane;
+    const int v = i < E_loc ? counts[i] : 0;
+    // inclusive prefix over the wavefront, then exclusive for entry i
+    int inc = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    const int excl = run + inc - v;
+    if (i <= E_loc) bad = bad || offsets[i] != (excl < R_cap ? excl : R_cap);
+    run += __shfl(inc, 63, 64);
+  }
+  if (__any(bad) && lane == 0) atomicOr(flags, CHECK_OFFSETS);
+}
+
+moe_status_t launch_check_routing(const int32_t* idx, int T, int k, int E, int e_lo, int e_hi,
+                                  int R_cap, const int32_t* offsets, int32_t* counts,
+                                  int32_t* flags, hipStream_t s) {
+  ProfScope prof("check_routing", s);
+  const int E_loc = e_hi - e_lo;
+  if (offsets) {
+    const moe_status_t z = launch_fill_zero(counts, (int64_t)E_loc * 4, nullptr, 0, nullptr, 0, s);
+    if (z != MOE_OK) return z;
+  }
+  check_table_kernel<<<(unsigned)ceil_div(T, 256), 256, 0, s>>>(idx, T, k, E, e_lo, e_hi,
+                                                               offsets ? counts : nullptr, flags);
+  moe_status_t st = check_launch("check_table_kernel");
+  if (st != MOE_OK || !offsets) return st;
+  check_offsets_kernel<<<1, 64, 0, s>>>(counts, E_loc, R_cap, offsets, flags);
+  return check_launch("check_offsets_kernel");
+}
+
 }  // namespace moe

@@ -375,3 +375,21 @@ def test_combine_ffn_bwd_gather_validation(lib):
     big = shape(T=65536, d=16384, E=8, k=2, I=64)
     st = lib.moe_combine_ffn_bwd_gather(ctypes.byref(big), *args, 1 << 40, None)
     assert B.STATUS[st] == "MOE_ERR_UNSUPPORTED" and "2^31" in lib.moe_last_error().decode()
+
+
+def test_check_routing_validation(lib):
+    s = shape(T=100, E=16, k=4, e_lo=4, e_hi=12)
+    assert B.workspace_size(s, "check_routing") == 256          # 8 local group sizes, aligned
+    assert B.workspace_size(shape(E=512, k=2), "check_routing") == 512 * 4
+    P = FAKE
+    st = lib.moe_check_routing(ctypes.byref(s), None, None, P, None, 0, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "topk_idx" in lib.moe_last_error().decode()
+    st = lib.moe_check_routing(ctypes.byref(s), P, None, None, None, 0, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG" and "flags" in lib.moe_last_error().decode()
+    # the group sizes need the workspace only when offsets are checked
+    st = lib.moe_check_routing(ctypes.byref(s), P, P, P, None, 0, None)
+    assert B.STATUS[st] == "MOE_ERR_WORKSPACE"
+    st = lib.moe_check_routing(ctypes.byref(s), P, P, P, P, 16, None)
+    assert B.STATUS[st] == "MOE_ERR_WORKSPACE"
+    st = lib.moe_check_routing(ctypes.byref(shape(k=9)), P, None, P, None, 0, None)
+    assert B.STATUS[st] == "MOE_ERR_ARG"
