@@ -15,8 +15,8 @@
 // up to TG tokens per pass.
 // Kernel 1, one workgroup per (column block of the expert width, active
 // expert, K split): partial sums of Hg = x[t] Wg[e] and Hu = x[t] Wu[e] over
-// the block's columns and one of KS ranges of d (KS > 1 only when there are
-// too few active experts to fill the GPU), into part[pair][ks].  It also
+// the block's columns and one of KS ranges of d (ranges of at most 512
+// rows), into part[pair][ks].  It also
 // zeroes the combine's counters and the output rows of tokens with no kept
 // slot (strided over the whole grid).  For one or two tokens it can also take
 // the gate's last step (SmallRoute): every workgroup adds the router's
@@ -517,13 +517,15 @@ static int small_tg(int64_t pairs, int64_t nexp, int a_len) {
   return tg;
 }
 
-// K splits of the gate/up kernel: only when there are too few active experts
-// to give every CU two workgroups (the split costs the down kernel a pass over
-// the partials); each split whole 64-row slices, at least 128 rows.
-static int small_ks(int64_t nexp, int d, int I, int elt_bytes) {
-  const int64_t blocks = nexp * (I / (8 * (16 / elt_bytes)));
+// K splits of the gate/up kernel: ranges of at most 512 rows of d (up to 8
+// splits, each whole 64-row slices, at least 128 rows).  Measured at the
+// Qwen3 shape (d = 2048, natural router), against splitting only while fewer
+// than 512 workgroups would run: the same at T = 1 to 4, gate/up kernel
+// 54 vs 63 us at T = 8 and 90 vs 102 us at T = 16; 256-row ranges were
+// slower at T = 2 and 4 (each workgroup's table set-up is repeated per split).
+static int small_ks(int d) {
   int ks = 1;
-  while (ks < 8 && blocks * ks < 512 && d % (2 * ks * 64) == 0 && d / (2 * ks) >= 128) ks *= 2;
+  while (ks < 8 && d / ks > 512 && d % (2 * ks * 64) == 0 && d / (2 * ks) >= 128) ks *= 2;
   return ks;
 }
 
@@ -535,7 +537,7 @@ static int64_t small_nexp(int T, int k, int e_lo, int e_hi) {
 // combine's arrival counters [T][d / (8 N)].
 int64_t small_ffn_ws_bytes(int T, int d, int k, int I, int e_lo, int e_hi, int elt_bytes) {
   const int64_t pairs = (int64_t)T * k;
-  const int KS = small_ks(small_nexp(T, k, e_lo, e_hi), d, I, elt_bytes);
+  const int KS = small_ks(d);
   const int CB = 8 * (16 / elt_bytes);
   return round_up(pairs * KS * 2 * I * 4, 256) + round_up(pairs * d * elt_bytes, 256) +
          round_up((int64_t)T * (d / CB) * 4, 256);
@@ -546,7 +548,7 @@ moe_status_t launch_small_ffn(const void* x, const int32_t* idx, const float* w_
                               int I, int e_lo, int e_hi, int elt_bytes, void* y, void* ws,
                               hipStream_t s, const SmallRoute* route) {
   const int64_t pairs = (int64_t)T * k, nexp = small_nexp(T, k, e_lo, e_hi);
-  const int KS = small_ks(nexp, d, I, elt_bytes);
+  const int KS = small_ks(d);
   char* base = static_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(base);
   const int64_t part_bytes = round_up(pairs * KS * 2 * I * 4, 256);

@@ -239,10 +239,9 @@ def test_small_batch_ffn_validation(lib):
     # fp32 [Hg | Hu] partials (one K range at d = 128), the slot outputs
     # [T*k, d] in bf16, the combine's arrival counters [T][d / 64] int32
     assert n == 128 * 2 * 256 * 4 + 128 * 128 * 2 + 64 * 2 * 4
-    # at T = 1 of the Qwen3 shape (8 active experts x 12 column blocks) d
-    # splits in 8 ranges
+    # at the Qwen3 shape d = 2048 splits in 4 ranges of 512 rows
     n1 = B.workspace_size(shape(T=1, d=2048, E=128, k=8, I=768), "small_fwd")
-    assert n1 == 8 * 8 * 2 * 768 * 4 + 8 * 2048 * 2 + 256  # counters: 32 int32, padded
+    assert n1 == 8 * 4 * 2 * 768 * 4 + 8 * 2048 * 2 + 256  # counters: 32 int32, padded
 
     def call(sh, ws_bytes=1 << 30, y=P):
         return B.STATUS[lib.moe_ffn_small_fwd(ctypes.byref(sh), P, P, P, P, P, P, y, P, ws_bytes,
