@@ -980,7 +980,8 @@ moe_status_t route_bwd(const char* fn, const moe_shape_t* shape, const void* x, 
     p.A = dl; p.lda = D.E;
     p.B0 = w_router; p.ldb = D.E;
     p.M = D.T; p.N = D.d; p.K = D.E;
-    p.m_tiles = (int)ceil_div(D.T, 64); p.n_tiles = (int)ceil_div(D.d, 64);
+    const TileCfg tc = role_tile(R_ROUTE_DX);
+    p.m_tiles = (int)ceil_div(D.T, tile_bm(tc)); p.n_tiles = (int)ceil_div(D.d, tile_bn(tc));
     p.groups = 1;
     p.C0 = dx; p.ldc = D.d;
     MOE_TRY(launch_gemm(D.bf16, R_ROUTE_DX, p, p.m_tiles, s));
