@@ -113,6 +113,10 @@ moe_status_t moe_workspace_size(const moe_shape_t* shape, int op, size_t* bytes)
 /* a1 -- route.  [P3] section 背景: route tokens across many experts.
  * softmax_topk: logits = x * w_router (+ bias) with fp32 accumulation, then the
  *   k largest per token (ties -> lower id), topk_w = softmax over those k.
+ *   For T <= 16 (and E * element bytes a multiple of 16) the logits come from
+ *   a kernel that walks all of d per group of experts instead of the MFMA
+ *   router: fixed-order sums in another order, so they may differ from the
+ *   MFMA router's in the last bits; both are deterministic.
  * balanced: topk_idx/topk_w from the balanced gate; x, w_router, bias and
  *   logits are not read or written (they may be NULL).
  * x [T,d] (dtype); w_router [d,E] (dtype); bias [E] fp32 or NULL;
@@ -270,15 +274,16 @@ moe_status_t moe_ffn_small_fwd(const moe_shape_t* shape, const void* x, const in
 
 /* a1 + a3 + a4 + a5 for a few tokens, in one call: the gate, then
  * moe_ffn_small_fwd's FFN and combine.  Under the softmax top-k gate with
- * T <= 16 the router runs split over d (partial logits of 64-row chunks of d
- * in parallel workgroups, then one workgroup per token adds them in chunk
- * order, adds the bias, takes the top k by rank -- the same selection and
- * tie rule as moe_route -- and the softmax over the k slots; the sums run in
- * another order than moe_route's, so logits may differ from it in the last
- * bits); when T*E <= 1024 and T*E*d/64 <= 8192 (one or two
- * tokens at E = 128, d = 2048) that last step runs inside the FFN's first
- * kernel, each of its workgroups taking the same top k (one launch less);
- * for more tokens moe_route's kernels run.  Outputs
+ * T*E <= 1024 and T*E*d/64 <= 8192 (one or two tokens at E = 128, d = 2048)
+ * the router runs split over d (partial logits of 64-row chunks of d in
+ * parallel workgroups) and every workgroup of the FFN's first kernel adds
+ * them in chunk order, adds the bias, takes the top k by rank -- the same
+ * selection and tie rule as moe_route -- and the softmax over the k slots
+ * (one launch less; the sums run in another order than moe_route's, so
+ * logits may differ from it in the last bits).  Otherwise moe_route's
+ * kernels run (for T <= 16 its few-token logits), or, for T <= 16 with E *
+ * element bytes not a multiple of 16, the split router with one workgroup
+ * per token for the top k.  Outputs
  * logits (softmax gate), topk_idx, topk_w and y as moe_route and
  * moe_ffn_small_fwd would; the same arguments and limits.  ws:
  * moe_workspace_size(MOE_OP_SMALL_ROUTED_FWD). */

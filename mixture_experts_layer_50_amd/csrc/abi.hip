@@ -399,6 +399,10 @@ extern "C" moe_status_t moe_route(const moe_shape_t* shape, const void* x, const
   if (D.balanced) return launch_balanced_gate(D.T, D.E, D.k, topk_idx, topk_w, S(stream));
   MOE_TRY(need(fn, {{"x", x}, {"w_router", w_router}, {"logits", logits}}));
   MOE_TRY(opt(fn, {{"bias", bias}}));
+  if (few_token_logits_fit(D.T, D.E, D.eb)) {
+    MOE_TRY(launch_few_token_logits(x, w_router, bias, D.T, D.d, D.E, D.eb, logits, S(stream)));
+    return launch_topk_softmax(logits, D.T, D.E, D.k, topk_idx, topk_w, S(stream));
+  }
   GemmParams p{};
   p.A = x; p.lda = D.d;
   p.B0 = w_router; p.ldb = D.E;
@@ -716,8 +720,13 @@ extern "C" moe_status_t moe_small_fwd(const moe_shape_t* shape, const void* x,
       return launch_small_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, D.T, D.d, D.k, D.I,
                               D.e_lo, D.e_hi, D.eb, y, wsb + ffn_at, s, &r);
     }
-    MOE_TRY(launch_small_router(x, w_router, bias, D.T, D.d, D.E, D.k, D.eb, logits, topk_idx,
-                                topk_w, rpart, s));
+    if (few_token_logits_fit(D.T, D.E, D.eb)) {  // moe_route's few-token logits and top-k
+      MOE_TRY(launch_few_token_logits(x, w_router, bias, D.T, D.d, D.E, D.eb, logits, s));
+      MOE_TRY(launch_topk_softmax(logits, D.T, D.E, D.k, topk_idx, topk_w, s));
+    } else {
+      MOE_TRY(launch_small_router(x, w_router, bias, D.T, D.d, D.E, D.k, D.eb, logits, topk_idx,
+                                  topk_w, rpart, s));
+    }
   } else {
     MOE_TRY(moe_route(shape, x, w_router, bias, logits, topk_idx, topk_w, stream));
   }

@@ -34,6 +34,12 @@ moe_status_t launch_small_router_part(const void* x, const void* wr, int T, int 
 moe_status_t launch_small_router(const void* x, const void* wr, const float* bias, int T, int d,
                                  int E, int k, int elt_bytes, float* logits, int32_t* idx,
                                  float* w, float* part, hipStream_t s);
+// moe_route's logits for T <= SMALL_ROUTE_MAX_T with no workspace (one
+// workgroup per 16 bytes of a router row and up to 4 tokens walks all of d); when
+// few_token_logits_fit.
+bool few_token_logits_fit(int T, int E, int elt_bytes);
+moe_status_t launch_few_token_logits(const void* x, const void* wr, const float* bias, int T,
+                                     int d, int E, int elt_bytes, float* logits, hipStream_t s);
 // Tokens per workgroup of the router backward (one bias-gradient partial each).
 constexpr int ROUTE_BWD_TOKENS = 32;
 // logits / aux_w (both or neither): add the auxiliary loss's logit gradient.

@@ -310,6 +310,121 @@ moe_status_t launch_small_router(const void* x, const void* wr, const float* bia
   return check_launch("small_router_final_kernel");
 }
 
+// moe_route's logits for a few tokens (T <= SMALL_ROUTE_MAX_T), with no
+// workspace: the MFMA router's two column tiles would each walk all of d on
+// one CU, one K slice after another.  Here one workgroup per (16-byte chunk
+// of a router row: N experts, group of up to MT tokens) walks all of d: lane
+// l of wave w takes 8 consecutive rows of each 2048-row pass, all its weight
+// and x loads of a pass in flight together, and accumulates them in row
+// order; the lanes' sums are added by a butterfly, then the four waves' in
+// wave order, then the bias: deterministic (another order than the MFMA
+// router's, so the logits may differ from it in the last bits).  Needs
+// E % N == 0 (16-byte row chunks).  MT: at most 4 tokens a workgroup (the
+// butterfly's work grows with MT * N).
+template <typename ELT, int MT>
+__global__ __launch_bounds__(256) void few_token_logits_kernel(const ELT* x, const ELT* wr,
+                                                               const float* bias, int T, int d,
+                                                               int E, float* logits) {
+  constexpr int N = 16 / sizeof(ELT);  // experts of the workgroup
+  constexpr int RP = 8;                // rows of d per lane and pass
+  __shared__ float red[4][MT][N];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e0 = blockIdx.x * N, t0 = blockIdx.y * MT;
+  x += (int64_t)t0 * d;
+  logits += (int64_t)t0 * E;
+  T = min(T - t0, MT);  // tokens of this workgroup
+  float acc[MT][N];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int n = 0; n < N; ++n) acc[t][n] = 0.f;
+  for (int r0 = threadIdx.x * RP; r0 < d; r0 += 256 * RP) {
+    uint4 wq[RP];
+#pragma unroll
+    for (int i = 0; i < RP; ++i)
+      wq[i] = *reinterpret_cast<const uint4*>(wr + (int64_t)(r0 + i) * E + e0);
+    uint4 xq[MT][RP / (16 / sizeof(ELT))];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int v = 0; v < RP / N; ++v)
+        xq[t][v] = *reinterpret_cast<const uint4*>(x + (int64_t)min(t, T - 1) * d + r0 + v * N);
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      float wv[N];
+      if constexpr (sizeof(ELT) == 2) {
+        const uint32_t q[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          wv[2 * h] = __uint_as_float(q[h] << 16);
+          wv[2 * h + 1] = __uint_as_float(q[h] & 0xffff0000u);
+        }
+      } else {
+        wv[0] = __uint_as_float(wq[i].x); wv[1] = __uint_as_float(wq[i].y);
+        wv[2] = __uint_as_float(wq[i].z); wv[3] = __uint_as_float(wq[i].w);
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const uint4 xv = xq[t][i / N];
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        float xf;
+        if constexpr (sizeof(ELT) == 2) {
+          const uint32_t u = xw[(i % N) / 2];
+          xf = __uint_as_float((i % 2) ? (u & 0xffff0000u) : (u << 16));
+        } else {
+          xf = __uint_as_float(xw[i % N]);
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[t][n] = fmaf(xf, wv[n], acc[t][n]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int n = 0; n < N; ++n) acc[t][n] += __shfl_xor(acc[t][n], off, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int n = 0; n < N; ++n) red[w][t][n] = acc[t][n];
+  __syncthreads();
+  if (threadIdx.x < T * N) {
+    const int t = threadIdx.x / N, n = threadIdx.x % N;
+    float v = red[0][t][n];
+    v += red[1][t][n];
+    v += red[2][t][n];
+    v += red[3][t][n];
+    if (bias) v += bias[e0 + n];
+    logits[(int64_t)t * E + e0 + n] = v;
+  }
+}
+
+bool few_token_logits_fit(int T, int E, int elt_bytes) {
+  return T >= 1 && T <= SMALL_ROUTE_MAX_T && E % (16 / elt_bytes) == 0;
+}
+
+moe_status_t launch_few_token_logits(const void* x, const void* wr, const float* bias, int T,
+                                     int d, int E, int elt_bytes, float* logits, hipStream_t s) {
+  ProfScope prof("route_logits", s);
+  const int mt = T <= 1 ? 1 : T <= 2 ? 2 : 4;
+  const dim3 grid((unsigned)(E / (16 / elt_bytes)), (unsigned)ceil_div(T, mt));
+#define L_(E_, MT_)                                                                       \
+  few_token_logits_kernel<E_, MT_><<<grid, 256, 0, s>>>(static_cast<const E_*>(x),        \
+                                                        static_cast<const E_*>(wr), bias, T, d, \
+                                                        E, logits)
+#define LM_(E_)                                   \
+  if (mt == 1) L_(E_, 1);                         \
+  else if (mt == 2) L_(E_, 2);                    \
+  else L_(E_, 4);
+  if (elt_bytes == 2) { LM_(bf16_t) } else { LM_(float) }
+#undef LM_
+#undef L_
+  return check_launch("few_token_logits_kernel");
+}
+
 moe_status_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                                  hipStream_t s) {
   ProfScope prof("route_topk", s);
