@@ -67,7 +67,7 @@ def _oracle_y(x, idx, g, Wg, Wu, Wd, E, e_lo, e_hi):
     return O.combine(f["Yp"], p["inv"], g, T, k)
 
 
-@pytest.mark.parametrize("T", [1, 2, 8, 16, 17, 64])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 8, 16, 17, 64])
 def test_decode_sizes_qwen3_shape(T):
     """Natural router at the Qwen3 shape on the first T tokens of its workload."""
     w0 = MI.WORKLOADS["qwen3_natural_fwd_T4096_d2048_E128_k8_I768"]
@@ -141,6 +141,10 @@ FEW = [
     # form with an odd E
     MI.small_workload("few_f32_T16_d128_E71_k5_I64", 16, 128, 71, 5, 64, dtype="f32",
                       bias_sigma=1.0, seed=79, x_sigma=0.5),
+    # too many split partials for the folded router: moe_route's few-token
+    # logits and top-k, then the FFN
+    MI.small_workload("few_f32_T6_d1024_E128_k4_I64", 6, 1024, 128, 4, 64, dtype="f32",
+                      bias_sigma=1.0, seed=81, x_sigma=0.5),
     MI.small_workload("few_f32_T3_d192_E7_k3_I64", 3, 192, 7, 3, 64, dtype="f32",
                       bias_sigma=1.0, seed=80, x_sigma=0.5),
 ]
